@@ -1,0 +1,44 @@
+"""The wring: re-solve codes and scales against the adapter-watered target (oracle, test infrastructure only).
+
+Wringer news article (second paragraph): the wring takes ``Wq + BA/r`` as the
+new target and re-solves the integer codes and scales, after which the adapter
+is dropped.  Qwen3-4B model card, "Recipe" (v0.3): nearest-point rounding of
+the watered weights onto the same grid, then the same joint closed-form scale
+solve with the watered weights as target.
+
+Readings: the adapter term is (alpha / r) B A (the usual LoRA scaling; with
+alpha = r it is B A); the "same grid" is the current fp16 scales; the prior of
+the scale solve is centred on those scales.
+"""
+
+import numpy as np
+
+from .grid import dequant, levels_count, nearest_code
+from .joint import joint_scales
+
+
+def wring_target(codes, scales, bits, group, B, A, alpha):
+    """W' = dequant(codes, scales) + (alpha / r) B A, in float64."""
+    W_hat = dequant(codes, scales, bits, group)
+    if B is None or A is None:
+        return W_hat
+    B = np.asarray(B, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    r = A.shape[0]
+    return W_hat + (float(alpha) / r) * (B @ A)
+
+
+def wring(codes, scales, bits, group, B, A, alpha, H, lam):
+    """Nearest-point recode of W' on the current scales, then joint scales against W'.
+
+    Returns dict(codes, scales, scales_unrounded, target, t).
+    """
+    codes = np.asarray(codes, dtype=np.int64)
+    rows, n = codes.shape
+    Wp = wring_target(codes, scales, bits, group, B, A, alpha)
+    L = np.broadcast_to(levels_count(bits), (rows,)).reshape(rows, 1)
+    s = np.repeat(np.asarray(scales, dtype=np.float64), group, axis=1)
+    t = np.divide(Wp, s, out=np.zeros_like(Wp), where=s > 0)
+    c_new = nearest_code(t, L)
+    s_new, s_raw = joint_scales(c_new, bits, group, H, Wp, scales, lam)
+    return {"codes": c_new, "scales": s_new, "scales_unrounded": s_raw, "target": Wp, "t": t}
