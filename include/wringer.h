@@ -1,0 +1,181 @@
+/*
+ * wringer.h -- C ABI of the MI355X (gfx950) per-linear-layer quantization solve.
+ *
+ * The solve quantizes one linear layer W (rows x n, rows = output channels)
+ * given calibration inputs X (N x n):
+ *
+ *   (a) H = X^T X / N + delta I          wr_hessian_accumulate, wr_hessian_finalize
+ *   (b) optional random-sign Hadamard    wr_hadamard_rotate
+ *   (c) GPTQ/LDLQ error-feedback sweep   wr_gptq_sweep
+ *   (d) joint scales / the wring         wr_wring_solve
+ *   (e) bit packing                      wr_pack, wr_unpack
+ *
+ * Conventions shared by every entry point:
+ *   - Matrices are row-major with an explicit leading dimension (in elements).
+ *   - Every data pointer is a DEVICE pointer owned by the caller; the library
+ *     never frees or retains it past the call.  Inputs are const.
+ *   - Work is enqueued on the context's HIP stream and the call returns
+ *     without synchronising.  Argument errors are detected on the host before
+ *     anything is launched and leave every output untouched.
+ *   - The library allocates no device memory.  Entry points that need scratch
+ *     space use the workspace registered with wr_set_workspace; its size comes
+ *     from wr_workspace_bytes.
+ *   - Numerical failures are reported LAPACK-style through a device int32
+ *     `dev_info` (read it after synchronising the stream): 0 = success;
+ *     k > 0 = the leading minor of order k of H is not positive definite;
+ *     -1 = a non-finite value in the weights/target.  On failure the kernels
+ *     that would write codes or scales return without writing them.
+ *   - Return value: WR_OK (0) or a positive WR_E* code; no exception crosses
+ *     the ABI.  One context per stream; a context is not thread-safe.
+ *
+ * Grid: for b bits, L = 2^b - 1, codes c in [0, L] stand for the signed odd
+ * levels 2c - L ({+-1, +-3} at 2 bits, {+-1..+-7} at 3 bits) times an fp16
+ * block scale shared by `group` consecutive weights of a row.
+ */
+#ifndef WRINGER_H
+#define WRINGER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum wr_status {
+  WR_OK = 0,
+  WR_EINVAL = 1,       /* invalid argument (null pointer, bad size, bad flag) */
+  WR_EWORKSPACE = 2,   /* registered workspace missing or too small */
+  WR_EHIP = 3,         /* a HIP runtime call failed */
+  WR_EUNSUPPORTED = 4  /* valid request this build does not implement */
+};
+
+enum wr_dtype { WR_F32 = 0, WR_BF16 = 1 };
+
+enum wr_op {             /* operations that need workspace, for wr_workspace_bytes */
+  WR_OP_HESSIAN = 0,     /* rows = calibration rows per call, n = input dim */
+  WR_OP_GPTQ = 1,        /* rows = weight rows, n = stored dim, group, lazy_batch */
+  WR_OP_WRING = 2,       /* rows = weight rows, n = stored dim, group, rank */
+  WR_OP_ROTATE = 3       /* none needed; returns 0 */
+};
+
+enum wr_hessian_flags { WR_H_ZERO = 1 };               /* zero S before accumulating */
+enum wr_rotate_mode { WR_ROT_ROWS = 0, WR_ROT_ROWS_INVERSE = 1, WR_ROT_SYM = 2 };
+enum wr_wring_flags { WR_RECODE_NEAREST = 1 };
+
+typedef struct wr_ctx wr_ctx;
+
+/* Create a context bound to HIP device `device` and stream `hip_stream`
+ * (a hipStream_t; NULL = the default stream).  *out receives the handle. */
+int wr_create(wr_ctx** out, int device, void* hip_stream);
+int wr_destroy(wr_ctx* ctx);
+
+/* Device scratch bytes an operation needs for the given problem size. */
+size_t wr_workspace_bytes(int op, int64_t rows, int64_t n, int32_t group, int32_t rank, int32_t lazy_batch);
+
+/* Register caller-owned device scratch memory (256-byte aligned) for later calls. */
+int wr_set_workspace(wr_ctx* ctx, void* dev_ptr, size_t bytes);
+
+/*
+ * (a) Calibration second moment.  H is the average of x x^T over the
+ * calibration inputs (Pingala-8 post "How We Shrank an AI Model by 85% and
+ * Kept 90% of Its Smarts", section "Trick 2: round with error feedback").
+ *
+ * S (n x n, fp64, ld n) += X^T X over the `rows` rows of X (rows x n, dtype
+ * WR_BF16 or WR_F32, leading dimension ldx).  Only the lower triangle
+ * (including the diagonal) of S is defined.  With WR_H_ZERO, S is zeroed
+ * first.  Call once per chunk of calibration rows.  Products are exact for
+ * bf16 inputs; sums run in fp32 over at most 512 rows and are then added in
+ * fp64.  Workspace: WR_OP_HESSIAN with (rows, n).  rows may be 0 (no-op
+ * unless WR_H_ZERO).
+ */
+int wr_hessian_accumulate(wr_ctx* ctx, const void* X, int x_dtype, int64_t rows, int64_t n, int64_t ldx,
+                          double* S, int flags);
+
+/*
+ * (a) Finalize and damp.  Writes the full symmetric H (n_store x n_store,
+ * fp32, ld ldh):  H = pad(S / total_rows) + delta I with
+ * delta = damp_frac * trace(S / total_rows) / n_store, where pad() zero-fills
+ * rows/columns n..n_store-1 (the zero-padded input dims of a rotation).  The
+ * damping is the Tikhonov regularisation the Wringer news article names for
+ * the GPTQ solve.  `delta_out` (device fp32, nullable) receives delta.
+ */
+int wr_hessian_finalize(wr_ctx* ctx, const double* S, int64_t n, int64_t total_rows, float damp_frac,
+                        int64_t n_store, float* H, int64_t ldh, float* delta_out);
+
+/*
+ * (b) Random-sign Hadamard rotation (Pingala-8 post, section "Trick 1:
+ * rotate the weights first": W x = (W R^T)(R x)).
+ * R = blockdiag_k(H_m diag(d_k)) / sqrt(m), H_m the natural-order (Sylvester)
+ * Hadamard matrix of order m = had_block (a power of two, 2..4096),
+ * d = signs (device int8, +-1, length n).  M is rows x n (fp32, ld), n a
+ * multiple of m, transformed in place:
+ *   WR_ROT_ROWS          each row v -> R v        (weights: W -> W R^T)
+ *   WR_ROT_ROWS_INVERSE  each row v -> R^T v
+ *   WR_ROT_SYM           M -> R M R^T             (H; requires rows == n)
+ */
+int wr_hadamard_rotate(wr_ctx* ctx, float* M, int64_t rows, int64_t n, int64_t ld, int32_t had_block,
+                       const int8_t* signs, int mode);
+
+/*
+ * (c) GPTQ / LDLQ sweep (Pingala-8 post, "Trick 2"; Wringer model cards,
+ * "Recipe": GPTQ codes on a fixed signed grid with fp16 block scales).
+ * For every row of W (rows x n, WR_BF16 or WR_F32, ld ldw) independently and
+ * the columns in natural order: at the start of each block of `group`
+ * columns the scale is fp16_rne(max |w~| / L) of the block's current
+ * feedback-updated values; each weight is rounded to the nearest level and
+ * its error is pushed onto the later columns in the proportions set by the
+ * damped H (n x n fp32, ld ldh, symmetric positive definite).
+ * bits: device uint8 per row (2, 3 or 4).  n % group == 0, group % 8 == 0,
+ * lazy_batch % group == 0 (lazy_batch in [group, 256]).
+ * Outputs: codes (rows x n uint8, ld n), scales (rows x n/group fp16 bit
+ * patterns).  dev_info as above.  Workspace: WR_OP_GPTQ.
+ */
+int wr_gptq_sweep(wr_ctx* ctx, const void* W, int w_dtype, int64_t rows, int64_t n, int64_t ldw,
+                  const float* H, int64_t ldh, const uint8_t* bits, int32_t group, int32_t lazy_batch,
+                  uint8_t* codes, uint16_t* scales, int32_t* dev_info);
+
+/*
+ * (d) Joint scales and the wring (Wringer model cards, "Recipe" and "Why the
+ * solver changed"; Wringer news article, second paragraph; Agents-A1 card,
+ * "Honest caveats": scales projected to fp16 at solve time).
+ *
+ * Target T (rows x n): `target` (WR_F32/WR_BF16, ld ldt) if non-null, else
+ * dequant(codes, scales); plus (alpha / rank) * B A when B (rows x rank) and
+ * A (rank x n) are both non-null (dtype ab_dtype, contiguous).
+ * With WR_RECODE_NEAREST the codes are first replaced by the nearest level of
+ * T / s on the current scales s.  Then every row's scales are re-solved:
+ *   s = argmin (t - Q s)^T H (t - Q s) + lambda mu ||s - s0||^2,
+ *   mu = trace(Q^T H Q) / nb,  s0 = the scales passed in,
+ * and projected to fp16 (round to nearest even).  codes and scales are
+ * in/out.  H: damped, n x n fp32 (ld ldh).  Workspace: WR_OP_WRING.
+ */
+int wr_wring_solve(wr_ctx* ctx, const void* target, int t_dtype, int64_t ldt,
+                   const void* B, const void* A, int32_t rank, float alpha, int ab_dtype,
+                   const float* H, int64_t ldh, int64_t rows, int64_t n, const uint8_t* bits,
+                   int32_t group, float lambda, int flags,
+                   uint8_t* codes, uint16_t* scales, int32_t* dev_info);
+
+/*
+ * (e) Packing (Wringer model cards, "What is in this repo": packed codes plus
+ * fp16 block scales).  Layout: per row, code j occupies bits [j b, (j+1) b)
+ * of the row's bit stream, LSB first in little-endian bytes (a row is
+ * n b / 8 bytes, so n * bits % 8 == 0); then the fp16 scales, little-endian,
+ * row-major [rows][n / group].  out_bytes must equal
+ * rows * n * bits / 8 + 2 * rows * (n / group).
+ */
+int wr_pack(wr_ctx* ctx, const uint8_t* codes, const uint16_t* scales, int64_t rows, int64_t n,
+            int32_t bits, int32_t group, uint8_t* out, size_t out_bytes);
+
+/* Inverse of wr_pack.  Each of codes, scales, dequant_bf16 (rows x n bf16 of
+ * (2c - L) s, round to nearest even) may be null. */
+int wr_unpack(wr_ctx* ctx, const uint8_t* in, size_t in_bytes, int64_t rows, int64_t n, int32_t bits,
+              int32_t group, uint8_t* codes, uint16_t* scales, uint16_t* dequant_bf16);
+
+/* Static description of a status code. */
+const char* wr_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WRINGER_H */

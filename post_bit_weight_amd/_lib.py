@@ -1,0 +1,254 @@
+"""ctypes binding of ``libwringer.so`` -- argument marshalling only.
+
+Every function here has the name of the C entry point it calls, takes torch
+tensors that already live on the GPU, checks their dtype / device / layout and
+passes raw pointers plus the current HIP stream.  No arithmetic of the method
+happens in Python; if the shared library is missing, importing any function
+raises instead of falling back to anything else.
+"""
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwringer.so")
+
+WR_OK, WR_EINVAL, WR_EWORKSPACE, WR_EHIP, WR_EUNSUPPORTED = 0, 1, 2, 3, 4
+WR_F32, WR_BF16 = 0, 1
+WR_OP_HESSIAN, WR_OP_GPTQ, WR_OP_WRING, WR_OP_ROTATE = 0, 1, 2, 3
+WR_H_ZERO = 1
+WR_ROT_ROWS, WR_ROT_ROWS_INVERSE, WR_ROT_SYM = 0, 1, 2
+WR_RECODE_NEAREST = 1
+
+EXPORTED = (
+    "wr_create", "wr_destroy", "wr_workspace_bytes", "wr_set_workspace",
+    "wr_hessian_accumulate", "wr_hessian_finalize", "wr_hadamard_rotate",
+    "wr_gptq_sweep", "wr_wring_solve", "wr_pack", "wr_unpack", "wr_strerror",
+)
+
+
+class WringerError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {_strerror(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def _open(path):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with post_bit_weight_amd/csrc/build.py")
+    return ctypes.CDLL(path)
+
+
+def load():
+    """Load the HIP library once; raise loudly if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    lib = _open(LIB_PATH)
+    c = ctypes
+    P, I, I64, F, SZ = c.c_void_p, c.c_int, c.c_int64, c.c_float, c.c_size_t
+    sig = {
+        "wr_create": (I, [c.POINTER(P), I, P]),
+        "wr_destroy": (I, [P]),
+        "wr_workspace_bytes": (SZ, [I, I64, I64, c.c_int32, c.c_int32, c.c_int32]),
+        "wr_set_workspace": (I, [P, P, SZ]),
+        "wr_hessian_accumulate": (I, [P, P, I, I64, I64, I64, P, I]),
+        "wr_hessian_finalize": (I, [P, P, I64, I64, F, I64, P, I64, P]),
+        "wr_hadamard_rotate": (I, [P, P, I64, I64, I64, c.c_int32, P, I]),
+        "wr_gptq_sweep": (I, [P, P, I, I64, I64, I64, P, I64, P, c.c_int32, c.c_int32, P, P, P]),
+        "wr_wring_solve": (I, [P, P, I, I64, P, P, c.c_int32, F, I, P, I64, I64, I64, P, c.c_int32, F, I, P, P, P]),
+        "wr_pack": (I, [P, P, P, I64, I64, c.c_int32, c.c_int32, P, SZ]),
+        "wr_unpack": (I, [P, P, SZ, I64, I64, c.c_int32, c.c_int32, P, P, P]),
+        "wr_strerror": (c.c_char_p, [I]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _strerror(status):
+    try:
+        return load().wr_strerror(status).decode()
+    except Exception:  # pragma: no cover - only when the library itself is missing
+        return "unknown"
+
+
+def _check(fn, status):
+    if status != WR_OK:
+        raise WringerError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtypes):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+
+
+def _rowmajor(t, name):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D row-major tensor")
+    return t.stride(0)
+
+
+def _wdtype(t):
+    return WR_BF16 if t.dtype == torch.bfloat16 else WR_F32
+
+
+FLOATS = (torch.float32, torch.bfloat16)
+
+
+class Context:
+    """One library context bound to a device and a HIP stream, plus its workspace tensor."""
+
+    def __init__(self, device=0, stream=None):
+        lib = load()
+        self.device = torch.device("cuda", device) if isinstance(device, int) else torch.device(device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        h = ctypes.c_void_p()
+        _check("wr_create", lib.wr_create(ctypes.byref(h), self.device.index or 0, ctypes.c_void_p(self.stream.cuda_stream)))
+        self.handle = h
+        self.workspace = None
+
+    def ensure_workspace(self, nbytes):
+        if self.workspace is None or self.workspace.numel() < nbytes:
+            self.workspace = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=self.device)
+            _check("wr_set_workspace", load().wr_set_workspace(self.handle, _ptr(self.workspace), self.workspace.numel()))
+
+    def close(self):
+        if self.handle:
+            load().wr_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def wr_workspace_bytes(op, rows, n, group=0, rank=0, lazy_batch=0):
+    return int(load().wr_workspace_bytes(op, rows, n, group, rank, lazy_batch))
+
+
+def wr_hessian_accumulate(ctx, X, S, zero=False):
+    """S (n x n fp64) += X^T X for the rows of X (bf16 or fp32)."""
+    _dev(X, "X", FLOATS)
+    _dev(S, "S", (torch.float64,))
+    rows, n = X.shape
+    ldx = _rowmajor(X, "X")
+    if tuple(S.shape) != (n, n) or not S.is_contiguous():
+        raise ValueError("S must be a contiguous n x n fp64 tensor")
+    ctx.ensure_workspace(wr_workspace_bytes(WR_OP_HESSIAN, rows, n))
+    _check("wr_hessian_accumulate", load().wr_hessian_accumulate(
+        ctx.handle, _ptr(X), _wdtype(X), rows, n, ldx, _ptr(S), WR_H_ZERO if zero else 0))
+
+
+def wr_hessian_finalize(ctx, S, total_rows, damp_frac, H, delta=None):
+    """H (n_store x n_store fp32) = pad(S / total_rows) + delta I."""
+    _dev(S, "S", (torch.float64,))
+    _dev(H, "H", (torch.float32,))
+    _dev(delta, "delta", (torch.float32,))
+    n = S.shape[0]
+    ldh = _rowmajor(H, "H")
+    ctx.ensure_workspace(256)
+    _check("wr_hessian_finalize", load().wr_hessian_finalize(
+        ctx.handle, _ptr(S), n, int(total_rows), float(damp_frac), H.shape[0], _ptr(H), ldh, _ptr(delta)))
+
+
+def wr_hadamard_rotate(ctx, M, had_block, signs, mode=WR_ROT_ROWS):
+    _dev(M, "M", (torch.float32,))
+    _dev(signs, "signs", (torch.int8,))
+    rows, n = M.shape
+    ld = _rowmajor(M, "M")
+    if signs.numel() != n or not signs.is_contiguous():
+        raise ValueError("signs must hold n contiguous int8 values")
+    _check("wr_hadamard_rotate", load().wr_hadamard_rotate(ctx.handle, _ptr(M), rows, n, ld, int(had_block), _ptr(signs), mode))
+
+
+def wr_gptq_sweep(ctx, W, H, bits, group, lazy_batch, codes, scales, dev_info):
+    _dev(W, "W", FLOATS)
+    _dev(H, "H", (torch.float32,))
+    _dev(bits, "bits", (torch.uint8,))
+    _dev(codes, "codes", (torch.uint8,))
+    _dev(scales, "scales", (torch.float16, torch.int16, torch.uint16))
+    _dev(dev_info, "dev_info", (torch.int32,))
+    rows, n = W.shape
+    ldw = _rowmajor(W, "W")
+    ldh = _rowmajor(H, "H")
+    if tuple(codes.shape) != (rows, n) or not codes.is_contiguous():
+        raise ValueError("codes must be a contiguous rows x n uint8 tensor")
+    if tuple(scales.shape) != (rows, n // group) or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous rows x n/group fp16 tensor")
+    if bits.numel() != rows:
+        raise ValueError("bits must hold one value per row")
+    ctx.ensure_workspace(wr_workspace_bytes(WR_OP_GPTQ, rows, n, group, 0, lazy_batch))
+    _check("wr_gptq_sweep", load().wr_gptq_sweep(
+        ctx.handle, _ptr(W), _wdtype(W), rows, n, ldw, _ptr(H), ldh, _ptr(bits), int(group), int(lazy_batch),
+        _ptr(codes), _ptr(scales), _ptr(dev_info)))
+
+
+def wr_wring_solve(ctx, H, bits, group, lam, codes, scales, dev_info, target=None, B=None, A=None, alpha=0.0,
+                   recode=False):
+    _dev(target, "target", FLOATS)
+    _dev(B, "B", FLOATS)
+    _dev(A, "A", FLOATS)
+    _dev(H, "H", (torch.float32,))
+    _dev(bits, "bits", (torch.uint8,))
+    _dev(codes, "codes", (torch.uint8,))
+    _dev(scales, "scales", (torch.float16, torch.int16, torch.uint16))
+    _dev(dev_info, "dev_info", (torch.int32,))
+    rows, n = codes.shape
+    ldh = _rowmajor(H, "H")
+    ldt = _rowmajor(target, "target") if target is not None else 0
+    rank = 0
+    ab_dtype = WR_F32
+    if B is not None:
+        if A is None or B.dtype != A.dtype or not B.is_contiguous() or not A.is_contiguous():
+            raise ValueError("B and A must be contiguous tensors of one dtype")
+        rank = A.shape[0]
+        if tuple(B.shape) != (rows, rank) or tuple(A.shape) != (rank, n):
+            raise ValueError("B must be rows x r and A r x n")
+        ab_dtype = _wdtype(A)
+    ctx.ensure_workspace(wr_workspace_bytes(WR_OP_WRING, rows, n, group, rank, 0))
+    _check("wr_wring_solve", load().wr_wring_solve(
+        ctx.handle, _ptr(target), _wdtype(target) if target is not None else WR_F32, ldt, _ptr(B), _ptr(A), rank,
+        float(alpha), ab_dtype, _ptr(H), ldh, rows, n, _ptr(bits), int(group), float(lam),
+        WR_RECODE_NEAREST if recode else 0, _ptr(codes), _ptr(scales), _ptr(dev_info)))
+
+
+def packed_nbytes(rows, n, bits, group):
+    return rows * n * bits // 8 + 2 * rows * (n // group)
+
+
+def wr_pack(ctx, codes, scales, bits, group, out):
+    _dev(codes, "codes", (torch.uint8,))
+    _dev(scales, "scales", (torch.float16, torch.int16, torch.uint16))
+    _dev(out, "out", (torch.uint8,))
+    rows, n = codes.shape
+    if not codes.is_contiguous() or not scales.is_contiguous() or not out.is_contiguous():
+        raise ValueError("codes, scales and out must be contiguous")
+    _check("wr_pack", load().wr_pack(ctx.handle, _ptr(codes), _ptr(scales), rows, n, int(bits), int(group), _ptr(out),
+                                     out.numel()))
+
+
+def wr_unpack(ctx, buf, rows, n, bits, group, codes=None, scales=None, dequant=None):
+    _dev(buf, "buf", (torch.uint8,))
+    _dev(codes, "codes", (torch.uint8,))
+    _dev(scales, "scales", (torch.float16, torch.int16, torch.uint16))
+    _dev(dequant, "dequant", (torch.bfloat16,))
+    _check("wr_unpack", load().wr_unpack(ctx.handle, _ptr(buf), buf.numel(), rows, n, int(bits), int(group),
+                                         _ptr(codes), _ptr(scales), _ptr(dequant)))

@@ -1,0 +1,93 @@
+// Shared device helpers for the gfx950 quantization-solve kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "../../include/wringer.h"
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct wr_ctx {
+  int device;
+  hipStream_t stream;
+  void* ws;
+  size_t ws_bytes;
+  int num_cu;
+};
+
+#define WR_CHECK_LAUNCH()                                       \
+  do {                                                          \
+    if (hipGetLastError() != hipSuccess) return WR_EHIP;        \
+  } while (0)
+
+namespace wr {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// IEEE round-to-nearest-even fp32 -> bf16 bit pattern (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+  _Float16 v = __builtin_bit_cast(_Float16, h);
+  return (float)v;
+}
+
+// fp32 -> fp16 round-to-nearest-even, clamped to the finite range +-65504.
+__device__ __forceinline__ uint16_t f32_to_f16_bits_clamped(float f) {
+  f = fminf(fmaxf(f, -65504.0f), 65504.0f);
+  _Float16 v = (_Float16)f;
+  return __builtin_bit_cast(uint16_t, v);
+}
+
+// fp64 -> fp16 round-to-nearest-even with a single rounding, clamped to +-65504.
+// The fp16 quantum q of |d| is a power of two; |d|/q is exact and rint() rounds it
+// to nearest even, so r = rint(|d|/q) q is the correctly rounded value.
+__device__ __forceinline__ uint16_t f64_to_f16_bits_clamped(double d) {
+  if (d != d) return 0x7e00u;
+  double a = fabs(d);
+  uint16_t sign = d < 0.0 ? 0x8000u : 0u;
+  if (a >= 65504.0) return sign | 0x7bffu;
+  int e = ilogb(a);                       // a in [2^e, 2^(e+1))
+  if (a == 0.0 || e < -14) e = -14;       // subnormal range shares the quantum 2^-24
+  double q = ldexp(1.0, e - 10);
+  double r = rint(a / q) * q;             // exact in fp16 (possibly the next binade)
+  if (r > 65504.0) r = 65504.0;
+  _Float16 v = (_Float16)(float)r;        // exact conversion
+  return sign | __builtin_bit_cast(uint16_t, v);
+}
+
+// ---------------------------------------------------------------- grid
+// Nearest code for t in level units: clamp(floor((t + L)/2 + 1/2), 0, L).
+__device__ __forceinline__ int nearest_code(float t, int L) {
+  float c = floorf(fmaf(t, 0.5f, 0.5f * (float)(L + 1)));
+  c = fminf(fmaxf(c, 0.0f), (float)L);
+  return (int)c;
+}
+
+// ---------------------------------------------------------------- MFMA
+__device__ __forceinline__ f32x16 mfma32x32x16_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32x32x2_f32(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+// Accumulator register v of lane l of a 32x32 MFMA block holds row acc_row(v, l), column l % 32.
+__device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+}  // namespace wr

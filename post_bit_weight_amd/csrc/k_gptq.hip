@@ -1,0 +1,348 @@
+// GPTQ / LDLQ error-feedback sweep (Pingala-8 post, "Trick 2: round with error
+// feedback"; Wringer model cards, "Recipe": GPTQ codes on a fixed signed grid
+// with fp16 block scales).
+//
+// Factorisation.  With J the reversal permutation, L = chol_lower(J H J) gives
+// H = V V^T with V = J L J upper triangular, and H = M D M^T with the unit upper
+// M = V diag(V)^-1.  The sweep needs only M: no triangular inverse.  The
+// Cholesky is blocked by 64: the diagonal block is factored (in fp64) and
+// inverted in LDS by one workgroup, the panel below is multiplied by that
+// inverse and the trailing lower matrix is updated on the fp32 matrix cores.
+//
+// Sweep (LDLQ pull form).  Every row is independent.  With delta_i = w_i - q_i,
+// column k is rounded from v_k = w_k + sum_{i<k} M_ik delta_i.  The corrections
+// C_k = sum_{i<k} M_ik delta_i are kept in a rows x n buffer: inside a lazy
+// batch of columns they are updated one column at a time, and when a batch is
+// done the remaining columns receive C += E M[batch, rest] as one GEMM.
+// The block scale is fixed at the first column of a block from the values the
+// GPTQ push form holds there, w_j + x_j with x = M_bb^-T C_b (M_bb the block's
+// diagonal block of M): the optimal compensation of everything rounded so far.
+// In exact arithmetic this gives the same codes and scales as the push form.
+//
+// Threads: P lanes share one row; lane p owns the batch columns p, p+P, ...
+// The owner of column k rounds it and the error is broadcast within the
+// P-lane group; every lane then updates its own columns from M's row k, which
+// is staged in LDS in a lane-major order.
+#include "common.hpp"
+
+int wr_gemm_f32(hipStream_t st, int M, int N, int K, const float* A, int64_t lda, const float* B, int64_t ldb,
+                bool b_kn, float* C, int64_t ldc, float alpha, bool accumulate, bool lower_tiles,
+                const int32_t* dev_info);
+
+namespace wr {
+
+constexpr int CH_NB = 64;
+
+// A = J H J (lower triangle only).
+__global__ void reverse_copy_kernel(const float* __restrict__ H, int64_t ldh, int n, float* __restrict__ A) {
+  const int i = blockIdx.x;
+  for (int j = threadIdx.x; j <= i; j += blockDim.x) A[(int64_t)i * n + j] = H[(int64_t)(n - 1 - i) * ldh + (n - 1 - j)];
+}
+
+// Factor the diagonal block at kb in fp64 in LDS; write L_kk back and L_kk^-1 to Linv.
+__global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ A, int n, int kb, float* __restrict__ Linv,
+                                                        int32_t* __restrict__ dev_info) {
+  __shared__ double a[CH_NB][CH_NB + 1];
+  __shared__ double inv[CH_NB][CH_NB + 1];
+  __shared__ int failed;
+  if (*dev_info != 0) return;
+  const int tid = threadIdx.x;
+  const int nb = min(CH_NB, n - kb);
+  for (int e = tid; e < CH_NB * CH_NB; e += 256) {
+    const int i = e / CH_NB, j = e % CH_NB;
+    a[i][j] = (i < nb && j <= i) ? (double)A[(int64_t)(kb + i) * n + kb + j] : (i == j ? 1.0 : 0.0);
+  }
+  if (tid == 0) failed = 0;
+  __syncthreads();
+  for (int k = 0; k < nb; ++k) {
+    if (tid == 0) {
+      const double d = a[k][k];
+      if (!(d > 0.0)) {
+        failed = 1;
+        *dev_info = kb + k + 1;
+      } else {
+        a[k][k] = sqrt(d);
+      }
+    }
+    __syncthreads();
+    if (failed) return;
+    const double dk = a[k][k];
+    for (int i = k + 1 + tid; i < nb; i += 256) a[i][k] /= dk;
+    __syncthreads();
+    const int m = nb - k - 1;
+    for (int e = tid; e < m * m; e += 256) {
+      const int i = k + 1 + e / m, j = k + 1 + e % m;
+      if (j <= i) a[i][j] -= a[i][k] * a[j][k];
+    }
+    __syncthreads();
+  }
+  // inverse of the lower-triangular block, one column per thread
+  if (tid < CH_NB) {
+    const int c = tid;
+    for (int i = 0; i < CH_NB; ++i) {
+      double s = (i == c) ? 1.0 : 0.0;
+      for (int k = c; k < i; ++k) s -= a[i][k] * inv[k][c];
+      inv[i][c] = i < c ? 0.0 : s / a[i][i];
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < CH_NB * CH_NB; e += 256) {
+    const int i = e / CH_NB, j = e % CH_NB;
+    if (i < nb && j <= i) A[(int64_t)(kb + i) * n + kb + j] = (float)a[i][j];
+    Linv[e] = (float)inv[i][j];
+  }
+}
+
+// M[i][j] = L[n-1-i][n-1-j] / L[n-1-j][n-1-j] for i < j; 0 on and below the diagonal
+// (the unit diagonal is implicit and never used).
+__global__ void build_m_kernel(const float* __restrict__ A, int n, float* __restrict__ M,
+                               const int32_t* __restrict__ dev_info) {
+  if (*dev_info != 0) return;
+  const int i = blockIdx.x;
+  const int64_t ri = n - 1 - i;
+  for (int j = threadIdx.x; j < n; j += blockDim.x) {
+    float v = 0.0f;
+    if (j > i) {
+      const int64_t rj = n - 1 - j;
+      v = A[ri * n + rj] / A[rj * n + rj];
+    }
+    M[(int64_t)i * n + j] = v;
+  }
+}
+
+__global__ void check_finite_kernel(const void* __restrict__ W, int w_dtype, int64_t rows, int n, int64_t ldw,
+                                    int32_t* __restrict__ dev_info) {
+  const int64_t r = blockIdx.x;
+  bool bad = false;
+  for (int j = threadIdx.x; j < n; j += blockDim.x) {
+    float v = w_dtype == WR_BF16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(W)[r * ldw + j])
+                                 : static_cast<const float*>(W)[r * ldw + j];
+    bad |= !(fabsf(v) <= 3.0e38f);
+  }
+  if (__syncthreads_or(bad) && threadIdx.x == 0) atomicCAS(dev_info, 0, -1);
+}
+
+__global__ void sweep_set_int_kernel(int32_t* p, int32_t v) { *p = v; }
+
+__global__ void zero_f32_kernel(float* __restrict__ p, int64_t count) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.0f;
+}
+
+template <int P>
+__device__ __forceinline__ float group_bcast(float v, int src) {
+  return __shfl(v, src, P);
+}
+
+template <int P>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = P / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, P));
+  return v;
+}
+
+// One lazy batch of BATCH columns starting at b0 (ncols <= BATCH valid columns).
+template <int P, int BATCH, int G>
+__global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict__ W, int w_dtype, int64_t rows,
+                                                          int n, int64_t ldw, const float* __restrict__ M,
+                                                          const uint8_t* __restrict__ bits, int b0, int ncols,
+                                                          float* __restrict__ Cbuf, float* __restrict__ E,
+                                                          uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
+                                                          const int32_t* __restrict__ dev_info) {
+  constexpr int S = BATCH / P;       // columns per lane
+  constexpr int NBLK = BATCH / G;    // blocks per batch
+  constexpr int SB = G / P;          // columns per lane per block
+  __shared__ __attribute__((aligned(16))) float Ms[BATCH * BATCH];  // [k][p][slot]
+  if (*dev_info != 0) return;
+  const int tid = threadIdx.x;
+  const int p = tid % P;
+  const int64_t row = (int64_t)blockIdx.x * (256 / P) + tid / P;
+  const bool active = row < rows;
+
+  for (int e = tid; e < BATCH * BATCH; e += 256) {
+    const int k = e / BATCH, j = e % BATCH;
+    const float v = (k < ncols && j < ncols) ? M[(int64_t)(b0 + k) * n + b0 + j] : 0.0f;
+    Ms[k * BATCH + (j % P) * S + j / P] = v;
+  }
+
+  float w[S], c[S], d[S];
+  uint8_t code[S];
+  float sc[NBLK];
+  const int L = active ? (1 << bits[row]) - 1 : 3;
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const int col = p + P * i;
+    w[i] = 0.0f;
+    c[i] = 0.0f;
+    d[i] = 0.0f;
+    code[i] = 0;
+    if (active && col < ncols) {
+      const int64_t gc = b0 + col;
+      w[i] = w_dtype == WR_BF16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(W)[row * ldw + gc])
+                                : static_cast<const float*>(W)[row * ldw + gc];
+      c[i] = Cbuf[row * n + gc];
+    }
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int blk = 0; blk < NBLK; ++blk) {
+    sc[blk] = 0.0f;
+    if (blk * G >= ncols) continue;  // uniform
+    // push-form values at the block start: x = M_bb^-T c_b
+    float x[SB];
+#pragma unroll
+    for (int q = 0; q < SB; ++q) x[q] = c[blk * SB + q];
+#pragma unroll
+    for (int jj = 0; jj < G; ++jj) {
+      const int j = blk * G + jj;
+      const int owner = j % P, qo = jj / P;
+      const float xj = group_bcast<P>(x[qo], owner);
+      const float* mrow = &Ms[j * BATCH + p * S + blk * SB];
+#pragma unroll
+      for (int q = qo; q < SB; ++q) x[q] = fmaf(-mrow[q], xj, x[q]);
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int q = 0; q < SB; ++q) m = fmaxf(m, fabsf(w[blk * SB + q] + x[q]));
+    m = group_max<P>(m);
+    const float s = f16_bits_to_f32(f32_to_f16_bits_clamped(m / (float)L));
+    sc[blk] = s;
+    const float inv_s = s > 0.0f ? 1.0f / s : 0.0f;
+    // round the block's columns one at a time, pushing each error to the later batch columns
+#pragma unroll
+    for (int jj = 0; jj < G; ++jj) {
+      const int j = blk * G + jj;
+      const int owner = j % P, io = j / P;
+      const float v = w[io] + c[io];
+      const int cd = nearest_code(v * inv_s, L);
+      const float dl = w[io] - (float)(2 * cd - L) * s;
+      if (p == owner) {
+        code[io] = (uint8_t)cd;
+        d[io] = dl;
+      }
+      const float dj = group_bcast<P>(dl, owner);
+      const float* mrow = &Ms[j * BATCH + p * S];
+#pragma unroll
+      for (int i = io; i < S; ++i) c[i] = fmaf(mrow[i], dj, c[i]);
+    }
+  }
+
+  if (!active) return;
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const int col = p + P * i;
+    if (col < ncols) {
+      codes[row * n + b0 + col] = code[i];
+      E[row * BATCH + col] = d[i];
+    }
+  }
+  if (p == 0) {
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk)
+      if (blk * G < ncols) scales[row * (n / G) + (b0 / G) + blk] = f32_to_f16_bits_clamped(sc[blk]);
+  }
+}
+
+}  // namespace wr
+
+using namespace wr;
+
+static constexpr int kBatch = 128;
+
+size_t wr_gptq_ws_bytes(int64_t rows, int64_t n) {
+  size_t b = 0;
+  b += (size_t)n * n * 4;          // A (J H J, then L)
+  b += (size_t)n * n * 4;          // M
+  b += (size_t)CH_NB * CH_NB * 4;  // inverse of the current diagonal block
+  b += (size_t)rows * n * 4;       // corrections C
+  b += (size_t)rows * kBatch * 4;  // batch errors E
+  return b + 1024;
+}
+
+// Blocked Cholesky of J H J and M; shared with nothing else.
+static int factor_m(wr_ctx* ctx, const float* H, int64_t ldh, int n, float* A, float* Mm, float* Linv,
+                    int32_t* dev_info) {
+  hipStream_t st = ctx->stream;
+  hipLaunchKernelGGL(reverse_copy_kernel, dim3(n), dim3(256), 0, st, H, ldh, n, A);
+  WR_CHECK_LAUNCH();
+  for (int kb = 0; kb < n; kb += CH_NB) {
+    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, st, A, n, kb, Linv, dev_info);
+    WR_CHECK_LAUNCH();
+    const int rem = n - kb - CH_NB;
+    if (rem <= 0) break;
+    float* panel = A + (int64_t)(kb + CH_NB) * n + kb;
+    // panel <- panel * L_kk^-T
+    int rc = wr_gemm_f32(st, rem, CH_NB, CH_NB, panel, n, Linv, CH_NB, false, panel, n, 1.0f, false, false, dev_info);
+    if (rc) return rc;
+    // trailing lower matrix -= panel panel^T
+    float* trail = A + (int64_t)(kb + CH_NB) * n + kb + CH_NB;
+    rc = wr_gemm_f32(st, rem, rem, CH_NB, panel, n, panel, n, false, trail, n, -1.0f, true, true, dev_info);
+    if (rc) return rc;
+  }
+  hipLaunchKernelGGL(build_m_kernel, dim3(n), dim3(256), 0, st, A, n, Mm, dev_info);
+  WR_CHECK_LAUNCH();
+  return WR_OK;
+}
+
+template <int P, int G>
+static void launch_panel(hipStream_t st, const void* W, int w_dtype, int64_t rows, int n, int64_t ldw, const float* Mm,
+                         const uint8_t* bits, int b0, int ncols, float* Cb, float* E, uint8_t* codes, uint16_t* scales,
+                         const int32_t* dev_info) {
+  const unsigned grid = (unsigned)((rows + (256 / P) - 1) / (256 / P));
+  hipLaunchKernelGGL((sweep_panel_kernel<P, kBatch, G>), dim3(grid), dim3(256), 0, st, W, w_dtype, rows, n, ldw, Mm,
+                     bits, b0, ncols, Cb, E, codes, scales, dev_info);
+}
+
+template <int P>
+static int launch_panel_g(hipStream_t st, int G, const void* W, int w_dtype, int64_t rows, int n, int64_t ldw,
+                          const float* Mm, const uint8_t* bits, int b0, int ncols, float* Cb, float* E, uint8_t* codes,
+                          uint16_t* scales, const int32_t* dev_info) {
+  switch (G) {
+    case 32: launch_panel<P, 32>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, codes, scales, dev_info); break;
+    case 64: launch_panel<P, 64>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, codes, scales, dev_info); break;
+    case 128: launch_panel<P, 128>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, codes, scales, dev_info); break;
+    default: return WR_EUNSUPPORTED;
+  }
+  WR_CHECK_LAUNCH();
+  return WR_OK;
+}
+
+int wr_gptq_sweep_impl(wr_ctx* ctx, const void* W, int w_dtype, int64_t rows, int64_t n64, int64_t ldw,
+                       const float* H, int64_t ldh, const uint8_t* bits, int32_t group, int32_t lazy_batch,
+                       uint8_t* codes, uint16_t* scales, int32_t* dev_info) {
+  if (lazy_batch != kBatch || (group != 32 && group != 64 && group != 128)) return WR_EUNSUPPORTED;
+  if (ctx->ws_bytes < wr_gptq_ws_bytes(rows, n64)) return WR_EWORKSPACE;
+  const int n = (int)n64;
+  hipStream_t st = ctx->stream;
+  char* ws = static_cast<char*>(ctx->ws);
+  float* A = reinterpret_cast<float*>(ws);
+  float* Mm = A + (size_t)n * n;
+  float* Linv = Mm + (size_t)n * n;
+  float* Cb = Linv + CH_NB * CH_NB;
+  float* E = Cb + (size_t)rows * n;
+
+  hipLaunchKernelGGL(sweep_set_int_kernel, dim3(1), dim3(1), 0, st, dev_info, 0);
+  WR_CHECK_LAUNCH();
+  if (rows > 0) {
+    hipLaunchKernelGGL(check_finite_kernel, dim3((unsigned)rows), dim3(256), 0, st, W, w_dtype, rows, n, ldw, dev_info);
+    WR_CHECK_LAUNCH();
+  }
+  int rc = factor_m(ctx, H, ldh, n, A, Mm, Linv, dev_info);
+  if (rc) return rc;
+  if (rows == 0) return WR_OK;
+  hipLaunchKernelGGL(zero_f32_kernel, dim3(1024), dim3(256), 0, st, Cb, (int64_t)rows * n);
+  WR_CHECK_LAUNCH();
+  for (int b0 = 0; b0 < n; b0 += kBatch) {
+    const int ncols = std::min(kBatch, n - b0);
+    rc = launch_panel_g<16>(st, group, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, codes, scales, dev_info);
+    if (rc) return rc;
+    const int rest = n - b0 - ncols;
+    if (rest > 0) {
+      rc = wr_gemm_f32(st, (int)rows, rest, ncols, E, kBatch, Mm + (int64_t)b0 * n + b0 + ncols, n, true,
+                       Cb + b0 + ncols, n, 1.0f, true, false, dev_info);
+      if (rc) return rc;
+    }
+  }
+  return WR_OK;
+}

@@ -1,0 +1,352 @@
+// Joint least-squares block scales with a prior, and the wring.
+//
+// Wringer model cards, "Recipe" / "Why the solver changed": scales by a joint
+// least-squares closed form with a prior (lambda = 0.01); the wring rounds the
+// watered weights W' = W_hat + (alpha/r) B A to the nearest point of the same
+// grid and re-solves the scales against W'.  Agents-A1 card, "Honest
+// caveats": scales projected to fp16 at solve time.
+//
+// Per row, with levels l_j = 2 c_j - L, Q[j, block(j)] = l_j, G = Q^T H Q,
+// mu = trace(G)/nb and residual R = T - Q s0, the minimiser of
+//   (t - Q s)^T H (t - Q s) + lambda mu ||s - s0||^2
+// is s = s0 + (G + lambda mu I)^-1 Q^T H R.  Solving for the step from s0
+// (instead of for s) keeps the rounding error of G and of the right-hand side
+// proportional to the step, which is what lets both be formed on the bf16
+// matrix cores:
+//   G[r][b][c] = sum_{j in b} l_j (H_{b,c} l_c)_j    two passes, H = H_hi + H_lo
+//   h[r][b]    = sum_{j in b} l_j (H R_r)_j          three passes, R = R_hi + R_lo
+// (levels are exact in bf16; H_hi/H_lo and R_hi/R_lo are bf16 splits).  The
+// MFMA computes D[j][r] = sum_l H[j][l] X[r][l] with j down the accumulator
+// rows, so the level-weighted sum over a block's j stays mostly inside a lane.
+// Each row's nb x nb system is then factored and solved in fp64.
+#include "common.hpp"
+
+int wr_gemm_f32(hipStream_t st, int M, int N, int K, const float* A, int64_t lda, const float* B, int64_t ldb,
+                bool b_kn, float* C, int64_t ldc, float alpha, bool accumulate, bool lower_tiles,
+                const int32_t* dev_info);
+
+namespace wr {
+
+__global__ void set_int_kernel(int32_t* p, int32_t v) { *p = v; }
+
+__global__ void to_f32_kernel(const void* __restrict__ src, int dtype, int64_t count, float* __restrict__ dst) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = dtype == WR_BF16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(src)[i]) : static_cast<const float*>(src)[i];
+}
+
+// T = target, or dequant(codes, scales) when target is null.
+__global__ void target_kernel(const void* __restrict__ target, int t_dtype, int64_t ldt, const uint8_t* __restrict__ codes,
+                              const uint16_t* __restrict__ scales, const uint8_t* __restrict__ bits, int64_t rows, int n,
+                              int group, float* __restrict__ T) {
+  const int64_t r = blockIdx.y;
+  const int nb = n / group;
+  const int L = (1 << bits[r]) - 1;
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x) {
+    float v;
+    if (target) {
+      v = t_dtype == WR_BF16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(target)[r * ldt + j])
+                             : static_cast<const float*>(target)[r * ldt + j];
+    } else {
+      v = (float)(2 * (int)codes[r * n + j] - L) * f16_bits_to_f32(scales[r * nb + j / group]);
+    }
+    T[r * n + j] = v;
+  }
+}
+
+// Optional nearest-point recode on the incoming scales, then levels and the bf16-split residual.
+__global__ void recode_residual_kernel(const float* __restrict__ T, uint8_t* __restrict__ codes,
+                                       const uint16_t* __restrict__ scales, const uint8_t* __restrict__ bits,
+                                       int64_t rows, int n, int group, int recode, uint16_t* __restrict__ Lev,
+                                       uint16_t* __restrict__ Rhi, uint16_t* __restrict__ Rlo,
+                                       int32_t* __restrict__ dev_info) {
+  const int64_t r = blockIdx.y;
+  const int nb = n / group;
+  const int L = (1 << bits[r]) - 1;
+  bool bad = false;
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x) {
+    const int64_t e = r * n + j;
+    const float t = T[e];
+    bad |= !(fabsf(t) <= 3.0e38f);
+    const float s = f16_bits_to_f32(scales[r * nb + j / group]);
+    int c;
+    if (recode) {
+      c = nearest_code(s > 0.0f ? t / s : 0.0f, L);
+      codes[e] = (uint8_t)c;
+    } else {
+      c = codes[e];
+    }
+    const float lev = (float)(2 * c - L);
+    const float res = t - lev * s;  // lev * s is exact in fp32
+    const uint32_t hi = f32_to_bf16_bits(res);
+    Lev[e] = (uint16_t)f32_to_bf16_bits(lev);
+    Rhi[e] = (uint16_t)hi;
+    Rlo[e] = (uint16_t)f32_to_bf16_bits(res - bf16_bits_to_f32(hi));
+  }
+  if (bad) atomicCAS(dev_info, 0, -1);
+}
+
+__global__ void split_h_kernel(const float* __restrict__ H, int64_t ldh, int n, uint16_t* __restrict__ Hhi,
+                               uint16_t* __restrict__ Hlo) {
+  const int64_t i = blockIdx.y;
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x) {
+    const float h = H[i * ldh + j];
+    const uint32_t hi = f32_to_bf16_bits(h);
+    Hhi[i * n + j] = (uint16_t)hi;
+    Hlo[i * n + j] = (uint16_t)f32_to_bf16_bits(h - bf16_bits_to_f32(hi));
+  }
+}
+
+// One workgroup: 128 rows (four waves of 32) x one block b.  Loops over all column blocks c.
+template <int G>
+__global__ __launch_bounds__(256) void gram_kernel(const uint16_t* __restrict__ Lev, const uint16_t* __restrict__ Rhi,
+                                                   const uint16_t* __restrict__ Rlo, int64_t rows, int n,
+                                                   const uint16_t* __restrict__ Hhi, const uint16_t* __restrict__ Hlo,
+                                                   float* __restrict__ Gm, float* __restrict__ rhs,
+                                                   const int32_t* __restrict__ dev_info) {
+  constexpr int IB = G / 32;
+  constexpr int PITCH = G + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t sHh[G * PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t sHl[G * PITCH];
+  if (*dev_info != 0) return;
+  const int nb = n / G;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t r = (int64_t)blockIdx.x * 128 + wave * 32 + (lane & 31);
+  const bool rok = r < rows;
+  const int64_t rr = rok ? r : 0;
+
+  float levj[IB][16];
+#pragma unroll
+  for (int ib = 0; ib < IB; ++ib)
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      levj[ib][v] = rok ? bf16_bits_to_f32(Lev[rr * n + b * G + ib * 32 + acc_row(v, lane)]) : 0.0f;
+
+  float rtot[IB][16];
+#pragma unroll
+  for (int ib = 0; ib < IB; ++ib)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) rtot[ib][v] = 0.0f;
+
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  for (int c = 0; c < nb; ++c) {
+    __syncthreads();
+    for (int e = tid; e < G * G / 8; e += 256) {
+      const int j = e / (G / 8), l8 = (e % (G / 8)) * 8;
+      const int64_t src = (int64_t)(b * G + j) * n + c * G + l8;
+      *reinterpret_cast<u32x4*>(&sHh[j * PITCH + l8]) = *reinterpret_cast<const u32x4*>(Hhi + src);
+      *reinterpret_cast<u32x4*>(&sHl[j * PITCH + l8]) = *reinterpret_cast<const u32x4*>(Hlo + src);
+    }
+    __syncthreads();
+    const bool doG = c >= b;
+    f32x16 accG[IB], accR[IB];
+#pragma unroll
+    for (int ib = 0; ib < IB; ++ib) {
+      accG[ib] = f32x16{};
+      accR[ib] = f32x16{};
+    }
+#pragma unroll
+    for (int ks = 0; ks < G / 16; ++ks) {
+      const int lk = ks * 16 + 8 * (lane >> 5);
+      const int64_t src = rr * n + c * G + lk;
+      const bf16x8 fRh = as_bf16x8(rok ? *reinterpret_cast<const u32x4*>(Rhi + src) : zero4);
+      const bf16x8 fRl = as_bf16x8(rok ? *reinterpret_cast<const u32x4*>(Rlo + src) : zero4);
+      bf16x8 fL = as_bf16x8(zero4);
+      if (doG) fL = as_bf16x8(rok ? *reinterpret_cast<const u32x4*>(Lev + src) : zero4);
+#pragma unroll
+      for (int ib = 0; ib < IB; ++ib) {
+        const int ja = ib * 32 + (lane & 31);
+        const bf16x8 ah = as_bf16x8(*reinterpret_cast<const u32x4*>(&sHh[ja * PITCH + lk]));
+        const bf16x8 al = as_bf16x8(*reinterpret_cast<const u32x4*>(&sHl[ja * PITCH + lk]));
+        accR[ib] = mfma32x32x16_bf16(ah, fRh, accR[ib]);
+        accR[ib] = mfma32x32x16_bf16(al, fRh, accR[ib]);
+        accR[ib] = mfma32x32x16_bf16(ah, fRl, accR[ib]);
+        if (doG) {
+          accG[ib] = mfma32x32x16_bf16(ah, fL, accG[ib]);
+          accG[ib] = mfma32x32x16_bf16(al, fL, accG[ib]);
+        }
+      }
+    }
+#pragma unroll
+    for (int ib = 0; ib < IB; ++ib)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) rtot[ib][v] += accR[ib][v];
+    if (doG) {
+      float part = 0.0f;
+#pragma unroll
+      for (int ib = 0; ib < IB; ++ib)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) part = fmaf(levj[ib][v], accG[ib][v], part);
+      part += __shfl_xor(part, 32);
+      if (lane < 32 && rok) Gm[((size_t)r * nb + b) * nb + c] = part;
+    }
+  }
+  float part = 0.0f;
+#pragma unroll
+  for (int ib = 0; ib < IB; ++ib)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) part = fmaf(levj[ib][v], rtot[ib][v], part);
+  part += __shfl_xor(part, 32);
+  if (lane < 32 && rok) rhs[(size_t)r * nb + b] = part;
+}
+
+// Per row: (G + lambda mu I) u = h in fp64 (packed lower Cholesky in LDS), s = s0 + u -> fp16.
+__global__ __launch_bounds__(64) void row_solve_kernel(const float* __restrict__ Gm, const float* __restrict__ rhs,
+                                                       int64_t rows, int nb, float lambda, uint16_t* __restrict__ scales,
+                                                       const int32_t* __restrict__ dev_info) {
+  extern __shared__ double sh[];
+  if (*dev_info != 0) return;
+  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x;
+  double* a = sh;                               // packed lower: a[i(i+1)/2 + j]
+  double* y = sh + (size_t)nb * (nb + 1) / 2;
+  __shared__ int failed;
+  const float* g = Gm + (size_t)row * nb * nb;
+  double tr = 0.0;
+  for (int i = lane; i < nb; i += 64) tr += (double)g[(size_t)i * nb + i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) tr += __shfl_xor(tr, o);
+  const double reg = (double)lambda * tr / nb;
+  for (int i = 0; i < nb; ++i)
+    for (int j = lane; j <= i; j += 64) a[(size_t)i * (i + 1) / 2 + j] = (double)g[(size_t)j * nb + i] + (i == j ? reg : 0.0);
+  for (int i = lane; i < nb; i += 64) y[i] = (double)rhs[(size_t)row * nb + i];
+  if (lane == 0) failed = 0;
+  __syncthreads();
+  for (int k = 0; k < nb; ++k) {
+    const size_t kk = (size_t)k * (k + 1) / 2 + k;
+    if (lane == 0) {
+      const double d = a[kk];
+      if (!(d > 0.0)) failed = 1;
+      else a[kk] = sqrt(d);
+    }
+    __syncthreads();
+    if (failed) return;  // only reachable with lambda == 0 and a singular G: keep the incoming scales
+    const double dk = a[kk];
+    for (int i = k + 1 + lane; i < nb; i += 64) a[(size_t)i * (i + 1) / 2 + k] /= dk;
+    __syncthreads();
+    for (int i = k + 1; i < nb; ++i) {
+      const double aik = a[(size_t)i * (i + 1) / 2 + k];
+      for (int j = k + 1 + lane; j <= i; j += 64) a[(size_t)i * (i + 1) / 2 + j] -= aik * a[(size_t)j * (j + 1) / 2 + k];
+    }
+    __syncthreads();
+  }
+  // L z = y
+  for (int k = 0; k < nb; ++k) {
+    if (lane == 0) y[k] /= a[(size_t)k * (k + 1) / 2 + k];
+    __syncthreads();
+    const double zk = y[k];
+    for (int i = k + 1 + lane; i < nb; i += 64) y[i] -= a[(size_t)i * (i + 1) / 2 + k] * zk;
+    __syncthreads();
+  }
+  // L^T u = z
+  for (int k = nb - 1; k >= 0; --k) {
+    if (lane == 0) y[k] /= a[(size_t)k * (k + 1) / 2 + k];
+    __syncthreads();
+    const double uk = y[k];
+    for (int i = lane; i < k; i += 64) y[i] -= a[(size_t)k * (k + 1) / 2 + i] * uk;
+    __syncthreads();
+  }
+  for (int i = lane; i < nb; i += 64) {
+    uint16_t* sp = scales + (size_t)row * nb + i;
+    const double s = (double)f16_bits_to_f32(*sp) + y[i];
+    *sp = f64_to_f16_bits_clamped(s);
+  }
+}
+
+}  // namespace wr
+
+using namespace wr;
+
+struct WringLayout {
+  size_t T, Lev, Rhi, Rlo, Hhi, Hlo, Gm, rhs, Bf, Af, total;
+};
+
+static WringLayout wring_layout(int64_t rows, int64_t n, int32_t group, int32_t rank) {
+  WringLayout l{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  const int64_t nb = n / group;
+  l.T = take((size_t)rows * n * 4);
+  l.Lev = take((size_t)rows * n * 2);
+  l.Rhi = take((size_t)rows * n * 2);
+  l.Rlo = take((size_t)rows * n * 2);
+  l.Hhi = take((size_t)n * n * 2);
+  l.Hlo = take((size_t)n * n * 2);
+  l.Gm = take((size_t)rows * nb * nb * 4);
+  l.rhs = take((size_t)rows * nb * 4);
+  l.Bf = take((size_t)rows * (rank > 0 ? rank : 0) * 4);
+  l.Af = take((size_t)n * (rank > 0 ? rank : 0) * 4);
+  l.total = off;
+  return l;
+}
+
+size_t wr_wring_ws_bytes(int64_t rows, int64_t n, int32_t group, int32_t rank) {
+  return wring_layout(rows, n, group, rank).total;
+}
+
+int wr_wring_solve_impl(wr_ctx* ctx, const void* target, int t_dtype, int64_t ldt, const void* B, const void* A,
+                        int32_t rank, float alpha, int ab_dtype, const float* H, int64_t ldh, int64_t rows, int64_t n64,
+                        const uint8_t* bits, int32_t group, float lambda, int flags, uint8_t* codes, uint16_t* scales,
+                        int32_t* dev_info) {
+  if (group != 32 && group != 64 && group != 128) return WR_EUNSUPPORTED;
+  const bool adapter = B && A && rank > 0;
+  const WringLayout lay = wring_layout(rows, n64, group, adapter ? rank : 0);
+  if (ctx->ws_bytes < lay.total) return WR_EWORKSPACE;
+  const int n = (int)n64;
+  const int nb = n / group;
+  hipStream_t st = ctx->stream;
+  char* ws = static_cast<char*>(ctx->ws);
+  float* T = reinterpret_cast<float*>(ws + lay.T);
+  uint16_t* Lev = reinterpret_cast<uint16_t*>(ws + lay.Lev);
+  uint16_t* Rhi = reinterpret_cast<uint16_t*>(ws + lay.Rhi);
+  uint16_t* Rlo = reinterpret_cast<uint16_t*>(ws + lay.Rlo);
+  uint16_t* Hhi = reinterpret_cast<uint16_t*>(ws + lay.Hhi);
+  uint16_t* Hlo = reinterpret_cast<uint16_t*>(ws + lay.Hlo);
+  float* Gm = reinterpret_cast<float*>(ws + lay.Gm);
+  float* rh = reinterpret_cast<float*>(ws + lay.rhs);
+
+  hipLaunchKernelGGL(set_int_kernel, dim3(1), dim3(1), 0, st, dev_info, 0);
+  WR_CHECK_LAUNCH();
+  if (rows == 0) return WR_OK;
+  const unsigned gx = (unsigned)std::min<int64_t>((n + 255) / 256, 16);
+  hipLaunchKernelGGL(target_kernel, dim3(gx, (unsigned)rows), dim3(256), 0, st, target, t_dtype, ldt, codes, scales,
+                     bits, rows, n, group, T);
+  WR_CHECK_LAUNCH();
+  if (adapter) {
+    float* Bf = reinterpret_cast<float*>(ws + lay.Bf);
+    float* Af = reinterpret_cast<float*>(ws + lay.Af);
+    hipLaunchKernelGGL(to_f32_kernel, dim3(256), dim3(256), 0, st, B, ab_dtype, rows * rank, Bf);
+    WR_CHECK_LAUNCH();
+    hipLaunchKernelGGL(to_f32_kernel, dim3(256), dim3(256), 0, st, A, ab_dtype, (int64_t)rank * n, Af);
+    WR_CHECK_LAUNCH();
+    const int rc = wr_gemm_f32(st, (int)rows, n, rank, Bf, rank, Af, n, true, T, n, alpha / (float)rank, true, false,
+                               nullptr);
+    if (rc) return rc;
+  }
+  hipLaunchKernelGGL(recode_residual_kernel, dim3(gx, (unsigned)rows), dim3(256), 0, st, T, codes, scales, bits, rows,
+                     n, group, (flags & WR_RECODE_NEAREST) ? 1 : 0, Lev, Rhi, Rlo, dev_info);
+  WR_CHECK_LAUNCH();
+  hipLaunchKernelGGL(split_h_kernel, dim3(gx, (unsigned)n), dim3(256), 0, st, H, ldh, n, Hhi, Hlo);
+  WR_CHECK_LAUNCH();
+  dim3 ggrid((unsigned)((rows + 127) / 128), (unsigned)nb);
+  switch (group) {
+    case 32: hipLaunchKernelGGL(gram_kernel<32>, ggrid, dim3(256), 0, st, Lev, Rhi, Rlo, rows, n, Hhi, Hlo, Gm, rh, dev_info); break;
+    case 64: hipLaunchKernelGGL(gram_kernel<64>, ggrid, dim3(256), 0, st, Lev, Rhi, Rlo, rows, n, Hhi, Hlo, Gm, rh, dev_info); break;
+    default: hipLaunchKernelGGL(gram_kernel<128>, ggrid, dim3(256), 0, st, Lev, Rhi, Rlo, rows, n, Hhi, Hlo, Gm, rh, dev_info); break;
+  }
+  WR_CHECK_LAUNCH();
+  const size_t shbytes = ((size_t)nb * (nb + 1) / 2 + nb) * sizeof(double);
+  if (shbytes > 160 * 1024) return WR_EUNSUPPORTED;
+  if (shbytes > 64 * 1024 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(row_solve_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)shbytes) != hipSuccess)
+    return WR_EHIP;
+  hipLaunchKernelGGL(row_solve_kernel, dim3((unsigned)rows), dim3(64), shbytes, st, Gm, rh, rows, nb, lambda, scales,
+                     dev_info);
+  WR_CHECK_LAUNCH();
+  return WR_OK;
+}

@@ -1,0 +1,283 @@
+"""GPU parity of each library entry point against the CPU oracle on the toy-layer workload.
+
+Toy layer: W 256 x 512 fp32 ~ N(0, 0.02^2); X 4096 x 512 fp32 from the spectral model with 5
+outlier channels; 2-bit grid, group 32, damping 0.01 mean(diag H); rank-8 adapter, alpha 8;
+lambda 0.01.  Smaller ragged shapes cover tile edges.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import code_parity, f16_bits, scale_ulps
+
+pytestmark = pytest.mark.gpu
+
+TIE = 5e-3  # a code may differ only where the oracle's pre-rounding value is this close to a threshold
+
+
+@pytest.fixture(scope="module")
+def wr():
+    from post_bit_weight_amd import _lib
+    return _lib
+
+
+@pytest.fixture(scope="module")
+def ctx(wr):
+    return wr.Context(0)
+
+
+@pytest.fixture(scope="module")
+def toy():
+    from post_bit_weight_amd import synth
+    W = synth.gaussian((256, 512), 0.02, seed=101)
+    X = synth.SpectralSource(512, seed=102, n_outliers=5).chunk(0, 4096, dtype=torch.float32)
+    B = synth.gaussian((256, 8), 0.01, seed=103)
+    A = synth.gaussian((8, 512), 0.01, seed=104)
+    H0 = oracle.second_moment(X.double().numpy())
+    H, delta = oracle.damp(H0, 0.01)
+    return dict(W=W, X=X, B=B, A=A, H0=H0, H=H, delta=delta)
+
+
+def dev(t):
+    return t.contiguous().cuda()
+
+
+# ------------------------------------------------------------------------- pack
+@pytest.mark.parametrize("bits,rows,n,g", [(2, 37, 96, 32), (3, 5, 64, 32), (3, 33, 2560, 64), (4, 9, 128, 128)])
+def test_pack_unpack_bit_exact(wr, ctx, bits, rows, n, g):
+    rng = np.random.default_rng(bits * 100 + rows)
+    codes = rng.integers(0, 2 ** bits, size=(rows, n))
+    scales = oracle.fp16_rne(rng.uniform(-2, 2, size=(rows, n // g)))
+    ref = oracle.pack(codes, scales, bits, g)
+    c_t = dev(torch.from_numpy(codes.astype(np.uint8)))
+    s_t = dev(torch.from_numpy(scales.astype(np.float16)))
+    buf = torch.empty(ref.shape[0], dtype=torch.uint8, device="cuda")
+    wr.wr_pack(ctx, c_t, s_t, bits, g, buf)
+    assert np.array_equal(buf.cpu().numpy(), ref)
+    c2 = torch.empty_like(c_t)
+    s2 = torch.empty_like(s_t)
+    dq = torch.empty(rows, n, dtype=torch.bfloat16, device="cuda")
+    wr.wr_unpack(ctx, buf, rows, n, bits, g, c2, s2, dq)
+    assert torch.equal(c2, c_t) and torch.equal(s2.view(torch.int16), s_t.view(torch.int16))
+    expect = torch.from_numpy(oracle.dequant(codes, scales, bits, g)).to(torch.bfloat16)
+    assert torch.equal(dq.cpu().view(torch.int16), expect.view(torch.int16))
+
+
+def test_pack_rejects_wrong_size(wr, ctx):
+    c = torch.zeros(4, 64, dtype=torch.uint8, device="cuda")
+    s = torch.zeros(4, 2, dtype=torch.float16, device="cuda")
+    with pytest.raises(wr.WringerError):
+        wr.wr_pack(ctx, c, s, 2, 32, torch.empty(10, dtype=torch.uint8, device="cuda"))
+
+
+# ------------------------------------------------------------------------- hessian
+def _rel(a, b):
+    return np.linalg.norm(a - b) / np.linalg.norm(b)
+
+
+def test_hessian_fp32_toy(wr, ctx, toy):
+    S = torch.empty(512, 512, dtype=torch.float64, device="cuda")
+    wr.wr_hessian_accumulate(ctx, dev(toy["X"]), S, zero=True)
+    got = np.tril(S.cpu().numpy())
+    ref = np.tril(toy["X"].double().numpy().T @ toy["X"].double().numpy())
+    assert _rel(got, ref) < 1e-6
+
+
+@pytest.mark.parametrize("rows,n", [(1000, 200), (130, 136), (65536, 256), (3, 8)])
+def test_hessian_bf16_ragged(wr, ctx, rows, n):
+    g = torch.Generator().manual_seed(rows + n)
+    X = (torch.randn(rows, n, generator=g) * torch.linspace(0.1, 3, n)).to(torch.bfloat16)
+    S = torch.empty(n, n, dtype=torch.float64, device="cuda")
+    wr.wr_hessian_accumulate(ctx, dev(X), S, zero=True)
+    Xd = X.double().numpy()
+    ref = Xd.T @ Xd
+    got = S.cpu().numpy()
+    assert _rel(np.tril(got), np.tril(ref)) < 2e-7
+
+
+def test_hessian_chunks_and_strided_input(wr, ctx):
+    g = torch.Generator().manual_seed(7)
+    big = torch.randn(3000, 400, generator=g).to(torch.bfloat16)
+    X = big[:, :392]                      # row stride 400 (a multiple of 8), 392 columns
+    S1 = torch.empty(392, 392, dtype=torch.float64, device="cuda")
+    Xd = dev(big)[:, :392]
+    wr.wr_hessian_accumulate(ctx, Xd, S1, zero=True)
+    S2 = torch.empty_like(S1)
+    for k, (a, b) in enumerate([(0, 1000), (1000, 1001), (1001, 3000)]):
+        wr.wr_hessian_accumulate(ctx, Xd[a:b], S2, zero=(k == 0))
+    ref = np.tril(X.double().numpy().T @ X.double().numpy())
+    assert _rel(np.tril(S1.cpu().numpy()), ref) < 2e-7
+    assert _rel(np.tril(S2.cpu().numpy()), ref) < 2e-7
+
+
+def test_hessian_finalize_pads_and_damps(wr, ctx, toy):
+    S = torch.empty(512, 512, dtype=torch.float64, device="cuda")
+    wr.wr_hessian_accumulate(ctx, dev(toy["X"]), S, zero=True)
+    H = torch.empty(640, 640, dtype=torch.float32, device="cuda")
+    delta = torch.empty(1, dtype=torch.float32, device="cuda")
+    wr.wr_hessian_finalize(ctx, S, 4096, 0.01, H, delta)
+    ref, d = oracle.damp(oracle.pad_square(toy["H0"], 640), 0.01)
+    assert abs(delta.item() - d) <= 1e-6 * d
+    assert _rel(H.cpu().double().numpy(), ref) < 1e-6
+    assert np.array_equal(H.cpu().numpy(), H.cpu().numpy().T)
+
+
+# ------------------------------------------------------------------------- rotation
+@pytest.mark.parametrize("m,n,rows", [(4, 8, 3), (64, 256, 17), (1024, 2048, 5), (512, 1536, 4)])
+def test_rotation_rows_and_inverse(wr, ctx, m, n, rows):
+    rng = np.random.default_rng(m + n)
+    M = rng.standard_normal((rows, n)).astype(np.float32)
+    s = rng.choice([-1, 1], size=n).astype(np.int8)
+    t = dev(torch.from_numpy(M))
+    st = dev(torch.from_numpy(s))
+    wr.wr_hadamard_rotate(ctx, t, m, st, wr.WR_ROT_ROWS)
+    ref = oracle.rotate_rows(M.astype(np.float64), m, s.astype(np.float64))
+    assert np.abs(t.cpu().numpy() - ref).max() < 1e-5
+    wr.wr_hadamard_rotate(ctx, t, m, st, wr.WR_ROT_ROWS_INVERSE)
+    assert np.abs(t.cpu().numpy() - M).max() < 1e-5
+
+
+def test_rotation_page_example(wr, ctx, golden):
+    g = golden("hadamard_trick1.txt")
+    t = dev(torch.tensor([g["input"]], dtype=torch.float32))
+    wr.wr_hadamard_rotate(ctx, t, 4, dev(torch.ones(4, dtype=torch.int8)), wr.WR_ROT_ROWS)
+    assert np.allclose(t.cpu().numpy()[0], g["output"], atol=1e-6)
+
+
+def test_rotation_sym(wr, ctx, toy):
+    rng = np.random.default_rng(3)
+    s = rng.choice([-1, 1], size=512).astype(np.int8)
+    H = dev(torch.from_numpy(toy["H"].astype(np.float32)))
+    wr.wr_hadamard_rotate(ctx, H, 128, dev(torch.from_numpy(s)), wr.WR_ROT_SYM)
+    ref = oracle.rotate_sym(toy["H"], 128, s.astype(np.float64))
+    assert _rel(H.cpu().double().numpy(), ref) < 1e-6
+
+
+# ------------------------------------------------------------------------- GPTQ sweep
+def _sweep(wr, ctx, W, H32, bits, g):
+    rows, n = W.shape
+    codes = torch.empty(rows, n, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(rows, n // g, dtype=torch.float16, device="cuda")
+    info = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bits_t = torch.as_tensor(np.broadcast_to(bits, (rows,)).astype(np.uint8)).cuda()
+    wr.wr_gptq_sweep(ctx, dev(W), dev(torch.from_numpy(H32)), bits_t, g, 128, codes, scales, info)
+    return codes.cpu().numpy().astype(np.int64), scales.cpu().numpy().astype(np.float64), int(info.item())
+
+
+def test_gptq_toy_same_H(wr, ctx, toy):
+    H32 = toy["H"].astype(np.float32)
+    W = toy["W"]
+    codes, scales, info = _sweep(wr, ctx, W, H32, 2, 32)
+    assert info == 0
+    ref = oracle.gptq_sweep(W.double().numpy(), H32.astype(np.float64), 2, 32)
+    cp = code_parity(codes, ref["codes"], ref["t"], 3)
+    assert cp["frac"] <= 1e-3 and cp["worst_first"] <= TIE, cp
+    ok = cp["identical_rows"]
+    assert scale_ulps(scales[ok], ref["scales"][ok]).max() <= 1
+    lg = oracle.proxy_loss(W.double().numpy(), oracle.dequant(codes, scales, 2, 32), toy["H0"])
+    lr = oracle.proxy_loss(W.double().numpy(), oracle.dequant(ref["codes"], ref["scales"], 2, 32), toy["H0"])
+    assert abs(lg - lr) <= 1e-4 * lr
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_gptq_mixed_bits_and_groups(wr, ctx, bits):
+    rng = np.random.default_rng(11 + bits)
+    rows, n = 40, 384
+    A = rng.standard_normal((4 * n, n))
+    A += 0.5 * A[:, :1]
+    H = A.T @ A / (4 * n)
+    H, _ = oracle.damp(H, 0.01)
+    H32 = H.astype(np.float32)
+    W = torch.from_numpy(0.02 * rng.standard_normal((rows, n))).to(torch.bfloat16)
+    bits_rows = np.where(np.arange(rows) % 3 == 0, 3, bits)
+    for g in (32, 64, 128):
+        codes, scales, info = _sweep(wr, ctx, W, H32, bits_rows, g)
+        assert info == 0
+        ref = oracle.gptq_sweep(W.double().numpy(), H32.astype(np.float64), bits_rows, g)
+        cp = code_parity(codes, ref["codes"], ref["t"], oracle.levels_count(bits_rows))
+        assert cp["frac"] <= 1e-3 and cp["worst_first"] <= TIE, (g, cp)
+        ok = cp["identical_rows"]
+        assert scale_ulps(scales[ok], ref["scales"][ok]).max() <= 1
+
+
+def test_gptq_diagonal_H_is_plain_rounding(wr, ctx, toy):
+    W = toy["W"]
+    d = np.linspace(0.5, 2.0, 512)
+    codes, scales, info = _sweep(wr, ctx, W, np.diag(d).astype(np.float32), 2, 32)
+    ref = oracle.gptq_sweep(W.double().numpy(), np.diag(d), 2, 32)
+    assert info == 0
+    assert np.array_equal(codes, ref["codes"]) and np.array_equal(scales, ref["scales"])
+
+
+def test_gptq_reports_non_pd_and_non_finite(wr, ctx, toy):
+    W = toy["W"][:8]
+    H = np.eye(512, dtype=np.float32)
+    H[300, 300] = -1.0
+    rows, n = W.shape
+    codes = torch.full((rows, n), 7, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros(rows, n // 32, dtype=torch.float16, device="cuda")
+    info = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bits_t = torch.full((rows,), 2, dtype=torch.uint8, device="cuda")
+    wr.wr_gptq_sweep(ctx, dev(W), dev(torch.from_numpy(H)), bits_t, 32, 128, codes, scales, info)
+    assert info.item() == 512 - 300          # pivot of the reversed matrix (1-based)
+    assert (codes == 7).all()                 # outputs untouched
+    Wn = W.clone()
+    Wn[3, 5] = float("nan")
+    wr.wr_gptq_sweep(ctx, dev(Wn), dev(torch.from_numpy(np.eye(512, dtype=np.float32))), bits_t, 32, 128, codes,
+                     scales, info)
+    assert info.item() == -1 and (codes == 7).all()
+
+
+# ------------------------------------------------------------------------- joint scales / wring
+def _joint(wr, ctx, H32, codes, scales, bits, g, lam, target=None, B=None, A=None, alpha=0.0, recode=False):
+    rows, n = codes.shape
+    c = dev(torch.from_numpy(codes.astype(np.uint8)))
+    s = dev(torch.from_numpy(scales.astype(np.float16)))
+    info = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bits_t = torch.full((rows,), bits, dtype=torch.uint8, device="cuda")
+    wr.wr_wring_solve(ctx, dev(torch.from_numpy(H32)), bits_t, g, lam, c, s, info,
+                      target=None if target is None else dev(target), B=None if B is None else dev(B),
+                      A=None if A is None else dev(A), alpha=alpha, recode=recode)
+    return c.cpu().numpy().astype(np.int64), s.cpu().numpy().astype(np.float64), int(info.item())
+
+
+def test_joint_scales_toy(wr, ctx, toy):
+    H32 = toy["H"].astype(np.float32)
+    Hd = H32.astype(np.float64)
+    W = toy["W"]
+    g0 = oracle.gptq_sweep(W.double().numpy(), Hd, 2, 32)
+    codes, scales, info = _joint(wr, ctx, H32, g0["codes"], g0["scales"], 2, 32, 0.01, target=W)
+    assert info == 0 and np.array_equal(codes, g0["codes"])
+    ref, _ = oracle.joint_scales(g0["codes"], 2, 32, Hd, W.double().numpy(), g0["scales"], 0.01)
+    u = scale_ulps(scales, ref)
+    assert u.max() <= 1 and (u > 0).mean() < 0.01
+
+
+def test_wring_toy(wr, ctx, toy):
+    H32 = toy["H"].astype(np.float32)
+    Hd = H32.astype(np.float64)
+    W = toy["W"]
+    g0 = oracle.gptq_sweep(W.double().numpy(), Hd, 2, 32)
+    s1, _ = oracle.joint_scales(g0["codes"], 2, 32, Hd, W.double().numpy(), g0["scales"], 0.01)
+    codes, scales, info = _joint(wr, ctx, H32, g0["codes"], s1, 2, 32, 0.01, B=toy["B"], A=toy["A"], alpha=8.0,
+                                 recode=True)
+    ref = oracle.wring(g0["codes"], s1, 2, 32, toy["B"].double().numpy(), toy["A"].double().numpy(), 8.0, Hd, 0.01)
+    assert info == 0
+    cp = code_parity(codes, ref["codes"], ref["t"], 3)
+    assert cp["frac"] <= 1e-3 and cp["worst_first"] <= TIE, cp
+    ok = cp["identical_rows"]
+    assert scale_ulps(scales[ok], ref["scales"][ok]).max() <= 1
+    lg = oracle.proxy_loss(ref["target"], oracle.dequant(codes, scales, 2, 32), toy["H0"])
+    lr = oracle.proxy_loss(ref["target"], oracle.dequant(ref["codes"], ref["scales"], 2, 32), toy["H0"])
+    assert abs(lg - lr) <= 1e-4 * lr
+
+
+def test_wring_zero_adapter_is_a_fixed_point(wr, ctx, toy):
+    H32 = toy["H"].astype(np.float32)
+    rng = np.random.default_rng(5)
+    codes0 = rng.integers(0, 4, size=(64, 512))
+    s0 = oracle.fp16_rne(rng.uniform(0.005, 0.02, size=(64, 16)))
+    codes, scales, info = _joint(wr, ctx, H32, codes0, s0, 2, 32, 0.01, B=torch.zeros(64, 8), A=torch.zeros(8, 512),
+                                 alpha=8.0, recode=True)
+    assert info == 0 and np.array_equal(codes, codes0) and np.array_equal(f16_bits(scales), f16_bits(s0))
