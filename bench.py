@@ -1,0 +1,213 @@
+"""Throughput of the whole per-module quantization solve on one MI355X.
+
+One step = H accumulation over all calibration rows + finalize/damping + GPTQ
+sweep + joint scales + wring (rank-128 adapter, nearest-point recode, joint
+scales) + packing, for a Qwen3-4B-shaped q_proj (W 4096 x 2560 bf16, X
+131072 x 2560 bf16, 2-bit, group 64, lazy batch 128, lambda 0.01).  Inputs are
+synthetic and resident in HBM before the timed region.  The metric is weights
+quantized per second.
+
+Also reported: the roofline of the dominant kernel (the bf16 SYRK that
+accumulates H: N n (n + 1) useful flops per call, timed live with HIP events on
+the stream it runs on) and the CPU oracle timed on a bounded sample of the same
+workload on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+WORKLOAD = {
+    "workload": "q_proj 4096x2560 bf16 (Student-t nu=5, std 0.02), X 131072x2560 bf16 (spectral + 1% outlier "
+                "channels), 2-bit signed odd grid, group 64, fp16 scales, lazy batch 128, damping 0.01, "
+                "rank-128 wring alpha 128, lambda 0.01, pack",
+    "rows": 4096, "n": 2560, "calib_rows": 131072, "bits": 2, "group": 64, "lazy_batch": 128, "rank": 128,
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=128, help="weight rows in the oracle sample")
+    p.add_argument("--cpu-calib", type=int, default=8192, help="calibration rows in the oracle sample")
+    return p.parse_args()
+
+
+def traffic_from_profile():
+    """HBM bytes per SYRK launch from the committed rocprofv3 counter summary, if it matches this source."""
+    path = os.path.join(ROOT, "profiles", "syrk_bf16_q_proj_traffic.json")
+    src = os.path.join(ROOT, "post_bit_weight_amd", "csrc", "k_hessian.hip")
+    try:
+        rec = json.load(open(path))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec.get("source_sha256") != digest:
+            return None
+        return rec.get("bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(X_host, W_host, B_host, A_host, cfg, n_rows, n_calib):
+    """The oracle, unchanged, on a bounded sample; extrapolated to the full workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    n, g, bits, rank = cfg["n"], cfg["group"], cfg["bits"], cfg["rank"]
+    t0 = time.perf_counter()
+    H0 = oracle.second_moment(X_host[:n_calib].astype(np.float64))
+    t_h = time.perf_counter() - t0
+    H, _ = oracle.damp(H0, 0.01)
+    W = W_host[:n_rows].astype(np.float64)
+    t0 = time.perf_counter()
+    g0 = oracle.gptq_sweep(W, H, bits, g)
+    t_sweep = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    s1, _ = oracle.joint_scales(g0["codes"], bits, g, H, W, g0["scales"], 0.01)
+    w = oracle.wring(g0["codes"], s1, bits, g, B_host[:n_rows].astype(np.float64), A_host.astype(np.float64),
+                     float(rank), H, 0.01)
+    oracle.pack(w["codes"], w["scales"], bits, g)
+    t_rest = time.perf_counter() - t0
+    # the factorisation inside gptq_sweep is done once per module; time it alone to split it off
+    t0 = time.perf_counter()
+    oracle.upper_cholesky_of_inverse(H)
+    t_fact = time.perf_counter() - t0
+    per_row = (t_sweep - t_fact + t_rest) / n_rows
+    full = t_h * cfg["calib_rows"] / n_calib + t_fact + per_row * cfg["rows"]
+    return {
+        "value": cfg["rows"] * n / full, "unit": "weights/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"H over {n_calib} of {cfg['calib_rows']} calibration rows, sweep/joint/wring/pack over "
+                  f"{n_rows} of {cfg['rows']} weight rows, one factorisation; extrapolated linearly "
+                  f"(measured {t_h + t_sweep + t_rest + t_fact:.1f} s)",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+              "(the solve shards over calibration rows and weight rows, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from post_bit_weight_amd import _lib as wr
+    from post_bit_weight_amd import synth
+
+    cfg = WORKLOAD
+    rows, n, N, g, bits, rank = cfg["rows"], cfg["n"], cfg["calib_rows"], cfg["group"], cfg["bits"], cfg["rank"]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    ctx = wr.Context(0)
+    st = ctx.stream
+
+    src = synth.SpectralSource(n, seed=20261204, device="cuda", outlier_frac=0.01)
+    X = torch.cat([src.chunk(k, 16384) for k in range(N // 16384)])
+    W = synth.student_t((rows, n), seed=20261205, device="cuda", dtype=torch.bfloat16)
+    B = synth.gaussian((rows, rank), 0.01, seed=20261206, device="cuda", dtype=torch.bfloat16)
+    A = synth.gaussian((rank, n), 0.01, seed=20261207, device="cuda", dtype=torch.bfloat16)
+
+    S = torch.empty(n, n, dtype=torch.float64, device=dev)
+    H = torch.empty(n, n, dtype=torch.float32, device=dev)
+    delta = torch.empty(1, dtype=torch.float32, device=dev)
+    bits_t = torch.full((rows,), bits, dtype=torch.uint8, device=dev)
+    codes = torch.empty(rows, n, dtype=torch.uint8, device=dev)
+    scales = torch.empty(rows, n // g, dtype=torch.float16, device=dev)
+    info = torch.zeros(3, dtype=torch.int32, device=dev)
+    packed = torch.empty(wr.packed_nbytes(rows, n, bits, g), dtype=torch.uint8, device=dev)
+    ws = max(wr.wr_workspace_bytes(wr.WR_OP_HESSIAN, N, n), wr.wr_workspace_bytes(wr.WR_OP_GPTQ, rows, n, g, 0, 128),
+             wr.wr_workspace_bytes(wr.WR_OP_FINALIZE, 0, n),
+             wr.wr_workspace_bytes(wr.WR_OP_WRING, rows, n, g, rank, 0))
+    ctx.ensure_workspace(ws)
+
+    stages = ["hessian", "finalize", "gptq", "joint", "wring", "pack"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(st)
+        mark(0)
+        wr.wr_hessian_accumulate(ctx, X, S, zero=True)
+        mark(1)
+        wr.wr_hessian_finalize(ctx, S, N, 0.01, H, delta)
+        mark(2)
+        wr.wr_gptq_sweep(ctx, W, H, bits_t, g, 128, codes, scales, info[0:1])
+        mark(3)
+        wr.wr_wring_solve(ctx, H, bits_t, g, 0.01, codes, scales, info[1:2], target=W)
+        mark(4)
+        wr.wr_wring_solve(ctx, H, bits_t, g, 0.01, codes, scales, info[2:3], B=B, A=A, alpha=float(rank), recode=True)
+        mark(5)
+        wr.wr_pack(ctx, codes, scales, bits, g, packed)
+        mark(6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(info.abs().sum().item()) != 0:
+        raise RuntimeError(f"dev_info reports a failure: {info.tolist()}")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1e3 / args.steps
+    per_stage = {name: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+                 for i, name in enumerate(stages)}
+
+    flops_h = float(N) * n * (n + 1)
+    t_h = per_stage["hessian"] * 1e-3
+    achieved = flops_h / t_h / 1e12
+    traffic = traffic_from_profile()
+    line = {
+        "metric": "weights quantized/s (H accum+GPTQ sweep+wring); % MFMA/HBM peak, 1 GPU",
+        "value": rows * n / (ms * 1e-3),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16-mfma/fp32",
+        "data": "synthetic",
+        "config": {**cfg, "parallelism": "none (1 GPU)"},
+        "roofline": {
+            "kernel": "syrk_bf16 (H accumulation incl. its split-K reduction)",
+            "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+            "algorithmic_flops_per_launch": flops_h, "launch_ms": per_stage["hessian"],
+        },
+        "stage_ms": per_stage,
+    }
+    if not args.no_cpu_baseline:
+        Xh = X[: args.cpu_calib].float().cpu().numpy()
+        Wh = W.float().cpu().numpy()
+        Bh = B.float().cpu().numpy()
+        Ah = A.float().cpu().numpy()
+        line["cpu_baseline"] = cpu_baseline(Xh, Wh, Bh, Ah, cfg, args.cpu_rows, args.cpu_calib)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,7 +22,8 @@
  *     from wr_workspace_bytes.
  *   - Numerical failures are reported LAPACK-style through a device int32
  *     `dev_info` (read it after synchronising the stream): 0 = success;
- *     k > 0 = the leading minor of order k of H is not positive definite;
+ *     k > 0 = H is not numerically positive definite (the Cholesky
+ *     factorisation of the reversed H, J H J, failed at pivot k, 1-based);
  *     -1 = a non-finite value in the weights/target.  On failure the kernels
  *     that would write codes or scales return without writing them.
  *   - Return value: WR_OK (0) or a positive WR_E* code; no exception crosses
@@ -56,7 +57,8 @@ enum wr_op {             /* operations that need workspace, for wr_workspace_byt
   WR_OP_HESSIAN = 0,     /* rows = calibration rows per call, n = input dim */
   WR_OP_GPTQ = 1,        /* rows = weight rows, n = stored dim, group, lazy_batch */
   WR_OP_WRING = 2,       /* rows = weight rows, n = stored dim, group, rank */
-  WR_OP_ROTATE = 3       /* none needed; returns 0 */
+  WR_OP_ROTATE = 3,      /* none needed; returns 0 */
+  WR_OP_FINALIZE = 4     /* n = n_store; needed by wr_hessian_finalize with a rotation */
 };
 
 enum wr_hessian_flags { WR_H_ZERO = 1 };               /* zero S before accumulating */
@@ -93,15 +95,23 @@ int wr_hessian_accumulate(wr_ctx* ctx, const void* X, int x_dtype, int64_t rows,
                           double* S, int flags);
 
 /*
- * (a) Finalize and damp.  Writes the full symmetric H (n_store x n_store,
- * fp32, ld ldh):  H = pad(S / total_rows) + delta I with
- * delta = damp_frac * trace(S / total_rows) / n_store, where pad() zero-fills
- * rows/columns n..n_store-1 (the zero-padded input dims of a rotation).  The
- * damping is the Tikhonov regularisation the Wringer news article names for
- * the GPTQ solve.  `delta_out` (device fp32, nullable) receives delta.
+ * (a)+(b) Finalize, rotate and damp.  Writes the full symmetric H (n_store x
+ * n_store, fp32, ld ldh):
+ *   H = R pad(S / total_rows) R^T + delta I,
+ *   delta = damp_frac * trace(S / total_rows) / n_store,
+ * where pad() zero-fills rows/columns n..n_store-1 (the zero-padded input
+ * dims) and R is the random-sign Hadamard rotation of wr_hadamard_rotate with
+ * block had_block and signs (device int8, length n_store); had_block = 0 means
+ * R = I.  The rotation runs in fp64 and H is rounded to fp32 once: rotating an
+ * fp32 H would smear the rounding error of the large (outlier-channel)
+ * entries over the small ones.  The damping is the Tikhonov regularisation
+ * the Wringer news article names for the GPTQ solve (the trace is invariant
+ * under R).  `delta_out` (device fp32, nullable) receives delta.
+ * Workspace: 256 bytes, or WR_OP_FINALIZE (n = n_store) with a rotation.
  */
 int wr_hessian_finalize(wr_ctx* ctx, const double* S, int64_t n, int64_t total_rows, float damp_frac,
-                        int64_t n_store, float* H, int64_t ldh, float* delta_out);
+                        int64_t n_store, float* H, int64_t ldh, float* delta_out, int32_t had_block,
+                        const int8_t* signs);
 
 /*
  * (b) Random-sign Hadamard rotation (Pingala-8 post, section "Trick 1:
@@ -112,7 +122,8 @@ int wr_hessian_finalize(wr_ctx* ctx, const double* S, int64_t n, int64_t total_r
  * multiple of m, transformed in place:
  *   WR_ROT_ROWS          each row v -> R v        (weights: W -> W R^T)
  *   WR_ROT_ROWS_INVERSE  each row v -> R^T v
- *   WR_ROT_SYM           M -> R M R^T             (H; requires rows == n)
+ *   WR_ROT_SYM           M -> R M R^T             (requires rows == n; in fp32 --
+ *                                                  wr_hessian_finalize rotates H in fp64)
  */
 int wr_hadamard_rotate(wr_ctx* ctx, float* M, int64_t rows, int64_t n, int64_t ld, int32_t had_block,
                        const int8_t* signs, int mode);
@@ -127,7 +138,8 @@ int wr_hadamard_rotate(wr_ctx* ctx, float* M, int64_t rows, int64_t n, int64_t l
  * its error is pushed onto the later columns in the proportions set by the
  * damped H (n x n fp32, ld ldh, symmetric positive definite).
  * bits: device uint8 per row (2, 3 or 4).  n % group == 0, group % 8 == 0,
- * lazy_batch % group == 0 (lazy_batch in [group, 256]).
+ * lazy_batch % group == 0; this build implements group in {32, 64, 128} and
+ * lazy_batch = 128 (other valid values return WR_EUNSUPPORTED).
  * Outputs: codes (rows x n uint8, ld n), scales (rows x n/group fp16 bit
  * patterns).  dev_info as above.  Workspace: WR_OP_GPTQ.
  */

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwringer.
 
 WR_OK, WR_EINVAL, WR_EWORKSPACE, WR_EHIP, WR_EUNSUPPORTED = 0, 1, 2, 3, 4
 WR_F32, WR_BF16 = 0, 1
-WR_OP_HESSIAN, WR_OP_GPTQ, WR_OP_WRING, WR_OP_ROTATE = 0, 1, 2, 3
+WR_OP_HESSIAN, WR_OP_GPTQ, WR_OP_WRING, WR_OP_ROTATE, WR_OP_FINALIZE = 0, 1, 2, 3, 4
 WR_H_ZERO = 1
 WR_ROT_ROWS, WR_ROT_ROWS_INVERSE, WR_ROT_SYM = 0, 1, 2
 WR_RECODE_NEAREST = 1
@@ -57,7 +57,7 @@ def load():
         "wr_workspace_bytes": (SZ, [I, I64, I64, c.c_int32, c.c_int32, c.c_int32]),
         "wr_set_workspace": (I, [P, P, SZ]),
         "wr_hessian_accumulate": (I, [P, P, I, I64, I64, I64, P, I]),
-        "wr_hessian_finalize": (I, [P, P, I64, I64, F, I64, P, I64, P]),
+        "wr_hessian_finalize": (I, [P, P, I64, I64, F, I64, P, I64, P, c.c_int32, P]),
         "wr_hadamard_rotate": (I, [P, P, I64, I64, I64, c.c_int32, P, I]),
         "wr_gptq_sweep": (I, [P, P, I, I64, I64, I64, P, I64, P, c.c_int32, c.c_int32, P, P, P]),
         "wr_wring_solve": (I, [P, P, I, I64, P, P, c.c_int32, F, I, P, I64, I64, I64, P, c.c_int32, F, I, P, P, P]),
@@ -157,16 +157,23 @@ def wr_hessian_accumulate(ctx, X, S, zero=False):
         ctx.handle, _ptr(X), _wdtype(X), rows, n, ldx, _ptr(S), WR_H_ZERO if zero else 0))
 
 
-def wr_hessian_finalize(ctx, S, total_rows, damp_frac, H, delta=None):
-    """H (n_store x n_store fp32) = pad(S / total_rows) + delta I."""
+def wr_hessian_finalize(ctx, S, total_rows, damp_frac, H, delta=None, had_block=0, signs=None):
+    """H (n_store x n_store fp32) = R pad(S / total_rows) R^T + delta I (R = I when had_block is 0)."""
     _dev(S, "S", (torch.float64,))
     _dev(H, "H", (torch.float32,))
     _dev(delta, "delta", (torch.float32,))
+    _dev(signs, "signs", (torch.int8,))
     n = S.shape[0]
     ldh = _rowmajor(H, "H")
-    ctx.ensure_workspace(256)
+    if had_block:
+        if signs is None or signs.numel() != H.shape[0] or not signs.is_contiguous():
+            raise ValueError("signs must hold n_store contiguous int8 values")
+        ctx.ensure_workspace(wr_workspace_bytes(WR_OP_FINALIZE, 0, H.shape[0]))
+    else:
+        ctx.ensure_workspace(256)
     _check("wr_hessian_finalize", load().wr_hessian_finalize(
-        ctx.handle, _ptr(S), n, int(total_rows), float(damp_frac), H.shape[0], _ptr(H), ldh, _ptr(delta)))
+        ctx.handle, _ptr(S), n, int(total_rows), float(damp_frac), H.shape[0], _ptr(H), ldh, _ptr(delta),
+        int(had_block or 0), _ptr(signs)))
 
 
 def wr_hadamard_rotate(ctx, M, had_block, signs, mode=WR_ROT_ROWS):

@@ -7,7 +7,9 @@ size_t wr_hessian_ws_bytes(int64_t rows, int64_t n, int x_dtype, int num_cu);
 size_t wr_gptq_ws_bytes(int64_t rows, int64_t n);
 size_t wr_wring_ws_bytes(int64_t rows, int64_t n, int32_t group, int32_t rank);
 int wr_hessian_accumulate_impl(wr_ctx*, const void*, int, int64_t, int64_t, int64_t, double*, int);
-int wr_hessian_finalize_impl(wr_ctx*, const double*, int64_t, int64_t, float, int64_t, float*, int64_t, float*);
+int wr_hessian_finalize_impl(wr_ctx*, const double*, int64_t, int64_t, float, int64_t, float*, int64_t, float*, int32_t,
+                             const int8_t*);
+size_t wr_finalize_ws_bytes(int64_t n_store);
 int wr_hadamard_rotate_impl(wr_ctx*, float*, int64_t, int64_t, int64_t, int32_t, const int8_t*, int);
 int wr_gptq_sweep_impl(wr_ctx*, const void*, int, int64_t, int64_t, int64_t, const float*, int64_t, const uint8_t*,
                        int32_t, int32_t, uint8_t*, uint16_t*, int32_t*);
@@ -78,6 +80,7 @@ size_t wr_workspace_bytes(int op, int64_t rows, int64_t n, int32_t group, int32_
       return a > b ? a : b;
     }
     case WR_OP_GPTQ: return wr_gptq_ws_bytes(rows, n);
+    case WR_OP_FINALIZE: return wr_finalize_ws_bytes(n);
     case WR_OP_WRING: return group > 0 ? wr_wring_ws_bytes(rows, n, group, rank > 0 ? rank : 0) : 0;
     default: return 0;
   }
@@ -103,13 +106,15 @@ int wr_hessian_accumulate(wr_ctx* ctx, const void* X, int x_dtype, int64_t rows,
 }
 
 int wr_hessian_finalize(wr_ctx* ctx, const double* S, int64_t n, int64_t total_rows, float damp_frac, int64_t n_store,
-                        float* H, int64_t ldh, float* delta_out) {
+                        float* H, int64_t ldh, float* delta_out, int32_t had_block, const int8_t* signs) {
   if (!ctx || !S || !H || n <= 0 || n > 65536 || total_rows <= 0 || n_store < n || n_store > 65535 || ldh < n_store ||
       !(damp_frac >= 0.0f))
     return WR_EINVAL;
+  if (had_block != 0 && (!signs || !pow2(had_block) || had_block < 2 || had_block > 4096 || n_store % had_block != 0))
+    return WR_EINVAL;
   DeviceScope ds(ctx->device);
   if (!ds.ok) return WR_EHIP;
-  return wr_hessian_finalize_impl(ctx, S, n, total_rows, damp_frac, n_store, H, ldh, delta_out);
+  return wr_hessian_finalize_impl(ctx, S, n, total_rows, damp_frac, n_store, H, ldh, delta_out, had_block, signs);
 }
 
 int wr_hadamard_rotate(wr_ctx* ctx, float* M, int64_t rows, int64_t n, int64_t ld, int32_t had_block,

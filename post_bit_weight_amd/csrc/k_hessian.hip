@@ -259,6 +259,25 @@ __global__ __launch_bounds__(1024) void trace_kernel(const double* __restrict__ 
   }
 }
 
+// Hd (n_store x n_store fp64, full) = pad(S / N), for a rotation in fp64 before rounding to fp32.
+__global__ void expand_kernel(const double* __restrict__ S, int n, int64_t n_store, double inv_rows,
+                              double* __restrict__ Hd) {
+  const int64_t i = blockIdx.y;
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n_store; j += (int64_t)gridDim.x * blockDim.x) {
+    double v = 0.0;
+    if (i < n && j < n) v = (i >= j ? S[i * n + j] : S[j * n + i]) * inv_rows;
+    Hd[i * n_store + j] = v;
+  }
+}
+
+__global__ void damp_round_kernel(const double* __restrict__ Hd, int64_t n_store, const double* __restrict__ delta64,
+                                  float* __restrict__ H, int64_t ldh) {
+  const int64_t i = blockIdx.y;
+  const double delta = *delta64;
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n_store; j += (int64_t)gridDim.x * blockDim.x)
+    H[i * ldh + j] = (float)(Hd[i * n_store + j] + (i == j ? delta : 0.0));
+}
+
 __global__ void finalize_kernel(const double* __restrict__ S, int n, int64_t n_store, double inv_rows,
                                 const double* __restrict__ delta64, float* __restrict__ H, int64_t ldh) {
   const int64_t i = blockIdx.y;
@@ -344,17 +363,36 @@ int wr_hessian_accumulate_impl(wr_ctx* ctx, const void* X, int x_dtype, int64_t 
   return WR_OK;
 }
 
+int wr_rotate_sym_f64(wr_ctx* ctx, double* M, int64_t n, int64_t ld, int32_t m, const int8_t* signs);
+
+size_t wr_finalize_ws_bytes(int64_t n_store) { return 256 + (size_t)n_store * n_store * sizeof(double); }
+
 int wr_hessian_finalize_impl(wr_ctx* ctx, const double* S, int64_t n, int64_t total_rows, float damp_frac,
-                             int64_t n_store, float* H, int64_t ldh, float* delta_out) {
-  if (ctx->ws_bytes < 256) return WR_EWORKSPACE;
+                             int64_t n_store, float* H, int64_t ldh, float* delta_out, int32_t had_block,
+                             const int8_t* signs) {
+  const size_t need = had_block ? wr_finalize_ws_bytes(n_store) : 256;
+  if (ctx->ws_bytes < need) return WR_EWORKSPACE;
   double* delta64 = static_cast<double*>(ctx->ws);
   const double inv_rows = 1.0 / (double)total_rows;
   hipLaunchKernelGGL(trace_kernel, dim3(1), dim3(1024), 0, ctx->stream, S, (int)n, inv_rows,
                      (double)damp_frac / (double)n_store, delta64, delta_out);
   WR_CHECK_LAUNCH();
   const unsigned gx = (unsigned)std::min<int64_t>((n_store + 255) / 256, 64);
-  hipLaunchKernelGGL(finalize_kernel, dim3(gx, (unsigned)n_store), dim3(256), 0, ctx->stream, S, (int)n, n_store,
-                     inv_rows, delta64, H, ldh);
+  if (!had_block) {
+    hipLaunchKernelGGL(finalize_kernel, dim3(gx, (unsigned)n_store), dim3(256), 0, ctx->stream, S, (int)n, n_store,
+                       inv_rows, delta64, H, ldh);
+    WR_CHECK_LAUNCH();
+    return WR_OK;
+  }
+  // H = R pad(S/N) R^T + delta I, rotated in fp64 and rounded to fp32 once
+  double* Hd = reinterpret_cast<double*>(static_cast<char*>(ctx->ws) + 256);
+  hipLaunchKernelGGL(expand_kernel, dim3(gx, (unsigned)n_store), dim3(256), 0, ctx->stream, S, (int)n, n_store,
+                     inv_rows, Hd);
+  WR_CHECK_LAUNCH();
+  const int rc = wr_rotate_sym_f64(ctx, Hd, n_store, n_store, had_block, signs);
+  if (rc) return rc;
+  hipLaunchKernelGGL(damp_round_kernel, dim3(gx, (unsigned)n_store), dim3(256), 0, ctx->stream, Hd, n_store, delta64,
+                     H, ldh);
   WR_CHECK_LAUNCH();
   return WR_OK;
 }

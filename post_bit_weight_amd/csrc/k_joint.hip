@@ -7,18 +7,21 @@
 // caveats": scales projected to fp16 at solve time.
 //
 // Per row, with levels l_j = 2 c_j - L, Q[j, block(j)] = l_j, G = Q^T H Q,
-// mu = trace(G)/nb and residual R = T - Q s0, the minimiser of
+// h = Q^T H t and mu = trace(G)/nb, the minimiser of
 //   (t - Q s)^T H (t - Q s) + lambda mu ||s - s0||^2
-// is s = s0 + (G + lambda mu I)^-1 Q^T H R.  Solving for the step from s0
-// (instead of for s) keeps the rounding error of G and of the right-hand side
-// proportional to the step, which is what lets both be formed on the bf16
-// matrix cores:
-//   G[r][b][c] = sum_{j in b} l_j (H_{b,c} l_c)_j    two passes, H = H_hi + H_lo
-//   h[r][b]    = sum_{j in b} l_j (H R_r)_j          three passes, R = R_hi + R_lo
-// (levels are exact in bf16; H_hi/H_lo and R_hi/R_lo are bf16 splits).  The
-// MFMA computes D[j][r] = sum_l H[j][l] X[r][l] with j down the accumulator
-// rows, so the level-weighted sum over a block's j stays mostly inside a lane.
-// Each row's nb x nb system is then factored and solved in fp64.
+// is s = (G + lambda mu I)^-1 (h + lambda mu s0).  G and h are formed on the
+// bf16 matrix cores from exact bf16 levels and three-way bf16 splits
+// x = x_0 + x_1 + x_2 (24 significant bits, as fp32):
+//   G[r][b][c] = sum_{j in b} l_j (H_{b,c} l_c)_j    three passes (H_0, H_1, H_2)
+//   h[r][b]    = sum_{j in b} l_j (H t_r)_j          six passes: H_i t_j for i + j <= 2
+// with fp32 accumulation.  Both need the full split: a two-way split (16
+// bits) is an H perturbed by ~1e-5, and after a Hadamard rotation that moves
+// some fp16 scales by two ulps.  The MFMA computes
+// D[j][r] = sum_l H[j][l] X[r][l] with j down the accumulator rows, so the
+// level-weighted sum over a block's j stays mostly inside a lane.  Each row's
+// nb x nb system is then factored and solved in fp64.  (Solving for the step
+// s - s0 instead would shrink the error only when the scales move little; the
+// joint solve routinely moves them by their own size.)
 #include "common.hpp"
 
 int wr_gemm_f32(hipStream_t st, int M, int N, int K, const float* A, int64_t lda, const float* B, int64_t ldb,
@@ -28,6 +31,18 @@ int wr_gemm_f32(hipStream_t st, int M, int N, int K, const float* A, int64_t lda
 namespace wr {
 
 __global__ void set_int_kernel(int32_t* p, int32_t v) { *p = v; }
+
+// x = x0 + x1 + x2 with each part rounded to bf16 in turn (exact for any fp32 x
+// whose parts stay in the normal range).
+__device__ __forceinline__ void split3(float x, uint16_t& p0, uint16_t& p1, uint16_t& p2) {
+  const uint32_t a = f32_to_bf16_bits(x);
+  const float r1 = x - bf16_bits_to_f32(a);
+  const uint32_t b = f32_to_bf16_bits(r1);
+  const float r2 = r1 - bf16_bits_to_f32(b);
+  p0 = (uint16_t)a;
+  p1 = (uint16_t)b;
+  p2 = (uint16_t)f32_to_bf16_bits(r2);
+}
 
 __global__ void to_f32_kernel(const void* __restrict__ src, int dtype, int64_t count, float* __restrict__ dst) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
@@ -53,11 +68,11 @@ __global__ void target_kernel(const void* __restrict__ target, int t_dtype, int6
   }
 }
 
-// Optional nearest-point recode on the incoming scales, then levels and the bf16-split residual.
+// Optional nearest-point recode on the incoming scales, then exact bf16 levels and the bf16-split target.
 __global__ void recode_residual_kernel(const float* __restrict__ T, uint8_t* __restrict__ codes,
                                        const uint16_t* __restrict__ scales, const uint8_t* __restrict__ bits,
                                        int64_t rows, int n, int group, int recode, uint16_t* __restrict__ Lev,
-                                       uint16_t* __restrict__ Rhi, uint16_t* __restrict__ Rlo,
+                                       uint16_t* __restrict__ T0, uint16_t* __restrict__ T1, uint16_t* __restrict__ T2,
                                        int32_t* __restrict__ dev_info) {
   const int64_t r = blockIdx.y;
   const int nb = n / group;
@@ -75,38 +90,30 @@ __global__ void recode_residual_kernel(const float* __restrict__ T, uint8_t* __r
     } else {
       c = codes[e];
     }
-    const float lev = (float)(2 * c - L);
-    const float res = t - lev * s;  // lev * s is exact in fp32
-    const uint32_t hi = f32_to_bf16_bits(res);
-    Lev[e] = (uint16_t)f32_to_bf16_bits(lev);
-    Rhi[e] = (uint16_t)hi;
-    Rlo[e] = (uint16_t)f32_to_bf16_bits(res - bf16_bits_to_f32(hi));
+    Lev[e] = (uint16_t)f32_to_bf16_bits((float)(2 * c - L));
+    split3(t, T0[e], T1[e], T2[e]);
   }
   if (bad) atomicCAS(dev_info, 0, -1);
 }
 
-__global__ void split_h_kernel(const float* __restrict__ H, int64_t ldh, int n, uint16_t* __restrict__ Hhi,
-                               uint16_t* __restrict__ Hlo) {
+__global__ void split_h_kernel(const float* __restrict__ H, int64_t ldh, int n, uint16_t* __restrict__ H0,
+                               uint16_t* __restrict__ H1, uint16_t* __restrict__ H2) {
   const int64_t i = blockIdx.y;
-  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x) {
-    const float h = H[i * ldh + j];
-    const uint32_t hi = f32_to_bf16_bits(h);
-    Hhi[i * n + j] = (uint16_t)hi;
-    Hlo[i * n + j] = (uint16_t)f32_to_bf16_bits(h - bf16_bits_to_f32(hi));
-  }
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x)
+    split3(H[i * ldh + j], H0[i * n + j], H1[i * n + j], H2[i * n + j]);
 }
 
 // One workgroup: 128 rows (four waves of 32) x one block b.  Loops over all column blocks c.
 template <int G>
-__global__ __launch_bounds__(256) void gram_kernel(const uint16_t* __restrict__ Lev, const uint16_t* __restrict__ Rhi,
-                                                   const uint16_t* __restrict__ Rlo, int64_t rows, int n,
-                                                   const uint16_t* __restrict__ Hhi, const uint16_t* __restrict__ Hlo,
+__global__ __launch_bounds__(256) void gram_kernel(const uint16_t* __restrict__ Lev, const uint16_t* __restrict__ T0,
+                                                   const uint16_t* __restrict__ T1, const uint16_t* __restrict__ T2,
+                                                   int64_t rows, int n, const uint16_t* __restrict__ H0,
+                                                   const uint16_t* __restrict__ H1, const uint16_t* __restrict__ H2,
                                                    float* __restrict__ Gm, float* __restrict__ rhs,
                                                    const int32_t* __restrict__ dev_info) {
   constexpr int IB = G / 32;
   constexpr int PITCH = G + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t sHh[G * PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t sHl[G * PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t sH[3][G * PITCH];
   if (*dev_info != 0) return;
   const int nb = n / G;
   const int b = blockIdx.y;
@@ -134,8 +141,9 @@ __global__ __launch_bounds__(256) void gram_kernel(const uint16_t* __restrict__ 
     for (int e = tid; e < G * G / 8; e += 256) {
       const int j = e / (G / 8), l8 = (e % (G / 8)) * 8;
       const int64_t src = (int64_t)(b * G + j) * n + c * G + l8;
-      *reinterpret_cast<u32x4*>(&sHh[j * PITCH + l8]) = *reinterpret_cast<const u32x4*>(Hhi + src);
-      *reinterpret_cast<u32x4*>(&sHl[j * PITCH + l8]) = *reinterpret_cast<const u32x4*>(Hlo + src);
+      *reinterpret_cast<u32x4*>(&sH[0][j * PITCH + l8]) = *reinterpret_cast<const u32x4*>(H0 + src);
+      *reinterpret_cast<u32x4*>(&sH[1][j * PITCH + l8]) = *reinterpret_cast<const u32x4*>(H1 + src);
+      *reinterpret_cast<u32x4*>(&sH[2][j * PITCH + l8]) = *reinterpret_cast<const u32x4*>(H2 + src);
     }
     __syncthreads();
     const bool doG = c >= b;
@@ -149,21 +157,28 @@ __global__ __launch_bounds__(256) void gram_kernel(const uint16_t* __restrict__ 
     for (int ks = 0; ks < G / 16; ++ks) {
       const int lk = ks * 16 + 8 * (lane >> 5);
       const int64_t src = rr * n + c * G + lk;
-      const bf16x8 fRh = as_bf16x8(rok ? *reinterpret_cast<const u32x4*>(Rhi + src) : zero4);
-      const bf16x8 fRl = as_bf16x8(rok ? *reinterpret_cast<const u32x4*>(Rlo + src) : zero4);
+      const bf16x8 t0 = as_bf16x8(rok ? *reinterpret_cast<const u32x4*>(T0 + src) : zero4);
+      const bf16x8 t1 = as_bf16x8(rok ? *reinterpret_cast<const u32x4*>(T1 + src) : zero4);
+      const bf16x8 t2 = as_bf16x8(rok ? *reinterpret_cast<const u32x4*>(T2 + src) : zero4);
       bf16x8 fL = as_bf16x8(zero4);
       if (doG) fL = as_bf16x8(rok ? *reinterpret_cast<const u32x4*>(Lev + src) : zero4);
 #pragma unroll
       for (int ib = 0; ib < IB; ++ib) {
-        const int ja = ib * 32 + (lane & 31);
-        const bf16x8 ah = as_bf16x8(*reinterpret_cast<const u32x4*>(&sHh[ja * PITCH + lk]));
-        const bf16x8 al = as_bf16x8(*reinterpret_cast<const u32x4*>(&sHl[ja * PITCH + lk]));
-        accR[ib] = mfma32x32x16_bf16(ah, fRh, accR[ib]);
-        accR[ib] = mfma32x32x16_bf16(al, fRh, accR[ib]);
-        accR[ib] = mfma32x32x16_bf16(ah, fRl, accR[ib]);
+        const int ja = (ib * 32 + (lane & 31)) * PITCH + lk;
+        const bf16x8 h0 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sH[0][ja]));
+        const bf16x8 h1 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sH[1][ja]));
+        const bf16x8 h2 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sH[2][ja]));
+        // smallest terms first
+        accR[ib] = mfma32x32x16_bf16(h2, t0, accR[ib]);
+        accR[ib] = mfma32x32x16_bf16(h1, t1, accR[ib]);
+        accR[ib] = mfma32x32x16_bf16(h0, t2, accR[ib]);
+        accR[ib] = mfma32x32x16_bf16(h1, t0, accR[ib]);
+        accR[ib] = mfma32x32x16_bf16(h0, t1, accR[ib]);
+        accR[ib] = mfma32x32x16_bf16(h0, t0, accR[ib]);
         if (doG) {
-          accG[ib] = mfma32x32x16_bf16(ah, fL, accG[ib]);
-          accG[ib] = mfma32x32x16_bf16(al, fL, accG[ib]);
+          accG[ib] = mfma32x32x16_bf16(h2, fL, accG[ib]);
+          accG[ib] = mfma32x32x16_bf16(h1, fL, accG[ib]);
+          accG[ib] = mfma32x32x16_bf16(h0, fL, accG[ib]);
         }
       }
     }
@@ -190,7 +205,7 @@ __global__ __launch_bounds__(256) void gram_kernel(const uint16_t* __restrict__ 
   if (lane < 32 && rok) rhs[(size_t)r * nb + b] = part;
 }
 
-// Per row: (G + lambda mu I) u = h in fp64 (packed lower Cholesky in LDS), s = s0 + u -> fp16.
+// Per row: (G + lambda mu I) s = h + lambda mu s0 in fp64 (packed lower Cholesky in LDS), s -> fp16.
 __global__ __launch_bounds__(64) void row_solve_kernel(const float* __restrict__ Gm, const float* __restrict__ rhs,
                                                        int64_t rows, int nb, float lambda, uint16_t* __restrict__ scales,
                                                        const int32_t* __restrict__ dev_info) {
@@ -209,7 +224,8 @@ __global__ __launch_bounds__(64) void row_solve_kernel(const float* __restrict__
   const double reg = (double)lambda * tr / nb;
   for (int i = 0; i < nb; ++i)
     for (int j = lane; j <= i; j += 64) a[(size_t)i * (i + 1) / 2 + j] = (double)g[(size_t)j * nb + i] + (i == j ? reg : 0.0);
-  for (int i = lane; i < nb; i += 64) y[i] = (double)rhs[(size_t)row * nb + i];
+  for (int i = lane; i < nb; i += 64)
+    y[i] = (double)rhs[(size_t)row * nb + i] + reg * (double)f16_bits_to_f32(scales[(size_t)row * nb + i]);
   if (lane == 0) failed = 0;
   __syncthreads();
   for (int k = 0; k < nb; ++k) {
@@ -238,7 +254,7 @@ __global__ __launch_bounds__(64) void row_solve_kernel(const float* __restrict__
     for (int i = k + 1 + lane; i < nb; i += 64) y[i] -= a[(size_t)i * (i + 1) / 2 + k] * zk;
     __syncthreads();
   }
-  // L^T u = z
+  // L^T s = z
   for (int k = nb - 1; k >= 0; --k) {
     if (lane == 0) y[k] /= a[(size_t)k * (k + 1) / 2 + k];
     __syncthreads();
@@ -246,11 +262,7 @@ __global__ __launch_bounds__(64) void row_solve_kernel(const float* __restrict__
     for (int i = lane; i < k; i += 64) y[i] -= a[(size_t)k * (k + 1) / 2 + i] * uk;
     __syncthreads();
   }
-  for (int i = lane; i < nb; i += 64) {
-    uint16_t* sp = scales + (size_t)row * nb + i;
-    const double s = (double)f16_bits_to_f32(*sp) + y[i];
-    *sp = f64_to_f16_bits_clamped(s);
-  }
+  for (int i = lane; i < nb; i += 64) scales[(size_t)row * nb + i] = f64_to_f16_bits_clamped(y[i]);
 }
 
 }  // namespace wr
@@ -258,7 +270,7 @@ __global__ __launch_bounds__(64) void row_solve_kernel(const float* __restrict__
 using namespace wr;
 
 struct WringLayout {
-  size_t T, Lev, Rhi, Rlo, Hhi, Hlo, Gm, rhs, Bf, Af, total;
+  size_t T, Lev, T0, T1, T2, H0, H1, H2, Gm, rhs, Bf, Af, total;
 };
 
 static WringLayout wring_layout(int64_t rows, int64_t n, int32_t group, int32_t rank) {
@@ -272,10 +284,12 @@ static WringLayout wring_layout(int64_t rows, int64_t n, int32_t group, int32_t 
   const int64_t nb = n / group;
   l.T = take((size_t)rows * n * 4);
   l.Lev = take((size_t)rows * n * 2);
-  l.Rhi = take((size_t)rows * n * 2);
-  l.Rlo = take((size_t)rows * n * 2);
-  l.Hhi = take((size_t)n * n * 2);
-  l.Hlo = take((size_t)n * n * 2);
+  l.T0 = take((size_t)rows * n * 2);
+  l.T1 = take((size_t)rows * n * 2);
+  l.T2 = take((size_t)rows * n * 2);
+  l.H0 = take((size_t)n * n * 2);
+  l.H1 = take((size_t)n * n * 2);
+  l.H2 = take((size_t)n * n * 2);
   l.Gm = take((size_t)rows * nb * nb * 4);
   l.rhs = take((size_t)rows * nb * 4);
   l.Bf = take((size_t)rows * (rank > 0 ? rank : 0) * 4);
@@ -302,10 +316,12 @@ int wr_wring_solve_impl(wr_ctx* ctx, const void* target, int t_dtype, int64_t ld
   char* ws = static_cast<char*>(ctx->ws);
   float* T = reinterpret_cast<float*>(ws + lay.T);
   uint16_t* Lev = reinterpret_cast<uint16_t*>(ws + lay.Lev);
-  uint16_t* Rhi = reinterpret_cast<uint16_t*>(ws + lay.Rhi);
-  uint16_t* Rlo = reinterpret_cast<uint16_t*>(ws + lay.Rlo);
-  uint16_t* Hhi = reinterpret_cast<uint16_t*>(ws + lay.Hhi);
-  uint16_t* Hlo = reinterpret_cast<uint16_t*>(ws + lay.Hlo);
+  uint16_t* T0 = reinterpret_cast<uint16_t*>(ws + lay.T0);
+  uint16_t* T1 = reinterpret_cast<uint16_t*>(ws + lay.T1);
+  uint16_t* T2 = reinterpret_cast<uint16_t*>(ws + lay.T2);
+  uint16_t* H0 = reinterpret_cast<uint16_t*>(ws + lay.H0);
+  uint16_t* H1 = reinterpret_cast<uint16_t*>(ws + lay.H1);
+  uint16_t* H2 = reinterpret_cast<uint16_t*>(ws + lay.H2);
   float* Gm = reinterpret_cast<float*>(ws + lay.Gm);
   float* rh = reinterpret_cast<float*>(ws + lay.rhs);
 
@@ -328,15 +344,15 @@ int wr_wring_solve_impl(wr_ctx* ctx, const void* target, int t_dtype, int64_t ld
     if (rc) return rc;
   }
   hipLaunchKernelGGL(recode_residual_kernel, dim3(gx, (unsigned)rows), dim3(256), 0, st, T, codes, scales, bits, rows,
-                     n, group, (flags & WR_RECODE_NEAREST) ? 1 : 0, Lev, Rhi, Rlo, dev_info);
+                     n, group, (flags & WR_RECODE_NEAREST) ? 1 : 0, Lev, T0, T1, T2, dev_info);
   WR_CHECK_LAUNCH();
-  hipLaunchKernelGGL(split_h_kernel, dim3(gx, (unsigned)n), dim3(256), 0, st, H, ldh, n, Hhi, Hlo);
+  hipLaunchKernelGGL(split_h_kernel, dim3(gx, (unsigned)n), dim3(256), 0, st, H, ldh, n, H0, H1, H2);
   WR_CHECK_LAUNCH();
   dim3 ggrid((unsigned)((rows + 127) / 128), (unsigned)nb);
   switch (group) {
-    case 32: hipLaunchKernelGGL(gram_kernel<32>, ggrid, dim3(256), 0, st, Lev, Rhi, Rlo, rows, n, Hhi, Hlo, Gm, rh, dev_info); break;
-    case 64: hipLaunchKernelGGL(gram_kernel<64>, ggrid, dim3(256), 0, st, Lev, Rhi, Rlo, rows, n, Hhi, Hlo, Gm, rh, dev_info); break;
-    default: hipLaunchKernelGGL(gram_kernel<128>, ggrid, dim3(256), 0, st, Lev, Rhi, Rlo, rows, n, Hhi, Hlo, Gm, rh, dev_info); break;
+    case 32: hipLaunchKernelGGL(gram_kernel<32>, ggrid, dim3(256), 0, st, Lev, T0, T1, T2, rows, n, H0, H1, H2, Gm, rh, dev_info); break;
+    case 64: hipLaunchKernelGGL(gram_kernel<64>, ggrid, dim3(256), 0, st, Lev, T0, T1, T2, rows, n, H0, H1, H2, Gm, rh, dev_info); break;
+    default: hipLaunchKernelGGL(gram_kernel<128>, ggrid, dim3(256), 0, st, Lev, T0, T1, T2, rows, n, H0, H1, H2, Gm, rh, dev_info); break;
   }
   WR_CHECK_LAUNCH();
   const size_t shbytes = ((size_t)nb * (nb + 1) / 2 + nb) * sizeof(double);

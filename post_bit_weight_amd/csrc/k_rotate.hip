@@ -13,34 +13,37 @@ namespace wr {
 
 constexpr int ROT_THREADS = 256;
 
-__global__ __launch_bounds__(ROT_THREADS) void fwht_rows_kernel(float* __restrict__ M, int64_t ld, int m, int log2m,
+template <typename T>
+__global__ __launch_bounds__(ROT_THREADS) void fwht_rows_kernel(T* __restrict__ M, int64_t ld, int m, int log2m,
                                                                 const int8_t* __restrict__ signs, int inverse,
-                                                                float scale) {
-  extern __shared__ float buf[];
+                                                                T scale) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char rot_smem[];
+  T* buf = reinterpret_cast<T*>(rot_smem);
   const int64_t row = blockIdx.y;
   const int64_t col0 = (int64_t)blockIdx.x * m;
-  float* p = M + row * ld + col0;
+  T* p = M + row * ld + col0;
   const int8_t* d = signs + col0;
-  for (int i = threadIdx.x; i < m; i += ROT_THREADS) buf[i] = inverse ? p[i] : p[i] * (float)d[i];
+  for (int i = threadIdx.x; i < m; i += ROT_THREADS) buf[i] = inverse ? p[i] : p[i] * (T)d[i];
   __syncthreads();
   for (int s = 0; s < log2m; ++s) {
     const int h = 1 << s;
     for (int q = threadIdx.x; q < (m >> 1); q += ROT_THREADS) {
       const int i = ((q >> s) << (s + 1)) | (q & (h - 1));
-      const float a = buf[i], b = buf[i + h];
+      const T a = buf[i], b = buf[i + h];
       buf[i] = a + b;
       buf[i + h] = a - b;
     }
     __syncthreads();
   }
-  for (int i = threadIdx.x; i < m; i += ROT_THREADS) p[i] = inverse ? buf[i] * scale * (float)d[i] : buf[i] * scale;
+  for (int i = threadIdx.x; i < m; i += ROT_THREADS) p[i] = inverse ? buf[i] * scale * (T)d[i] : buf[i] * scale;
 }
 
 // In-place transpose of a square n x n matrix: the workgroup for tile pair (I, J), I <= J, swaps them.
 constexpr int TR_T = 32;
-__global__ void transpose_inplace_kernel(float* __restrict__ M, int64_t n, int64_t ld, int ntile) {
-  __shared__ float a[TR_T][TR_T + 1];
-  __shared__ float b[TR_T][TR_T + 1];
+template <typename T>
+__global__ void transpose_inplace_kernel(T* __restrict__ M, int64_t n, int64_t ld, int ntile) {
+  __shared__ T a[TR_T][TR_T + 1];
+  __shared__ T b[TR_T][TR_T + 1];
   int t = blockIdx.x, I = 0;
   while (t >= ntile - I) {
     t -= ntile - I;
@@ -67,32 +70,39 @@ __global__ void transpose_inplace_kernel(float* __restrict__ M, int64_t n, int64
 
 using namespace wr;
 
-static int launch_rows(wr_ctx* ctx, float* M, int64_t rows, int64_t n, int64_t ld, int m, const int8_t* signs,
+template <typename T>
+static int launch_rows(wr_ctx* ctx, T* M, int64_t rows, int64_t n, int64_t ld, int m, const int8_t* signs,
                        int inverse) {
   int log2m = 0;
   while ((1 << log2m) < m) ++log2m;
-  const float scale = 1.0f / std::sqrt((float)m);
+  const T scale = (T)1 / std::sqrt((T)m);
   dim3 grid((unsigned)(n / m), (unsigned)rows);
-  hipLaunchKernelGGL(fwht_rows_kernel, grid, dim3(ROT_THREADS), (size_t)m * sizeof(float), ctx->stream, M, ld, m,
-                     log2m, signs, inverse, scale);
+  hipLaunchKernelGGL(fwht_rows_kernel<T>, grid, dim3(ROT_THREADS), (size_t)m * sizeof(T), ctx->stream, M, ld, m, log2m,
+                     signs, inverse, scale);
   WR_CHECK_LAUNCH();
   return WR_OK;
 }
 
-int wr_hadamard_rotate_impl(wr_ctx* ctx, float* M, int64_t rows, int64_t n, int64_t ld, int32_t m,
-                            const int8_t* signs, int mode) {
-  if (mode == WR_ROT_ROWS || mode == WR_ROT_ROWS_INVERSE) return launch_rows(ctx, M, rows, n, ld, m, signs, mode);
-  // R M R^T = rows( (rows(M))^T ) for symmetric M; for general square M the
-  // column pass is the row pass of the transpose, transposed back.
-  int rc = launch_rows(ctx, M, n, n, ld, m, signs, 0);  // M R^T
-  if (rc) return rc;
+// R M R^T for a square M: rows pass (M R^T), transpose, rows pass, transpose.
+template <typename T>
+static int rotate_sym(wr_ctx* ctx, T* M, int64_t n, int64_t ld, int m, const int8_t* signs) {
   const int ntile = (int)((n + TR_T - 1) / TR_T);
   const unsigned pairs = (unsigned)(ntile * (ntile + 1) / 2);
-  hipLaunchKernelGGL(transpose_inplace_kernel, dim3(pairs), dim3(256), 0, ctx->stream, M, n, ld, ntile);
-  WR_CHECK_LAUNCH();
-  rc = launch_rows(ctx, M, n, n, ld, m, signs, 0);       // (M R^T)^T R^T = R M^T R^T
-  if (rc) return rc;
-  hipLaunchKernelGGL(transpose_inplace_kernel, dim3(pairs), dim3(256), 0, ctx->stream, M, n, ld, ntile);
-  WR_CHECK_LAUNCH();
-  return WR_OK;                                          // (R M^T R^T)^T = R M R^T
+  for (int pass = 0; pass < 2; ++pass) {
+    int rc = launch_rows<T>(ctx, M, n, n, ld, m, signs, 0);
+    if (rc) return rc;
+    hipLaunchKernelGGL(transpose_inplace_kernel<T>, dim3(pairs), dim3(256), 0, ctx->stream, M, n, ld, ntile);
+    WR_CHECK_LAUNCH();
+  }
+  return WR_OK;
+}
+
+int wr_rotate_sym_f64(wr_ctx* ctx, double* M, int64_t n, int64_t ld, int32_t m, const int8_t* signs) {
+  return rotate_sym<double>(ctx, M, n, ld, m, signs);
+}
+
+int wr_hadamard_rotate_impl(wr_ctx* ctx, float* M, int64_t rows, int64_t n, int64_t ld, int32_t m,
+                            const int8_t* signs, int mode) {
+  if (mode == WR_ROT_ROWS || mode == WR_ROT_ROWS_INVERSE) return launch_rows<float>(ctx, M, rows, n, ld, m, signs, mode);
+  return rotate_sym<float>(ctx, M, n, ld, m, signs);
 }

@@ -31,9 +31,7 @@ def accumulate_hessian(ctx, chunks, n, S=None):
 def finalize_hessian(ctx, S, total_rows, damp_frac, n_store, had_block=None, signs=None):
     H = torch.empty(n_store, n_store, dtype=torch.float32, device=ctx.device)
     delta = torch.empty(1, dtype=torch.float32, device=ctx.device)
-    wr.wr_hessian_finalize(ctx, S, total_rows, damp_frac, H, delta)
-    if had_block:
-        wr.wr_hadamard_rotate(ctx, H, had_block, signs, wr.WR_ROT_SYM)
+    wr.wr_hessian_finalize(ctx, S, total_rows, damp_frac, H, delta, had_block or 0, signs)
     return H, delta
 
 
