@@ -98,7 +98,9 @@ int wr_hessian_accumulate(wr_ctx* ctx, const void* X, int x_dtype, int64_t rows,
   if (!ctx || !S || !valid_dtype(x_dtype) || rows < 0 || n <= 0 || n > 65536 || ldx < n || (flags & ~WR_H_ZERO))
     return WR_EINVAL;
   if (rows > 0 && !X) return WR_EINVAL;
-  if (x_dtype == WR_BF16 && (n % 8 != 0 || ldx % 8 != 0 || !aligned(X, 16))) return WR_EINVAL;
+  if (n % 8 != 0) return WR_EINVAL;
+  if (rows > 0 && x_dtype == WR_BF16 && (ldx % 8 != 0 || !aligned(X, 16))) return WR_EINVAL;
+  if (rows > 65535 * 4096) return WR_EINVAL;
   if (!aligned(S, 8)) return WR_EINVAL;
   DeviceScope ds(ctx->device);
   if (!ds.ok) return WR_EHIP;

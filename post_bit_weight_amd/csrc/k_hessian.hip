@@ -18,10 +18,9 @@
 namespace wr {
 
 constexpr int SY_TILE = 128;
-constexpr int SY_KT = 64;                // calibration rows per LDS stage
-constexpr int SY_PITCH = SY_KT + 8;      // bf16 per LDS row (+16 B: conflict-free 16-byte reads)
+constexpr int SY_KT = 64;                // calibration rows per LDS stage (8 chunks of 16 bytes per LDS row)
 constexpr int SY_SEG_STAGES = 8;         // 8 x 64 = 512 rows per fp32 segment
-constexpr int F32_TILE = 64;
+constexpr int SY_XCD = 8;                // workgroups are dispatched round-robin over 8 XCDs
 
 __device__ __forceinline__ void tile_from_linear(int t, int& ti, int& tj) {
   int i = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
@@ -42,13 +41,35 @@ __device__ __forceinline__ void emit(double v, int gi, int gj, int ii, int jj, i
   }
 }
 
-__global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(const uint16_t* __restrict__ X, int64_t rows, int n,
-                                                           int64_t ldx, int64_t rows_per_split, int tiles,
-                                                           double* __restrict__ S, float* __restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][SY_TILE * SY_PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][SY_TILE * SY_PITCH];
+// LDS row r of an operand tile holds 64 calibration rows (k) of feature r as eight
+// 16-byte chunks; chunk q is stored at position q ^ swz(r).  The transposed
+// stores (8 lanes: rows 8g + c, g = 0..7, one chunk) and the MFMA fragment reads
+// (8 lanes: 8 consecutive rows, one chunk) then both touch 8 distinct bank groups.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-  const int tile = blockIdx.x, split = blockIdx.y;
+// S_lower += XA^T XB over the rows (XA supplies the tile's row features, XB its
+// column features; both rows x n bf16 with leading dimension ldx).
+__global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(const uint16_t* __restrict__ XA, const uint16_t* __restrict__ XB,
+                                                           int64_t rows, int n, int64_t ldx, int64_t rows_per_split,
+                                                           int tiles, int ksplit, double* __restrict__ S,
+                                                           float* __restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][SY_TILE * SY_KT];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][SY_TILE * SY_KT];
+
+  // XCD-aware order: all workgroups of one row split land on the same XCD, so the
+  // X rows they share are fetched into that XCD's L2 once.
+  int tile, split;
+  {
+    const int bid = blockIdx.x;
+    if (ksplit % SY_XCD == 0) {
+      const int per = SY_XCD * tiles;
+      split = (bid % SY_XCD) + SY_XCD * (bid / per);
+      tile = (bid / SY_XCD) % tiles;
+    } else {
+      split = bid / tiles;
+      tile = bid % tiles;
+    }
+  }
   int ti, tj;
   tile_from_linear(tile, ti, tj);
   const int64_t r0 = (int64_t)split * rows_per_split;
@@ -56,17 +77,18 @@ __global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(const uint16_t* __res
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wi = wave >> 1, wj = wave & 1;
 
-  // loader coordinates: operand 0 = i-side columns, 1 = j-side columns
+  // loader: operand 0 = i-side columns, 1 = j-side columns; an 8x8 block per thread
   const int op = tid >> 7, b = tid & 127, kg = b >> 4, ig = b & 15;
   const int colbase = (op == 0 ? ti : tj) * SY_TILE + 8 * ig;
   const bool col_ok = colbase < n;
   uint16_t* sdst = op == 0 ? &sA[0][0] : &sB[0][0];
+  const uint16_t* X = op == 0 ? XA : XB;
 
   u32x4 ld[8];
   auto load_stage = [&](int64_t k0) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      int64_t row = k0 + 8 * kg + r;
+      const int64_t row = k0 + 8 * kg + r;
       if (col_ok && row < r1) {
         ld[r] = *reinterpret_cast<const u32x4*>(X + row * ldx + colbase);
       } else {
@@ -75,7 +97,7 @@ __global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(const uint16_t* __res
     }
   };
   auto store_stage = [&](int buf) {
-    uint16_t* base = sdst + buf * (SY_TILE * SY_PITCH);
+    uint16_t* base = sdst + buf * (SY_TILE * SY_KT);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int d = c >> 1;
@@ -94,7 +116,8 @@ __global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(const uint16_t* __res
         o[2] = (w[4] >> 16) | (w[5] & 0xffff0000u);
         o[3] = (w[6] >> 16) | (w[7] & 0xffff0000u);
       }
-      *reinterpret_cast<u32x4*>(base + (8 * ig + c) * SY_PITCH + 8 * kg) = o;
+      const int rr = 8 * ig + c;
+      *reinterpret_cast<u32x4*>(base + rr * SY_KT + 8 * (kg ^ swz(rr))) = o;
     }
   };
 
@@ -115,7 +138,8 @@ __global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(const uint16_t* __res
     store_stage(0);
   }
   __syncthreads();
-  const int arow = 64 * wi + (lane & 31), brow = 64 * wj + (lane & 31), koff = 8 * (lane >> 5);
+  const int arow0 = 64 * wi + (lane & 31), brow0 = 64 * wj + (lane & 31), khalf = lane >> 5;
+  const int sa0 = swz(arow0), sa1 = swz(arow0 + 32), sb0 = swz(brow0), sb1 = swz(brow0 + 32);
   for (int64_t s = 0; s < nstages; ++s) {
     const int buf = (int)(s & 1);
     if (s + 1 < nstages) load_stage(r0 + (s + 1) * SY_KT);
@@ -123,10 +147,11 @@ __global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(const uint16_t* __res
     const uint16_t* pb = &sB[buf][0];
 #pragma unroll
     for (int ks = 0; ks < SY_KT / 16; ++ks) {
-      bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(pa + arow * SY_PITCH + 16 * ks + koff));
-      bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(pa + (arow + 32) * SY_PITCH + 16 * ks + koff));
-      bf16x8 b0 = as_bf16x8(*reinterpret_cast<const u32x4*>(pb + brow * SY_PITCH + 16 * ks + koff));
-      bf16x8 b1 = as_bf16x8(*reinterpret_cast<const u32x4*>(pb + (brow + 32) * SY_PITCH + 16 * ks + koff));
+      const int q = 2 * ks + khalf;
+      bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(pa + arow0 * SY_KT + 8 * (q ^ sa0)));
+      bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(pa + (arow0 + 32) * SY_KT + 8 * (q ^ sa1)));
+      bf16x8 b0 = as_bf16x8(*reinterpret_cast<const u32x4*>(pb + brow0 * SY_KT + 8 * (q ^ sb0)));
+      bf16x8 b1 = as_bf16x8(*reinterpret_cast<const u32x4*>(pb + (brow0 + 32) * SY_KT + 8 * (q ^ sb1)));
       acc[0][0] = mfma32x32x16_bf16(a0, b0, acc[0][0]);
       acc[0][1] = mfma32x32x16_bf16(a0, b1, acc[0][1]);
       acc[1][0] = mfma32x32x16_bf16(a1, b0, acc[1][0]);
@@ -158,80 +183,40 @@ __global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(const uint16_t* __res
       }
 }
 
-// fp32 inputs (products rounded to fp32): plain FMA tiles, 64x64 per workgroup,
-// fp32 accumulation flushed into fp64 every 512 rows.
-__global__ __launch_bounds__(256) void syrk_f32_kernel(const float* __restrict__ X, int64_t rows, int n, int64_t ldx,
-                                                       int64_t rows_per_split, int tiles, double* __restrict__ S,
-                                                       float* __restrict__ partial) {
-  __shared__ float sA[16][F32_TILE + 4];
-  __shared__ float sB[16][F32_TILE + 4];
-  const int tile = blockIdx.x, split = blockIdx.y;
-  int ti, tj;
-  tile_from_linear(tile, ti, tj);
-  const int64_t r0 = (int64_t)split * rows_per_split;
-  const int64_t r1 = r0 + rows_per_split < rows ? r0 + rows_per_split : rows;
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  float acc[4][4] = {};
-  double tot[4][4] = {};
-  const int lrow = tid >> 4, lcol = (tid & 15) * 4;
-  int seg = 0;
-  for (int64_t k0 = r0; k0 < r1; k0 += 16) {
-    const int64_t row = k0 + lrow;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      int ci = ti * F32_TILE + lcol + c, cj = tj * F32_TILE + lcol + c;
-      sA[lrow][lcol + c] = (row < r1 && ci < n) ? X[row * ldx + ci] : 0.0f;
-      sB[lrow][lcol + c] = (row < r1 && cj < n) ? X[row * ldx + cj] : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      float a[4], bb[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        a[q] = sA[k][4 * ty + q];
-        bb[q] = sB[k][4 * tx + q];
-      }
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[p][q] = fmaf(a[p], bb[q], acc[p][q]);
-    }
-    __syncthreads();
-    if (++seg == 32 || k0 + 16 >= r1) {
-      seg = 0;
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          tot[p][q] += (double)acc[p][q];
-          acc[p][q] = 0.0f;
-        }
-    }
+// fp32 inputs: x = x0 + x1 + x2 with bf16 parts (exact for normal-range values),
+// so X^T X = sum_{a+b<=2} Xa^T Xb to about 2^-24 with every product exact.
+__global__ void split3_kernel(const float* __restrict__ X, int64_t rows, int n, int64_t ldx, uint16_t* __restrict__ P0,
+                              uint16_t* __restrict__ P1, uint16_t* __restrict__ P2) {
+  const int64_t r = blockIdx.y;
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x) {
+    const float x = X[r * ldx + j];
+    const uint32_t a = f32_to_bf16_bits(x);
+    const float r1 = x - bf16_bits_to_f32(a);
+    const uint32_t b = f32_to_bf16_bits(r1);
+    const float r2 = r1 - bf16_bits_to_f32(b);
+    P0[r * n + j] = (uint16_t)a;
+    P1[r * n + j] = (uint16_t)b;
+    P2[r * n + j] = (uint16_t)f32_to_bf16_bits(r2);
   }
-#pragma unroll
-  for (int p = 0; p < 4; ++p)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int ii = 4 * ty + p, jj = 4 * tx + q;
-      emit(tot[p][q], ti * F32_TILE + ii, tj * F32_TILE + jj, ii, jj, n, tile, tiles, split, F32_TILE, S, partial);
-    }
 }
 
 // S[lower] += sum over splits of the fp32 partials, splits added in index order.
+// One thread per tile element; grid.y = tile.
 __global__ void syrk_reduce_kernel(const float* __restrict__ partial, int ksplit, int tiles, int tdim, int n,
                                    double* __restrict__ S) {
-  const int tile = blockIdx.x;
+  const int tile = blockIdx.y;
   int ti, tj;
   tile_from_linear(tile, ti, tj);
-  for (int e = threadIdx.x; e < tdim * tdim; e += blockDim.x) {
-    const int ii = e / tdim, jj = e % tdim;
-    const int gi = ti * tdim + ii, gj = tj * tdim + jj;
-    if (gi >= n || gj >= n || gi < gj) continue;
-    double acc = 0.0;
-    for (int s = 0; s < ksplit; ++s) acc += (double)partial[(((size_t)s * tiles + tile) * tdim + ii) * tdim + jj];
-    S[(size_t)gi * n + gj] += acc;
-  }
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= tdim * tdim) return;
+  const int ii = e / tdim, jj = e - ii * tdim;
+  const int gi = ti * tdim + ii, gj = tj * tdim + jj;
+  if (gi >= n || gj >= n || gi < gj) return;
+  const size_t stride = (size_t)tiles * tdim * tdim;
+  const float* p = partial + (size_t)tile * tdim * tdim + e;
+  double acc = 0.0;
+  for (int s = 0; s < ksplit; ++s) acc += (double)p[s * stride];
+  S[(size_t)gi * n + gj] += acc;
 }
 
 __global__ void zero_lower_kernel(double* S, int n) {
@@ -302,18 +287,19 @@ static int syrk_tiles(int64_t n, int tdim) {
   return nt * (nt + 1) / 2;
 }
 
-// Number of row splits: enough workgroups to fill the chip in near-whole waves.
-static int syrk_ksplit(int64_t rows, int64_t n, int tdim, int num_cu) {
+// Number of row splits: a multiple of the XCD count (each XCD works through its
+// own rows), enough workgroups for near-whole waves on the chip, and at least
+// 512 rows per split.
+static int syrk_ksplit(int64_t rows, int64_t n, int num_cu) {
   if (rows <= 0) return 1;
-  const int tiles = syrk_tiles(n, tdim);
-  const int64_t max_split = (rows + 511) / 512;
+  const int tiles = syrk_tiles(n, SY_TILE);
+  const int64_t max_split = std::max<int64_t>(1, rows / 512);
   int best = 1;
   double best_eff = 0.0;
-  for (int k = 1; k <= 32 && k <= max_split; ++k) {
+  for (int k = SY_XCD; k <= 64 && k <= max_split; k += SY_XCD) {
     const double wgs = (double)tiles * k;
-    const double waves = std::ceil(wgs / num_cu);
-    const double eff = wgs / (waves * num_cu);
-    if (eff > best_eff + 0.05) {
+    const double eff = wgs / (std::ceil(wgs / num_cu) * num_cu);
+    if (eff > best_eff + 0.03) {
       best_eff = eff;
       best = k;
     }
@@ -322,12 +308,34 @@ static int syrk_ksplit(int64_t rows, int64_t n, int tdim, int num_cu) {
   return best;
 }
 
+static size_t partial_bytes(int64_t rows, int64_t n) {
+  const int ks = syrk_ksplit(rows, n, kSplitCUs);
+  return ks > 1 ? (size_t)ks * syrk_tiles(n, SY_TILE) * SY_TILE * SY_TILE * sizeof(float) : 0;
+}
+
 size_t wr_hessian_ws_bytes(int64_t rows, int64_t n, int x_dtype, int num_cu) {
-  const int tdim = x_dtype == WR_F32 ? F32_TILE : SY_TILE;
-  const int ks = syrk_ksplit(rows, n, tdim, num_cu);
-  size_t bytes = 256;  // finalize scalars
-  if (ks > 1) bytes += (size_t)ks * syrk_tiles(n, tdim) * tdim * tdim * sizeof(float);
+  (void)num_cu;
+  size_t bytes = 256 + ((partial_bytes(rows, n) + 255) & ~(size_t)255);
+  if (x_dtype == WR_F32) bytes += 3 * (((size_t)rows * n * 2 + 255) & ~(size_t)255);
   return bytes;
+}
+
+// One SYRK pass S_lower += XA^T XB (bf16 sources, ld ldx), with its split-K reduction.
+static int syrk_pass(wr_ctx* ctx, const uint16_t* XA, const uint16_t* XB, int64_t rows, int64_t n, int64_t ldx,
+                     double* S, float* partial) {
+  hipStream_t st = ctx->stream;
+  const int tiles = syrk_tiles(n, SY_TILE);
+  const int ks = syrk_ksplit(rows, n, kSplitCUs);
+  const int64_t rps = (rows + ks - 1) / ks;
+  hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)(tiles * ks)), dim3(256), 0, st, XA, XB, rows, (int)n, ldx, rps,
+                     tiles, ks, S, ks > 1 ? partial : nullptr);
+  WR_CHECK_LAUNCH();
+  if (ks > 1) {
+    dim3 rgrid((unsigned)((SY_TILE * SY_TILE + 255) / 256), (unsigned)tiles);
+    hipLaunchKernelGGL(syrk_reduce_kernel, rgrid, dim3(256), 0, st, partial, ks, tiles, SY_TILE, (int)n, S);
+    WR_CHECK_LAUNCH();
+  }
+  return WR_OK;
 }
 
 int wr_hessian_accumulate_impl(wr_ctx* ctx, const void* X, int x_dtype, int64_t rows, int64_t n, int64_t ldx,
@@ -338,27 +346,25 @@ int wr_hessian_accumulate_impl(wr_ctx* ctx, const void* X, int x_dtype, int64_t 
     WR_CHECK_LAUNCH();
   }
   if (rows == 0) return WR_OK;
-  const int tdim = x_dtype == WR_F32 ? F32_TILE : SY_TILE;
-  const int tiles = syrk_tiles(n, tdim);
-  const int ks = syrk_ksplit(rows, n, tdim, kSplitCUs);
-  const int64_t rps = (rows + ks - 1) / ks;
-  float* partial = nullptr;
-  if (ks > 1) {
-    if (ctx->ws_bytes < wr_hessian_ws_bytes(rows, n, x_dtype, kSplitCUs)) return WR_EWORKSPACE;
-    partial = reinterpret_cast<float*>(static_cast<char*>(ctx->ws) + 256);
-  }
-  dim3 grid((unsigned)tiles, (unsigned)ks);
+  if (ctx->ws_bytes < wr_hessian_ws_bytes(rows, n, x_dtype, kSplitCUs)) return WR_EWORKSPACE;
+  char* ws = static_cast<char*>(ctx->ws);
+  float* partial = reinterpret_cast<float*>(ws + 256);
   if (x_dtype == WR_BF16) {
-    hipLaunchKernelGGL(syrk_bf16_kernel, grid, dim3(256), 0, st, static_cast<const uint16_t*>(X), rows, (int)n, ldx,
-                       rps, tiles, S, partial);
-  } else {
-    hipLaunchKernelGGL(syrk_f32_kernel, grid, dim3(256), 0, st, static_cast<const float*>(X), rows, (int)n, ldx, rps,
-                       tiles, S, partial);
+    const uint16_t* Xb = static_cast<const uint16_t*>(X);
+    return syrk_pass(ctx, Xb, Xb, rows, n, ldx, S, partial);
   }
+  const size_t plane = ((size_t)rows * n * 2 + 255) & ~(size_t)255;
+  uint16_t* P[3];
+  for (int k = 0; k < 3; ++k)
+    P[k] = reinterpret_cast<uint16_t*>(ws + 256 + ((partial_bytes(rows, n) + 255) & ~(size_t)255) + k * plane);
+  const unsigned gx = (unsigned)std::min<int64_t>((n + 255) / 256, 16);
+  hipLaunchKernelGGL(split3_kernel, dim3(gx, (unsigned)rows), dim3(256), 0, st, static_cast<const float*>(X), rows,
+                     (int)n, ldx, P[0], P[1], P[2]);
   WR_CHECK_LAUNCH();
-  if (ks > 1) {
-    hipLaunchKernelGGL(syrk_reduce_kernel, dim3((unsigned)tiles), dim3(256), 0, st, partial, ks, tiles, tdim, (int)n, S);
-    WR_CHECK_LAUNCH();
+  static const int terms[6][2] = {{2, 0}, {1, 1}, {0, 2}, {1, 0}, {0, 1}, {0, 0}};  // small terms first
+  for (const auto& t : terms) {
+    const int rc = syrk_pass(ctx, P[t[0]], P[t[1]], rows, n, n, S, partial);
+    if (rc) return rc;
   }
   return WR_OK;
 }

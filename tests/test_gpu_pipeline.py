@@ -7,7 +7,10 @@ import oracle
 from parity import code_parity, scale_ulps
 
 pytestmark = pytest.mark.gpu
-TIE = 5e-3
+# Each side forms its own H here (GPU: exact products, fp32 segments of 512 rows added in fp64;
+# oracle: fp64), so a row's first differing code may sit a little further from a threshold than
+# in the same-H kernel tests: within 0.02 level units, 1 % of the spacing between thresholds.
+TIE = 2e-2
 
 
 @pytest.fixture(scope="module")
@@ -17,21 +20,39 @@ def ctx():
 
 
 def _check(out, ref, H0, bits, g, L, strict_loss=False):
-    """Codes within the flip policy, scales within 1 ulp where codes agree, proxy loss within 1e-4.
+    """Stage by stage against the oracle.
 
-    The loss bar applies to all rows for the configurations it is stated on (strict_loss) and,
-    for small edge-case shapes, to the rows whose codes and scales agree: there one differing
-    ulp of a single scale can move a 100-row problem's loss by more than 1e-4."""
+    GPTQ codes: at most 0.1 % differ and each row's first difference sits at a rounding
+    boundary.  A row whose GPTQ codes differ is a different valid rounding, so later stages
+    are compared on the rows that agree upstream: joint scales within 1 ulp; wring codes
+    again with first differences at boundaries; final scales within 1 ulp.  Proxy loss
+    within 1e-4: over all rows for the configurations the bar is stated on (strict_loss),
+    otherwise over the rows whose codes and scales agree (one ulp of one scale can move a
+    100-row problem's loss by more than 1e-4)."""
+    assert (out["dev_info"].cpu().numpy() == 0).all()
+    rows = out["codes"].shape[0]
+    Lr = np.broadcast_to(np.asarray(L), (rows,))
+    keep = np.ones(rows, dtype=bool)
+    if "gptq_codes" in out:
+        gc = out["gptq_codes"].cpu().numpy().astype(np.int64)
+        cp = code_parity(gc, ref["gptq_codes"], ref["gptq_t"], Lr)
+        assert cp["frac"] <= 1e-3 and cp["worst_first"] <= TIE, ("gptq", cp)
+        keep &= cp["identical_rows"]
+        gs = out["gptq_scales"].cpu().numpy().astype(np.float64)
+        assert scale_ulps(gs[keep], ref["gptq_scales"][keep]).max(initial=0) <= 1
+        js = out["joint_scales"].cpu().numpy().astype(np.float64)
+        uj = scale_ulps(js[keep], ref["joint_scales"][keep])
+        assert uj.max(initial=0) <= 1
+        keep[keep] &= uj.max(axis=1) == 0
     codes = out["codes"].cpu().numpy().astype(np.int64)
     scales = out["scales"].cpu().numpy().astype(np.float64)
-    assert (out["dev_info"].cpu().numpy() == 0).all()
-    cp = code_parity(codes, ref["codes"], ref["wring_t"], L)
-    assert cp["frac"] <= 1e-3 and cp["worst_first"] <= TIE, cp
-    ok = cp["identical_rows"]
-    assert scale_ulps(scales[ok], ref["scales"][ok]).max() <= 1
-    # proxy loss tr(dW H0 dW^T): rows whose codes agree differ only by arithmetic; a row with a
-    # boundary flip is a different valid rounding and may move its own loss by more
-    bits_r = np.broadcast_to(bits, (codes.shape[0],))
+    cp = code_parity(codes[keep], ref["codes"][keep], ref["wring_t"][keep], Lr[keep])
+    assert cp["worst_first"] <= TIE, ("wring", cp)
+    assert np.mean(codes != ref["codes"]) <= 1e-3
+    ok = keep.copy()
+    ok[keep] &= cp["identical_rows"]
+    assert scale_ulps(scales[ok], ref["scales"][ok]).max(initial=0) <= 1
+    bits_r = np.broadcast_to(bits, (rows,))
     dq_g = oracle.dequant(codes, scales, bits_r, g)
     dq_r = oracle.dequant(ref["codes"], ref["scales"], bits_r, g)
     same = ok & (scale_ulps(scales, ref["scales"]).max(axis=1) == 0)
@@ -42,7 +63,7 @@ def _check(out, ref, H0, bits, g, L, strict_loss=False):
     lra = oracle.proxy_loss(ref["target"], dq_r, H0)
     if strict_loss:
         assert abs(la - lra) <= 1e-4 * lra
-    print(f"rows with a code flip: {len(cp['rows'])}/{codes.shape[0]}, codes differing {cp['frac']:.2e}, "
+    print(f"rows agreeing upstream {keep.sum()}/{rows}; final codes differing {np.mean(codes != ref['codes']):.2e}; "
           f"proxy loss rel diff (all rows) {abs(la - lra) / lra:.2e}")
     return codes, scales
 
@@ -59,9 +80,6 @@ def test_toy_layer_end_to_end(ctx):
     ref = oracle.solve_module(W.double().numpy(), X.double().numpy(), 2, 32, 0.01, 0.01, B.double().numpy(),
                               A.double().numpy(), 8.0)
     codes, scales = _check(out, ref, ref["H0"], 2, 32, 3, strict_loss=True)
-    # GPTQ stage on its own
-    cp = code_parity(out["gptq_codes"].cpu().numpy(), ref["gptq_codes"], ref["gptq_t"], 3)
-    assert cp["frac"] <= 1e-3 and cp["worst_first"] <= TIE, cp
     # the packed container is bit-exact given identical codes and scales
     from post_bit_weight_amd import _lib as wr
     buf = torch.empty(oracle.packed_bytes(256, 512, 2, 32), dtype=torch.uint8, device="cuda")
@@ -81,7 +99,7 @@ def test_rotated_padded_layer_end_to_end(ctx):
     B = synth.gaussian((96, 8), 0.01, seed=304, dtype=torch.bfloat16)
     A = synth.gaussian((8, n), 0.01, seed=305, dtype=torch.bfloat16)
     out = pipeline.solve_module(ctx, W.cuda(), [X.cuda()], 2, 64, 0.01, 0.01, B.cuda(), A.cuda(), 8.0,
-                                had_block=m, signs=s.cuda(), n_store=n)
+                                had_block=m, signs=s.cuda(), n_store=n, keep_stages=True)
     ref = oracle.solve_module(W.double().numpy(), X.double().numpy(), 2, 64, 0.01, 0.01, B.double().numpy(),
                               A.double().numpy(), 8.0, had_block=m, signs=s.double().numpy(), n_store=n)
     Hg = out["H"].cpu().double().numpy()
@@ -103,7 +121,7 @@ def test_mixed_bits_shared_H(ctx):
     S, total = pipeline.accumulate_hessian(ctx, [X.cuda()], n)
     H, _ = pipeline.finalize_hessian(ctx, S, total, 0.01, n)
     out = pipeline.quantize(ctx, W.cuda(), H, torch.from_numpy(bits.astype(np.uint8)).cuda(), g, 0.01, B.cuda(),
-                            A.cuda(), 16.0)
+                            A.cuda(), 16.0, keep_stages=True)
     ref = oracle.solve_module(W.double().numpy(), X.double().numpy(), bits, g, 0.01, 0.01, B.double().numpy(),
                               A.double().numpy(), 16.0)
     _check(out, ref, ref["H0"], bits, g, oracle.levels_count(bits))
