@@ -86,11 +86,15 @@ int wr_set_workspace(wr_ctx* ctx, void* dev_ptr, size_t bytes);
  * S (n x n, fp64, ld n) += X^T X over the `rows` rows of X (rows x n, dtype
  * WR_BF16 or WR_F32, leading dimension ldx).  Only the lower triangle
  * (including the diagonal) of S is defined.  With WR_H_ZERO, S is zeroed
- * first.  Call once per chunk of calibration rows.  n % 8 == 0.  Products
- * are exact: bf16 inputs directly, fp32 inputs as three bf16 parts
- * (x = x0 + x1 + x2, six cross terms); sums run in fp32 over at most 512 rows
- * and are then added in fp64.  Workspace: WR_OP_HESSIAN with (rows, n).  rows
- * may be 0 (no-op unless WR_H_ZERO).
+ * first.  Call once per chunk of calibration rows.  n % 8 == 0; for bf16 X,
+ * ldx % 8 == 0 and X 16-byte aligned; ldx <= 2^24 (WR_EUNSUPPORTED above).
+ * Products are exact: bf16 inputs directly, fp32 inputs as three bf16 parts
+ * (x = x0 + x1 + x2, six cross terms).  Sums run in fp32 over 512-row
+ * segments, segments are added in fp32 within a split of the rows (at most a
+ * few thousand rows), and the splits are added into S in fp64 in a fixed
+ * order, so the result is deterministic with a relative error near 1e-7.
+ * Workspace: WR_OP_HESSIAN with (rows, n).  rows may be 0 (no-op unless
+ * WR_H_ZERO).
  */
 int wr_hessian_accumulate(wr_ctx* ctx, const void* X, int x_dtype, int64_t rows, int64_t n, int64_t ldx,
                           double* S, int flags);

@@ -101,6 +101,7 @@ int wr_hessian_accumulate(wr_ctx* ctx, const void* X, int x_dtype, int64_t rows,
   if (n % 8 != 0) return WR_EINVAL;
   if (rows > 0 && x_dtype == WR_BF16 && (ldx % 8 != 0 || !aligned(X, 16))) return WR_EINVAL;
   if (rows > 65535 * 4096) return WR_EINVAL;
+  if (ldx > ((int64_t)1 << 24)) return WR_EUNSUPPORTED;
   if (!aligned(S, 8)) return WR_EINVAL;
   DeviceScope ds(ctx->device);
   if (!ds.ok) return WR_EHIP;

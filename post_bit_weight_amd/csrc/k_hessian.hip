@@ -4,57 +4,89 @@
 // round with error feedback"); delta is the Tikhonov damping of the GPTQ solve
 // (Wringer news article, second paragraph).
 //
-// bf16 path: a SYRK on the bf16 matrix cores.  Each workgroup owns one 128x128
-// lower tile of S and a range of calibration rows.  X rows are row-major with
-// the feature index contiguous, while an MFMA operand wants 8 consecutive rows
-// per lane, so each thread loads an 8x8 bf16 block, transposes it in registers
-// and stores it to LDS with one 16-byte write.  bf16 x bf16 products are exact
-// in fp32; the fp32 accumulators are flushed into fp64 every 512 rows, which
-// keeps the relative error of S near 1e-8.  Tiles with a range of rows shorter
-// than the whole call write fp32 partials that a second kernel adds into S in
-// a fixed order (deterministic, no atomics).
+// bf16 path: a SYRK on the bf16 matrix cores.  Each workgroup owns one 256x128
+// tile of the lower triangle of S and a range of calibration rows.  X is
+// row-major (feature index contiguous), which is the wrong way round for an
+// MFMA operand (8 consecutive calibration rows of one feature per lane), so the
+// rows are copied untransposed into LDS by LDS-DMA loads (global_load_lds, no
+// registers, six stages in flight) and transposed on the way out by the gfx950
+// transposing LDS read (ds_read_b64_tr_b16).  bf16 x bf16 products are exact in
+// fp32; each 512-row segment is summed by the MFMAs in fp32 and added into fp32
+// totals, and the totals of the row splits are added in fp64 by a second kernel
+// in a fixed order (deterministic, no atomics).
 #include "common.hpp"
 
 namespace wr {
 
-constexpr int SY_TILE = 128;
-constexpr int SY_KT = 64;                // calibration rows per LDS stage (8 chunks of 16 bytes per LDS row)
-constexpr int SY_SEG_STAGES = 8;         // 8 x 64 = 512 rows per fp32 segment
+constexpr int SY_TI = 256;               // tile rows (row index of S)
+constexpr int SY_TJ = 128;               // tile columns
+constexpr int SY_KT = 32;                // calibration rows per LDS stage
+constexpr int SY_NS = 6;                 // stages in the LDS ring
+constexpr int SY_PF = SY_NS - 1;         // stages in flight ahead of the one being consumed
+constexpr int SY_SEG = 16;               // stages per fp32 segment (512 rows)
+constexpr int SY_A_BYTES = SY_KT * SY_TI * 2;
+constexpr int SY_B_BYTES = SY_KT * SY_TJ * 2;
+constexpr int SY_STAGE_BYTES = SY_A_BYTES + SY_B_BYTES;
+constexpr int SY_LDS_BYTES = SY_NS * SY_STAGE_BYTES;  // 144 KB
+constexpr int SY_DMA_PER_WAVE = (SY_STAGE_BYTES / 1024) / 4;  // 1 KB per wave-wide DMA, 4 waves
 constexpr int SY_XCD = 8;                // workgroups are dispatched round-robin over 8 XCDs
 
-__device__ __forceinline__ void tile_from_linear(int t, int& ti, int& tj) {
-  int i = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
-  while (i * (i + 1) / 2 > t) --i;
-  while ((i + 1) * (i + 2) / 2 <= t) ++i;
-  ti = i;
-  tj = t - i * (i + 1) / 2;
+// Tile t -> (I, J): row block I (256 rows) holds column blocks J = 0..2I+1 (128 columns),
+// the blocks that reach the diagonal or below it; I(I+1) tiles precede row block I.
+__device__ __forceinline__ void rect_tile(int t, int& I, int& J) {
+  int i = (int)((sqrtf(4.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+  while (i * (i + 1) > t) --i;
+  while ((i + 1) * (i + 2) <= t) ++i;
+  I = i;
+  J = t - i * (i + 1);
 }
 
-// Writes one tile element's contribution: directly into S (single range of rows)
-// or into the fp32 partial buffer of this split.
-__device__ __forceinline__ void emit(double v, int gi, int gj, int ii, int jj, int n, int tile, int tiles,
-                                     int split, int tdim, double* S, float* partial) {
-  if (partial) {
-    partial[(((size_t)split * tiles + tile) * tdim + ii) * tdim + jj] = (float)v;
-  } else if (gi < n && gj < n && gi >= gj) {
-    S[(size_t)gi * n + gj] += v;
-  }
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Wave-wide LDS DMA: lane l copies 16 bytes from sbase + voff to LDS byte address
+// m0 + 16 l.  Issued from inline assembly so that the compiler does not wait for it
+// before unrelated LDS reads; completion is awaited with vm_wait.  The M0 write
+// needs one wait state before the DMA.
+__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2" ::"v"(voff), "s"(m0), "s"(sbase)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// LDS row r of an operand tile holds 64 calibration rows (k) of feature r as eight
-// 16-byte chunks; chunk q is stored at position q ^ swz(r).  The transposed
-// stores (8 lanes: rows 8g + c, g = 0..7, one chunk) and the MFMA fragment reads
-// (8 lanes: 8 consecutive rows, one chunk) then both touch 8 distinct bank groups.
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// Two transposing reads give one MFMA operand: 8 consecutive calibration rows of one feature.
+__device__ __forceinline__ bf16x8 tr_frag(const lds_char* p, int half_stride) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + half_stride));
+  u32x4 u;
+  u[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+  u[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+  u[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+  u[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+  return as_bf16x8(u);
+}
 
-// S_lower += XA^T XB over the rows (XA supplies the tile's row features, XB its
-// column features; both rows x n bf16 with leading dimension ldx).
+// S_lower += XA^T XB over rows [split * rows_per_split, ...) of the call (XA gives the
+// tile's row features, XB its column features; both rows x n bf16, leading dimension
+// ldx).  With ksplit == 1 the tile is added into S (fp64); otherwise its fp32 totals
+// go to partial[split][tile][256][128].
+//
+// LDS stage layout: A panel = 32 calibration rows x 256 features (512 B per row), B
+// panel = 32 x 128 (256 B per row).  The 16-byte chunk c of row k sits at chunk
+// position c ^ 4 (k & 3), so the four rows that one transposing read touches fall
+// on disjoint bank groups.  Each DMA fills 1 KB (2 A rows or 4 B rows); every wave
+// issues SY_DMA_PER_WAVE of them per stage.
 __global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(const uint16_t* __restrict__ XA, const uint16_t* __restrict__ XB,
                                                            int64_t rows, int n, int64_t ldx, int64_t rows_per_split,
                                                            int tiles, int ksplit, double* __restrict__ S,
                                                            float* __restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][SY_TILE * SY_KT];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][SY_TILE * SY_KT];
+  extern __shared__ __attribute__((aligned(1024))) char sy_lds[];
+  lds_char* lds = (lds_char*)sy_lds;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
   // XCD-aware order: all workgroups of one row split land on the same XCD, so the
   // X rows they share are fetched into that XCD's L2 once.
@@ -70,116 +102,146 @@ __global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(const uint16_t* __res
       tile = bid % tiles;
     }
   }
-  int ti, tj;
-  tile_from_linear(tile, ti, tj);
+  int I, J;
+  rect_tile(tile, I, J);
   const int64_t r0 = (int64_t)split * rows_per_split;
   const int64_t r1 = r0 + rows_per_split < rows ? r0 + rows_per_split : rows;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wi = wave >> 1, wj = wave & 1;
 
-  // loader: operand 0 = i-side columns, 1 = j-side columns; an 8x8 block per thread
-  const int op = tid >> 7, b = tid & 127, kg = b >> 4, ig = b & 15;
-  const int colbase = (op == 0 ? ti : tj) * SY_TILE + 8 * ig;
-  const bool col_ok = colbase < n;
-  uint16_t* sdst = op == 0 ? &sA[0][0] : &sB[0][0];
-  const uint16_t* X = op == 0 ? XA : XB;
-
-  u32x4 ld[8];
-  auto load_stage = [&](int64_t k0) {
+  // DMA sources.  A block b = 4 wave + u holds rows 2b, 2b+1; B block b = 2 wave + u rows 4b..4b+3.
+  uint32_t offA[4], offB[2];
+  uint32_t ldsA[4], ldsB[2];  // byte offsets of the lane's chunk inside a stage
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int64_t row = k0 + 8 * kg + r;
-      if (col_ok && row < r1) {
-        ld[r] = *reinterpret_cast<const u32x4*>(X + row * ldx + colbase);
-      } else {
-        ld[r] = u32x4{0u, 0u, 0u, 0u};
+  for (int u = 0; u < 4; ++u) {
+    const int b = 4 * wave + u, row = 2 * b + (lane >> 5), c = (lane & 31) ^ (4 * (row & 3));
+    const int feat = min(SY_TI * I + 8 * c, n - 8);
+    offA[u] = (uint32_t)(row * ldx + feat) * 2u;
+    ldsA[u] = b * 1024 + lane * 16;
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int b = 2 * wave + u, row = 4 * b + (lane >> 4), c = (lane & 15) ^ (4 * (row & 3));
+    const int feat = min(SY_TJ * J + 8 * c, n - 8);
+    offB[u] = (uint32_t)(row * ldx + feat) * 2u;
+    ldsB[u] = SY_A_BYTES + b * 1024 + lane * 16;
+  }
+
+  auto issue = [&](int64_t st, int slot) {
+    const int64_t k0 = r0 + st * SY_KT;
+    const uint32_t sbase = lds_base + slot * SY_STAGE_BYTES;
+    if (k0 + SY_KT <= r1) {
+      const uint16_t* ga = XA + k0 * ldx;
+      const uint16_t* gb = XB + k0 * ldx;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) lds_dma16(ga, offA[u], sbase + (4 * wave + u) * 1024);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) lds_dma16(gb, offB[u], sbase + SY_A_BYTES + (2 * wave + u) * 1024);
+    } else {
+      // ragged last stage: bounds-checked loads through registers, zeros past r1
+      lds_char* dst = lds + slot * SY_STAGE_BYTES;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = 2 * (4 * wave + u) + (lane >> 5);
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (k0 + row < r1) v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(XA + k0 * ldx) + offA[u]);
+        *(__attribute__((address_space(3))) u32x4*)(dst + ldsA[u]) = v;
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int row = 4 * (2 * wave + u) + (lane >> 4);
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (k0 + row < r1) v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(XB + k0 * ldx) + offB[u]);
+        *(__attribute__((address_space(3))) u32x4*)(dst + ldsB[u]) = v;
       }
     }
   };
-  auto store_stage = [&](int buf) {
-    uint16_t* base = sdst + buf * (SY_TILE * SY_KT);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int d = c >> 1;
-      u32x4 o;
-      uint32_t w[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) w[r] = ld[r][d];
-      if ((c & 1) == 0) {
-        o[0] = (w[0] & 0xffffu) | (w[1] << 16);
-        o[1] = (w[2] & 0xffffu) | (w[3] << 16);
-        o[2] = (w[4] & 0xffffu) | (w[5] << 16);
-        o[3] = (w[6] & 0xffffu) | (w[7] << 16);
-      } else {
-        o[0] = (w[0] >> 16) | (w[1] & 0xffff0000u);
-        o[1] = (w[2] >> 16) | (w[3] & 0xffff0000u);
-        o[2] = (w[4] >> 16) | (w[5] & 0xffff0000u);
-        o[3] = (w[6] >> 16) | (w[7] & 0xffff0000u);
-      }
-      const int rr = 8 * ig + c;
-      *reinterpret_cast<u32x4*>(base + rr * SY_KT + 8 * (kg ^ swz(rr))) = o;
-    }
-  };
 
-  f32x16 acc[2][2];
-  double tot[2][2][16];
+  // Transposing-read addresses.  Lane l (g = l / 16, t = (l / 4) % 4, q = l % 4) reads
+  // row 8 (g / 2) + t (+ 4 for the second half) at features base + 16 (g % 2) + 4 q.
+  uint32_t rdA[4], rdB[2];
+  {
+    const int g = lane >> 4, t = (lane >> 2) & 3, q = lane & 3;
+    const int krow = 8 * (g >> 1) + t;
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+    for (int x = 0; x < 4; ++x) {
+      const int f = 128 * wi + 32 * x + 16 * (g & 1) + 4 * q;
+      rdA[x] = krow * (SY_TI * 2) + (((f >> 3) ^ (4 * t)) << 4) + (f & 7) * 2;
+    }
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
-      acc[x][y] = f32x16{};
-#pragma unroll
-      for (int v = 0; v < 16; ++v) tot[x][y][v] = 0.0;
+      const int f = 64 * wj + 32 * y + 16 * (g & 1) + 4 * q;
+      rdB[y] = SY_A_BYTES + krow * (SY_TJ * 2) + (((f >> 3) ^ (4 * t)) << 4) + (f & 7) * 2;
     }
-
-  const int64_t nstages = r1 > r0 ? (r1 - r0 + SY_KT - 1) / SY_KT : 0;
-  if (nstages > 0) {
-    load_stage(r0);
-    store_stage(0);
-  }
-  __syncthreads();
-  const int arow0 = 64 * wi + (lane & 31), brow0 = 64 * wj + (lane & 31), khalf = lane >> 5;
-  const int sa0 = swz(arow0), sa1 = swz(arow0 + 32), sb0 = swz(brow0), sb1 = swz(brow0 + 32);
-  for (int64_t s = 0; s < nstages; ++s) {
-    const int buf = (int)(s & 1);
-    if (s + 1 < nstages) load_stage(r0 + (s + 1) * SY_KT);
-    const uint16_t* pa = &sA[buf][0];
-    const uint16_t* pb = &sB[buf][0];
-#pragma unroll
-    for (int ks = 0; ks < SY_KT / 16; ++ks) {
-      const int q = 2 * ks + khalf;
-      bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(pa + arow0 * SY_KT + 8 * (q ^ sa0)));
-      bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(pa + (arow0 + 32) * SY_KT + 8 * (q ^ sa1)));
-      bf16x8 b0 = as_bf16x8(*reinterpret_cast<const u32x4*>(pb + brow0 * SY_KT + 8 * (q ^ sb0)));
-      bf16x8 b1 = as_bf16x8(*reinterpret_cast<const u32x4*>(pb + (brow0 + 32) * SY_KT + 8 * (q ^ sb1)));
-      acc[0][0] = mfma32x32x16_bf16(a0, b0, acc[0][0]);
-      acc[0][1] = mfma32x32x16_bf16(a0, b1, acc[0][1]);
-      acc[1][0] = mfma32x32x16_bf16(a1, b0, acc[1][0]);
-      acc[1][1] = mfma32x32x16_bf16(a1, b1, acc[1][1]);
-    }
-    if (s + 1 < nstages) store_stage(buf ^ 1);
-    if ((s + 1) % SY_SEG_STAGES == 0 || s + 1 == nstages) {
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) tot[x][y][v] += (double)acc[x][y][v];
-          acc[x][y] = f32x16{};
-        }
-    }
-    __syncthreads();
   }
 
+  float tot[4][2][16];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) tot[x][y][v] = 0.0f;
+
+  const int64_t nst = r1 > r0 ? (r1 - r0 + SY_KT - 1) / SY_KT : 0;
+  for (int64_t p = 0; p < SY_PF && p < nst; ++p) issue(p, (int)p);
+  int slot = 0;
+  for (int64_t s0 = 0; s0 < nst; s0 += SY_SEG) {
+    const int64_t s1 = s0 + SY_SEG < nst ? s0 + SY_SEG : nst;
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
+    for (int64_t s = s0; s < s1; ++s) {
+      // Stage s has landed once at most the DMAs of the SY_PF - 1 later stages are
+      // outstanding; those are all full DMA stages unless the ragged last one is among them.
+      if (nst - 1 - s > SY_PF - 1) {
+        vm_wait<SY_DMA_PER_WAVE * (SY_PF - 1)>();
+      } else {
+        vm_wait<0>();
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      if (s + SY_PF < nst) issue(s + SY_PF, slot == 0 ? SY_NS - 1 : slot - 1);
+      const lds_char* st = lds + slot * SY_STAGE_BYTES;
+#pragma unroll
+      for (int u = 0; u < SY_KT / 16; ++u) {
+        bf16x8 a[4], b[2];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) a[x] = tr_frag(st + rdA[x] + 16 * u * (SY_TI * 2), 4 * SY_TI * 2);
+#pragma unroll
+        for (int y = 0; y < 2; ++y) b[y] = tr_frag(st + rdB[y] + 16 * u * (SY_TJ * 2), 4 * SY_TJ * 2);
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int y = 0; y < 2; ++y) acc[x][y] = mfma32x32x16_bf16(a[x], b[y], acc[x][y]);
+      }
+      slot = slot == SY_NS - 1 ? 0 : slot + 1;
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tot[x][y][v] += acc[x][y][v];
+  }
+
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int ii = 64 * wi + 32 * x + acc_row(v, lane);
+        const int ii = 128 * wi + 32 * x + acc_row(v, lane);
         const int jj = 64 * wj + 32 * y + (lane & 31);
-        emit(tot[x][y][v], ti * SY_TILE + ii, tj * SY_TILE + jj, ii, jj, n, tile, tiles, split, SY_TILE, S, partial);
+        if (partial) {
+          partial[(((size_t)split * tiles + tile) * SY_TI + ii) * SY_TJ + jj] = tot[x][y][v];
+        } else {
+          const int gi = SY_TI * I + ii, gj = SY_TJ * J + jj;
+          if (gi < n && gj < n && gi >= gj) S[(size_t)gi * n + gj] += (double)tot[x][y][v];
+        }
       }
 }
 
@@ -202,18 +264,18 @@ __global__ void split3_kernel(const float* __restrict__ X, int64_t rows, int n, 
 
 // S[lower] += sum over splits of the fp32 partials, splits added in index order.
 // One thread per tile element; grid.y = tile.
-__global__ void syrk_reduce_kernel(const float* __restrict__ partial, int ksplit, int tiles, int tdim, int n,
+__global__ void syrk_reduce_kernel(const float* __restrict__ partial, int ksplit, int tiles, int n,
                                    double* __restrict__ S) {
   const int tile = blockIdx.y;
-  int ti, tj;
-  tile_from_linear(tile, ti, tj);
+  int I, J;
+  rect_tile(tile, I, J);
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= tdim * tdim) return;
-  const int ii = e / tdim, jj = e - ii * tdim;
-  const int gi = ti * tdim + ii, gj = tj * tdim + jj;
+  if (e >= SY_TI * SY_TJ) return;
+  const int ii = e / SY_TJ, jj = e - ii * SY_TJ;
+  const int gi = SY_TI * I + ii, gj = SY_TJ * J + jj;
   if (gi >= n || gj >= n || gi < gj) return;
-  const size_t stride = (size_t)tiles * tdim * tdim;
-  const float* p = partial + (size_t)tile * tdim * tdim + e;
+  const size_t stride = (size_t)tiles * SY_TI * SY_TJ;
+  const float* p = partial + (size_t)tile * SY_TI * SY_TJ + e;
   double acc = 0.0;
   for (int s = 0; s < ksplit; ++s) acc += (double)p[s * stride];
   S[(size_t)gi * n + gj] += acc;
@@ -282,18 +344,23 @@ using namespace wr;
 // Row splits are chosen for a 256-CU part so the workspace size does not depend on the device.
 static constexpr int kSplitCUs = 256;
 
-static int syrk_tiles(int64_t n, int tdim) {
-  const int nt = (int)((n + tdim - 1) / tdim);
-  return nt * (nt + 1) / 2;
+static int syrk_tiles(int64_t n) {
+  const int nI = (int)((n + SY_TI - 1) / SY_TI), nJ = (int)((n + SY_TJ - 1) / SY_TJ);
+  int t = 0;
+  for (int I = 0; I < nI; ++I) t += std::min(2 * I + 2, nJ);
+  return t;
 }
 
 // Number of row splits: a multiple of the XCD count (each XCD works through its
-// own rows), enough workgroups for near-whole waves on the chip, and at least
-// 512 rows per split.
-static int syrk_ksplit(int64_t rows, int64_t n, int num_cu) {
+// own rows), enough workgroups for near-whole waves on the chip (one workgroup
+// per CU), and at least 1024 rows per split.
+// With `precise` (the fp32-input path, whose six passes rebuild an fp32-accurate S)
+// every split is at most one 512-row segment, so no fp32 totals are formed.
+static int syrk_ksplit(int64_t rows, int64_t n, int num_cu, bool precise) {
   if (rows <= 0) return 1;
-  const int tiles = syrk_tiles(n, SY_TILE);
-  const int64_t max_split = std::max<int64_t>(1, rows / 512);
+  if (precise) return (int)std::min<int64_t>(64, (rows + 511) / 512);
+  const int tiles = syrk_tiles(n);
+  const int64_t max_split = std::max<int64_t>(1, rows / 1024);
   int best = 1;
   double best_eff = 0.0;
   for (int k = SY_XCD; k <= 64 && k <= max_split; k += SY_XCD) {
@@ -308,31 +375,38 @@ static int syrk_ksplit(int64_t rows, int64_t n, int num_cu) {
   return best;
 }
 
-static size_t partial_bytes(int64_t rows, int64_t n) {
-  const int ks = syrk_ksplit(rows, n, kSplitCUs);
-  return ks > 1 ? (size_t)ks * syrk_tiles(n, SY_TILE) * SY_TILE * SY_TILE * sizeof(float) : 0;
+static size_t partial_bytes(int64_t rows, int64_t n, bool precise) {
+  const int ks = syrk_ksplit(rows, n, kSplitCUs, precise);
+  return ks > 1 ? (size_t)ks * syrk_tiles(n) * SY_TI * SY_TJ * sizeof(float) : 0;
 }
 
 size_t wr_hessian_ws_bytes(int64_t rows, int64_t n, int x_dtype, int num_cu) {
   (void)num_cu;
-  size_t bytes = 256 + ((partial_bytes(rows, n) + 255) & ~(size_t)255);
+  size_t bytes = 256 + ((partial_bytes(rows, n, x_dtype == WR_F32) + 255) & ~(size_t)255);
   if (x_dtype == WR_F32) bytes += 3 * (((size_t)rows * n * 2 + 255) & ~(size_t)255);
   return bytes;
 }
 
 // One SYRK pass S_lower += XA^T XB (bf16 sources, ld ldx), with its split-K reduction.
 static int syrk_pass(wr_ctx* ctx, const uint16_t* XA, const uint16_t* XB, int64_t rows, int64_t n, int64_t ldx,
-                     double* S, float* partial) {
+                     double* S, float* partial, bool precise) {
+  static bool lds_attr = false;
+  if (!lds_attr) {
+    if (hipFuncSetAttribute((const void*)syrk_bf16_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            SY_LDS_BYTES) != hipSuccess)
+      return WR_EHIP;
+    lds_attr = true;
+  }
   hipStream_t st = ctx->stream;
-  const int tiles = syrk_tiles(n, SY_TILE);
-  const int ks = syrk_ksplit(rows, n, kSplitCUs);
-  const int64_t rps = (rows + ks - 1) / ks;
-  hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)(tiles * ks)), dim3(256), 0, st, XA, XB, rows, (int)n, ldx, rps,
-                     tiles, ks, S, ks > 1 ? partial : nullptr);
+  const int tiles = syrk_tiles(n);
+  const int ks = syrk_ksplit(rows, n, kSplitCUs, precise);
+  const int64_t rps = ((rows + ks - 1) / ks + SY_KT - 1) / SY_KT * SY_KT;
+  hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)(tiles * ks)), dim3(256), SY_LDS_BYTES, st, XA, XB, rows, (int)n,
+                     ldx, rps, tiles, ks, S, ks > 1 ? partial : nullptr);
   WR_CHECK_LAUNCH();
   if (ks > 1) {
-    dim3 rgrid((unsigned)((SY_TILE * SY_TILE + 255) / 256), (unsigned)tiles);
-    hipLaunchKernelGGL(syrk_reduce_kernel, rgrid, dim3(256), 0, st, partial, ks, tiles, SY_TILE, (int)n, S);
+    dim3 rgrid((unsigned)((SY_TI * SY_TJ + 255) / 256), (unsigned)tiles);
+    hipLaunchKernelGGL(syrk_reduce_kernel, rgrid, dim3(256), 0, st, partial, ks, tiles, (int)n, S);
     WR_CHECK_LAUNCH();
   }
   return WR_OK;
@@ -351,19 +425,19 @@ int wr_hessian_accumulate_impl(wr_ctx* ctx, const void* X, int x_dtype, int64_t 
   float* partial = reinterpret_cast<float*>(ws + 256);
   if (x_dtype == WR_BF16) {
     const uint16_t* Xb = static_cast<const uint16_t*>(X);
-    return syrk_pass(ctx, Xb, Xb, rows, n, ldx, S, partial);
+    return syrk_pass(ctx, Xb, Xb, rows, n, ldx, S, partial, false);
   }
   const size_t plane = ((size_t)rows * n * 2 + 255) & ~(size_t)255;
   uint16_t* P[3];
   for (int k = 0; k < 3; ++k)
-    P[k] = reinterpret_cast<uint16_t*>(ws + 256 + ((partial_bytes(rows, n) + 255) & ~(size_t)255) + k * plane);
+    P[k] = reinterpret_cast<uint16_t*>(ws + 256 + ((partial_bytes(rows, n, true) + 255) & ~(size_t)255) + k * plane);
   const unsigned gx = (unsigned)std::min<int64_t>((n + 255) / 256, 16);
   hipLaunchKernelGGL(split3_kernel, dim3(gx, (unsigned)rows), dim3(256), 0, st, static_cast<const float*>(X), rows,
                      (int)n, ldx, P[0], P[1], P[2]);
   WR_CHECK_LAUNCH();
   static const int terms[6][2] = {{2, 0}, {1, 1}, {0, 2}, {1, 0}, {0, 1}, {0, 0}};  // small terms first
   for (const auto& t : terms) {
-    const int rc = syrk_pass(ctx, P[t[0]], P[t[1]], rows, n, n, S, partial);
+    const int rc = syrk_pass(ctx, P[t[0]], P[t[1]], rows, n, n, S, partial, true);
     if (rc) return rc;
   }
   return WR_OK;

@@ -14,6 +14,11 @@ from parity import code_parity, f16_bits, scale_ulps
 pytestmark = pytest.mark.gpu
 
 TIE = 5e-3  # a code may differ only where the oracle's pre-rounding value is this close to a threshold
+# bf16 X: products are exact; the MFMAs sum 512-row segments in fp32 (rms relative error
+# about 2^-24 sqrt(32/3) of the segment) and a split of at most 8192 rows adds its 16
+# segments in fp32 (about 2^-24 sqrt(16/3)); splits are added in fp64.  Both stay near
+# 1e-7 of |S|_F; the bound leaves a factor of ten (the stated requirement is 1e-5).
+H_BF16_TOL = 1e-6
 
 
 @pytest.fixture(scope="module")
@@ -93,7 +98,7 @@ def test_hessian_bf16_ragged(wr, ctx, rows, n):
     Xd = X.double().numpy()
     ref = Xd.T @ Xd
     got = S.cpu().numpy()
-    assert _rel(np.tril(got), np.tril(ref)) < 2e-7
+    assert _rel(np.tril(got), np.tril(ref)) < H_BF16_TOL
 
 
 def test_hessian_chunks_and_strided_input(wr, ctx):
@@ -107,8 +112,8 @@ def test_hessian_chunks_and_strided_input(wr, ctx):
     for k, (a, b) in enumerate([(0, 1000), (1000, 1001), (1001, 3000)]):
         wr.wr_hessian_accumulate(ctx, Xd[a:b], S2, zero=(k == 0))
     ref = np.tril(X.double().numpy().T @ X.double().numpy())
-    assert _rel(np.tril(S1.cpu().numpy()), ref) < 2e-7
-    assert _rel(np.tril(S2.cpu().numpy()), ref) < 2e-7
+    assert _rel(np.tril(S1.cpu().numpy()), ref) < H_BF16_TOL
+    assert _rel(np.tril(S2.cpu().numpy()), ref) < H_BF16_TOL
 
 
 def test_hessian_finalize_pads_and_damps(wr, ctx, toy):
