@@ -4,41 +4,38 @@
 // round with error feedback"); delta is the Tikhonov damping of the GPTQ solve
 // (Wringer news article, second paragraph).
 //
-// bf16 path: a SYRK on the bf16 matrix cores.  Each workgroup owns one 256x128
-// tile of the lower triangle of S and a range of calibration rows.  X is
-// row-major (feature index contiguous), which is the wrong way round for an
-// MFMA operand (8 consecutive calibration rows of one feature per lane), so the
-// rows are copied untransposed into LDS by LDS-DMA loads (global_load_lds, no
-// registers, six stages in flight) and transposed on the way out by the gfx950
-// transposing LDS read (ds_read_b64_tr_b16).  bf16 x bf16 products are exact in
-// fp32; each 512-row segment is summed by the MFMAs in fp32 and added into fp32
-// totals, and the totals of the row splits are added in fp64 by a second kernel
-// in a fixed order (deterministic, no atomics).
+// bf16 path: a SYRK on the bf16 matrix cores.  Each workgroup owns one 256x256
+// tile of the lower triangle of S and a range of calibration rows; each of its
+// eight waves owns a 128x64 part.  X is row-major (feature index contiguous),
+// which is the wrong way round for an MFMA operand (8 consecutive calibration
+// rows of one feature per lane), so the rows are copied untransposed into LDS by
+// LDS-DMA loads (global_load_lds, no registers, several stages in flight) and
+// transposed on the way out by the gfx950 transposing LDS read
+// (ds_read_b64_tr_b16).  bf16 x bf16 products are exact in fp32; the MFMAs sum
+// a split of at most a few thousand rows in fp32, and the splits are added into
+// S in fp64 by a second kernel in a fixed order (deterministic, no atomics).
 #include "common.hpp"
 
 namespace wr {
 
-constexpr int SY_TI = 256;               // tile rows (row index of S)
-constexpr int SY_TJ = 128;               // tile columns
+constexpr int SY_T = 256;                // tile edge
 constexpr int SY_KT = 32;                // calibration rows per LDS stage
-constexpr int SY_NS = 6;                 // stages in the LDS ring
+constexpr int SY_NS = 5;                 // stages in the LDS ring
 constexpr int SY_PF = SY_NS - 1;         // stages in flight ahead of the one being consumed
-constexpr int SY_SEG = 16;               // stages per fp32 segment (512 rows)
-constexpr int SY_A_BYTES = SY_KT * SY_TI * 2;
-constexpr int SY_B_BYTES = SY_KT * SY_TJ * 2;
-constexpr int SY_STAGE_BYTES = SY_A_BYTES + SY_B_BYTES;
-constexpr int SY_LDS_BYTES = SY_NS * SY_STAGE_BYTES;  // 144 KB
-constexpr int SY_DMA_PER_WAVE = (SY_STAGE_BYTES / 1024) / 4;  // 1 KB per wave-wide DMA, 4 waves
+constexpr int SY_PANEL = SY_KT * SY_T * 2;            // one operand panel of a stage, bytes
+constexpr int SY_STAGE_BYTES = 2 * SY_PANEL;
+constexpr int SY_LDS_BYTES = SY_NS * SY_STAGE_BYTES;  // 160 KB
+constexpr int SY_THREADS = 512;          // eight waves
+constexpr int SY_DMA_PER_WAVE = (SY_STAGE_BYTES / 1024) / (SY_THREADS / 64);  // 1 KB per wave-wide DMA
 constexpr int SY_XCD = 8;                // workgroups are dispatched round-robin over 8 XCDs
 
-// Tile t -> (I, J): row block I (256 rows) holds column blocks J = 0..2I+1 (128 columns),
-// the blocks that reach the diagonal or below it; I(I+1) tiles precede row block I.
-__device__ __forceinline__ void rect_tile(int t, int& I, int& J) {
-  int i = (int)((sqrtf(4.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
-  while (i * (i + 1) > t) --i;
-  while ((i + 1) * (i + 2) <= t) ++i;
+// Lower-triangle tile t -> (I, J), J <= I, row-major over the block triangle.
+__device__ __forceinline__ void tri_tile(int t, int& I, int& J) {
+  int i = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+  while (i * (i + 1) / 2 > t) --i;
+  while ((i + 1) * (i + 2) / 2 <= t) ++i;
   I = i;
-  J = t - i * (i + 1);
+  J = t - i * (i + 1) / 2;
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -57,33 +54,35 @@ template <int N>
 __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// Workgroup barrier that the compiler cannot move LDS reads across.  Each wave's
+// own LDS reads are complete (waited before the MFMAs that use them) and its own
+// DMAs are waited with vm_wait, so after the barrier every wave sees every DMA.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Two transposing reads give one MFMA operand: 8 consecutive calibration rows of one feature.
 __device__ __forceinline__ bf16x8 tr_frag(const lds_char* p, int half_stride) {
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + half_stride));
-  u32x4 u;
-  u[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-  u[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-  u[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-  u[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
-  return as_bf16x8(u);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // S_lower += XA^T XB over rows [split * rows_per_split, ...) of the call (XA gives the
 // tile's row features, XB its column features; both rows x n bf16, leading dimension
-// ldx).  With ksplit == 1 the tile is added into S (fp64); otherwise its fp32 totals
-// go to partial[split][tile][256][128].
+// ldx).  With ksplit == 1 the tile is added into S (fp64); otherwise its fp32 sums
+// go to partial[split][tile][256][256].
 //
-// LDS stage layout: A panel = 32 calibration rows x 256 features (512 B per row), B
-// panel = 32 x 128 (256 B per row).  The 16-byte chunk c of row k sits at chunk
-// position c ^ 4 (k & 3), so the four rows that one transposing read touches fall
-// on disjoint bank groups.  Each DMA fills 1 KB (2 A rows or 4 B rows); every wave
-// issues SY_DMA_PER_WAVE of them per stage.
-__global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(const uint16_t* __restrict__ XA, const uint16_t* __restrict__ XB,
-                                                           int64_t rows, int n, int64_t ldx, int64_t rows_per_split,
-                                                           int tiles, int ksplit, double* __restrict__ S,
-                                                           float* __restrict__ partial) {
+// Eight waves (two per SIMD, so one issues MFMAs while the other waits on LDS or
+// the barrier); wave w owns rows 128 (w / 4) .. +127 and columns 64 (w % 4) .. +63.
+// LDS stage layout: panel A (row features) then panel B (column features), each 32
+// calibration rows x 256 features, 512 bytes per row.  The 16-byte chunk c of row k
+// sits at chunk position c ^ 4 (k & 3), so the four rows that one transposing read
+// touches fall on disjoint bank groups.  Each DMA fills 1 KB (2 rows); every wave
+// issues two per panel per stage.
+__global__ __launch_bounds__(SY_THREADS, 1) void syrk_bf16_kernel(const uint16_t* __restrict__ XA,
+                                                                  const uint16_t* __restrict__ XB, int64_t rows, int n,
+                                                                  int64_t ldx, int64_t rows_per_split, int tiles,
+                                                                  int ksplit, double* __restrict__ S,
+                                                                  float* __restrict__ partial) {
   extern __shared__ __attribute__((aligned(1024))) char sy_lds[];
   lds_char* lds = (lds_char*)sy_lds;
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
@@ -103,29 +102,21 @@ __global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(const uint16_t* __res
     }
   }
   int I, J;
-  rect_tile(tile, I, J);
+  tri_tile(tile, I, J);
   const int64_t r0 = (int64_t)split * rows_per_split;
   const int64_t r1 = r0 + rows_per_split < rows ? r0 + rows_per_split : rows;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wi = wave >> 1, wj = wave & 1;
+  const int wi = wave >> 2, wj = wave & 3;
 
-  // DMA sources.  A block b = 4 wave + u holds rows 2b, 2b+1; B block b = 2 wave + u rows 4b..4b+3.
-  uint32_t offA[4], offB[2];
-  uint32_t ldsA[4], ldsB[2];  // byte offsets of the lane's chunk inside a stage
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int b = 4 * wave + u, row = 2 * b + (lane >> 5), c = (lane & 31) ^ (4 * (row & 3));
-    const int feat = min(SY_TI * I + 8 * c, n - 8);
-    offA[u] = (uint32_t)(row * ldx + feat) * 2u;
-    ldsA[u] = b * 1024 + lane * 16;
-  }
+  // DMA sources: block b = 2 wave + u of a panel holds stage rows 2b, 2b + 1.
+  uint32_t offA[2], offB[2], ldsoff[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int b = 2 * wave + u, row = 4 * b + (lane >> 4), c = (lane & 15) ^ (4 * (row & 3));
-    const int feat = min(SY_TJ * J + 8 * c, n - 8);
-    offB[u] = (uint32_t)(row * ldx + feat) * 2u;
-    ldsB[u] = SY_A_BYTES + b * 1024 + lane * 16;
+    const int b = 2 * wave + u, row = 2 * b + (lane >> 5), c = (lane & 31) ^ (4 * (row & 3));
+    offA[u] = (uint32_t)(row * ldx + min(SY_T * I + 8 * c, n - 8)) * 2u;
+    offB[u] = (uint32_t)(row * ldx + min(SY_T * J + 8 * c, n - 8)) * 2u;
+    ldsoff[u] = b * 1024 + lane * 16;
   }
 
   auto issue = [&](int64_t st, int slot) {
@@ -135,25 +126,22 @@ __global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(const uint16_t* __res
       const uint16_t* ga = XA + k0 * ldx;
       const uint16_t* gb = XB + k0 * ldx;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) lds_dma16(ga, offA[u], sbase + (4 * wave + u) * 1024);
+      for (int u = 0; u < 2; ++u) lds_dma16(ga, offA[u], sbase + (2 * wave + u) * 1024);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) lds_dma16(gb, offB[u], sbase + SY_A_BYTES + (2 * wave + u) * 1024);
+      for (int u = 0; u < 2; ++u) lds_dma16(gb, offB[u], sbase + SY_PANEL + (2 * wave + u) * 1024);
     } else {
       // ragged last stage: bounds-checked loads through registers, zeros past r1
       lds_char* dst = lds + slot * SY_STAGE_BYTES;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int row = 2 * (4 * wave + u) + (lane >> 5);
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (k0 + row < r1) v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(XA + k0 * ldx) + offA[u]);
-        *(__attribute__((address_space(3))) u32x4*)(dst + ldsA[u]) = v;
-      }
-#pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int row = 4 * (2 * wave + u) + (lane >> 4);
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (k0 + row < r1) v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(XB + k0 * ldx) + offB[u]);
-        *(__attribute__((address_space(3))) u32x4*)(dst + ldsB[u]) = v;
+        const int row = 2 * (2 * wave + u) + (lane >> 5);
+        u32x4 va = u32x4{0u, 0u, 0u, 0u}, vb = va;
+        if (k0 + row < r1) {
+          va = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(XA + k0 * ldx) + offA[u]);
+          vb = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(XB + k0 * ldx) + offB[u]);
+        }
+        *(__attribute__((address_space(3))) u32x4*)(dst + ldsoff[u]) = va;
+        *(__attribute__((address_space(3))) u32x4*)(dst + SY_PANEL + ldsoff[u]) = vb;
       }
     }
   };
@@ -167,65 +155,73 @@ __global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(const uint16_t* __res
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int f = 128 * wi + 32 * x + 16 * (g & 1) + 4 * q;
-      rdA[x] = krow * (SY_TI * 2) + (((f >> 3) ^ (4 * t)) << 4) + (f & 7) * 2;
+      rdA[x] = krow * (SY_T * 2) + (((f >> 3) ^ (4 * t)) << 4) + (f & 7) * 2;
     }
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
       const int f = 64 * wj + 32 * y + 16 * (g & 1) + 4 * q;
-      rdB[y] = SY_A_BYTES + krow * (SY_TJ * 2) + (((f >> 3) ^ (4 * t)) << 4) + (f & 7) * 2;
+      rdB[y] = SY_PANEL + krow * (SY_T * 2) + (((f >> 3) ^ (4 * t)) << 4) + (f & 7) * 2;
     }
   }
 
-  float tot[4][2][16];
+  static_assert(SY_KT == 32, "two 16-row steps per stage");
+  // Operand double buffer: set 0 holds rows 0..15 of a stage, set 1 rows 16..31.
+  bf16x8 a0[4], b0[2], a1[4], b1[2];
+  auto read_frags = [&](int slot, int u, bf16x8 (&fa)[4], bf16x8 (&fb)[2]) {
+    const lds_char* st = lds + slot * SY_STAGE_BYTES + 16 * u * (SY_T * 2);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) fa[x] = tr_frag(st + rdA[x], 4 * SY_T * 2);
+#pragma unroll
+    for (int y = 0; y < 2; ++y) fb[y] = tr_frag(st + rdB[y], 4 * SY_T * 2);
+  };
+
+  f32x16 acc[4][2];
 #pragma unroll
   for (int x = 0; x < 4; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) tot[x][y][v] = 0.0f;
-
-  const int64_t nst = r1 > r0 ? (r1 - r0 + SY_KT - 1) / SY_KT : 0;
-  for (int64_t p = 0; p < SY_PF && p < nst; ++p) issue(p, (int)p);
-  int slot = 0;
-  for (int64_t s0 = 0; s0 < nst; s0 += SY_SEG) {
-    const int64_t s1 = s0 + SY_SEG < nst ? s0 + SY_SEG : nst;
-    f32x16 acc[4][2];
+    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
+  auto mfma_step = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[2]) {
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
-      for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
-    for (int64_t s = s0; s < s1; ++s) {
-      // Stage s has landed once at most the DMAs of the SY_PF - 1 later stages are
-      // outstanding; those are all full DMA stages unless the ragged last one is among them.
-      if (nst - 1 - s > SY_PF - 1) {
-        vm_wait<SY_DMA_PER_WAVE * (SY_PF - 1)>();
+      for (int y = 0; y < 2; ++y) acc[x][y] = mfma32x32x16_bf16(fa[x], fb[y], acc[x][y]);
+  };
+
+  // Pipeline: DMAs run SY_PF stages ahead; the operands of the first 16 rows of
+  // stage s + 1 are read (after the barrier that publishes that stage) while the
+  // MFMAs of the last 16 rows of stage s execute.
+  const int64_t nst = r1 > r0 ? (r1 - r0 + SY_KT - 1) / SY_KT : 0;
+  for (int64_t p = 0; p < SY_PF && p < nst; ++p) issue(p, (int)p);
+  if (nst > 0) {
+    if (nst - 1 > SY_PF - 1) {
+      vm_wait<SY_DMA_PER_WAVE * (SY_PF - 1)>();
+    } else {
+      vm_wait<0>();
+    }
+    lds_barrier();
+    read_frags(0, 0, a0, b0);
+  }
+  int slot = 0;
+  for (int64_t s = 0; s < nst; ++s) {
+    read_frags(slot, 1, a1, b1);
+    mfma_step(a0, b0);
+    const int next = slot == SY_NS - 1 ? 0 : slot + 1;
+    if (s + 1 < nst) {
+      // Stage s + 1 has landed once at most the DMAs of stages s + 2 .. s + SY_PF - 1
+      // are outstanding; those are all full DMA stages unless the ragged last one
+      // (or a stage past the end) is among them.
+      if (s + SY_PF - 1 <= nst - 2) {
+        vm_wait<SY_DMA_PER_WAVE * (SY_PF - 2)>();
       } else {
         vm_wait<0>();
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
+      lds_barrier();
+      // the slot of stage s - 1 is free: every wave consumed it before this barrier
       if (s + SY_PF < nst) issue(s + SY_PF, slot == 0 ? SY_NS - 1 : slot - 1);
-      const lds_char* st = lds + slot * SY_STAGE_BYTES;
-#pragma unroll
-      for (int u = 0; u < SY_KT / 16; ++u) {
-        bf16x8 a[4], b[2];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) a[x] = tr_frag(st + rdA[x] + 16 * u * (SY_TI * 2), 4 * SY_TI * 2);
-#pragma unroll
-        for (int y = 0; y < 2; ++y) b[y] = tr_frag(st + rdB[y] + 16 * u * (SY_TJ * 2), 4 * SY_TJ * 2);
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-          for (int y = 0; y < 2; ++y) acc[x][y] = mfma32x32x16_bf16(a[x], b[y], acc[x][y]);
-      }
-      slot = slot == SY_NS - 1 ? 0 : slot + 1;
+      read_frags(next, 0, a0, b0);
     }
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int y = 0; y < 2; ++y)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) tot[x][y][v] += acc[x][y][v];
+    mfma_step(a1, b1);
+    slot = next;
   }
 
 #pragma unroll
@@ -237,10 +233,10 @@ __global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(const uint16_t* __res
         const int ii = 128 * wi + 32 * x + acc_row(v, lane);
         const int jj = 64 * wj + 32 * y + (lane & 31);
         if (partial) {
-          partial[(((size_t)split * tiles + tile) * SY_TI + ii) * SY_TJ + jj] = tot[x][y][v];
+          partial[(((size_t)split * tiles + tile) * SY_T + ii) * SY_T + jj] = acc[x][y][v];
         } else {
-          const int gi = SY_TI * I + ii, gj = SY_TJ * J + jj;
-          if (gi < n && gj < n && gi >= gj) S[(size_t)gi * n + gj] += (double)tot[x][y][v];
+          const int gi = SY_T * I + ii, gj = SY_T * J + jj;
+          if (gi < n && gj < n && gi >= gj) S[(size_t)gi * n + gj] += (double)acc[x][y][v];
         }
       }
 }
@@ -268,16 +264,25 @@ __global__ void syrk_reduce_kernel(const float* __restrict__ partial, int ksplit
                                    double* __restrict__ S) {
   const int tile = blockIdx.y;
   int I, J;
-  rect_tile(tile, I, J);
+  tri_tile(tile, I, J);
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= SY_TI * SY_TJ) return;
-  const int ii = e / SY_TJ, jj = e - ii * SY_TJ;
-  const int gi = SY_TI * I + ii, gj = SY_TJ * J + jj;
+  if (e >= SY_T * SY_T) return;
+  const int ii = e / SY_T, jj = e - ii * SY_T;
+  const int gi = SY_T * I + ii, gj = SY_T * J + jj;
   if (gi >= n || gj >= n || gi < gj) return;
-  const size_t stride = (size_t)tiles * SY_TI * SY_TJ;
-  const float* p = partial + (size_t)tile * SY_TI * SY_TJ + e;
+  const size_t stride = (size_t)tiles * SY_T * SY_T;
+  const float* p = partial + (size_t)tile * SY_T * SY_T + e;
   double acc = 0.0;
-  for (int s = 0; s < ksplit; ++s) acc += (double)p[s * stride];
+  int s = 0;
+  for (; s + 4 <= ksplit; s += 4) {
+    const float a = p[(size_t)s * stride], b = p[(size_t)(s + 1) * stride], c = p[(size_t)(s + 2) * stride],
+                d = p[(size_t)(s + 3) * stride];
+    acc += (double)a;
+    acc += (double)b;
+    acc += (double)c;
+    acc += (double)d;
+  }
+  for (; s < ksplit; ++s) acc += (double)p[(size_t)s * stride];
   S[(size_t)gi * n + gj] += acc;
 }
 
@@ -345,39 +350,29 @@ using namespace wr;
 static constexpr int kSplitCUs = 256;
 
 static int syrk_tiles(int64_t n) {
-  const int nI = (int)((n + SY_TI - 1) / SY_TI), nJ = (int)((n + SY_TJ - 1) / SY_TJ);
-  int t = 0;
-  for (int I = 0; I < nI; ++I) t += std::min(2 * I + 2, nJ);
-  return t;
+  const int nt = (int)((n + SY_T - 1) / SY_T);
+  return nt * (nt + 1) / 2;
 }
 
-// Number of row splits: a multiple of the XCD count (each XCD works through its
-// own rows), enough workgroups for near-whole waves on the chip (one workgroup
-// per CU), and at least 1024 rows per split.
-// With `precise` (the fp32-input path, whose six passes rebuild an fp32-accurate S)
-// every split is at most one 512-row segment, so no fp32 totals are formed.
+// Number of row splits.  Each split is summed in fp32 by the MFMAs, so a split holds
+// at most 16384 rows (more splits only for calls beyond 2^20 rows, capped at 64).
+// Splits come in multiples of the XCD count (each XCD works through its own rows)
+// and are added while the chip has fewer workgroups than CUs.  With `precise` (the
+// fp32-input path, whose six passes rebuild an fp32-accurate S) a split is at most
+// 512 rows.
 static int syrk_ksplit(int64_t rows, int64_t n, int num_cu, bool precise) {
   if (rows <= 0) return 1;
   if (precise) return (int)std::min<int64_t>(64, (rows + 511) / 512);
+  if (rows < SY_XCD * 1024) return (int)std::max<int64_t>(1, rows / 1024);
   const int tiles = syrk_tiles(n);
-  const int64_t max_split = std::max<int64_t>(1, rows / 1024);
-  int best = 1;
-  double best_eff = 0.0;
-  for (int k = SY_XCD; k <= 64 && k <= max_split; k += SY_XCD) {
-    const double wgs = (double)tiles * k;
-    const double eff = wgs / (std::ceil(wgs / num_cu) * num_cu);
-    if (eff > best_eff + 0.03) {
-      best_eff = eff;
-      best = k;
-    }
-    if (eff >= 0.9) break;
-  }
-  return best;
+  int64_t ks = ((rows + 16383) / 16384 + SY_XCD - 1) / SY_XCD * SY_XCD;
+  while (ks < 64 && tiles * ks < num_cu && rows / (ks + SY_XCD) >= 1024) ks += SY_XCD;
+  return (int)std::min<int64_t>(ks, 64);
 }
 
 static size_t partial_bytes(int64_t rows, int64_t n, bool precise) {
   const int ks = syrk_ksplit(rows, n, kSplitCUs, precise);
-  return ks > 1 ? (size_t)ks * syrk_tiles(n) * SY_TI * SY_TJ * sizeof(float) : 0;
+  return ks > 1 ? (size_t)ks * syrk_tiles(n) * SY_T * SY_T * sizeof(float) : 0;
 }
 
 size_t wr_hessian_ws_bytes(int64_t rows, int64_t n, int x_dtype, int num_cu) {
@@ -401,11 +396,11 @@ static int syrk_pass(wr_ctx* ctx, const uint16_t* XA, const uint16_t* XB, int64_
   const int tiles = syrk_tiles(n);
   const int ks = syrk_ksplit(rows, n, kSplitCUs, precise);
   const int64_t rps = ((rows + ks - 1) / ks + SY_KT - 1) / SY_KT * SY_KT;
-  hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)(tiles * ks)), dim3(256), SY_LDS_BYTES, st, XA, XB, rows, (int)n,
+  hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)(tiles * ks)), dim3(SY_THREADS), SY_LDS_BYTES, st, XA, XB, rows, (int)n,
                      ldx, rps, tiles, ks, S, ks > 1 ? partial : nullptr);
   WR_CHECK_LAUNCH();
   if (ks > 1) {
-    dim3 rgrid((unsigned)((SY_TI * SY_TJ + 255) / 256), (unsigned)tiles);
+    dim3 rgrid((unsigned)((SY_T * SY_T + 255) / 256), (unsigned)tiles);
     hipLaunchKernelGGL(syrk_reduce_kernel, rgrid, dim3(256), 0, st, partial, ks, tiles, (int)n, S);
     WR_CHECK_LAUNCH();
   }

@@ -14,10 +14,10 @@ from parity import code_parity, f16_bits, scale_ulps
 pytestmark = pytest.mark.gpu
 
 TIE = 5e-3  # a code may differ only where the oracle's pre-rounding value is this close to a threshold
-# bf16 X: products are exact; the MFMAs sum 512-row segments in fp32 (rms relative error
-# about 2^-24 sqrt(32/3) of the segment) and a split of at most 8192 rows adds its 16
-# segments in fp32 (about 2^-24 sqrt(16/3)); splits are added in fp64.  Both stay near
-# 1e-7 of |S|_F; the bound leaves a factor of ten (the stated requirement is 1e-5).
+# bf16 X: products are exact; the MFMAs sum a split of m <= 1024 steps of 16 rows in
+# fp32 (rms relative error about 2^-24 sqrt(m / 3) of the split's sum, under 6e-7) and
+# the splits are added in fp64, so |S_gpu - S|_F / |S|_F stays near 2e-7 or below.  The
+# bound leaves a margin of five (the stated requirement is 1e-5).
 H_BF16_TOL = 1e-6
 
 
