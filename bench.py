@@ -45,20 +45,32 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=128, help="weight rows in the oracle sample")
     p.add_argument("--cpu-calib", type=int, default=8192, help="calibration rows in the oracle sample")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="before the warmup, copy MIB mebibytes device to device once (a plain copy kernel of known "
+                        "size, the yardstick for the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
 
 
 def traffic_from_profile():
-    """HBM bytes per SYRK launch from the committed rocprofv3 counter summary, if it matches this source."""
-    path = os.path.join(ROOT, "profiles", "syrk_bf16_q_proj_traffic.json")
+    """HBM bytes per SYRK launch from the committed rocprofv3 counter summary, if it matches this source.
+
+    The summary holds `bytes_per_launch:` (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the
+    counter reads for a plain 512 MiB copy) and `source_sha256:` of the kernel source it was taken on; once
+    the source has changed the figure no longer describes the kernel and None is returned.
+    """
+    path = os.path.join(ROOT, "profiles", "syrk_bf16_q_proj_traffic.txt")
     src = os.path.join(ROOT, "post_bit_weight_amd", "csrc", "k_hessian.hip")
     try:
-        rec = json.load(open(path))
+        rec = {}
+        for line in open(path):
+            if ":" in line and not line.startswith((" ", "#")):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
         digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
         if rec.get("source_sha256") != digest:
             return None
-        return rec.get("bytes_per_launch")
-    except (OSError, ValueError):
+        return float(rec["bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
         return None
 
 
@@ -136,6 +148,14 @@ def main():
              wr.wr_workspace_bytes(wr.WR_OP_FINALIZE, 0, n),
              wr.wr_workspace_bytes(wr.WR_OP_WRING, rows, n, g, rank, 0))
     ctx.ensure_workspace(ws)
+
+    if args.copy_calibration > 0:
+        nbytes = args.copy_calibration << 20
+        src_buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst_buf = torch.empty_like(src_buf)
+        dst_buf.copy_(src_buf)
+        torch.cuda.synchronize()
+        del src_buf, dst_buf
 
     stages = ["hessian", "finalize", "gptq", "joint", "wring", "pack"]
 
