@@ -2,14 +2,10 @@
 // feedback"; Wringer model cards, "Recipe": GPTQ codes on a fixed signed grid
 // with fp16 block scales).
 //
-// Factorisation.  With J the reversal permutation, L = chol_lower(J H J) gives
-// H = V V^T with V = J L J upper triangular, and H = M D M^T with the unit upper
-// M = V diag(V)^-1.  The sweep needs only M: no triangular inverse.  The
-// Cholesky runs in fp64, blocked by 32: per block column one single-wave kernel
-// factors the diagonal block in registers, then one kernel solves the panel
-// and updates the trailing lower matrix on the fp64 matrix cores; M is rounded
-// to fp32 once.  (An fp32 factorisation moves GPTQ block scales by up to two fp16 ulps
-// against an fp64 reference; fp64 keeps them within one.)
+// The unit upper factor M of H = M D M^T comes from the fp64 blocked Cholesky
+// of the reversed H (k_chol.hip), rounded to fp32 once.  (An fp32 factorisation
+// moves GPTQ block scales by up to two fp16 ulps against an fp64 reference; fp64
+// keeps them within one.)
 //
 // Sweep (LDLQ pull form).  Every row is independent.  With delta_i = w_i - q_i,
 // column k is rounded from v_k = w_k + sum_{i<k} M_ik delta_i.  The corrections
@@ -30,183 +26,10 @@
 int wr_gemm_f32(hipStream_t st, int M, int N, int K, const float* A, int64_t lda, const float* B, int64_t ldb,
                 bool b_kn, float* C, int64_t ldc, float alpha, bool accumulate, bool lower_tiles,
                 const int32_t* dev_info);
+size_t wr_factor_ws_bytes(int64_t n);
+int wr_factor_m(hipStream_t st, const float* H, int64_t ldh, int n, void* ws, float* M, int32_t* dev_info);
 
 namespace wr {
-
-constexpr int CH_NB = 32;
-
-// 1/sqrt(d) to fp64 precision: fp32 estimate and two Newton steps.
-__device__ __forceinline__ double rsqrt_f64(double d) {
-  double r = (double)rsqrtf((float)d);
-  r = r * (1.5 - 0.5 * d * r * r);
-  r = r * (1.5 - 0.5 * d * r * r);
-  return r;
-}
-
-__device__ __forceinline__ double lane_bcast(double v, int lane) {
-  const int64_t u = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_readlane((int)(u & 0xffffffff), lane);
-  const int hi = __builtin_amdgcn_readlane((int)(u >> 32), lane);
-  return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
-}
-
-// Triangular solve x L_kk^T = b for one panel row per lane (x overwrites b);
-// Lt[j][i] = L_ij (staged in LDS), rinv[j] = 1 / L_jj.
-template <int NB>
-__device__ __forceinline__ void panel_solve(double (&b)[NB], const double (*Lt)[NB + 1], const double* rinv) {
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    b[j] *= rinv[j];
-#pragma unroll
-    for (int jj = j + 1; jj < NB; ++jj) b[jj] = fma(-b[j], Lt[j][jj], b[jj]);
-  }
-}
-
-
-// A = J H J (lower triangle only), widened to fp64.
-__global__ void reverse_copy_kernel(const float* __restrict__ H, int64_t ldh, int n, double* __restrict__ A) {
-  const int i = blockIdx.x;
-  for (int j = threadIdx.x; j <= i; j += blockDim.x)
-    A[(int64_t)i * n + j] = (double)H[(int64_t)(n - 1 - i) * ldh + (n - 1 - j)];
-}
-
-typedef double f64x4 __attribute__((ext_vector_type(4)));
-
-// Trailing update of one step, fused with the panel solve.  Tile (i, j) of the
-// lower trailing matrix (rows/cols from kb + NB on, 64 x 64 per workgroup):
-// waves 0-1 solve the 64 panel rows of block i against L_kk, waves 2-3 those
-// of block j (the panel itself is read from A, which this step does not
-// modify there); the diagonal tile's workgroup stores its solved rows into
-// Lout.  Then A[i][j] -= P_i P_j^T on the fp64 matrix cores
-// (v_mfma_f64_16x16x4f64: operand lane l holds row/column l % 16 at k = l / 16;
-// accumulator v of lane l is row l / 16 + 4 v, column l % 16).
-__global__ __launch_bounds__(256) void panel_update_kernel(double* __restrict__ A, double* __restrict__ Lout, int n,
-                                                           int kb, const int32_t* __restrict__ dev_info) {
-  if (*dev_info != 0) return;
-  __shared__ double sp[2][CH_NB][64 + 1];  // solved panel blocks, k-major
-  __shared__ double Lt[CH_NB][CH_NB + 1];  // L_kk transposed
-  __shared__ double rinv[CH_NB];
-  int ti, tj;
-  {
-    const int t = blockIdx.x;
-    int i = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
-    while (i * (i + 1) / 2 > t) --i;
-    while ((i + 1) * (i + 2) / 2 <= t) ++i;
-    ti = i;
-    tj = t - i * (i + 1) / 2;
-  }
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int base = kb + CH_NB;  // first trailing row/column
-  for (int e = tid; e < CH_NB * CH_NB; e += 256) {
-    const int i = e / CH_NB, j = e % CH_NB;
-    const double v = Lout[(int64_t)(kb + i) * n + kb + j];
-    Lt[j][i] = v;
-    if (i == j) rinv[i] = 1.0 / v;
-  }
-  __syncthreads();
-  {
-    const int side = wave >> 1;  // 0: block i, 1: block j
-    const int blk = side == 0 ? ti : tj;
-    const int rloc = 32 * (wave & 1) + (lane & 31);
-    const int64_t prow = (int64_t)base + blk * 64 + rloc;
-    if (lane < 32 && (side == 0 || ti != tj)) {
-      double b[CH_NB];
-#pragma unroll
-      for (int j = 0; j < CH_NB; ++j) b[j] = prow < n ? A[prow * n + kb + j] : 0.0;
-      panel_solve<CH_NB>(b, Lt, rinv);
-#pragma unroll
-      for (int j = 0; j < CH_NB; ++j) sp[side][j][rloc] = b[j];
-      if (side == 0 && ti == tj && prow < n) {
-#pragma unroll
-        for (int j = 0; j < CH_NB; ++j) Lout[prow * n + kb + j] = b[j];
-      }
-    }
-  }
-  __syncthreads();
-  const int wi = wave >> 1, wj = wave & 1;
-  const int sj = ti == tj ? 0 : 1;
-  f64x4 acc[2][2];
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
-  const int li = lane & 15, lk = lane >> 4;
-#pragma unroll
-  for (int k0 = 0; k0 < CH_NB; k0 += 4) {
-    double a[2], b[2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      a[x] = sp[0][k0 + lk][32 * wi + 16 * x + li];
-      b[x] = sp[sj][k0 + lk][32 * wj + 16 * x + li];
-    }
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
-  }
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int gi = base + ti * 64 + 32 * wi + 16 * x + (lane >> 4) + 4 * v;
-        const int gj = base + tj * 64 + 32 * wj + 16 * y + (lane & 15);
-        if (gi < n && gj < n && gj <= gi) A[(int64_t)gi * n + gj] -= acc[x][y][v];
-      }
-}
-
-
-// Factor the NB x NB diagonal block at kb of the (updated) matrix A in fp64 and
-// write L_kk into Lout; one wave, lane i holds row i in registers and column k
-// is broadcast with readlane.
-template <int NB>
-__global__ __launch_bounds__(64) void chol_diag_kernel(const double* __restrict__ A, double* __restrict__ Lout, int n,
-                                                       int kb, int32_t* __restrict__ dev_info) {
-  if (*dev_info != 0) return;
-  const int lane = threadIdx.x;
-  const int r = lane < NB ? lane : NB - 1;
-  const int row = kb + r;
-  double a[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j)
-    a[j] = (row < n && kb + j < n && j <= r) ? A[(int64_t)row * n + kb + j] : (j == r ? 1.0 : 0.0);
-  int bad = -1;
-#pragma unroll
-  for (int k = 0; k < NB; ++k) {
-    const double d = lane_bcast(a[k], k);
-    if (!(d > 0.0) && bad < 0) bad = k;
-    const double l = a[k] * rsqrt_f64(d);  // lane k: L_kk; lanes below: L_ik
-    a[k] = l;
-#pragma unroll
-    for (int j = k + 1; j < NB; ++j) a[j] = fma(-l, lane_bcast(l, j), a[j]);
-  }
-  if (bad >= 0) {
-    if (lane == 0) atomicCAS(dev_info, 0, kb + bad + 1);
-    return;
-  }
-  if (lane < NB && row < n) {
-#pragma unroll
-    for (int j = 0; j < NB; ++j) Lout[(int64_t)row * n + kb + j] = j <= lane ? a[j] : 0.0;
-  }
-}
-
-// M[i][j] = L[n-1-i][n-1-j] / L[n-1-j][n-1-j] for i < j; 0 on and below the diagonal
-// (the unit diagonal is implicit and never used).
-__global__ void build_m_kernel(const double* __restrict__ A, int n, float* __restrict__ M,
-                               const int32_t* __restrict__ dev_info) {
-  if (*dev_info != 0) return;
-  const int i = blockIdx.x;
-  const int64_t ri = n - 1 - i;
-  for (int j = threadIdx.x; j < n; j += blockDim.x) {
-    float v = 0.0f;
-    if (j > i) {
-      const int64_t rj = n - 1 - j;
-      v = (float)(A[ri * n + rj] / A[rj * n + rj]);
-    }
-    M[(int64_t)i * n + j] = v;
-  }
-}
 
 __global__ void check_finite_kernel(const void* __restrict__ W, int w_dtype, int64_t rows, int n, int64_t ldw,
                                     int32_t* __restrict__ dev_info) {
@@ -348,36 +171,15 @@ using namespace wr;
 
 static constexpr int kBatch = 128;
 
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
 size_t wr_gptq_ws_bytes(int64_t rows, int64_t n) {
   size_t b = 0;
-  b += (size_t)n * n * 8;          // A (J H J, reduced step by step), fp64
-  b += (size_t)n * n * 8;          // L, fp64
-  b += (size_t)n * n * 4;          // M
-  b += (size_t)rows * n * 4;       // corrections C
-  b += (size_t)rows * kBatch * 4;  // batch errors E
-  return b + 1024;
-}
-
-// Blocked fp64 Cholesky of J H J: A holds the matrix being reduced, L collects
-// the factor; then M rounded to fp32.
-static int factor_m(wr_ctx* ctx, const float* H, int64_t ldh, int n, double* A, double* L, float* Mm,
-                    int32_t* dev_info) {
-  hipStream_t st = ctx->stream;
-  hipLaunchKernelGGL(reverse_copy_kernel, dim3(n), dim3(256), 0, st, H, ldh, n, A);
-  WR_CHECK_LAUNCH();
-  for (int kb = 0; kb < n; kb += CH_NB) {
-    hipLaunchKernelGGL(chol_diag_kernel<CH_NB>, dim3(1), dim3(64), 0, st, A, L, n, kb, dev_info);
-    WR_CHECK_LAUNCH();
-    const int rem = n - kb - CH_NB;
-    if (rem <= 0) break;
-    const int nt = (rem + 63) / 64;
-    hipLaunchKernelGGL(panel_update_kernel, dim3((unsigned)(nt * (nt + 1) / 2)), dim3(256), 0, st, A, L, n, kb,
-                       dev_info);
-    WR_CHECK_LAUNCH();
-  }
-  hipLaunchKernelGGL(build_m_kernel, dim3(n), dim3(256), 0, st, L, n, Mm, dev_info);
-  WR_CHECK_LAUNCH();
-  return WR_OK;
+  b += align256(wr_factor_ws_bytes(n));      // factorisation scratch (fp64)
+  b += align256((size_t)n * n * 4);          // M
+  b += align256((size_t)rows * n * 4);       // corrections C
+  b += align256((size_t)rows * kBatch * 4);  // batch errors E
+  return b;
 }
 
 template <int P, int G>
@@ -411,11 +213,10 @@ int wr_gptq_sweep_impl(wr_ctx* ctx, const void* W, int w_dtype, int64_t rows, in
   const int n = (int)n64;
   hipStream_t st = ctx->stream;
   char* ws = static_cast<char*>(ctx->ws);
-  double* A = reinterpret_cast<double*>(ws);
-  double* Lf = A + (size_t)n * n;
-  float* Mm = reinterpret_cast<float*>(Lf + (size_t)n * n);
-  float* Cb = Mm + (size_t)n * n;
-  float* E = Cb + (size_t)rows * n;
+  void* fws = ws;
+  float* Mm = reinterpret_cast<float*>(ws + align256(wr_factor_ws_bytes(n)));
+  float* Cb = reinterpret_cast<float*>(reinterpret_cast<char*>(Mm) + align256((size_t)n * n * 4));
+  float* E = reinterpret_cast<float*>(reinterpret_cast<char*>(Cb) + align256((size_t)rows * n * 4));
 
   hipLaunchKernelGGL(sweep_set_int_kernel, dim3(1), dim3(1), 0, st, dev_info, 0);
   WR_CHECK_LAUNCH();
@@ -423,7 +224,7 @@ int wr_gptq_sweep_impl(wr_ctx* ctx, const void* W, int w_dtype, int64_t rows, in
     hipLaunchKernelGGL(check_finite_kernel, dim3((unsigned)rows), dim3(256), 0, st, W, w_dtype, rows, n, ldw, dev_info);
     WR_CHECK_LAUNCH();
   }
-  int rc = factor_m(ctx, H, ldh, n, A, Lf, Mm, dev_info);
+  int rc = wr_factor_m(st, H, ldh, n, fws, Mm, dev_info);
   if (rc) return rc;
   if (rows == 0) return WR_OK;
   hipLaunchKernelGGL(zero_f32_kernel, dim3(1024), dim3(256), 0, st, Cb, (int64_t)rows * n);
