@@ -29,7 +29,7 @@ Every function here is pinned by a CPU test in ``tests/test_oracle_*.py``
 against worked examples, closed forms, invariants or brute force.
 """
 
-from .hessian import second_moment, pad_square, damp
+from .hessian import second_moment, second_moment_chunks, sum_of_products, pad_square, damp
 from .rotation import sylvester, rotation_matrix, rotate_rows, rotate_rows_inverse, rotate_sym
 from .grid import fp16_rne, levels_count, nearest_code, level_of, dequant
 from .gptq import upper_cholesky_of_inverse, feedback_sweep, gptq_sweep, integer_feedback_round
@@ -37,10 +37,10 @@ from .joint import joint_scales, row_gram
 from .wring import wring_target, wring
 from .pack import pack, unpack, packed_bytes, code_bytes_per_row
 from .metrics import proxy_loss, ledger_bits_per_weight, threshold_distance
-from .solve import solve_module
+from .solve import solve_module, solve_rows
 
 __all__ = [
-    "second_moment", "pad_square", "damp",
+    "second_moment", "second_moment_chunks", "sum_of_products", "pad_square", "damp",
     "sylvester", "rotation_matrix", "rotate_rows", "rotate_rows_inverse", "rotate_sym",
     "fp16_rne", "levels_count", "nearest_code", "level_of", "dequant",
     "upper_cholesky_of_inverse", "feedback_sweep", "gptq_sweep", "integer_feedback_round",
@@ -48,5 +48,5 @@ __all__ = [
     "wring_target", "wring",
     "pack", "unpack", "packed_bytes", "code_bytes_per_row",
     "proxy_loss", "ledger_bits_per_weight", "threshold_distance",
-    "solve_module",
+    "solve_module", "solve_rows",
 ]

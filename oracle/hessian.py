@@ -17,6 +17,27 @@ def second_moment(X):
     return (X.T @ X) / X.shape[0]
 
 
+def second_moment_chunks(chunks):
+    """H0 = (1/N) sum over chunks of X_k^T X_k: the same average as second_moment, for calibration
+    rows that arrive in chunks (N = total rows).  Each chunk is widened to float64."""
+    S = None
+    N = 0
+    for X in chunks:
+        Xd = np.asarray(X, dtype=np.float64)
+        part = Xd.T @ Xd
+        S = part if S is None else S + part
+        N += Xd.shape[0]
+    if S is None or N == 0:
+        raise ValueError("no calibration rows")
+    return S / N
+
+
+def sum_of_products(X, pairs):
+    """S[i, j] = sum over rows of x_i x_j for each (i, j) in pairs, one entry at a time (float64)."""
+    X = np.asarray(X, dtype=np.float64)
+    return np.array([float(np.dot(X[:, i], X[:, j])) for i, j in pairs])
+
+
 def pad_square(H0, n_store):
     """Zero-pad an n x n matrix to n_store x n_store (the padded input dims carry no signal)."""
     n = H0.shape[0]

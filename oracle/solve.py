@@ -17,6 +17,20 @@ from .wring import wring
 from .pack import pack
 
 
+def solve_rows(W, H, bits, group, lam, B=None, A=None, alpha=None):
+    """GPTQ codes and scales -> joint scales against W -> wring against W_hat + (alpha/r) B A, for
+    the rows of W (stored basis) given the damped H.  Rows are independent given H, so any subset of
+    a layer's rows gives the same result as the whole layer restricted to that subset."""
+    g = gptq_sweep(W, H, bits, group)
+    s1, _ = joint_scales(g["codes"], bits, group, H, W, g["scales"], lam)
+    w = wring(g["codes"], s1, bits, group, B, A, alpha, H, lam)
+    return {
+        "gptq_codes": g["codes"], "gptq_scales": g["scales"], "gptq_t": g["t"],
+        "joint_scales": s1,
+        "codes": w["codes"], "scales": w["scales"], "target": w["target"], "wring_t": w["t"],
+    }
+
+
 def solve_module(W, X, bits, group, damp_frac, lam, B=None, A=None, alpha=None,
                  had_block=None, signs=None, n_store=None):
     """Run the solve for one linear layer W (rows x n0) with calibration rows X (N x n0).
@@ -34,15 +48,8 @@ def solve_module(W, X, bits, group, damp_frac, lam, B=None, A=None, alpha=None,
         H0 = rotate_sym(H0, had_block, signs)
         Wn = rotate_rows(Wn, had_block, signs)
     H, delta = damp(H0, damp_frac)
-    g = gptq_sweep(Wn, H, bits, group)
-    s1, _ = joint_scales(g["codes"], bits, group, H, Wn, g["scales"], lam)
-    w = wring(g["codes"], s1, bits, group, B, A, alpha, H, lam)
-    out = {
-        "H0": H0, "H": H, "delta": delta, "W": Wn,
-        "gptq_codes": g["codes"], "gptq_scales": g["scales"], "gptq_t": g["t"],
-        "joint_scales": s1,
-        "codes": w["codes"], "scales": w["scales"], "target": w["target"], "wring_t": w["t"],
-    }
+    out = {"H0": H0, "H": H, "delta": delta, "W": Wn}
+    out.update(solve_rows(Wn, H, bits, group, lam, B, A, alpha))
     if np.ndim(bits) == 0:
-        out["packed"] = pack(w["codes"], w["scales"], int(bits), group)
+        out["packed"] = pack(out["codes"], out["scales"], int(bits), group)
     return out

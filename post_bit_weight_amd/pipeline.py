@@ -91,3 +91,61 @@ def solve_module(ctx, W, chunks, bits, group, damp_frac=0.01, lam=0.01, B=None, 
         out["packed"] = pack(ctx, out["codes"], out["scales"], bits, group)
     out.update(H=H, delta=delta, S=S, W=Wst)
     return out
+
+
+def solve_group(ctx, modules, H, group, lam=0.01, lazy_batch=128, keep_stages=False):
+    """Quantize several modules that share one damped H (n_store x n_store).
+
+    modules: list of dicts with keys name, W (rows x n_store, device, stored basis), bits (int),
+    and optionally B (rows x r), A (r x n_store), alpha.  One batched GPTQ sweep and one joint
+    scale solve run over the concatenated rows with a per-row bit width; then each module is
+    wrung against its own adapter and packed.  Returns {name: dict(codes, scales, packed, ...)}
+    with codes/scales as views into the batched buffers.
+    """
+    n = H.shape[0]
+    sizes = [m["W"].shape[0] for m in modules]
+    W = torch.cat([m["W"] for m in modules]) if len(modules) > 1 else modules[0]["W"]
+    bits_t = torch.cat([torch.full((r,), int(m["bits"]), dtype=torch.uint8, device=ctx.device)
+                        for m, r in zip(modules, sizes)])
+    rows = W.shape[0]
+    codes = torch.empty(rows, n, dtype=torch.uint8, device=ctx.device)
+    scales = torch.empty(rows, n // group, dtype=torch.float16, device=ctx.device)
+    info = torch.zeros(2 + len(modules), dtype=torch.int32, device=ctx.device)
+    wr.wr_gptq_sweep(ctx, W, H, bits_t, group, lazy_batch, codes, scales, info[0:1])
+    stages = {}
+    if keep_stages:
+        stages["gptq_codes"], stages["gptq_scales"] = codes.clone(), scales.clone()
+    wr.wr_wring_solve(ctx, H, bits_t, group, lam, codes, scales, info[1:2], target=W)
+    if keep_stages:
+        stages["joint_scales"] = scales.clone()
+    out = {}
+    r0 = 0
+    for k, (m, r) in enumerate(zip(modules, sizes)):
+        c, s, b = codes[r0:r0 + r], scales[r0:r0 + r], bits_t[r0:r0 + r]
+        if m.get("B") is not None:
+            wr.wr_wring_solve(ctx, H, b, group, lam, c, s, info[2 + k:3 + k], B=m["B"], A=m["A"],
+                              alpha=m.get("alpha", m["A"].shape[0]), recode=True)
+        res = {"codes": c, "scales": s, "packed": pack(ctx, c, s, int(m["bits"]), group), "rows": (r0, r0 + r),
+               "bits": int(m["bits"])}
+        for key, val in stages.items():
+            res[key] = val[r0:r0 + r]
+        out[m["name"]] = res
+        r0 += r
+    out["_dev_info"] = info
+    return out
+
+
+def container_bytes(entries, meta):
+    """A safetensors-format container: an 8-byte little-endian header length, a JSON header naming
+    each packed buffer (dtype U8, 1-D) and carrying `wringer_meta` (JSON text) under __metadata__,
+    then the raw bytes in order.  entries: list of (name, host uint8 numpy array)."""
+    import json
+    import struct
+    header = {"__metadata__": {"wringer_meta": json.dumps(meta, sort_keys=True)}}
+    off = 0
+    for name, buf in entries:
+        header[name] = {"dtype": "U8", "shape": [int(buf.size)], "data_offsets": [off, off + int(buf.size)]}
+        off += int(buf.size)
+    text = json.dumps(header, separators=(",", ":")).encode()
+    text += b" " * ((8 - len(text) % 8) % 8)
+    return b"".join([struct.pack("<Q", len(text)), text] + [buf.tobytes() for _, buf in entries])

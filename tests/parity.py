@@ -26,3 +26,180 @@ def code_parity(gpu_codes, ref_codes, ref_t, L):
 
 def scale_ulps(gpu_scales, ref_scales):
     return np.abs(f16_bits(gpu_scales) - f16_bits(ref_scales))
+
+
+def assert_scales_close(u, two_ulp_frac):
+    """u: fp16 ulp distances.  All within 1 ulp when two_ulp_frac is 0; otherwise at most
+    two_ulp_frac of them may sit 2 ulps away and none further."""
+    if u.size == 0:
+        return
+    if two_ulp_frac == 0:
+        assert u.max() <= 1, np.bincount(u.ravel())
+    else:
+        assert u.max() <= 2 and np.mean(u > 1) <= two_ulp_frac, np.bincount(u.ravel())
+
+
+def stage_check(out, ref, H0, bits, g, L, tie, strict_loss=False, two_ulp_frac=0.0):
+    """Stage by stage against the oracle.
+
+    two_ulp_frac > 0 is for runs in which each side forms its own H: the GPU's H differs from
+    the oracle's fp64 H by about 2e-7 (fp32 sums of the split products, fp32 storage), and the
+    block scales depend on H through the factorisation with a condition number near 1e4 on
+    these inputs, so a scale's unrounded value can move by ~2e-3, i.e. up to 2 fp16 ulps, on
+    rare blocks.  With the same H the scales agree within 1 ulp (the kernel tests).
+
+    GPTQ codes: at most 0.1 % differ and each row's first difference sits at a rounding
+    boundary.  A row whose GPTQ codes differ is a different valid rounding, so later stages
+    are compared on the rows that agree upstream: joint scales within 1 ulp; wring codes
+    again with first differences at boundaries; final scales within 1 ulp.  Proxy loss
+    within 1e-4: over all rows for the configurations the bar is stated on (strict_loss),
+    otherwise over the rows whose codes and scales agree (one ulp of one scale can move a
+    100-row problem's loss by more than 1e-4)."""
+    if "dev_info" in out:
+        assert (out["dev_info"].cpu().numpy() == 0).all()
+    rows = out["codes"].shape[0]
+    Lr = np.broadcast_to(np.asarray(L), (rows,))
+    keep = np.ones(rows, dtype=bool)
+    if "gptq_codes" in out:
+        gc = out["gptq_codes"].cpu().numpy().astype(np.int64)
+        cp = code_parity(gc, ref["gptq_codes"], ref["gptq_t"], Lr)
+        assert cp["frac"] <= 1e-3 and cp["worst_first"] <= tie, ("gptq", cp)
+        keep &= cp["identical_rows"]
+        gs = out["gptq_scales"].cpu().numpy().astype(np.float64)
+        assert_scales_close(scale_ulps(gs[keep], ref["gptq_scales"][keep]), two_ulp_frac)
+        js = out["joint_scales"].cpu().numpy().astype(np.float64)
+        uj = scale_ulps(js[keep], ref["joint_scales"][keep])
+        assert_scales_close(uj, two_ulp_frac)
+        keep[keep] &= uj.max(axis=1, initial=0) == 0
+    codes = out["codes"].cpu().numpy().astype(np.int64)
+    scales = out["scales"].cpu().numpy().astype(np.float64)
+    cp = code_parity(codes[keep], ref["codes"][keep], ref["wring_t"][keep], Lr[keep])
+    assert cp["worst_first"] <= tie, ("wring", cp)
+    assert np.mean(codes != ref["codes"]) <= 1e-3
+    ok = keep.copy()
+    ok[keep] &= cp["identical_rows"]
+    assert_scales_close(scale_ulps(scales[ok], ref["scales"][ok]), two_ulp_frac)
+    bits_r = np.broadcast_to(bits, (rows,))
+    dq_g = oracle.dequant(codes, scales, bits_r, g)
+    dq_r = oracle.dequant(ref["codes"], ref["scales"], bits_r, g)
+    same = ok & (scale_ulps(scales, ref["scales"]).max(axis=1) == 0)
+    lg = oracle.proxy_loss(ref["target"][same], dq_g[same], H0)
+    lr = oracle.proxy_loss(ref["target"][same], dq_r[same], H0)
+    assert abs(lg - lr) <= 1e-4 * lr
+    la = oracle.proxy_loss(ref["target"], dq_g, H0)
+    lra = oracle.proxy_loss(ref["target"], dq_r, H0)
+    if strict_loss:
+        assert abs(la - lra) <= 1e-4 * lra
+    print(f"rows agreeing upstream {keep.sum()}/{rows}; final codes differing {np.mean(codes != ref['codes']):.2e}; "
+          f"proxy loss rel diff (all rows) {abs(la - lra) / lra:.2e}")
+    return codes, scales
+
+
+def _near_neighbour(choice_gpu, choice_ref, dist, tie):
+    """Decisions where the GPU took the adjacent code of a value within `tie` of a threshold."""
+    return (choice_gpu != choice_ref) & (np.abs(choice_gpu - choice_ref) == 1) & (dist <= tie)
+
+
+def guided_solve_rows(W, H, bits, g, lam, B, A, alpha, gpu, tie, max_scale_ulps=2):
+    """The oracle's solve of some rows, following the GPU at genuine ties.
+
+    GPTQ's error feedback makes every later column depend on every earlier rounding, so after a
+    legitimate near-tie decision the rest of the row follows a different valid trajectory.  This
+    runs the oracle's own primitives (feedback sweep, nearest code, fp16 projection, joint scales,
+    wring) in the oracle's order, and wherever the GPU's decision differs from the oracle's it
+    takes the GPU's decision only if that decision is one the definition allows up to rounding:
+      * a code one level away from the oracle's, with the oracle's value within `tie` (level
+        units) of the threshold between them;
+      * an fp16 scale within max_scale_ulps ulps of the oracle's (rounding of a value computed
+        from an H that differs by the accumulation error, see stage_check).
+    Any other disagreement is reported.  Returns (ref, stats): ref has the keys of
+    oracle.solve_rows; stats counts the decisions taken from the GPU per stage and lists the
+    unexplained disagreements (which must be empty).
+    """
+    W = np.asarray(W, dtype=np.float64)
+    rows, n = W.shape
+    nb = n // g
+    L = np.broadcast_to(oracle.levels_count(bits), (rows,)).astype(np.float64)
+    gc = {k: np.asarray(v.cpu().numpy() if hasattr(v, "cpu") else v).astype(np.int64 if "codes" in k else np.float64)
+          for k, v in gpu.items()}
+    stats = {"codes_forced": 0, "scales_forced": 0, "scales_2ulp": 0, "unexplained": [], "by_stage": {}}
+
+    def take_scales(s_ref, s_gpu, where):
+        u = np.abs(f16_bits(s_gpu) - f16_bits(s_ref))
+        ok = u <= max_scale_ulps
+        if not np.all(ok):
+            stats["unexplained"].append((where, "scale", int(np.sum(~ok)), int(u.max())))
+        force = (u > 0) & ok
+        stats["scales_forced"] += int(np.sum(force))
+        stats["scales_2ulp"] += int(np.sum(u == 2))
+        key = where[0]
+        c = stats["by_stage"].setdefault(key, [0, 0])
+        c[0] += int(np.sum(u == 1))
+        c[1] += int(np.sum(u == 2))
+        return np.where(force, s_gpu, s_ref)
+
+    def take_codes(c_ref, c_gpu, t, Lr, where):
+        dist = oracle.threshold_distance(t, Lr)
+        force = _near_neighbour(c_gpu, c_ref, dist, tie)
+        bad = (c_gpu != c_ref) & ~force
+        if np.any(bad):
+            stats["unexplained"].append((where, "code", int(np.sum(bad)), float(dist[bad].min())))
+        stats["codes_forced"] += int(np.sum(force))
+        return np.where(force, c_gpu, c_ref)
+
+    # GPTQ sweep with guided decisions
+    U = oracle.upper_cholesky_of_inverse(H)
+    codes = np.zeros((rows, n), dtype=np.int64)
+    scales = np.zeros((rows, nb))
+    tvals = np.zeros((rows, n))
+
+    def round_column(k, Wt):
+        b = k // g
+        if k % g == 0:
+            s_ref = oracle.fp16_rne(np.max(np.abs(Wt[:, k:k + g]), axis=1) / L)
+            scales[:, b] = take_scales(s_ref, gc["gptq_scales"][:, b], ("gptq", b))
+        s = scales[:, b]
+        t = np.divide(Wt[:, k], s, out=np.zeros(rows), where=s > 0)
+        c = take_codes(oracle.nearest_code(t, L), gc["gptq_codes"][:, k], t, L, ("gptq", k))
+        codes[:, k] = c
+        tvals[:, k] = t
+        return (2 * c - L) * s
+
+    oracle.feedback_sweep(W, U, round_column)
+    # joint scales against W
+    s1, _ = oracle.joint_scales(codes, bits, g, H, W, scales, lam)
+    s1 = take_scales(s1, gc["joint_scales"], ("joint", -1))
+    # wring: nearest-point recode of W' on the current scales, then joint scales against W'
+    Wp = oracle.wring_target(codes, s1, bits, g, B, A, alpha)
+    srep = np.repeat(s1, g, axis=1)
+    t = np.divide(Wp, srep, out=np.zeros_like(Wp), where=srep > 0)
+    c2 = take_codes(oracle.nearest_code(t, L[:, None]), gc["codes"], t, L[:, None], ("wring", -1))
+    s2, _ = oracle.joint_scales(c2, bits, g, H, Wp, s1, lam)
+    s2 = take_scales(s2, gc["scales"], ("final", -1))
+    ref = {"gptq_codes": codes, "gptq_scales": scales, "gptq_t": tvals, "joint_scales": s1,
+           "codes": c2, "scales": s2, "target": Wp, "wring_t": t}
+    return ref, stats
+
+
+def guided_check(gpu, W, H, H0, bits, g, lam, B, A, alpha, tie, max_forced_frac=1e-3):
+    """Parity of the GPU's sampled rows with the guided oracle: every GPU decision is either the
+    oracle's or a near-tie alternative; at most max_forced_frac of the codes are taken from the GPU
+    at ties; every scale is within 1 fp16 ulp of the oracle's except at most max_forced_frac of them
+    (and at least 2) at 2 ulps; the GPU's proxy loss equals the guided oracle's within 1e-4."""
+    ref, st = guided_solve_rows(W, H, bits, g, lam, B, A, alpha, gpu, tie)
+    rows, n = np.asarray(W).shape
+    assert not st["unexplained"], st["unexplained"][:5]
+    ncodes = 2 * rows * n
+    nscales = 3 * rows * (n // g)
+    assert st["codes_forced"] <= max_forced_frac * ncodes, st
+    assert st["scales_2ulp"] <= max(2, max_forced_frac * nscales), st
+    codes = gpu["codes"].cpu().numpy().astype(np.int64)
+    scales = gpu["scales"].cpu().numpy().astype(np.float64)
+    assert np.array_equal(codes, ref["codes"]) and np.array_equal(f16_bits(scales), f16_bits(ref["scales"]))
+    bits_r = np.broadcast_to(bits, (rows,))
+    lg = oracle.proxy_loss(ref["target"], oracle.dequant(codes, scales, bits_r, g), H0)
+    lr = oracle.proxy_loss(ref["target"], oracle.dequant(ref["codes"], ref["scales"], bits_r, g), H0)
+    assert abs(lg - lr) <= 1e-4 * lr
+    print(f"guided oracle: {rows} rows; codes taken at ties {st['codes_forced']} of {ncodes}; scales off by "
+          f"[1, 2] ulps per stage {st['by_stage']} of {nscales // 3} each", flush=True)
+    return ref, st

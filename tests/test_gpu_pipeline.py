@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import oracle
-from parity import code_parity, scale_ulps
+from parity import stage_check
 
 pytestmark = pytest.mark.gpu
 # Each side forms its own H here (GPU: exact products, fp32 segments of 512 rows added in fp64;
@@ -19,55 +19,6 @@ def ctx():
     return _lib.Context(0)
 
 
-def _check(out, ref, H0, bits, g, L, strict_loss=False):
-    """Stage by stage against the oracle.
-
-    GPTQ codes: at most 0.1 % differ and each row's first difference sits at a rounding
-    boundary.  A row whose GPTQ codes differ is a different valid rounding, so later stages
-    are compared on the rows that agree upstream: joint scales within 1 ulp; wring codes
-    again with first differences at boundaries; final scales within 1 ulp.  Proxy loss
-    within 1e-4: over all rows for the configurations the bar is stated on (strict_loss),
-    otherwise over the rows whose codes and scales agree (one ulp of one scale can move a
-    100-row problem's loss by more than 1e-4)."""
-    assert (out["dev_info"].cpu().numpy() == 0).all()
-    rows = out["codes"].shape[0]
-    Lr = np.broadcast_to(np.asarray(L), (rows,))
-    keep = np.ones(rows, dtype=bool)
-    if "gptq_codes" in out:
-        gc = out["gptq_codes"].cpu().numpy().astype(np.int64)
-        cp = code_parity(gc, ref["gptq_codes"], ref["gptq_t"], Lr)
-        assert cp["frac"] <= 1e-3 and cp["worst_first"] <= TIE, ("gptq", cp)
-        keep &= cp["identical_rows"]
-        gs = out["gptq_scales"].cpu().numpy().astype(np.float64)
-        assert scale_ulps(gs[keep], ref["gptq_scales"][keep]).max(initial=0) <= 1
-        js = out["joint_scales"].cpu().numpy().astype(np.float64)
-        uj = scale_ulps(js[keep], ref["joint_scales"][keep])
-        assert uj.max(initial=0) <= 1
-        keep[keep] &= uj.max(axis=1) == 0
-    codes = out["codes"].cpu().numpy().astype(np.int64)
-    scales = out["scales"].cpu().numpy().astype(np.float64)
-    cp = code_parity(codes[keep], ref["codes"][keep], ref["wring_t"][keep], Lr[keep])
-    assert cp["worst_first"] <= TIE, ("wring", cp)
-    assert np.mean(codes != ref["codes"]) <= 1e-3
-    ok = keep.copy()
-    ok[keep] &= cp["identical_rows"]
-    assert scale_ulps(scales[ok], ref["scales"][ok]).max(initial=0) <= 1
-    bits_r = np.broadcast_to(bits, (rows,))
-    dq_g = oracle.dequant(codes, scales, bits_r, g)
-    dq_r = oracle.dequant(ref["codes"], ref["scales"], bits_r, g)
-    same = ok & (scale_ulps(scales, ref["scales"]).max(axis=1) == 0)
-    lg = oracle.proxy_loss(ref["target"][same], dq_g[same], H0)
-    lr = oracle.proxy_loss(ref["target"][same], dq_r[same], H0)
-    assert abs(lg - lr) <= 1e-4 * lr
-    la = oracle.proxy_loss(ref["target"], dq_g, H0)
-    lra = oracle.proxy_loss(ref["target"], dq_r, H0)
-    if strict_loss:
-        assert abs(la - lra) <= 1e-4 * lra
-    print(f"rows agreeing upstream {keep.sum()}/{rows}; final codes differing {np.mean(codes != ref['codes']):.2e}; "
-          f"proxy loss rel diff (all rows) {abs(la - lra) / lra:.2e}")
-    return codes, scales
-
-
 def test_toy_layer_end_to_end(ctx):
     """W 256x512 fp32, X 4096x512 fp32 (5 outlier channels), 2-bit g32, rank-8 adapter alpha 8, lambda 0.01."""
     from post_bit_weight_amd import pipeline, synth
@@ -79,7 +30,7 @@ def test_toy_layer_end_to_end(ctx):
                                 A.cuda(), 8.0, keep_stages=True)
     ref = oracle.solve_module(W.double().numpy(), X.double().numpy(), 2, 32, 0.01, 0.01, B.double().numpy(),
                               A.double().numpy(), 8.0)
-    codes, scales = _check(out, ref, ref["H0"], 2, 32, 3, strict_loss=True)
+    codes, scales = stage_check(out, ref, ref["H0"], 2, 32, 3, TIE, strict_loss=True)
     # the packed container is bit-exact given identical codes and scales
     from post_bit_weight_amd import _lib as wr
     buf = torch.empty(oracle.packed_bytes(256, 512, 2, 32), dtype=torch.uint8, device="cuda")
@@ -104,7 +55,7 @@ def test_rotated_padded_layer_end_to_end(ctx):
                               A.double().numpy(), 8.0, had_block=m, signs=s.double().numpy(), n_store=n)
     Hg = out["H"].cpu().double().numpy()
     assert np.linalg.norm(Hg - ref["H"]) <= 1e-5 * np.linalg.norm(ref["H"])
-    _check(out, ref, ref["H0"], 2, 64, 3)
+    stage_check(out, ref, ref["H0"], 2, 64, 3, TIE)
 
 
 def test_mixed_bits_shared_H(ctx):
@@ -124,4 +75,4 @@ def test_mixed_bits_shared_H(ctx):
                             A.cuda(), 16.0, keep_stages=True)
     ref = oracle.solve_module(W.double().numpy(), X.double().numpy(), bits, g, 0.01, 0.01, B.double().numpy(),
                               A.double().numpy(), 16.0)
-    _check(out, ref, ref["H0"], bits, g, oracle.levels_count(bits))
+    stage_check(out, ref, ref["H0"], bits, g, oracle.levels_count(bits), TIE)

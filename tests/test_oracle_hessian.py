@@ -43,3 +43,17 @@ def test_damping_uses_stored_dimension_and_reaches_padding():
     assert np.isclose(delta, 0.01 * 15.0 / 4)
     assert np.allclose(np.diag(H), [5.0 + delta, 10.0 + delta, delta, delta])
     assert np.all(H[2:, :2] == 0) and np.all(H[:2, 2:] == 0)
+
+
+def test_chunked_second_moment_and_single_entries_match_the_hand_sum():
+    rng = np.random.default_rng(2)
+    X = rng.integers(-3, 4, size=(9, 4)).astype(np.float64)
+    brute = np.zeros((4, 4))
+    for row in X.tolist():
+        for i in range(4):
+            for j in range(4):
+                brute[i, j] += row[i] * row[j]
+    H0 = oracle.second_moment_chunks([X[:2], X[2:7], X[7:]])
+    assert np.array_equal(H0, brute / 9.0)
+    pairs = [(0, 0), (3, 1), (2, 3)]
+    assert np.array_equal(oracle.sum_of_products(X, pairs), [brute[i, j] for i, j in pairs])
