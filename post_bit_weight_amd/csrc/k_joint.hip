@@ -193,7 +193,10 @@ __global__ __launch_bounds__(256) void gram_kernel(const uint16_t* __restrict__ 
 #pragma unroll
         for (int v = 0; v < 16; ++v) part = fmaf(levj[ib][v], accG[ib][v], part);
       part += __shfl_xor(part, 32);
-      if (lane < 32 && rok) Gm[((size_t)r * nb + b) * nb + c] = part;
+      if (lane < 32 && rok) {
+        Gm[((size_t)r * nb + b) * nb + c] = part;
+        Gm[((size_t)r * nb + c) * nb + b] = part;
+      }
     }
   }
   float part = 0.0f;
@@ -203,6 +206,85 @@ __global__ __launch_bounds__(256) void gram_kernel(const uint16_t* __restrict__ 
     for (int v = 0; v < 16; ++v) part = fmaf(levj[ib][v], rtot[ib][v], part);
   part += __shfl_xor(part, 32);
   if (lane < 32 && rok) rhs[(size_t)r * nb + b] = part;
+}
+
+__device__ __forceinline__ double wave_bcast_f64(double v, int lane) {
+  const int64_t u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(u & 0xffffffff), lane);
+  const int hi = __builtin_amdgcn_readlane((int)(u >> 32), lane);
+  return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
+}
+
+__device__ __forceinline__ double rsqrt_refined(double d) {
+  double r = (double)rsqrtf((float)d);
+  r = r * (1.5 - 0.5 * d * r * r);
+  r = r * (1.5 - 0.5 * d * r * r);
+  return r;
+}
+
+// Per row, nb <= NB: (G + lambda mu I) s = h + lambda mu s0 in fp64, s -> fp16.  One wave per
+// row (G full symmetric, row-major nb x nb fp32): lane i holds row i of the matrix in registers
+// (identity rows past nb), the Cholesky factor L is formed in place with the pivot columns
+// broadcast by readlane, z = L^-1 y by forward substitution in the same layout, then L goes
+// through LDS once so that lane i holds column i for the back substitution L^T s = z.
+template <int NB>
+__global__ __launch_bounds__(64) void row_solve_wave_kernel(const float* __restrict__ Gm, const float* __restrict__ rhs,
+                                                            int64_t rows, int nb, float lambda,
+                                                            uint16_t* __restrict__ scales,
+                                                            const int32_t* __restrict__ dev_info) {
+  __shared__ double lt[NB * (NB + 1)];
+  if (*dev_info != 0) return;
+  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x;
+  const bool live = lane < nb;
+  const float* g = Gm + (size_t)row * nb * nb;
+  double tr = live ? (double)g[(size_t)lane * nb + lane] : 0.0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) tr += __shfl_xor(tr, o);
+  const double reg = (double)lambda * tr / nb;
+  double a[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    double v = j == lane ? 1.0 : 0.0;
+    if (live && j < nb) v = (double)g[(size_t)lane * nb + j] + (j == lane ? reg : 0.0);
+    a[j] = v;
+  }
+  double y = live ? (double)rhs[(size_t)row * nb + lane] + reg * (double)f16_bits_to_f32(scales[(size_t)row * nb + lane])
+                  : 0.0;
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const double d = wave_bcast_f64(a[k], k);
+    bad |= !(d > 0.0);
+    const double l = a[k] * rsqrt_refined(d);  // lane k: L_kk; lanes below: L_ik
+    a[k] = l;
+#pragma unroll
+    for (int j = k + 1; j < NB; ++j) a[j] = fma(-l, wave_bcast_f64(l, j), a[j]);
+  }
+  if (bad) return;  // only reachable with lambda == 0 and a singular G: keep the incoming scales
+  // z = L^-1 y (lane i: row i of L)
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const double zk = wave_bcast_f64(y, k) / wave_bcast_f64(a[k], k);
+    y = lane == k ? zk : (lane > k ? fma(-a[k], zk, y) : y);
+  }
+  // transpose L through LDS: lane i then holds L_ki (k >= i) in a[k]
+  if (lane < NB) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) lt[lane * (NB + 1) + j] = j <= lane ? a[j] : 0.0;
+  }
+  __syncthreads();
+  if (lane < NB) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) a[k] = lt[k * (NB + 1) + lane];
+  }
+  // L^T s = z, last unknown first
+#pragma unroll
+  for (int k = NB - 1; k >= 0; --k) {
+    const double sk = wave_bcast_f64(y, k) / wave_bcast_f64(a[k], k);
+    y = lane == k ? sk : (lane < k ? fma(-a[k], sk, y) : y);
+  }
+  if (live) scales[(size_t)row * nb + lane] = f64_to_f16_bits_clamped(y);
 }
 
 // Per row: (G + lambda mu I) s = h + lambda mu s0 in fp64 (packed lower Cholesky in LDS), s -> fp16.
@@ -355,6 +437,19 @@ int wr_wring_solve_impl(wr_ctx* ctx, const void* target, int t_dtype, int64_t ld
     default: hipLaunchKernelGGL(gram_kernel<128>, ggrid, dim3(256), 0, st, Lev, T0, T1, T2, rows, n, H0, H1, H2, Gm, rh, dev_info); break;
   }
   WR_CHECK_LAUNCH();
+  if (nb <= 64) {
+    const dim3 grid((unsigned)rows);
+    if (nb <= 16)
+      hipLaunchKernelGGL(row_solve_wave_kernel<16>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, dev_info);
+    else if (nb <= 32)
+      hipLaunchKernelGGL(row_solve_wave_kernel<32>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, dev_info);
+    else if (nb <= 48)
+      hipLaunchKernelGGL(row_solve_wave_kernel<48>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, dev_info);
+    else
+      hipLaunchKernelGGL(row_solve_wave_kernel<64>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, dev_info);
+    WR_CHECK_LAUNCH();
+    return WR_OK;
+  }
   const size_t shbytes = ((size_t)nb * (nb + 1) / 2 + nb) * sizeof(double);
   if (shbytes > 160 * 1024) return WR_EUNSUPPORTED;
   if (shbytes > 64 * 1024 &&
