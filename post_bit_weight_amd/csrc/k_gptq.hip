@@ -80,10 +80,22 @@ __global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict
   const int64_t row = (int64_t)blockIdx.x * (256 / P) + tid / P;
   const bool active = row < rows;
 
-  for (int e = tid; e < BATCH * BATCH; e += 256) {
-    const int k = e / BATCH, j = e % BATCH;
-    const float v = (k < ncols && j < ncols) ? M[(int64_t)(b0 + k) * n + b0 + j] : 0.0f;
-    Ms[k * BATCH + (j % P) * S + j / P] = v;
+  {
+    // M's diagonal batch block: every thread's 16 four-wide loads are in flight before the LDS stores
+    static_assert(BATCH * BATCH == 256 * 64, "16 loads of four floats per thread");
+    f32x4 mv[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = 4 * (tid + 256 * q), k = e / BATCH, j = e % BATCH;
+      mv[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (k < ncols && j < ncols) mv[q] = *reinterpret_cast<const f32x4*>(M + (int64_t)(b0 + k) * n + b0 + j);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = 4 * (tid + 256 * q), k = e / BATCH, j = e % BATCH;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Ms[k * BATCH + ((j + u) % P) * S + (j + u) / P] = mv[q][u];
+    }
   }
 
   float w[S], c[S], d[S];
