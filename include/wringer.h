@@ -89,11 +89,9 @@ int wr_set_workspace(wr_ctx* ctx, void* dev_ptr, size_t bytes);
  * first.  Call once per chunk of calibration rows.  n % 8 == 0; for bf16 X,
  * ldx % 8 == 0 and X 16-byte aligned; ldx <= 2^24 (WR_EUNSUPPORTED above).
  * Products are exact: bf16 inputs directly, fp32 inputs as three bf16 parts
- * (x = x0 + x1 + x2, six cross terms).  The call's rows are cut into splits
- * (at most 16384 rows each for calls of up to 2^20 rows; for fp32 X, 512
- * rows in calls of up to 32768 rows), each split is summed in fp32 on the matrix cores, and the splits are
- * added into S in fp64 in a fixed order: the result is deterministic with a
- * relative error near 1e-7.
+ * (x = x0 + x1 + x2, six cross terms).  The matrix cores sum at most 16384 rows
+ * (512 for fp32 X) in fp32 before the sums are added into S in fp64, in a fixed
+ * order: the result is deterministic with a relative error near 1e-7.
  * Workspace: WR_OP_HESSIAN with (rows, n).  rows may be 0 (no-op unless
  * WR_H_ZERO).
  */

@@ -11,9 +11,12 @@
 // rows of one feature per lane), so the rows are copied untransposed into LDS by
 // LDS-DMA loads (global_load_lds, no registers, several stages in flight) and
 // transposed on the way out by the gfx950 transposing LDS read
-// (ds_read_b64_tr_b16).  bf16 x bf16 products are exact in fp32; the MFMAs sum
-// a split of at most a few thousand rows in fp32, and the splits are added into
-// S in fp64 by a second kernel in a fixed order (deterministic, no atomics).
+// (ds_read_b64_tr_b16).  bf16 x bf16 products are exact in fp32; the MFMAs sum at
+// most 16384 rows in fp32 before the sums reach S in fp64: either every
+// workgroup adds its tile into S itself (one split per tile, when the tiles alone
+// fill the chip; calls longer than 16384 rows become one launch per 16384-row
+// slice), or the rows are cut into splits whose fp32 sums a second kernel adds
+// into S in a fixed order.  Deterministic, no atomics.
 #include "common.hpp"
 
 namespace wr {
@@ -28,6 +31,7 @@ constexpr int SY_LDS_BYTES = SY_NS * SY_STAGE_BYTES;  // 160 KB
 constexpr int SY_THREADS = 512;          // eight waves
 constexpr int SY_DMA_PER_WAVE = (SY_STAGE_BYTES / 1024) / (SY_THREADS / 64);  // 1 KB per wave-wide DMA
 constexpr int SY_XCD = 8;                // workgroups are dispatched round-robin over 8 XCDs
+constexpr int SY_MAX_ROWS = 16384;       // rows summed in fp32 before the sums reach S in fp64
 
 // Lower-triangle tile t -> (I, J), J <= I, row-major over the block triangle.
 __device__ __forceinline__ void tri_tile(int t, int& I, int& J) {
@@ -354,19 +358,25 @@ static int syrk_tiles(int64_t n) {
   return nt * (nt + 1) / 2;
 }
 
-// Number of row splits.  Each split is summed in fp32 by the MFMAs, so a split holds
-// at most 16384 rows (more splits only for calls beyond 2^20 rows, capped at 64).
-// Splits come in multiples of the XCD count (each XCD works through its own rows)
-// and are added while the chip has fewer workgroups than CUs.  With `precise` (the
-// fp32-input path, whose six passes rebuild an fp32-accurate S) a split is at most
-// 512 rows.
+// Number of row splits.  A split is summed in fp32 by the MFMAs over at most 16384 rows.  When
+// the lower 256 x 256 tiles alone give at least one workgroup per CU there is one split per tile
+// and each workgroup adds its sums into S (fp64) itself: no partial buffer (the host then
+// launches once per 16384-row slice).
+// Otherwise the rows are cut into enough splits to fill the CUs (and to keep each at most 16384
+// rows); from 8 splits up their number is a multiple of the XCD count (each XCD works through its
+// own rows).  With `precise` (the fp32-input path, whose six passes rebuild an fp32-accurate S)
+// a split is at most 512 rows.
 static int syrk_ksplit(int64_t rows, int64_t n, int num_cu, bool precise) {
   if (rows <= 0) return 1;
   if (precise) return (int)std::min<int64_t>(64, (rows + 511) / 512);
-  if (rows < SY_XCD * 1024) return (int)std::max<int64_t>(1, rows / 1024);
   const int tiles = syrk_tiles(n);
-  int64_t ks = ((rows + 16383) / 16384 + SY_XCD - 1) / SY_XCD * SY_XCD;
-  while (ks < 64 && tiles * ks < num_cu && rows / (ks + SY_XCD) >= 1024) ks += SY_XCD;
+  if (tiles >= num_cu) return 1;
+  if (rows < SY_XCD * 1024) return (int)std::max<int64_t>(1, rows / 1024);
+  int64_t ks = std::max<int64_t>((rows + 16383) / 16384, (num_cu + tiles - 1) / tiles);
+  if (ks >= SY_XCD) {
+    ks = (ks + SY_XCD - 1) / SY_XCD * SY_XCD;
+    while (ks < 64 && tiles * ks < num_cu && rows / (ks + SY_XCD) >= 1024) ks += SY_XCD;
+  }
   return (int)std::min<int64_t>(ks, 64);
 }
 
@@ -395,6 +405,15 @@ static int syrk_pass(wr_ctx* ctx, const uint16_t* XA, const uint16_t* XB, int64_
   hipStream_t st = ctx->stream;
   const int tiles = syrk_tiles(n);
   const int ks = syrk_ksplit(rows, n, kSplitCUs, precise);
+  if (ks == 1 && rows > SY_MAX_ROWS) {
+    for (int64_t r0 = 0; r0 < rows; r0 += SY_MAX_ROWS) {
+      const int64_t rc = std::min<int64_t>(SY_MAX_ROWS, rows - r0);
+      hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)tiles), dim3(SY_THREADS), SY_LDS_BYTES, st, XA + r0 * ldx,
+                         XB + r0 * ldx, rc, (int)n, ldx, rc, tiles, 1, S, nullptr);
+      WR_CHECK_LAUNCH();
+    }
+    return WR_OK;
+  }
   const int64_t rps = ((rows + ks - 1) / ks + SY_KT - 1) / SY_KT * SY_KT;
   hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)(tiles * ks)), dim3(SY_THREADS), SY_LDS_BYTES, st, XA, XB, rows, (int)n,
                      ldx, rps, tiles, ks, S, ks > 1 ? partial : nullptr);
