@@ -112,6 +112,10 @@ def cpu_baseline(X_host, W_host, B_host, A_host, cfg, n_rows, n_calib):
     }
 
 
+def progress(msg):
+    print(f"bench.py: {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -130,6 +134,7 @@ def main():
     ctx = wr.Context(0)
     st = ctx.stream
 
+    progress("drawing the synthetic inputs")
     src = synth.SpectralSource(n, seed=20261204, device="cuda", outlier_frac=0.01)
     X = torch.cat([src.chunk(k, 16384) for k in range(N // 16384)])
     W = synth.student_t((rows, n), seed=20261205, device="cuda", dtype=torch.bfloat16)
@@ -177,12 +182,14 @@ def main():
         wr.wr_pack(ctx, codes, scales, bits, g, packed)
         mark(6)
 
+    progress("warmup")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     if int(info.abs().sum().item()) != 0:
         raise RuntimeError(f"dev_info reports a failure: {info.tolist()}")
 
+    progress(f"timing {args.steps} steps")
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -221,6 +228,7 @@ def main():
         "stage_ms": per_stage,
     }
     if not args.no_cpu_baseline:
+        progress("timing the oracle on a bounded sample")
         Xh = X[: args.cpu_calib].float().cpu().numpy()
         Wh = W.float().cpu().numpy()
         Bh = B.float().cpu().numpy()
