@@ -8,17 +8,19 @@
 // inverse of the whole matrix.
 //
 // fp64 blocked right-looking Cholesky, block CB = 64.  A diagonal block is
-// factored and its factor inverted by one workgroup: two 32 x 32 halves, each
-// factored and inverted by one wave in registers (rows in lanes, pivot columns
-// broadcast with readlane), glued by fp64 MFMA products in LDS.  Per block
-// column kb two kernels:
-//   chol_panel_kernel  the block column below, P = A_panel L_kk^-T = A_panel X^T,
-//                      on the fp64 matrix cores (the factor's final block
-//                      column, written to L);
+// factored by one workgroup in 16 x 16 blocks: each diagonal 16 x 16 block is
+// factored and its factor inverted at once by one wave in registers (rows of A
+// and columns of the identity side by side in the lanes, pivot columns broadcast
+// with readlane), the rest are fp64 MFMA products in LDS.  Per block column kb
+// two kernels:
+//   chol_panel_kernel  the block column below, P = A_panel L_kk^-T, as a blocked
+//                      triangular solve with the inverted 16 x 16 diagonal
+//                      blocks on the fp64 matrix cores (the factor's final
+//                      block column, written to L);
 //   chol_step_kernel   the trailing lower matrix, A_ij -= P_i P_j^T, one 64 x 64
 //                      tile per workgroup on the fp64 matrix cores, while
-//                      workgroup 0 updates, factors and inverts the next
-//                      diagonal block (lookahead).
+//                      workgroup 0 updates and factors the next diagonal block
+//                      (lookahead).
 // A pivot that is not positive sets dev_info (1-based pivot of J H J) and every
 // later kernel returns at once.
 #include "common.hpp"
@@ -37,11 +39,13 @@ __device__ __forceinline__ double bcast_f64(double v, int lane) {
   return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
 }
 
-// 1/sqrt(d) to fp64 precision: fp32 estimate, two Newton steps.
-__device__ __forceinline__ double rsqrt_newton(double d) {
-  double r = (double)rsqrtf((float)d);
-  r = r * (1.5 - 0.5 * d * r * r);
-  r = r * (1.5 - 0.5 * d * r * r);
+// 1/sqrt(d) to fp64 precision: the hardware estimate (about 23 correct bits over the
+// whole fp64 range), two Newton steps r <- r (3 - d r^2) / 2.
+__device__ __forceinline__ double rsqrt_f64(double d) {
+  const double h = 0.5 * d;
+  double r = __builtin_amdgcn_rsq(d);
+  r = r * fma(-h * r, r, 1.5);
+  r = r * fma(-h * r, r, 1.5);
   return r;
 }
 
@@ -69,11 +73,11 @@ __device__ __forceinline__ void load_block64(const double* __restrict__ G, int64
   }
 }
 
-// acc += sum_{k < K} A(r, k) B(k, c) for one 16 x 16 block (v_mfma_f64_16x16x4f64).
-// A(r, k) = SA[(r0 + r) * lda + k].  B(k, c) = SB[(c0 + c) * ldb + k] when BT (the
-// "A B^T" form), else SB[k * ldb + c0 + c].  Operand lane l supplies row/column
-// l % 16 at k = l / 16; accumulator v of lane l is row l / 16 + 4 v, column l % 16.
-template <bool BT>
+// acc += sum_{k < K} A(r, k) B(k, c) for one 16 x 16 block (v_mfma_f64_16x16x4f64);
+// acc -= ... when NEG.  A(r, k) = SA[(r0 + r) * lda + k].  B(k, c) = SB[(c0 + c) * ldb + k]
+// when BT (the "A B^T" form), else SB[k * ldb + c0 + c].  Operand lane l supplies
+// row/column l % 16 at k = l / 16; accumulator v of lane l is row l / 16 + 4 v, column l % 16.
+template <bool BT, bool NEG = false>
 __device__ __forceinline__ f64x4 mma16(const double* SA, int lda, int r0, const double* SB, int ldb, int c0, int K,
                                        f64x4 acc, int lane) {
   const int li = lane & 15, lk = lane >> 4;
@@ -81,115 +85,117 @@ __device__ __forceinline__ f64x4 mma16(const double* SA, int lda, int r0, const 
   for (int k0 = 0; k0 < K; k0 += 4) {
     const double a = SA[(r0 + li) * lda + k0 + lk];
     const double b = BT ? SB[(c0 + li) * ldb + k0 + lk] : SB[(k0 + lk) * ldb + c0 + li];
-    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(NEG ? -a : a, b, acc, 0, 0, 0);
   }
   return acc;
 }
 
-// Cholesky of the 32 x 32 block of sM at (o, o) in place (lower part; the strict
-// upper part is cleared).  One wave: lane i < 32 holds row i in registers; the
-// column of pivot k is broadcast lane by lane; rinv[o + k] receives 1 / L_kk.
+// Cholesky of the 16 x 16 block of sM at (o, o) together with the inverse of its
+// factor, by one wave.  Lanes 0-15 hold the rows of the block (row r = lane & 15),
+// lanes 16-31 the columns of the identity; lanes 32-63 repeat lanes 0-31.  At pivot k
+// every lane forms m = v[k] / L_kk and subtracts m times column k of L (broadcast
+// from lanes k+1..15) from its later entries: for a row of A this is the
+// right-looking Cholesky update, for a column e_c it is the column-oriented forward
+// substitution of L x = e_c, so lanes 16-31 end with the columns of X = L^-1.  The
+// next pivot is formed from values read before the update (the same arithmetic as
+// the update itself), so its reciprocal square root overlaps the update.
+// L goes back to sM (zeros above the diagonal), X to sX at (o, o) (zeros above).
 // Returns the first pivot (0-based) that is not positive, or -1.  Wave-uniform.
-__device__ __forceinline__ int chol32_wave(double* sM, double* rinv, int o, int lane) {
-  const int r = lane & 31;
-  double a[32];
+__device__ __forceinline__ int chol16_inv_wave(double* sM, double* sX, int o, int lane) {
+  const int r = lane & 15;
+  const bool xcol = (lane & 16) != 0;
+  double v[16];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) a[j] = sM[(o + r) * CP + o + j];
+  for (int j = 0; j < 16; ++j) v[j] = xcol ? (j == r ? 1.0 : 0.0) : sM[(o + r) * CP + o + j];
   int bad = -1;
+  double d = bcast_f64(v[0], 0);
+  if (!(d > 0.0)) bad = 0;
+  double rs = rsqrt_f64(d);
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const double d = bcast_f64(a[k], k);
-    if (!(d > 0.0) && bad < 0) bad = k;
-    const double rs = rsqrt_newton(d);
-    const double l = a[k] * rs;  // lane k: sqrt(d); lanes below: L_ik
-    a[k] = l;
-    if (lane == 0) rinv[o + k] = rs;
+  for (int k = 0; k < 16; ++k) {
+    // All of this pivot's broadcasts are issued before its updates (a readlane result
+    // is ready only ~16 ns after issue); at most 34 scalar registers are live.
+    double an = 0.0, bn = 0.0;
+    if (k + 1 < 16) {
+      an = bcast_f64(v[k + 1], k + 1);  // next diagonal entry before this update
+      bn = bcast_f64(v[k], k + 1);      // its entry in column k
+    }
+    const double m = v[k] * rs;  // rows: L_rk (L_kk on lane k); columns: x_k
+    v[k] = m;
+    double col[16];
 #pragma unroll
-    for (int j = k + 1; j < 32; ++j) a[j] = fma(-l, bcast_f64(l, j), a[j]);
+    for (int j = k + 1; j < 16; ++j) col[j] = bcast_f64(m, j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = k + 1; j < 16; ++j) v[j] = fma(-m, col[j], v[j]);
+    if (k + 1 < 16) {
+      const double t = bn * rs;
+      d = fma(-t, t, an);  // equals the updated v[k + 1] of lane k + 1
+      if (!(d > 0.0) && bad < 0) bad = k + 1;
+      rs = rsqrt_f64(d);
+    }
   }
-  if (lane < 32) {
+  if (lane < 16) {
 #pragma unroll
-    for (int j = 0; j < 32; ++j) sM[(o + r) * CP + o + j] = j <= r ? a[j] : 0.0;
+    for (int j = 0; j < 16; ++j) sM[(o + r) * CP + o + j] = j <= r ? v[j] : 0.0;
+  } else if (lane < 32) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sX[(o + i) * CP + o + r] = i >= r ? v[i] : 0.0;
   }
   return bad;
 }
 
-// X = L^-1 for the lower 32 x 32 block L of sM at (o, o), into sX at (o, o)
-// (zeros above the diagonal); rinv[i] = 1 / L_ii.  One wave: lane c < 32 solves
-// L x = e_c by forward substitution (two interleaved partial sums shorten the
-// dependency chain); the entries of L are read as LDS broadcasts.
-__device__ __forceinline__ void inv32_wave(const double* sM, const double* rinv, double* sX, int o, int lane) {
-  const int c = lane & 31;
-  double x[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    double s0 = i == c ? 1.0 : 0.0, s1 = 0.0;
-#pragma unroll
-    for (int m = 0; m + 1 < i; m += 2) {
-      s0 = fma(-sM[(o + i) * CP + o + m], x[m], s0);
-      s1 = fma(-sM[(o + i) * CP + o + m + 1], x[m + 1], s1);
-    }
-    if (i & 1) s0 = fma(-sM[(o + i) * CP + o + i - 1], x[i - 1], s0);
-    x[i] = (s0 + s1) * rinv[o + i];
-  }
-  if (lane < 32) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) sX[(o + i) * CP + o + c] = x[i];
-  }
-}
-
-// Factor and invert the 64 x 64 diagonal block at kb held in sA (lower part valid,
-// strict upper part zero, identity past n): L_kk goes to L and X = L_kk^-1 (64 x 64,
-// zeros above the diagonal) to Xinv.  Two 32 x 32 halves: L00 = chol(A00),
-// X00 = L00^-1, L10 = A10 X00^T, A11 -= L10 L10^T, L11 = chol(A11), X11 = L11^-1,
-// X10 = -X11 (L10 X00).  sX needs no initial contents; the product L10 X00 is kept
-// in the unused upper right quarter of sA.  A pivot that is not positive sets
-// dev_info (first failure wins).
-__device__ __forceinline__ void diag_factor(double* sA, double* sX, double* rinv, int n, int kb, double* L,
-                                            double* Xinv, int32_t* dev_info, int tid) {
+// Factor the 64 x 64 diagonal block at kb held in sA (lower part valid, strict upper
+// part zero, identity past n) as L_kk, by 16 x 16 blocks: per block column s, wave 0
+// factors the diagonal block and inverts its factor (X_ss), the blocks below become
+// L_is = A_is X_ss^T, and the trailing blocks take A_ij -= L_is L_js^T on the fp64
+// matrix cores.  Wave 0 updates and factors the next diagonal block while waves 1-3
+// update the rest.  L_kk goes to L; the four X_ss to Xinv (64 x 64, zero outside the
+// diagonal 16 x 16 blocks).  sX needs no initial contents.  A pivot that is not
+// positive sets dev_info (first failure wins).
+__device__ __forceinline__ void diag_factor(double* sA, double* sX, int n, int kb, double* L, double* Xinv,
+                                            int32_t* dev_info, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
-  int bad = -1;
-  if (wave == 0) {
-    bad = chol32_wave(sA, rinv, 0, lane);
-    inv32_wave(sA, rinv, sX, 0, lane);
-  }
-  __syncthreads();
-  // L10 = A10 X00^T
-  const int bi = wave >> 1, bj = wave & 1;
   const f64x4 zero = {0.0, 0.0, 0.0, 0.0};
-  f64x4 acc = mma16<true>(sA, CP, 32 + 16 * bi, sX, CP, 16 * bj, 32, zero, lane);
+  int bad = -1;
+  if (wave == 0) bad = chol16_inv_wave(sA, sX, 0, lane);
   __syncthreads();
 #pragma unroll
-  for (int v = 0; v < 4; ++v) sA[(32 + 16 * bi + (lane >> 4) + 4 * v) * CP + 16 * bj + (lane & 15)] = acc[v];
-  __syncthreads();
-  // A11 -= L10 L10^T (reads columns 0..31, writes columns 32..63)
-  acc = mma16<true>(sA, CP, 32 + 16 * bi, sA, CP, 32 + 16 * bj, 32, zero, lane);
+  for (int s = 0; s < 4; ++s) {
+    const int o = 16 * s;
+    if (wave < 3 - s) {  // L_is = A_is X_ss^T
+      const int i0 = 16 * (s + 1 + wave);
+      const f64x4 acc = mma16<true>(sA + o, CP, i0, sX + o, CP, o, 16, zero, lane);
 #pragma unroll
-  for (int v = 0; v < 4; ++v) sA[(32 + 16 * bi + (lane >> 4) + 4 * v) * CP + 32 + 16 * bj + (lane & 15)] -= acc[v];
-  __syncthreads();
-  // wave 0: L11 = chol(A11), X11 = L11^-1; waves 1-3 meanwhile: T = L10 X00 into sA[0..31][32..63]
-  if (wave == 0) {
-    const int b2 = chol32_wave(sA, rinv, 32, lane);
-    if (bad < 0 && b2 >= 0) bad = 32 + b2;
-    inv32_wave(sA, rinv, sX, 32, lane);
-  } else {
-    for (int blk = wave - 1; blk < 4; blk += 3) {
-      const int ti = blk >> 1, tj = blk & 1;
-      const f64x4 t = mma16<false>(sA, CP, 32 + 16 * ti, sX, CP, 16 * tj, 32, zero, lane);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) sA[(16 * ti + (lane >> 4) + 4 * v) * CP + 32 + 16 * tj + (lane & 15)] = t[v];
+      for (int v = 0; v < 4; ++v) sA[(i0 + (lane >> 4) + 4 * v) * CP + o + (lane & 15)] = acc[v];
     }
-  }
-  __syncthreads();
-  // X10 = -X11 T
-  acc = mma16<false>(sX + 32 * CP + 32, CP, 16 * bi, sA + 32, CP, 16 * bj, 32, zero, lane);
+    __syncthreads();
+    if (s == 3) break;
+    const int nx = 16 * (s + 1);
+    if (wave == 0) {
+      const f64x4 acc = mma16<true>(sA + o, CP, nx, sA + o, CP, nx, 16, zero, lane);
 #pragma unroll
-  for (int v = 0; v < 4; ++v) sX[(32 + 16 * bi + (lane >> 4) + 4 * v) * CP + 16 * bj + (lane & 15)] = -acc[v];
+      for (int v = 0; v < 4; ++v) sA[(nx + (lane >> 4) + 4 * v) * CP + nx + (lane & 15)] -= acc[v];
+      const int b = chol16_inv_wave(sA, sX, nx, lane);
+      if (bad < 0 && b >= 0) bad = nx + b;
+    } else {
+      // trailing blocks (i, j), s + 1 <= j <= i <= 3, other than (s + 1, s + 1)
+      int t = 0;
+      for (int i = s + 1; i < 4; ++i)
+        for (int j = s + 1; j <= i; ++j) {
+          if (i == s + 1 && j == s + 1) continue;
+          if (t++ % 3 != wave - 1) continue;
+          const f64x4 acc = mma16<true>(sA + o, CP, 16 * i, sA + o, CP, 16 * j, 16, zero, lane);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sA[(16 * i + (lane >> 4) + 4 * v) * CP + 16 * j + (lane & 15)] -= acc[v];
+        }
+    }
+    __syncthreads();
+  }
   if (wave == 0 && lane == 0 && bad >= 0) atomicCAS(dev_info, 0, kb + bad + 1);
-  __syncthreads();
   for (int e = tid; e < CB * CB; e += 256) {
     const int r = e / CB, c = e % CB;
-    Xinv[e] = c <= r ? sX[r * CP + c] : 0.0;
+    Xinv[e] = (r >> 4) == (c >> 4) && c <= r ? sX[r * CP + c] : 0.0;
     if (c <= r && kb + r < n) L[(int64_t)(kb + r) * n + kb + c] = sA[r * CP + c];
   }
 }
@@ -210,39 +216,51 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(const double* __restrict
   if (*dev_info != 0) return;
   __shared__ double sA[CB * CP];
   __shared__ double sX[CB * CP];
-  __shared__ double rinv[CB];
   const int tid = threadIdx.x;
   load_block64(A, n, 0, 0, n, n, sA, tid);
   __syncthreads();
   prepare_diag(sA, n, 0, tid);
   __syncthreads();
-  diag_factor(sA, sX, rinv, n, 0, L, Xinv, dev_info, tid);
+  diag_factor(sA, sX, n, 0, L, Xinv, dev_info, tid);
 }
 
-// P = A[rows, kb..kb+63] X^T for the 64 rows below the diagonal block at `row0`:
-// the factor's block column (written to L).
+// The factor's block column below the diagonal block at kb: P L_kk^T = A_panel for the
+// 64 rows from row0, by 16-column blocks, P_s = (A_s - sum_{t<s} P_t L_st^T) X_ss^T with
+// X_ss the inverted diagonal 16 x 16 blocks of L_kk (written to L).  Wave w owns rows
+// 16 w .. 16 w + 15 of the panel and needs no other wave's results.
 __global__ __launch_bounds__(256) void chol_panel_kernel(const double* __restrict__ A, int n, int kb,
                                                          const double* __restrict__ Xinv, double* __restrict__ L,
                                                          const int32_t* __restrict__ dev_info) {
   if (*dev_info != 0) return;
   __shared__ double sX[CB * CP];
+  __shared__ double sL[CB * CP];
   __shared__ double sP[CB * CP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row0 = kb + CB + CB * blockIdx.x;
   load_block64(Xinv, CB, 0, 0, CB, CB, sX, tid);
+  load_block64(L, n, kb, kb, n, n, sL, tid);
   load_block64(A, n, row0, kb, n, n, sP, tid);
   __syncthreads();
-  f64x4 acc[4];
+  const int w0 = 16 * wave;
+  const f64x4 zero = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
-    acc[cb] = mma16<true>(sP, CP, 16 * wave, sX, CP, 16 * cb, CB, f64x4{0.0, 0.0, 0.0, 0.0}, lane);
+  for (int s = 0; s < 4; ++s) {
+    const int o = 16 * s;
+    f64x4 acc;
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+    for (int v = 0; v < 4; ++v) acc[v] = sP[(w0 + (lane >> 4) + 4 * v) * CP + o + (lane & 15)];
+#pragma unroll
+    for (int t = 0; t < s; ++t) acc = mma16<true, true>(sP + 16 * t, CP, w0, sL + 16 * t, CP, o, 16, acc, lane);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sP[(w0 + (lane >> 4) + 4 * v) * CP + o + (lane & 15)] = acc[v];
+    acc = mma16<true>(sP + o, CP, w0, sX + o, CP, o, 16, zero, lane);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int r = row0 + 16 * wave + (lane >> 4) + 4 * v, c = kb + 16 * cb + (lane & 15);
-      if (r < n && c < n) L[(int64_t)r * n + c] = acc[cb][v];
+      const int rl = w0 + (lane >> 4) + 4 * v;
+      sP[rl * CP + o + (lane & 15)] = acc[v];
+      if (row0 + rl < n) L[(int64_t)(row0 + rl) * n + kb + o + (lane & 15)] = acc[v];
     }
+  }
 }
 
 // Step kb, after chol_panel_kernel has written the block column P = L[kb + 64.., kb..]:
@@ -256,7 +274,6 @@ __global__ __launch_bounds__(256) void chol_step_kernel(double* __restrict__ A, 
   if (*dev_info != 0) return;
   __shared__ double sPi[CB * CP];
   __shared__ double sPj[CB * CP];
-  __shared__ double rinv[CB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int base = kb + CB;
   const f64x4 zero = {0.0, 0.0, 0.0, 0.0};
@@ -283,7 +300,7 @@ __global__ __launch_bounds__(256) void chol_step_kernel(double* __restrict__ A, 
     __syncthreads();
     prepare_diag(sA, n, base, tid);
     __syncthreads();
-    diag_factor(sA, sP, rinv, n, base, L, Xinv, dev_info, tid);
+    diag_factor(sA, sP, n, base, L, Xinv, dev_info, tid);
     return;
   }
   int ti, tj;
