@@ -91,7 +91,7 @@ __global__ void recode_residual_kernel(const float* __restrict__ T, uint8_t* __r
       c = codes[e];
     }
     Lev[e] = (uint16_t)f32_to_bf16_bits((float)(2 * c - L));
-    split3(t, T0[e], T1[e], T2[e]);
+    if (T0) split3(t, T0[e], T1[e], T2[e]);
   }
   if (bad) atomicCAS(dev_info, 0, -1);
 }
@@ -206,6 +206,174 @@ __global__ __launch_bounds__(256) void gram_kernel(const uint16_t* __restrict__ 
     for (int v = 0; v < 16; ++v) part = fmaf(levj[ib][v], rtot[ib][v], part);
   part += __shfl_xor(part, 32);
   if (lane < 32 && rok) rhs[(size_t)r * nb + b] = part;
+}
+
+// ------------------------------------------------------------------ group 64
+// With Z = H Q (column c of Z is H restricted to the columns of block c, times the
+// levels there), G = Q^T Z and h = Q^T H t = Z^T t.  So one product per block pair,
+//   D^(b,c)_j = sum_{k in c} H_jk l_k      (j in block b),
+// gives both G[b][c] = sum_{j in b} l_j D_j and block b's share of h_c,
+// sum_{j in b} t_j D_j: three bf16 passes (H_0, H_1, H_2 against the exact levels)
+// over all block pairs instead of six passes for H t plus three for G.  The shares
+// of h_c from the nb blocks b are summed afterwards in a fixed order.
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Wave-wide LDS DMA: lane l copies 16 bytes from sbase + voff to LDS byte m0 + 16 l.
+// Inline assembly so that the compiler does not wait for it before unrelated LDS
+// reads; completion is awaited with vm_wait.  The M0 write needs one wait state.
+__device__ __forceinline__ void lh_dma16(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2" ::"v"(voff), "s"(m0), "s"(sbase)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void lh_vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Barrier the compiler cannot move LDS accesses across; the wave's own LDS reads are
+// complete before it.
+__device__ __forceinline__ void lh_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+constexpr int LH_ROWS = 128;                      // weight rows per workgroup (32 per wave)
+constexpr int LH_PLANE = 64 * 64 * 2;             // one H split tile, bf16
+constexpr int LH_STAGE = 3 * LH_PLANE + LH_ROWS * 64 * 2;  // + the level tile: 40 KB
+constexpr int LH_DMA = LH_STAGE / 1024 / 4;       // 1 KB DMAs per wave per stage
+
+// Position of the 16-byte unit (row j, 8-column octet q) in a tile of 64 bf16 columns:
+// eight consecutive rows at one octet fall on eight distinct 16-byte bank groups of a
+// 128-byte line, and sixteen consecutive rows on sixteen of a 256-byte line.
+__device__ __forceinline__ int lh_unit(int j, int q) { return j * 8 + (q ^ (j & 7) ^ ((j >> 3) & 1)); }
+
+__device__ __forceinline__ bf16x8 lh_frag(const lds_char* p) {
+  const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)p;
+  return as_bf16x8(v);
+}
+
+// One workgroup: 128 weight rows x block b, looping over the column blocks c.  Per c the
+// three H split tiles H_i[b, c] and the rows' levels on block c are DMAed into LDS one
+// stage ahead; wave w multiplies them into D (64 j x its 32 rows, two 32 x 32 MFMA
+// blocks) and reduces D with the rows' levels and targets on block b (kept in
+// registers).  Outputs: G[r][b][c] = G[r][c][b] for b <= c; hp[b][c][r] = block b's
+// share of h_c.
+__global__ __launch_bounds__(256, 2) void gram_lh_kernel(const uint16_t* __restrict__ Lev, const float* __restrict__ T,
+                                                         int64_t rows, int n, const uint16_t* __restrict__ H0,
+                                                         const uint16_t* __restrict__ H1, const uint16_t* __restrict__ H2,
+                                                         float* __restrict__ Gm, float* __restrict__ hp,
+                                                         const int32_t* __restrict__ dev_info) {
+  extern __shared__ __attribute__((aligned(1024))) char lh_lds[];
+  if (*dev_info != 0) return;
+  const lds_char* lds = (const lds_char*)lh_lds;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+  const int nb = n / 64;
+  const int b = blockIdx.y;
+  const int64_t r0 = (int64_t)blockIdx.x * LH_ROWS;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rl = 32 * wave + (lane & 31);
+  const int64_t r = r0 + rl;
+  const bool rok = r < rows;
+  const int rmax = (int)std::min<int64_t>(rows - 1 - r0, LH_ROWS - 1);
+
+  // DMA q (0..39 per stage) fills LDS bytes [1024 q, 1024 q + 1024) of the stage:
+  // q < 24 the H split tile q / 8, else the level tile.  Wave w issues q = w + 4 i.
+  uint32_t voff[LH_DMA];
+#pragma unroll
+  for (int i = 0; i < LH_DMA; ++i) {
+    const int q = wave + 4 * i;
+    if (q < 24) {
+      const int u = (q & 7) * 64 + lane, j = u >> 3;
+      const int oct = (u & 7) ^ (j & 7) ^ ((j >> 3) & 1);
+      voff[i] = (uint32_t)((j * n + oct * 8) * 2);
+    } else {
+      const int u = (q - 24) * 64 + lane, row = u >> 3;
+      const int oct = (u & 7) ^ (row & 7) ^ ((row >> 3) & 1);
+      voff[i] = (uint32_t)((std::min(row, rmax) * n + oct * 8) * 2);
+    }
+  }
+  auto issue = [&](int c, int slot) {
+    const uint32_t base = lds_base + slot * LH_STAGE;
+    const int64_t hoff = (int64_t)64 * b * n + 64 * c;
+    const int64_t loff = r0 * n + 64 * c;
+#pragma unroll
+    for (int i = 0; i < LH_DMA; ++i) {
+      const int q = wave + 4 * i;
+      const uint16_t* src = q < 8 ? H0 + hoff : q < 16 ? H1 + hoff : q < 24 ? H2 + hoff : Lev + loff;
+      lh_dma16(src, voff[i], base + q * 1024);
+    }
+  };
+
+  // levels and targets of this lane's row on block b at the accumulator rows
+  float lv[2][16], tv[2][16];
+#pragma unroll
+  for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t e = (rok ? r : 0) * n + 64 * b + 32 * jt + acc_row(v, lane);
+      lv[jt][v] = rok ? bf16_bits_to_f32(Lev[e]) : 0.0f;
+      tv[jt][v] = rok ? T[e] : 0.0f;
+    }
+
+  issue(0, 0);
+  for (int c = 0; c < nb; ++c) {
+    const int slot = c & 1;
+    if (c + 1 < nb) {
+      issue(c + 1, slot ^ 1);
+      lh_vm_wait<LH_DMA>();
+    } else {
+      lh_vm_wait<0>();
+    }
+    lh_barrier();
+    const lds_char* st = lds + slot * LH_STAGE;
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int oct = 2 * ks + (lane >> 5);
+      const bf16x8 fb = lh_frag(st + 3 * LH_PLANE + lh_unit(rl, oct) * 16);
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        const int ua = lh_unit(32 * jt + (lane & 31), oct) * 16;
+        const bf16x8 a2 = lh_frag(st + 2 * LH_PLANE + ua);
+        const bf16x8 a1 = lh_frag(st + LH_PLANE + ua);
+        const bf16x8 a0 = lh_frag(st + ua);
+        acc[jt] = mfma32x32x16_bf16(a2, fb, acc[jt]);  // smallest terms first
+        acc[jt] = mfma32x32x16_bf16(a1, fb, acc[jt]);
+        acc[jt] = mfma32x32x16_bf16(a0, fb, acc[jt]);
+      }
+    }
+    lh_barrier();  // every wave is done with this slot before the next stage's DMA into it
+    float hpart = 0.0f, gpart = 0.0f;
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) hpart = fmaf(tv[jt][v], acc[jt][v], hpart);
+    hpart += __shfl_xor(hpart, 32);
+    if (b <= c) {
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) gpart = fmaf(lv[jt][v], acc[jt][v], gpart);
+      gpart += __shfl_xor(gpart, 32);
+    }
+    if (lane < 32 && rok) {
+      hp[((size_t)b * nb + c) * rows + r] = hpart;
+      if (b <= c) {
+        Gm[((size_t)r * nb + b) * nb + c] = gpart;
+        Gm[((size_t)r * nb + c) * nb + b] = gpart;
+      }
+    }
+  }
+}
+
+// rhs[r][c] = sum over b of hp[b][c][r], in fp64 and in the order of b.
+__global__ void rhs_sum_kernel(const float* __restrict__ hp, int64_t rows, int nb, float* __restrict__ rhs,
+                               const int32_t* __restrict__ dev_info) {
+  if (*dev_info != 0) return;
+  const int c = blockIdx.y;
+  for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < rows; r += (int64_t)gridDim.x * blockDim.x) {
+    double s = 0.0;
+    for (int b = 0; b < nb; ++b) s += (double)hp[((size_t)b * nb + c) * rows + r];
+    rhs[(size_t)r * nb + c] = (float)s;
+  }
 }
 
 __device__ __forceinline__ double wave_bcast_f64(double v, int lane) {
@@ -352,7 +520,7 @@ __global__ __launch_bounds__(64) void row_solve_kernel(const float* __restrict__
 using namespace wr;
 
 struct WringLayout {
-  size_t T, Lev, T0, T1, T2, H0, H1, H2, Gm, rhs, Bf, Af, total;
+  size_t T, Lev, T0, T1, T2, H0, H1, H2, Gm, rhs, hp, Bf, Af, total;
 };
 
 static WringLayout wring_layout(int64_t rows, int64_t n, int32_t group, int32_t rank) {
@@ -364,11 +532,13 @@ static WringLayout wring_layout(int64_t rows, int64_t n, int32_t group, int32_t 
     return o;
   };
   const int64_t nb = n / group;
+  const bool lh = group == 64;  // gram_lh_kernel: no split target, per-block shares of h
   l.T = take((size_t)rows * n * 4);
   l.Lev = take((size_t)rows * n * 2);
-  l.T0 = take((size_t)rows * n * 2);
-  l.T1 = take((size_t)rows * n * 2);
-  l.T2 = take((size_t)rows * n * 2);
+  l.T0 = take(lh ? 0 : (size_t)rows * n * 2);
+  l.T1 = take(lh ? 0 : (size_t)rows * n * 2);
+  l.T2 = take(lh ? 0 : (size_t)rows * n * 2);
+  l.hp = take(lh ? (size_t)nb * nb * rows * 4 : 0);
   l.H0 = take((size_t)n * n * 2);
   l.H1 = take((size_t)n * n * 2);
   l.H2 = take((size_t)n * n * 2);
@@ -398,9 +568,10 @@ int wr_wring_solve_impl(wr_ctx* ctx, const void* target, int t_dtype, int64_t ld
   char* ws = static_cast<char*>(ctx->ws);
   float* T = reinterpret_cast<float*>(ws + lay.T);
   uint16_t* Lev = reinterpret_cast<uint16_t*>(ws + lay.Lev);
-  uint16_t* T0 = reinterpret_cast<uint16_t*>(ws + lay.T0);
-  uint16_t* T1 = reinterpret_cast<uint16_t*>(ws + lay.T1);
-  uint16_t* T2 = reinterpret_cast<uint16_t*>(ws + lay.T2);
+  const bool lh = group == 64;
+  uint16_t* T0 = lh ? nullptr : reinterpret_cast<uint16_t*>(ws + lay.T0);
+  uint16_t* T1 = lh ? nullptr : reinterpret_cast<uint16_t*>(ws + lay.T1);
+  uint16_t* T2 = lh ? nullptr : reinterpret_cast<uint16_t*>(ws + lay.T2);
   uint16_t* H0 = reinterpret_cast<uint16_t*>(ws + lay.H0);
   uint16_t* H1 = reinterpret_cast<uint16_t*>(ws + lay.H1);
   uint16_t* H2 = reinterpret_cast<uint16_t*>(ws + lay.H2);
@@ -431,10 +602,23 @@ int wr_wring_solve_impl(wr_ctx* ctx, const void* target, int t_dtype, int64_t ld
   hipLaunchKernelGGL(split_h_kernel, dim3(gx, (unsigned)n), dim3(256), 0, st, H, ldh, n, H0, H1, H2);
   WR_CHECK_LAUNCH();
   dim3 ggrid((unsigned)((rows + 127) / 128), (unsigned)nb);
-  switch (group) {
-    case 32: hipLaunchKernelGGL(gram_kernel<32>, ggrid, dim3(256), 0, st, Lev, T0, T1, T2, rows, n, H0, H1, H2, Gm, rh, dev_info); break;
-    case 64: hipLaunchKernelGGL(gram_kernel<64>, ggrid, dim3(256), 0, st, Lev, T0, T1, T2, rows, n, H0, H1, H2, Gm, rh, dev_info); break;
-    default: hipLaunchKernelGGL(gram_kernel<128>, ggrid, dim3(256), 0, st, Lev, T0, T1, T2, rows, n, H0, H1, H2, Gm, rh, dev_info); break;
+  if (lh) {
+    static bool lds_attr = false;
+    if (!lds_attr) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(gram_lh_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              2 * LH_STAGE) != hipSuccess)
+        return WR_EHIP;
+      lds_attr = true;
+    }
+    float* hp = reinterpret_cast<float*>(ws + lay.hp);
+    hipLaunchKernelGGL(gram_lh_kernel, ggrid, dim3(256), 2 * LH_STAGE, st, Lev, T, rows, n, H0, H1, H2, Gm, hp, dev_info);
+    WR_CHECK_LAUNCH();
+    const unsigned sx = (unsigned)std::min<int64_t>((rows + 255) / 256, 64);
+    hipLaunchKernelGGL(rhs_sum_kernel, dim3(sx, (unsigned)nb), dim3(256), 0, st, hp, rows, nb, rh, dev_info);
+  } else if (group == 32) {
+    hipLaunchKernelGGL(gram_kernel<32>, ggrid, dim3(256), 0, st, Lev, T0, T1, T2, rows, n, H0, H1, H2, Gm, rh, dev_info);
+  } else {
+    hipLaunchKernelGGL(gram_kernel<128>, ggrid, dim3(256), 0, st, Lev, T0, T1, T2, rows, n, H0, H1, H2, Gm, rh, dev_info);
   }
   WR_CHECK_LAUNCH();
   if (nb <= 64) {
