@@ -70,6 +70,18 @@ __device__ __forceinline__ uint16_t f64_to_f16_bits_clamped(double d) {
   return sign | __builtin_bit_cast(uint16_t, v);
 }
 
+// x = x0 + x1 + x2 with each part rounded to bf16 in turn (exact for any fp32 x whose
+// parts stay in the normal range): 24 significant bits as three bf16 matrix-core operands.
+__device__ __forceinline__ void split3(float x, uint16_t& p0, uint16_t& p1, uint16_t& p2) {
+  const uint32_t a = f32_to_bf16_bits(x);
+  const float r1 = x - bf16_bits_to_f32(a);
+  const uint32_t b = f32_to_bf16_bits(r1);
+  const float r2 = r1 - bf16_bits_to_f32(b);
+  p0 = (uint16_t)a;
+  p1 = (uint16_t)b;
+  p2 = (uint16_t)f32_to_bf16_bits(r2);
+}
+
 // ---------------------------------------------------------------- grid
 // Nearest code for t in level units: clamp(floor((t + L)/2 + 1/2), 0, L).
 __device__ __forceinline__ int nearest_code(float t, int L) {

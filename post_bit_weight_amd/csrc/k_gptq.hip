@@ -11,7 +11,10 @@
 // column k is rounded from v_k = w_k + sum_{i<k} M_ik delta_i.  The corrections
 // C_k = sum_{i<k} M_ik delta_i are kept in a rows x n buffer: inside a lazy
 // batch of columns they are updated one column at a time, and when a batch is
-// done the remaining columns receive C += E M[batch, rest] as one GEMM.
+// done the remaining columns receive C += E M[batch, rest] as one product on
+// the bf16 matrix cores: E and M split into three bf16 parts each (24
+// significant bits, as fp32), the six part products with i + j <= 2 summed in
+// fp32, smallest first.
 // The block scale is fixed at the first column of a block from the values the
 // GPTQ push form holds there, w_j + x_j with x = M_bb^-T C_b (M_bb the block's
 // diagonal block of M): the optimal compensation of everything rounded so far.
@@ -23,9 +26,6 @@
 // is staged in LDS in a lane-major order.
 #include "common.hpp"
 
-int wr_gemm_f32(hipStream_t st, int M, int N, int K, const float* A, int64_t lda, const float* B, int64_t ldb,
-                bool b_kn, float* C, int64_t ldc, float alpha, bool accumulate, bool lower_tiles,
-                const int32_t* dev_info);
 size_t wr_factor_ws_bytes(int64_t n);
 int wr_factor_m(hipStream_t st, const float* H, int64_t ldh, int n, void* ws, float* M, int32_t* dev_info);
 
@@ -67,7 +67,8 @@ template <int P, int BATCH, int G>
 __global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict__ W, int w_dtype, int64_t rows,
                                                           int n, int64_t ldw, const float* __restrict__ M,
                                                           const uint8_t* __restrict__ bits, int b0, int ncols,
-                                                          float* __restrict__ Cbuf, float* __restrict__ E,
+                                                          float* __restrict__ Cbuf, uint16_t* __restrict__ E0,
+                                                          uint16_t* __restrict__ E1, uint16_t* __restrict__ E2,
                                                           uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
                                                           const int32_t* __restrict__ dev_info) {
   constexpr int S = BATCH / P;       // columns per lane
@@ -167,13 +168,112 @@ __global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict
     const int col = p + P * i;
     if (col < ncols) {
       codes[row * n + b0 + col] = code[i];
-      E[row * BATCH + col] = d[i];
+      const int64_t e = row * BATCH + col;
+      split3(d[i], E0[e], E1[e], E2[e]);
     }
   }
   if (p == 0) {
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk)
       if (blk * G < ncols) scales[row * (n / G) + (b0 / G) + blk] = f32_to_f16_bits_clamped(sc[blk]);
+  }
+}
+
+// Mt_i[c][k] = part i of M[k][c] (three bf16 planes of M transposed), for the
+// trailing update.  64 x 64 tiles through LDS; tiles below the diagonal (M = 0 there)
+// are skipped.
+__global__ __launch_bounds__(256) void split_mt_kernel(const float* __restrict__ M, int n, uint16_t* __restrict__ Mt0,
+                                                       uint16_t* __restrict__ Mt1, uint16_t* __restrict__ Mt2,
+                                                       const int32_t* __restrict__ dev_info) {
+  __shared__ float t[64][65];
+  if (*dev_info != 0) return;
+  const int k0 = 64 * blockIdx.y, c0 = 64 * blockIdx.x;
+  if (k0 > c0 + 63) return;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int i = e >> 6, j = e & 63;
+    t[i][j] = k0 + i < n && c0 + j < n ? M[(int64_t)(k0 + i) * n + c0 + j] : 0.0f;
+  }
+  __syncthreads();
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int j = e >> 6, i = e & 63;  // output row c0 + j, column k0 + i
+    if (c0 + j < n && k0 + i < n) {
+      const int64_t o = (int64_t)(c0 + j) * n + k0 + i;
+      split3(t[i][j], Mt0[o], Mt1[o], Mt2[o]);
+    }
+  }
+}
+
+// C[r][c0 + c] += sum_k E[r][k] M[b0 + k][c0 + c] for r < rows, c < N, k < 128, with E
+// and M given as three bf16 planes each (E_i: rows x 128; Mt_i: n x n, transposed).
+// 64 x 64 output tile per workgroup.  Wave w takes k in [32 w, 32 w + 32) for the whole
+// tile (2 x 2 blocks of 32 x 32, v_mfma_f32_32x32x16_bf16: operand lane l supplies row
+// or column l % 32 at k = 8 (l / 32) .. +7 of a 16-wide step), so each wave issues all
+// of its operand loads at once (16 contiguous bytes per lane, straight from global
+// memory) together with the C tile; the four partial tiles are summed through LDS in
+// wave order and added to C.
+__global__ __launch_bounds__(256, 2) void trail_s6_kernel(int64_t rows, int N, int n, int b0, int c0,
+                                                          const uint16_t* __restrict__ E0,
+                                                          const uint16_t* __restrict__ E1,
+                                                          const uint16_t* __restrict__ E2,
+                                                          const uint16_t* __restrict__ Mt0,
+                                                          const uint16_t* __restrict__ Mt1,
+                                                          const uint16_t* __restrict__ Mt2, float* __restrict__ C,
+                                                          const int32_t* __restrict__ dev_info) {
+  __shared__ float red[4][64][65];
+  if (*dev_info != 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t R0 = (int64_t)blockIdx.y * 64;
+  const int C0 = blockIdx.x * 64;
+  // the C tile: thread tid holds elements tid + 256 q (row e / 64, column e % 64)
+  float cv[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = tid + 256 * q, r = e >> 6, c = e & 63;
+    cv[q] = R0 + r < rows && C0 + c < N ? C[(R0 + r) * n + c0 + C0 + c] : 0.0f;
+  }
+  const int kofs = 32 * wave + 8 * (lane >> 5);
+  bf16x8 a[3][2][2], b[3][2][2];  // [part][block][step]
+  auto ld = [](const uint16_t* p) { return as_bf16x8(*reinterpret_cast<const u32x4*>(p)); };
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int64_t r = std::min<int64_t>(R0 + 32 * t + (lane & 31), rows - 1);
+    const int c = std::min(C0 + 32 * t + (lane & 31), N - 1);
+    const int64_t ao = r * 128 + kofs;
+    const int64_t bo = (int64_t)(c0 + c) * n + b0 + kofs;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      a[0][t][kk] = ld(E0 + ao + 16 * kk);
+      a[1][t][kk] = ld(E1 + ao + 16 * kk);
+      a[2][t][kk] = ld(E2 + ao + 16 * kk);
+      b[0][t][kk] = ld(Mt0 + bo + 16 * kk);
+      b[1][t][kk] = ld(Mt1 + bo + 16 * kk);
+      b[2][t][kk] = ld(Mt2 + bo + 16 * kk);
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      f32x16 v = {};
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        v = mfma32x32x16_bf16(a[2][x][kk], b[0][y][kk], v);  // smallest terms first
+        v = mfma32x32x16_bf16(a[1][x][kk], b[1][y][kk], v);
+        v = mfma32x32x16_bf16(a[0][x][kk], b[2][y][kk], v);
+        v = mfma32x32x16_bf16(a[1][x][kk], b[0][y][kk], v);
+        v = mfma32x32x16_bf16(a[0][x][kk], b[1][y][kk], v);
+        v = mfma32x32x16_bf16(a[0][x][kk], b[0][y][kk], v);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) red[wave][32 * x + acc_row(i, lane)][32 * y + (lane & 31)] = v[i];
+    }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = tid + 256 * q, r = e >> 6, c = e & 63;
+    if (R0 + r < rows && C0 + c < N)
+      C[(R0 + r) * n + c0 + C0 + c] = cv[q] + (((red[0][r][c] + red[1][r][c]) + red[2][r][c]) + red[3][r][c]);
   }
 }
 
@@ -185,28 +285,41 @@ static constexpr int kBatch = 128;
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-size_t wr_gptq_ws_bytes(int64_t rows, int64_t n) {
-  size_t b = 0;
-  b += align256(wr_factor_ws_bytes(n));      // factorisation scratch (fp64)
-  b += align256((size_t)n * n * 4);          // M
-  b += align256((size_t)rows * n * 4);       // corrections C
-  b += align256((size_t)rows * kBatch * 4);  // batch errors E
-  return b;
+struct GptqLayout {
+  size_t M, C, E[3], Mt[3], total;
+};
+
+static GptqLayout gptq_layout(int64_t rows, int64_t n) {
+  GptqLayout l{};
+  size_t off = align256(wr_factor_ws_bytes(n));  // factorisation scratch (fp64) at the start
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  l.M = take((size_t)n * n * 4);                                       // M, fp32
+  l.C = take((size_t)rows * n * 4);                                    // corrections C
+  for (int i = 0; i < 3; ++i) l.E[i] = take((size_t)rows * kBatch * 2);  // batch errors, bf16 parts
+  for (int i = 0; i < 3; ++i) l.Mt[i] = take((size_t)n * n * 2);          // M transposed, bf16 parts
+  l.total = off;
+  return l;
 }
+
+size_t wr_gptq_ws_bytes(int64_t rows, int64_t n) { return gptq_layout(rows, n).total; }
 
 template <int P, int G>
 static void launch_panel(hipStream_t st, const void* W, int w_dtype, int64_t rows, int n, int64_t ldw, const float* Mm,
-                         const uint8_t* bits, int b0, int ncols, float* Cb, float* E, uint8_t* codes, uint16_t* scales,
-                         const int32_t* dev_info) {
+                         const uint8_t* bits, int b0, int ncols, float* Cb, uint16_t* const* E, uint8_t* codes,
+                         uint16_t* scales, const int32_t* dev_info) {
   const unsigned grid = (unsigned)((rows + (256 / P) - 1) / (256 / P));
   hipLaunchKernelGGL((sweep_panel_kernel<P, kBatch, G>), dim3(grid), dim3(256), 0, st, W, w_dtype, rows, n, ldw, Mm,
-                     bits, b0, ncols, Cb, E, codes, scales, dev_info);
+                     bits, b0, ncols, Cb, E[0], E[1], E[2], codes, scales, dev_info);
 }
 
 template <int P>
 static int launch_panel_g(hipStream_t st, int G, const void* W, int w_dtype, int64_t rows, int n, int64_t ldw,
-                          const float* Mm, const uint8_t* bits, int b0, int ncols, float* Cb, float* E, uint8_t* codes,
-                          uint16_t* scales, const int32_t* dev_info) {
+                          const float* Mm, const uint8_t* bits, int b0, int ncols, float* Cb, uint16_t* const* E,
+                          uint8_t* codes, uint16_t* scales, const int32_t* dev_info) {
   switch (G) {
     case 32: launch_panel<P, 32>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, codes, scales, dev_info); break;
     case 64: launch_panel<P, 64>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, codes, scales, dev_info); break;
@@ -221,14 +334,20 @@ int wr_gptq_sweep_impl(wr_ctx* ctx, const void* W, int w_dtype, int64_t rows, in
                        const float* H, int64_t ldh, const uint8_t* bits, int32_t group, int32_t lazy_batch,
                        uint8_t* codes, uint16_t* scales, int32_t* dev_info) {
   if (lazy_batch != kBatch || (group != 32 && group != 64 && group != 128)) return WR_EUNSUPPORTED;
-  if (ctx->ws_bytes < wr_gptq_ws_bytes(rows, n64)) return WR_EWORKSPACE;
+  const GptqLayout lay = gptq_layout(rows, n64);
+  if (ctx->ws_bytes < lay.total) return WR_EWORKSPACE;
   const int n = (int)n64;
   hipStream_t st = ctx->stream;
   char* ws = static_cast<char*>(ctx->ws);
   void* fws = ws;
-  float* Mm = reinterpret_cast<float*>(ws + align256(wr_factor_ws_bytes(n)));
-  float* Cb = reinterpret_cast<float*>(reinterpret_cast<char*>(Mm) + align256((size_t)n * n * 4));
-  float* E = reinterpret_cast<float*>(reinterpret_cast<char*>(Cb) + align256((size_t)rows * n * 4));
+  float* Mm = reinterpret_cast<float*>(ws + lay.M);
+  float* Cb = reinterpret_cast<float*>(ws + lay.C);
+  uint16_t* E[3];
+  uint16_t* Mt[3];
+  for (int i = 0; i < 3; ++i) {
+    E[i] = reinterpret_cast<uint16_t*>(ws + lay.E[i]);
+    Mt[i] = reinterpret_cast<uint16_t*>(ws + lay.Mt[i]);
+  }
 
   hipLaunchKernelGGL(sweep_set_int_kernel, dim3(1), dim3(1), 0, st, dev_info, 0);
   WR_CHECK_LAUNCH();
@@ -241,15 +360,21 @@ int wr_gptq_sweep_impl(wr_ctx* ctx, const void* W, int w_dtype, int64_t rows, in
   if (rows == 0) return WR_OK;
   hipLaunchKernelGGL(zero_f32_kernel, dim3(1024), dim3(256), 0, st, Cb, (int64_t)rows * n);
   WR_CHECK_LAUNCH();
+  if (n > kBatch) {
+    const unsigned nt = (unsigned)((n + 63) / 64);
+    hipLaunchKernelGGL(split_mt_kernel, dim3(nt, nt), dim3(256), 0, st, Mm, n, Mt[0], Mt[1], Mt[2], dev_info);
+    WR_CHECK_LAUNCH();
+  }
   for (int b0 = 0; b0 < n; b0 += kBatch) {
     const int ncols = std::min(kBatch, n - b0);
     rc = launch_panel_g<16>(st, group, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, codes, scales, dev_info);
     if (rc) return rc;
     const int rest = n - b0 - ncols;
-    if (rest > 0) {
-      rc = wr_gemm_f32(st, (int)rows, rest, ncols, E, kBatch, Mm + (int64_t)b0 * n + b0 + ncols, n, true,
-                       Cb + b0 + ncols, n, 1.0f, true, false, dev_info);
-      if (rc) return rc;
+    if (rest > 0) {  // ncols == kBatch here: only the last batch can be short
+      const dim3 grid((unsigned)((rest + 63) / 64), (unsigned)((rows + 63) / 64));
+      hipLaunchKernelGGL(trail_s6_kernel, grid, dim3(256), 0, st, rows, rest, n, b0, b0 + ncols, E[0], E[1], E[2],
+                         Mt[0], Mt[1], Mt[2], Cb, dev_info);
+      WR_CHECK_LAUNCH();
     }
   }
   return WR_OK;

@@ -32,18 +32,6 @@ namespace wr {
 
 __global__ void set_int_kernel(int32_t* p, int32_t v) { *p = v; }
 
-// x = x0 + x1 + x2 with each part rounded to bf16 in turn (exact for any fp32 x
-// whose parts stay in the normal range).
-__device__ __forceinline__ void split3(float x, uint16_t& p0, uint16_t& p1, uint16_t& p2) {
-  const uint32_t a = f32_to_bf16_bits(x);
-  const float r1 = x - bf16_bits_to_f32(a);
-  const uint32_t b = f32_to_bf16_bits(r1);
-  const float r2 = r1 - bf16_bits_to_f32(b);
-  p0 = (uint16_t)a;
-  p1 = (uint16_t)b;
-  p2 = (uint16_t)f32_to_bf16_bits(r2);
-}
-
 __global__ void to_f32_kernel(const void* __restrict__ src, int dtype, int64_t count, float* __restrict__ dst) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
     dst[i] = dtype == WR_BF16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(src)[i]) : static_cast<const float*>(src)[i];
