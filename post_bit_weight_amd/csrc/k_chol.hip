@@ -11,16 +11,14 @@
 // factored by one workgroup in 16 x 16 blocks: each diagonal 16 x 16 block is
 // factored and its factor inverted at once by one wave in registers (rows of A
 // and columns of the identity side by side in the lanes, pivot columns broadcast
-// with readlane), the rest are fp64 MFMA products in LDS.  Per block column kb
-// two kernels:
-//   chol_panel_kernel  the block column below, P = A_panel L_kk^-T, as a blocked
-//                      triangular solve with the inverted 16 x 16 diagonal
-//                      blocks on the fp64 matrix cores (the factor's final
-//                      block column, written to L);
-//   chol_step_kernel   the trailing lower matrix, A_ij -= P_i P_j^T, one 64 x 64
-//                      tile per workgroup on the fp64 matrix cores, while
-//                      workgroup 0 updates and factors the next diagonal block
-//                      (lookahead).
+// with readlane), the rest are fp64 MFMA products in LDS.  Per block column kb one
+// kernel, chol_step_kernel: every workgroup solves for the blocks of the factor's
+// block column kb that it needs (a blocked triangular solve with the inverted
+// 16 x 16 diagonal blocks, on the fp64 matrix cores), then workgroup 0 updates and
+// factors the next diagonal block while the others update one trailing tile each,
+// A_ij -= L_ik L_jk^T.  Recomputing a block column's solve per tile costs fp64
+// matrix-core time that runs in parallel; it removes a dependent launch, a global
+// round trip and a reload from the serial chain of diagonal blocks.
 // A pivot that is not positive sets dev_info (1-based pivot of J H J) and every
 // later kernel returns at once.
 #include "common.hpp"
@@ -38,6 +36,10 @@ __device__ __forceinline__ double bcast_f64(double v, int lane) {
   const int hi = __builtin_amdgcn_readlane((int)(u >> 32), lane);
   return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
 }
+
+// Workgroup barrier for data exchanged through LDS only: each wave waits for its own LDS
+// operations, not for its global stores (which no other wave of the kernel reads).
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // 1/sqrt(d) to fp64 precision: the hardware estimate (about 23 correct bits over the
 // whole fp64 range), two Newton steps r <- r (3 - d r^2) / 2.
@@ -150,16 +152,19 @@ __device__ __forceinline__ int chol16_inv_wave(double* sM, double* sX, int o, in
 // factors the diagonal block and inverts its factor (X_ss), the blocks below become
 // L_is = A_is X_ss^T, and the trailing blocks take A_ij -= L_is L_js^T on the fp64
 // matrix cores.  Wave 0 updates and factors the next diagonal block while waves 1-3
-// update the rest.  L_kk goes to L; the four X_ss to Xinv (64 x 64, zero outside the
-// diagonal 16 x 16 blocks).  sX needs no initial contents.  A pivot that is not
+// update the rest.  L_kk goes to L; the four X_ss to Xinv ([4][16][16], compact).
+// With first_done, wave 0 has already factored the first 16 x 16 block (its first bad
+// pivot, or -1, in bad0).  sX needs no initial contents.  A pivot that is not
 // positive sets dev_info (first failure wins).
 __device__ __forceinline__ void diag_factor(double* sA, double* sX, int n, int kb, double* L, double* Xinv,
-                                            int32_t* dev_info, int tid) {
+                                            int32_t* dev_info, int tid, bool first_done = false, int bad0 = -1) {
   const int lane = tid & 63, wave = tid >> 6;
   const f64x4 zero = {0.0, 0.0, 0.0, 0.0};
-  int bad = -1;
-  if (wave == 0) bad = chol16_inv_wave(sA, sX, 0, lane);
-  __syncthreads();
+  int bad = bad0;
+  if (!first_done) {
+    if (wave == 0) bad = chol16_inv_wave(sA, sX, 0, lane);
+    lds_sync();
+  }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int o = 16 * s;
@@ -169,7 +174,7 @@ __device__ __forceinline__ void diag_factor(double* sA, double* sX, int n, int k
 #pragma unroll
       for (int v = 0; v < 4; ++v) sA[(i0 + (lane >> 4) + 4 * v) * CP + o + (lane & 15)] = acc[v];
     }
-    __syncthreads();
+    lds_sync();
     if (s == 3) break;
     const int nx = 16 * (s + 1);
     if (wave == 0) {
@@ -190,23 +195,39 @@ __device__ __forceinline__ void diag_factor(double* sA, double* sX, int n, int k
           for (int v = 0; v < 4; ++v) sA[(16 * i + (lane >> 4) + 4 * v) * CP + 16 * j + (lane & 15)] -= acc[v];
         }
     }
-    __syncthreads();
+    lds_sync();
   }
   if (wave == 0 && lane == 0 && bad >= 0) atomicCAS(dev_info, 0, kb + bad + 1);
+  for (int e = tid; e < 4 * 256; e += 256) {  // X_ss, compact: [s][16][16]
+    const int b = e >> 8, r = (e >> 4) & 15, c = e & 15;
+    Xinv[e] = sX[(16 * b + r) * CP + 16 * b + c];
+  }
   for (int e = tid; e < CB * CB; e += 256) {
     const int r = e / CB, c = e % CB;
-    Xinv[e] = (r >> 4) == (c >> 4) && c <= r ? sX[r * CP + c] : 0.0;
     if (c <= r && kb + r < n) L[(int64_t)(kb + r) * n + kb + c] = sA[r * CP + c];
   }
 }
 
-// Only the lower part of A is maintained: clear the strict upper part of the block in
-// sA and pad rows past n with the identity.
-__device__ __forceinline__ void prepare_diag(double* sA, int n, int kb, int tid) {
+// The inverted diagonal 16 x 16 blocks, stored compactly as [4][16][16], into sX at (16 s, 16 s).
+__device__ __forceinline__ void load_xd(const double* __restrict__ Xc, double* sX, int tid) {
+  double2 v[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) v[q] = *reinterpret_cast<const double2*>(Xc + 2 * (tid + 256 * q));
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = 2 * (tid + 256 * q), b = e >> 8, r = (e >> 4) & 15, c = e & 15;
+    sX[(16 * b + r) * CP + 16 * b + c] = v[q].x;
+    sX[(16 * b + r) * CP + 16 * b + c + 1] = v[q].y;
+  }
+}
+
+// Rows past n of the last, partial block: the identity.  (Entries above the diagonal
+// of a diagonal block are never read into the lower part, so they need no clearing.)
+__device__ __forceinline__ void pad_diag(double* sA, int n, int kb, int tid) {
+  if (kb + CB <= n) return;
   for (int e = tid; e < CB * CB; e += 256) {
     const int r = e / CB, c = e % CB;
-    if (c > r) sA[r * CP + c] = 0.0;
-    else if (kb + r >= n) sA[r * CP + c] = r == c ? 1.0 : 0.0;
+    if (kb + r >= n && c <= r) sA[r * CP + c] = r == c ? 1.0 : 0.0;
   }
 }
 
@@ -219,28 +240,16 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(const double* __restrict
   const int tid = threadIdx.x;
   load_block64(A, n, 0, 0, n, n, sA, tid);
   __syncthreads();
-  prepare_diag(sA, n, 0, tid);
+  pad_diag(sA, n, 0, tid);
   __syncthreads();
   diag_factor(sA, sX, n, 0, L, Xinv, dev_info, tid);
 }
 
-// The factor's block column below the diagonal block at kb: P L_kk^T = A_panel for the
-// 64 rows from row0, by 16-column blocks, P_s = (A_s - sum_{t<s} P_t L_st^T) X_ss^T with
-// X_ss the inverted diagonal 16 x 16 blocks of L_kk (written to L).  Wave w owns rows
-// 16 w .. 16 w + 15 of the panel and needs no other wave's results.
-__global__ __launch_bounds__(256) void chol_panel_kernel(const double* __restrict__ A, int n, int kb,
-                                                         const double* __restrict__ Xinv, double* __restrict__ L,
-                                                         const int32_t* __restrict__ dev_info) {
-  if (*dev_info != 0) return;
-  __shared__ double sX[CB * CP];
-  __shared__ double sL[CB * CP];
-  __shared__ double sP[CB * CP];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int row0 = kb + CB + CB * blockIdx.x;
-  load_block64(Xinv, CB, 0, 0, CB, CB, sX, tid);
-  load_block64(L, n, kb, kb, n, n, sL, tid);
-  load_block64(A, n, row0, kb, n, n, sP, tid);
-  __syncthreads();
+// Blocked triangular solve P L_kk^T = A in place for rows 16 w .. 16 w + 15 of a 64-row
+// tile in sP (one wave): P_s = (A_s - sum_{t<s} P_t L_st^T) X_ss^T per 16-column block,
+// with L_kk in sL and its inverted diagonal 16 x 16 blocks X_ss in sX.  The wave only
+// touches its own rows of sP.
+__device__ __forceinline__ void panel_rows(double* sP, const double* sL, const double* sX, int wave, int lane) {
   const int w0 = 16 * wave;
   const f64x4 zero = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
@@ -255,52 +264,66 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(const double* __restric
     for (int v = 0; v < 4; ++v) sP[(w0 + (lane >> 4) + 4 * v) * CP + o + (lane & 15)] = acc[v];
     acc = mma16<true>(sP + o, CP, w0, sX + o, CP, o, 16, zero, lane);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int rl = w0 + (lane >> 4) + 4 * v;
-      sP[rl * CP + o + (lane & 15)] = acc[v];
-      if (row0 + rl < n) L[(int64_t)(row0 + rl) * n + kb + o + (lane & 15)] = acc[v];
-    }
+    for (int v = 0; v < 4; ++v) sP[(w0 + (lane >> 4) + 4 * v) * CP + o + (lane & 15)] = acc[v];
   }
 }
 
-// Step kb, after chol_panel_kernel has written the block column P = L[kb + 64.., kb..]:
-// workgroup 0 updates the next diagonal block, A_00 - P_0 P_0^T (not stored back), and
-// factors and inverts it (lookahead: the serial part of the next step overlaps this
-// step's trailing update); every other workgroup owns one lower tile (ti, tj) != (0, 0)
-// of the trailing matrix (rows/columns from kb + 64 on) and applies A_ij -= P_i P_j^T.
+// Store the 64 x 64 block sM to L at (r0, c0) (rows past n skipped).
+__device__ __forceinline__ void store_block64(const double* sM, double* __restrict__ L, int n, int r0, int c0, int tid) {
+  for (int e = tid; e < CB * CB; e += 256) {
+    const int r = e / CB, c = e % CB;
+    if (r0 + r < n) L[(int64_t)(r0 + r) * n + c0 + c] = sM[r * CP + c];
+  }
+}
+
+// Step kb, after the diagonal block kb is factored (L_kk in L, its inverted 16 x 16
+// diagonal blocks in Xin).  Every workgroup solves for the factor's blocks that it needs
+// from the block column A[.., kb..kb+63] itself, so no workgroup waits for another.
+//   workgroup 0:   L_{k+1,k}, then the next diagonal block A_{k+1,k+1} - L_{k+1,k} L_{k+1,k}^T,
+//                  factored and inverted (to L and Xout), then L_{k+1,k} to L;
+//   workgroup t:   trailing lower tile (ti, tj) != (0, 0): L_ik, L_jk, A_ij -= L_ik L_jk^T;
+//                  the tiles of the first trailing column (tj = 0) also write L_ik.
+// Xin and Xout are different buffers (workgroup 0 writes Xout while the others read Xin).
 __global__ __launch_bounds__(256) void chol_step_kernel(double* __restrict__ A, double* __restrict__ L,
-                                                        double* __restrict__ Xinv, int n, int kb,
-                                                        int32_t* __restrict__ dev_info) {
+                                                        const double* __restrict__ Xin, double* __restrict__ Xout,
+                                                        int n, int kb, int32_t* __restrict__ dev_info) {
   if (*dev_info != 0) return;
-  __shared__ double sPi[CB * CP];
-  __shared__ double sPj[CB * CP];
+  __shared__ double sL[CB * CP];
+  __shared__ double sX[CB * CP];
+  __shared__ double sP[CB * CP];
+  __shared__ double sQ[CB * CP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int base = kb + CB;
   const f64x4 zero = {0.0, 0.0, 0.0, 0.0};
   if (blockIdx.x == 0) {
-    double* sA = sPi;  // the next diagonal block
-    double* sP = sPj;  // its panel rows, later X
-    load_block64(A, n, base, base, n, n, sA, tid);
-    load_block64(L, n, base, kb, n, n, sP, tid);
-    __syncthreads();
-    const int wi = wave >> 1, wj = wave & 1;
-    f64x4 acc[2][2];
+    load_xd(Xin, sX, tid);
+    load_block64(L, n, kb, kb, n, n, sL, tid);
+    load_block64(A, n, base, kb, n, n, sP, tid);
+    load_block64(A, n, base, base, n, n, sQ, tid);
+    lds_sync();
+    pad_diag(sQ, n, base, tid);
+    panel_rows(sP, sL, sX, wave, lane);
+    lds_sync();
+    store_block64(sP, L, n, base, kb, tid);  // L_{k+1,k}; nothing in this kernel reads it back
+    // next diagonal block sQ -= sP sP^T: wave 0 takes the first 16 x 16 block and factors it
+    // at once, waves 1-3 take the other nine lower blocks
+    int bad0 = -1;
+    if (wave == 0) {
+      const f64x4 acc = mma16<true>(sP, CP, 0, sP, CP, 0, CB, zero, lane);
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+      for (int v = 0; v < 4; ++v) sQ[((lane >> 4) + 4 * v) * CP + (lane & 15)] -= acc[v];
+      bad0 = chol16_inv_wave(sQ, sX, 0, lane);
+    } else {
+      for (int t = wave; t < 10; t += 3) {
+        const int bi = t < 3 ? 1 : t < 6 ? 2 : 3;
+        const int bj = t - bi * (bi + 1) / 2;
+        const f64x4 acc = mma16<true>(sP, CP, 16 * bi, sP, CP, 16 * bj, CB, zero, lane);
 #pragma unroll
-      for (int y = 0; y < 2; ++y)
-        acc[x][y] = wj > wi ? zero : mma16<true>(sP, CP, 32 * wi + 16 * x, sP, CP, 32 * wj + 16 * y, CB, zero, lane);
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int y = 0; y < 2; ++y)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          sA[(32 * wi + 16 * x + (lane >> 4) + 4 * v) * CP + 32 * wj + 16 * y + (lane & 15)] -= acc[x][y][v];
-    __syncthreads();
-    prepare_diag(sA, n, base, tid);
-    __syncthreads();
-    diag_factor(sA, sP, n, base, L, Xinv, dev_info, tid);
+        for (int v = 0; v < 4; ++v) sQ[(16 * bi + (lane >> 4) + 4 * v) * CP + 16 * bj + (lane & 15)] -= acc[v];
+      }
+    }
+    lds_sync();
+    diag_factor(sQ, sX, n, base, L, Xout, dev_info, tid, true, bad0);
     return;
   }
   int ti, tj;
@@ -316,7 +339,7 @@ __global__ __launch_bounds__(256) void chol_step_kernel(double* __restrict__ A, 
   const bool diag = ti == tj;
   const int wi = wave >> 1, wj = wave & 1;
   const bool active = !(diag && wj > wi);  // strictly upper 32 x 32 quarter of a diagonal tile: nothing to do
-  // the wave's 32 x 32 part of A_ij, fetched before the panels so its latency overlaps the MFMAs
+  // the wave's 32 x 32 part of A_ij, fetched first so that its latency overlaps the solves
   double cur[2][2][4];
 #pragma unroll
   for (int x = 0; x < 2; ++x)
@@ -328,17 +351,22 @@ __global__ __launch_bounds__(256) void chol_step_kernel(double* __restrict__ A, 
         const int gj = j0 + 32 * wj + 16 * y + (lane & 15);
         cur[x][y][v] = active && gi < n && gj < n ? A[(int64_t)gi * n + gj] : 0.0;
       }
-  load_block64(L, n, i0, kb, n, n, sPi, tid);
-  if (!diag) load_block64(L, n, j0, kb, n, n, sPj, tid);
-  __syncthreads();
+  load_xd(Xin, sX, tid);
+  load_block64(L, n, kb, kb, n, n, sL, tid);
+  load_block64(A, n, i0, kb, n, n, sP, tid);
+  if (!diag) load_block64(A, n, j0, kb, n, n, sQ, tid);
+  lds_sync();
+  panel_rows(sP, sL, sX, wave, lane);
+  if (!diag) panel_rows(sQ, sL, sX, wave, lane);
+  lds_sync();
+  if (tj == 0) store_block64(sP, L, n, i0, kb, tid);
   if (!active) return;
-  const double* Pj = diag ? sPi : sPj;
+  const double* Pj = diag ? sP : sQ;
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
-      const f64x4 acc = mma16<true>(sPi, CP, 32 * wi + 16 * x, Pj, CP, 32 * wj + 16 * y, CB,
-                                    f64x4{0.0, 0.0, 0.0, 0.0}, lane);
+      const f64x4 acc = mma16<true>(sP, CP, 32 * wi + 16 * x, Pj, CP, 32 * wj + 16 * y, CB, zero, lane);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int gi = i0 + 32 * wi + 16 * x + (lane >> 4) + 4 * v;
@@ -376,22 +404,23 @@ __global__ void build_m_kernel(const double* __restrict__ L, int n, float* __res
 
 using namespace wr;
 
-size_t wr_factor_ws_bytes(int64_t n) { return 2 * (size_t)n * n * sizeof(double) + (size_t)CB * CB * sizeof(double); }
+size_t wr_factor_ws_bytes(int64_t n) {
+  return 2 * (size_t)n * n * sizeof(double) + 2 * 4 * 256 * sizeof(double);
+}
 
 // M (n x n fp32, row-major) from the damped H.  ws: wr_factor_ws_bytes(n) bytes.
 int wr_factor_m(hipStream_t st, const float* H, int64_t ldh, int n, void* ws, float* M, int32_t* dev_info) {
   double* A = static_cast<double*>(ws);
   double* Lf = A + (size_t)n * n;
-  double* Xinv = Lf + (size_t)n * n;
+  double* Xinv[2] = {Lf + (size_t)n * n, Lf + (size_t)n * n + 4 * 256};  // alternate per block column
   hipLaunchKernelGGL(reverse_copy_kernel, dim3(n), dim3(256), 0, st, H, ldh, n, A);
   WR_CHECK_LAUNCH();
-  hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, st, A, n, Lf, Xinv, dev_info);
+  hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, st, A, n, Lf, Xinv[0], dev_info);
   WR_CHECK_LAUNCH();
-  for (int kb = 0; kb + CB < n; kb += CB) {
+  for (int kb = 0, s = 0; kb + CB < n; kb += CB, ++s) {
     const int nt = (n - kb - CB + CB - 1) / CB;
-    hipLaunchKernelGGL(chol_panel_kernel, dim3(nt), dim3(256), 0, st, A, n, kb, Xinv, Lf, dev_info);
-    WR_CHECK_LAUNCH();
-    hipLaunchKernelGGL(chol_step_kernel, dim3(nt * (nt + 1) / 2), dim3(256), 0, st, A, Lf, Xinv, n, kb, dev_info);
+    hipLaunchKernelGGL(chol_step_kernel, dim3(nt * (nt + 1) / 2), dim3(256), 0, st, A, Lf, Xinv[s & 1],
+                       Xinv[(s + 1) & 1], n, kb, dev_info);
     WR_CHECK_LAUNCH();
   }
   hipLaunchKernelGGL(build_m_kernel, dim3(n), dim3(256), 0, st, Lf, n, M, dev_info);
