@@ -26,6 +26,8 @@
 // is staged in LDS in a lane-major order.
 #include "common.hpp"
 
+#include <type_traits>
+
 size_t wr_factor_ws_bytes(int64_t n);
 int wr_factor_m(hipStream_t st, const float* H, int64_t ldh, int n, void* ws, float* M, int32_t* dev_info);
 
@@ -50,9 +52,29 @@ __global__ void zero_f32_kernel(float* __restrict__ p, int64_t count) {
     p[i] = 0.0f;
 }
 
-template <int P>
-__device__ __forceinline__ float group_bcast(float v, int src) {
-  return __shfl(v, src, P);
+// Value of lane N of each 16-lane row (DPP row broadcast: one VALU op, no LDS round trip).
+template <int N>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + N, 0xf, 0xf, false));
+}
+
+// Value of lane SRC of each P-lane group.
+template <int P, int SRC>
+__device__ __forceinline__ float group_bcast(float v) {
+  if constexpr (P == 16) {
+    return row_bcast<SRC>(v);
+  } else {
+    return __shfl(v, SRC, P);
+  }
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1, each with I a compile-time constant.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 template <int P>
@@ -119,23 +141,35 @@ __global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict
   }
   __syncthreads();
 
-#pragma unroll
-  for (int blk = 0; blk < NBLK; ++blk) {
+  static_for<0, NBLK>([&](auto BLK) {
+    constexpr int blk = BLK;
     sc[blk] = 0.0f;
-    if (blk * G >= ncols) continue;  // uniform
+    if (blk * G >= ncols) return;  // uniform
     // push-form values at the block start: x = M_bb^-T c_b
     float x[SB];
 #pragma unroll
     for (int q = 0; q < SB; ++q) x[q] = c[blk * SB + q];
+    // M's rows are read one step ahead so that their LDS latency stays off the serial chain
+    float mx[SB];
 #pragma unroll
-    for (int jj = 0; jj < G; ++jj) {
-      const int j = blk * G + jj;
-      const int owner = j % P, qo = jj / P;
-      const float xj = group_bcast<P>(x[qo], owner);
-      const float* mrow = &Ms[j * BATCH + p * S + blk * SB];
+    for (int q = 0; q < SB; ++q) mx[q] = Ms[(blk * G) * BATCH + p * S + blk * SB + q];
+    static_for<0, G>([&](auto JJ) {
+      constexpr int jj = JJ;
+      constexpr int j = blk * G + jj;
+      constexpr int owner = j % P, qo = jj / P;
+      float mn[SB];
+      if constexpr (jj + 1 < G) {
 #pragma unroll
-      for (int q = qo; q < SB; ++q) x[q] = fmaf(-mrow[q], xj, x[q]);
-    }
+        for (int q = 0; q < SB; ++q) mn[q] = Ms[(j + 1) * BATCH + p * S + blk * SB + q];
+      }
+      const float xj = group_bcast<P, owner>(x[qo]);
+#pragma unroll
+      for (int q = qo; q < SB; ++q) x[q] = fmaf(-mx[q], xj, x[q]);
+      if constexpr (jj + 1 < G) {
+#pragma unroll
+        for (int q = 0; q < SB; ++q) mx[q] = mn[q];
+      }
+    });
     float m = 0.0f;
 #pragma unroll
     for (int q = 0; q < SB; ++q) m = fmaxf(m, fabsf(w[blk * SB + q] + x[q]));
@@ -144,10 +178,18 @@ __global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict
     sc[blk] = s;
     const float inv_s = s > 0.0f ? 1.0f / s : 0.0f;
     // round the block's columns one at a time, pushing each error to the later batch columns
+    float mc[S];
 #pragma unroll
-    for (int jj = 0; jj < G; ++jj) {
-      const int j = blk * G + jj;
-      const int owner = j % P, io = j / P;
+    for (int i = 0; i < S; ++i) mc[i] = Ms[(blk * G) * BATCH + p * S + i];
+    static_for<0, G>([&](auto JJ) {
+      constexpr int jj = JJ;
+      constexpr int j = blk * G + jj;
+      constexpr int owner = j % P, io = j / P;
+      float mn[S];
+      if constexpr (jj + 1 < G) {
+#pragma unroll
+        for (int i = 0; i < S; ++i) mn[i] = Ms[(j + 1) * BATCH + p * S + i];
+      }
       const float v = w[io] + c[io];
       const int cd = nearest_code(v * inv_s, L);
       const float dl = w[io] - (float)(2 * cd - L) * s;
@@ -155,12 +197,15 @@ __global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict
         code[io] = (uint8_t)cd;
         d[io] = dl;
       }
-      const float dj = group_bcast<P>(dl, owner);
-      const float* mrow = &Ms[j * BATCH + p * S];
+      const float dj = group_bcast<P, owner>(dl);
 #pragma unroll
-      for (int i = io; i < S; ++i) c[i] = fmaf(mrow[i], dj, c[i]);
-    }
-  }
+      for (int i = io; i < S; ++i) c[i] = fmaf(mc[i], dj, c[i]);
+      if constexpr (jj + 1 < G) {
+#pragma unroll
+        for (int i = 0; i < S; ++i) mc[i] = mn[i];
+      }
+    });
+  });
 
   if (!active) return;
 #pragma unroll
