@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "../../include/wringer.h"
 
@@ -88,6 +89,17 @@ __device__ __forceinline__ int nearest_code(float t, int L) {
   float c = floorf(fmaf(t, 0.5f, 0.5f * (float)(L + 1)));
   c = fminf(fmaxf(c, 0.0f), (float)L);
   return (int)c;
+}
+
+// ---------------------------------------------------------------- unrolling
+// f(integral_constant<int, I>) for I = B .. E-1, each with I a compile-time constant
+// (for lane indices of DPP and readlane that must be immediates).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 // ---------------------------------------------------------------- MFMA

@@ -26,8 +26,6 @@
 // is staged in LDS in a lane-major order.
 #include "common.hpp"
 
-#include <type_traits>
-
 size_t wr_factor_ws_bytes(int64_t n);
 int wr_factor_m(hipStream_t st, const float* H, int64_t ldh, int n, void* ws, float* M, int32_t* dev_info);
 
@@ -65,15 +63,6 @@ __device__ __forceinline__ float group_bcast(float v) {
     return row_bcast<SRC>(v);
   } else {
     return __shfl(v, SRC, P);
-  }
-}
-
-// f(integral_constant<int, I>) for I = B .. E-1, each with I a compile-time constant.
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
   }
 }
 

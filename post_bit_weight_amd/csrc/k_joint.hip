@@ -84,6 +84,103 @@ __global__ void recode_residual_kernel(const float* __restrict__ T, uint8_t* __r
   if (bad) atomicCAS(dev_info, 0, -1);
 }
 
+// At[c][k] = A[k][c] (the rank x n adapter factor transposed, bf16 bits).
+__global__ void transpose_ab_kernel(const uint16_t* __restrict__ A, int rank, int n, uint16_t* __restrict__ At) {
+  const int k = blockIdx.y;
+  for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < n; c += gridDim.x * blockDim.x)
+    At[(int64_t)c * rank + k] = A[(int64_t)k * n + c];
+}
+
+// The target, recode and levels in one pass, for a 64 x 64 tile per workgroup (group 64):
+//   t = target (or dequant(codes, scales) when target is null) + scale_ab (B A)[r][c],
+// with B A (rank a multiple of 16, bf16 B and At = A^T) on the bf16 matrix cores (exact
+// products, fp32 sums); with recode, c = nearest code of t / s on the current scales;
+// writes T = t, the level 2 c - L (bf16, exact) and the codes.  A non-finite t sets
+// dev_info = -1.  Wave w owns the 32 x 32 block (w / 2, w % 2) of the product, which goes
+// through LDS; then thread i handles 16 consecutive columns of tile row i / 4.
+__global__ __launch_bounds__(256) void wring_prep_kernel(const void* __restrict__ target, int t_dtype, int64_t ldt,
+                                                         const uint16_t* __restrict__ B,
+                                                         const uint16_t* __restrict__ At, int rank, float scale_ab,
+                                                         const uint8_t* __restrict__ bits, int64_t rows, int n,
+                                                         int recode, uint8_t* __restrict__ codes,
+                                                         const uint16_t* __restrict__ scales, float* __restrict__ T,
+                                                         uint16_t* __restrict__ Lev, int32_t* __restrict__ dev_info) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t R0 = (int64_t)blockIdx.y * 64 + 32 * (wave >> 1);
+  const int C0 = blockIdx.x * 64 + 32 * (wave & 1);
+  f32x16 acc = {};
+  if (rank > 0) {
+    const int64_t ra = std::min<int64_t>(R0 + (lane & 31), rows - 1);
+    const int ca = std::min(C0 + (lane & 31), n - 1);
+    const uint16_t* pa = B + ra * rank + 8 * (lane >> 5);
+    const uint16_t* pb = At + (int64_t)ca * rank + 8 * (lane >> 5);
+    for (int k0 = 0; k0 < rank; k0 += 64) {
+      bf16x8 a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool ok = k0 + 16 * u < rank;
+        a[u] = as_bf16x8(ok ? *reinterpret_cast<const u32x4*>(pa + k0 + 16 * u) : u32x4{0u, 0u, 0u, 0u});
+        b[u] = as_bf16x8(ok ? *reinterpret_cast<const u32x4*>(pb + k0 + 16 * u) : u32x4{0u, 0u, 0u, 0u});
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc = mfma32x32x16_bf16(a[u], b[u], acc);
+    }
+  }
+  // the tile's B A through LDS, so that each thread then works on 16 consecutive columns
+  __shared__ float ab[64][65];
+  if (rank > 0) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) ab[32 * (wave >> 1) + acc_row(v, lane)][32 * (wave & 1) + (lane & 31)] = acc[v];
+  }
+  __syncthreads();
+  const int nb = n / 64;
+  const int lr = tid >> 2, lc = 16 * (tid & 3);
+  const int64_t r = (int64_t)blockIdx.y * 64 + lr;
+  const int c0 = blockIdx.x * 64 + lc;  // 16 columns inside one group of 64 (n % 64 == 0)
+  bool bad = false;
+  if (r < rows) {
+    const int L = (1 << bits[r]) - 1;
+    const int64_t e0 = r * n + c0;
+    const float s = f16_bits_to_f32(scales[r * nb + (c0 >> 6)]);
+    uint8_t cin[16];
+    *reinterpret_cast<u32x4*>(cin) = *reinterpret_cast<const u32x4*>(codes + e0);
+    float t[16];
+    if (target) {
+      if (t_dtype == WR_BF16) {
+        const uint16_t* tp = static_cast<const uint16_t*>(target) + r * ldt + c0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) t[i] = bf16_bits_to_f32(tp[i]);
+      } else {
+        const float* tp = static_cast<const float*>(target) + r * ldt + c0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) t[i] = tp[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) t[i] = (float)(2 * (int)cin[i] - L) * s;
+    }
+    uint8_t cout[16];
+    uint32_t lev[8];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float x = t[i];
+      if (rank > 0) x = x + scale_ab * ab[lr][lc + i];
+      bad |= !(fabsf(x) <= 3.0e38f);
+      const int cd = recode ? nearest_code(s > 0.0f ? x / s : 0.0f, L) : (int)cin[i];
+      t[i] = x;
+      cout[i] = (uint8_t)cd;
+      const uint32_t lb = __float_as_uint((float)(2 * cd - L)) >> 16;  // small odd integer: exact in bf16
+      lev[i >> 1] = (i & 1) ? (lev[i >> 1] | (lb << 16)) : lb;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; q += 4) *reinterpret_cast<f32x4*>(T + e0 + q) = f32x4{t[q], t[q + 1], t[q + 2], t[q + 3]};
+    *reinterpret_cast<u32x4*>(Lev + e0) = u32x4{lev[0], lev[1], lev[2], lev[3]};
+    *reinterpret_cast<u32x4*>(Lev + e0 + 8) = u32x4{lev[4], lev[5], lev[6], lev[7]};
+    if (recode) *reinterpret_cast<u32x4*>(codes + e0) = *reinterpret_cast<const u32x4*>(cout);
+  }
+  if (bad) atomicCAS(dev_info, 0, -1);
+}
+
 __global__ void split_h_kernel(const float* __restrict__ H, int64_t ldh, int n, uint16_t* __restrict__ H0,
                                uint16_t* __restrict__ H1, uint16_t* __restrict__ H2) {
   const int64_t i = blockIdx.y;
@@ -570,23 +667,39 @@ int wr_wring_solve_impl(wr_ctx* ctx, const void* target, int t_dtype, int64_t ld
   WR_CHECK_LAUNCH();
   if (rows == 0) return WR_OK;
   const unsigned gx = (unsigned)std::min<int64_t>((n + 255) / 256, 16);
-  hipLaunchKernelGGL(target_kernel, dim3(gx, (unsigned)rows), dim3(256), 0, st, target, t_dtype, ldt, codes, scales,
-                     bits, rows, n, group, T);
-  WR_CHECK_LAUNCH();
-  if (adapter) {
-    float* Bf = reinterpret_cast<float*>(ws + lay.Bf);
-    float* Af = reinterpret_cast<float*>(ws + lay.Af);
-    hipLaunchKernelGGL(to_f32_kernel, dim3(256), dim3(256), 0, st, B, ab_dtype, rows * rank, Bf);
+  const bool fused = lh && (!adapter || (ab_dtype == WR_BF16 && rank % 16 == 0 &&
+                                         reinterpret_cast<uintptr_t>(B) % 16 == 0));
+  if (fused) {
+    uint16_t* At = reinterpret_cast<uint16_t*>(ws + lay.Af);
+    if (adapter) {
+      hipLaunchKernelGGL(transpose_ab_kernel, dim3((unsigned)std::min((n + 255) / 256, 64), (unsigned)rank), dim3(256),
+                         0, st, static_cast<const uint16_t*>(A), rank, n, At);
+      WR_CHECK_LAUNCH();
+    }
+    const dim3 pgrid((unsigned)((n + 63) / 64), (unsigned)((rows + 63) / 64));
+    hipLaunchKernelGGL(wring_prep_kernel, pgrid, dim3(256), 0, st, target, t_dtype, ldt,
+                       static_cast<const uint16_t*>(B), At, adapter ? rank : 0, adapter ? alpha / (float)rank : 0.0f,
+                       bits, rows, n, (flags & WR_RECODE_NEAREST) ? 1 : 0, codes, scales, T, Lev, dev_info);
     WR_CHECK_LAUNCH();
-    hipLaunchKernelGGL(to_f32_kernel, dim3(256), dim3(256), 0, st, A, ab_dtype, (int64_t)rank * n, Af);
+  } else {
+    hipLaunchKernelGGL(target_kernel, dim3(gx, (unsigned)rows), dim3(256), 0, st, target, t_dtype, ldt, codes, scales,
+                       bits, rows, n, group, T);
     WR_CHECK_LAUNCH();
-    const int rc = wr_gemm_f32(st, (int)rows, n, rank, Bf, rank, Af, n, true, T, n, alpha / (float)rank, true, false,
-                               nullptr);
-    if (rc) return rc;
+    if (adapter) {
+      float* Bf = reinterpret_cast<float*>(ws + lay.Bf);
+      float* Af = reinterpret_cast<float*>(ws + lay.Af);
+      hipLaunchKernelGGL(to_f32_kernel, dim3(256), dim3(256), 0, st, B, ab_dtype, rows * rank, Bf);
+      WR_CHECK_LAUNCH();
+      hipLaunchKernelGGL(to_f32_kernel, dim3(256), dim3(256), 0, st, A, ab_dtype, (int64_t)rank * n, Af);
+      WR_CHECK_LAUNCH();
+      const int rc = wr_gemm_f32(st, (int)rows, n, rank, Bf, rank, Af, n, true, T, n, alpha / (float)rank, true, false,
+                                 nullptr);
+      if (rc) return rc;
+    }
+    hipLaunchKernelGGL(recode_residual_kernel, dim3(gx, (unsigned)rows), dim3(256), 0, st, T, codes, scales, bits, rows,
+                       n, group, (flags & WR_RECODE_NEAREST) ? 1 : 0, Lev, T0, T1, T2, dev_info);
+    WR_CHECK_LAUNCH();
   }
-  hipLaunchKernelGGL(recode_residual_kernel, dim3(gx, (unsigned)rows), dim3(256), 0, st, T, codes, scales, bits, rows,
-                     n, group, (flags & WR_RECODE_NEAREST) ? 1 : 0, Lev, T0, T1, T2, dev_info);
-  WR_CHECK_LAUNCH();
   hipLaunchKernelGGL(split_h_kernel, dim3(gx, (unsigned)n), dim3(256), 0, st, H, ldh, n, H0, H1, H2);
   WR_CHECK_LAUNCH();
   dim3 ggrid((unsigned)((rows + 127) / 128), (unsigned)nb);
