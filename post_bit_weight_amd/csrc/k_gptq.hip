@@ -73,25 +73,91 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
-// One lazy batch of BATCH columns starting at b0 (ncols <= BATCH valid columns).
+// One lazy batch of BATCH columns starting at b0 (ncols <= BATCH valid columns).  The
+// errors of the kprev columns before b0 in the batch's group (E0..E2: three bf16 parts,
+// leading dimension lde, this batch's slot at column kprev) are first applied to this
+// batch's corrections, C_b += E M[b0 - kprev.., b0..] with M's transposed bf16 parts
+// Mt0..Mt2, on the bf16 matrix cores; Cbuf holds the corrections from the groups before.
+// The batch's errors go to E0..E2 at its slot.
 template <int P, int BATCH, int G>
 __global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict__ W, int w_dtype, int64_t rows,
                                                           int n, int64_t ldw, const float* __restrict__ M,
                                                           const uint8_t* __restrict__ bits, int b0, int ncols,
-                                                          float* __restrict__ Cbuf, uint16_t* __restrict__ E0,
+                                                          float* __restrict__ Cbuf, int lde, int kprev,
+                                                          uint16_t* __restrict__ E0,
                                                           uint16_t* __restrict__ E1, uint16_t* __restrict__ E2,
+                                                          const uint16_t* __restrict__ Mt0,
+                                                          const uint16_t* __restrict__ Mt1,
+                                                          const uint16_t* __restrict__ Mt2,
                                                           uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
                                                           const int32_t* __restrict__ dev_info) {
   constexpr int S = BATCH / P;       // columns per lane
   constexpr int NBLK = BATCH / G;    // blocks per batch
   constexpr int SB = G / P;          // columns per lane per block
+  constexpr int R = 256 / P;         // rows per workgroup
   __shared__ __attribute__((aligned(16))) float Ms[BATCH * BATCH];  // [k][p][slot]
+  __shared__ __attribute__((aligned(16))) float La[R * BATCH];      // earlier errors of the group, [row][col]
   if (*dev_info != 0) return;
   const int tid = threadIdx.x;
   const int p = tid % P;
-  const int64_t row = (int64_t)blockIdx.x * (256 / P) + tid / P;
+  const int64_t row = (int64_t)blockIdx.x * R + tid / P;
   const bool active = row < rows;
 
+  if (kprev > 0) {
+    // wave w: columns 32 w .. 32 w + 31 as two 16 x 16 blocks on v_mfma_f32_16x16x32_bf16
+    // (operand lane l supplies row/column l % 16 at k = 8 (l / 16) .. +7; result v of lane l
+    // is row 4 (l / 16) + v), the errors and M as three bf16 parts each, the six part
+    // products with i + j <= 2 summed smallest first.
+    static_assert(R == 16 && BATCH == 128, "16 rows x 128 columns: two 16 x 16 blocks per wave");
+    const int lane = tid & 63, wave = tid >> 6, li = lane & 15, lk = lane >> 4;
+    const int64_t er = std::min<int64_t>((int64_t)blockIdx.x * R + li, rows - 1);
+    const int64_t eo = er * lde - kprev + 8 * lk;  // relative to this batch's slot
+    int64_t mo[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int col = std::min(32 * wave + 16 * t + li, ncols - 1);
+      mo[t] = (int64_t)(b0 + col) * n + (b0 - kprev) + 8 * lk;
+    }
+    auto ld = [](const uint16_t* q) { return as_bf16x8(*reinterpret_cast<const u32x4*>(q)); };
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // one batch (128 k, four 32-wide steps) at a time: all of its loads are issued before
+    // its MFMAs, so each batch costs one memory round trip
+    for (int kb = 0; kb < kprev; kb += 128) {
+      bf16x8 ea[4][3], mb[4][3][2];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k0 = kb + 32 * u;
+        ea[u][0] = ld(E0 + eo + k0);
+        ea[u][1] = ld(E1 + eo + k0);
+        ea[u][2] = ld(E2 + eo + k0);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          mb[u][0][t] = ld(Mt0 + mo[t] + k0);
+          mb[u][1][t] = ld(Mt1 + mo[t] + k0);
+          mb[u][2][t] = ld(Mt2 + mo[t] + k0);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          f32x4 v = acc[t];
+          v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ea[u][2], mb[u][0][t], v, 0, 0, 0);
+          v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ea[u][1], mb[u][1][t], v, 0, 0, 0);
+          v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ea[u][0], mb[u][2][t], v, 0, 0, 0);
+          v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ea[u][1], mb[u][0][t], v, 0, 0, 0);
+          v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ea[u][0], mb[u][1][t], v, 0, 0, 0);
+          v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ea[u][0], mb[u][0][t], v, 0, 0, 0);
+          acc[t] = v;
+        }
+    }
+    const bool c0ok = 32 * wave + li < ncols, c1ok = 32 * wave + 16 + li < ncols;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      La[(4 * lk + v) * BATCH + 32 * wave + li] = c0ok ? acc[0][v] : 0.0f;
+      La[(4 * lk + v) * BATCH + 32 * wave + 16 + li] = c1ok ? acc[1][v] : 0.0f;
+    }
+  }
   {
     // M's diagonal batch block: every thread's 16 four-wide loads are in flight before the LDS stores
     static_assert(BATCH * BATCH == 256 * 64, "16 loads of four floats per thread");
@@ -129,6 +195,10 @@ __global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict
     }
   }
   __syncthreads();
+  if (kprev > 0) {
+#pragma unroll
+    for (int i = 0; i < S; ++i) c[i] += La[(tid / P) * BATCH + p + P * i];
+  }
 
   static_for<0, NBLK>([&](auto BLK) {
     constexpr int blk = BLK;
@@ -202,7 +272,7 @@ __global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict
     const int col = p + P * i;
     if (col < ncols) {
       codes[row * n + b0 + col] = code[i];
-      const int64_t e = row * BATCH + col;
+      const int64_t e = row * lde + col;
       split3(d[i], E0[e], E1[e], E2[e]);
     }
   }
@@ -238,77 +308,143 @@ __global__ __launch_bounds__(256) void split_mt_kernel(const float* __restrict__
   }
 }
 
-// C[r][c0 + c] += sum_k E[r][k] M[b0 + k][c0 + c] for r < rows, c < N, k < 128, with E
-// and M given as three bf16 planes each (E_i: rows x 128; Mt_i: n x n, transposed).
-// 64 x 64 output tile per workgroup.  Wave w takes k in [32 w, 32 w + 32) for the whole
-// tile (2 x 2 blocks of 32 x 32, v_mfma_f32_32x32x16_bf16: operand lane l supplies row
-// or column l % 32 at k = 8 (l / 32) .. +7 of a 16-wide step), so each wave issues all
-// of its operand loads at once (16 contiguous bytes per lane, straight from global
-// memory) together with the C tile; the four partial tiles are summed through LDS in
-// wave order and added to C.
-__global__ __launch_bounds__(256, 2) void trail_s6_kernel(int64_t rows, int N, int n, int b0, int c0,
-                                                          const uint16_t* __restrict__ E0,
-                                                          const uint16_t* __restrict__ E1,
-                                                          const uint16_t* __restrict__ E2,
-                                                          const uint16_t* __restrict__ Mt0,
-                                                          const uint16_t* __restrict__ Mt1,
-                                                          const uint16_t* __restrict__ Mt2, float* __restrict__ C,
-                                                          const int32_t* __restrict__ dev_info) {
-  __shared__ float red[4][64][65];
+typedef __attribute__((address_space(3))) char tw_lds_char;
+
+// Wave-wide LDS DMA: lane l copies 16 bytes from sbase + voff to LDS byte m0 + 16 l (inline
+// assembly so that the compiler does not wait for it before unrelated LDS reads; completion
+// is awaited with tw_vm_wait).  The M0 write needs one wait state.
+__device__ __forceinline__ void tw_dma16(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2" ::"v"(voff), "s"(m0), "s"(sbase)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void tw_vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void tw_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+constexpr int TW_T = 128;                  // output tile edge
+constexpr int TW_KC = 32;                  // k per stage
+constexpr int TW_PLANE = TW_T * TW_KC * 2; // one bf16 part of one operand tile: 8 KB
+constexpr int TW_STAGE = 6 * TW_PLANE;     // E0..2 then Mt0..2: 48 KB
+constexpr int TW_DMA = TW_STAGE / 1024 / 4;  // 1 KB DMAs per wave per stage: 12
+
+// 16-byte unit (row r, k-octet q) of a 128 x 32 bf16 tile: sixteen consecutive rows at one
+// octet fall on sixteen distinct 16-byte bank groups of a 256-byte line.
+__device__ __forceinline__ int tw_unit(int r, int q) { return r * 4 + (q ^ ((r >> 2) & 3)); }
+
+// The wide trailing update C[r][c0 + c] += sum_{k < K} E[r][k] M[b0 + k][c0 + c] (K a multiple
+// of 32; E and M as three bf16 planes each, E_i rows x K with leading dimension lde, Mt_i n x n
+// transposed; the six part products with i + j <= 2, smallest first).  128 x 128 tile per
+// workgroup, wave w owns rows 64 (w / 2).., columns 64 (w % 2).. as 2 x 2 blocks of 32 x 32.
+// The operand tiles go to LDS by DMA two 32-wide k stages ahead (three stages, 144 KB).
+__global__ __launch_bounds__(256, 1) void trail_wide_kernel(int64_t rows, int N, int n, int K, int b0, int c0,
+                                                            const uint16_t* __restrict__ E0,
+                                                            const uint16_t* __restrict__ E1,
+                                                            const uint16_t* __restrict__ E2, int lde,
+                                                            const uint16_t* __restrict__ Mt0,
+                                                            const uint16_t* __restrict__ Mt1,
+                                                            const uint16_t* __restrict__ Mt2, float* __restrict__ C,
+                                                            const int32_t* __restrict__ dev_info) {
+  extern __shared__ __attribute__((aligned(1024))) char tw_lds[];
   if (*dev_info != 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t R0 = (int64_t)blockIdx.y * 64;
-  const int C0 = blockIdx.x * 64;
-  // the C tile: thread tid holds elements tid + 256 q (row e / 64, column e % 64)
-  float cv[16];
+  const tw_lds_char* lds = (const tw_lds_char*)tw_lds;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t R0 = (int64_t)blockIdx.y * TW_T;
+  const int C0 = blockIdx.x * TW_T;
+  const int rmax = (int)std::min<int64_t>(rows - 1 - R0, TW_T - 1);
+  const int cmax = std::min(N - 1 - C0, TW_T - 1);
+  // DMA q (0..47 per stage) fills LDS bytes [1024 q, +1024): q / 8 is the plane (E0, E1, E2,
+  // Mt0, Mt1, Mt2), q % 8 the 1 KB part of it.  Wave w issues q = w + 4 i.
+  uint32_t voff[TW_DMA];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int e = tid + 256 * q, r = e >> 6, c = e & 63;
-    cv[q] = R0 + r < rows && C0 + c < N ? C[(R0 + r) * n + c0 + C0 + c] : 0.0f;
+  for (int i = 0; i < TW_DMA; ++i) {
+    const int q = wave + 4 * i;
+    const int u = (q & 7) * 64 + lane, r = u >> 2;
+    const int oct = (u & 3) ^ ((r >> 2) & 3);
+    voff[i] = q < 24 ? (uint32_t)((std::min(r, rmax) * (int64_t)lde + 8 * oct) * 2)
+                     : (uint32_t)(((int64_t)std::min(r, cmax) * n + 8 * oct) * 2);
   }
-  const int kofs = 32 * wave + 8 * (lane >> 5);
-  bf16x8 a[3][2][2], b[3][2][2];  // [part][block][step]
-  auto ld = [](const uint16_t* p) { return as_bf16x8(*reinterpret_cast<const u32x4*>(p)); };
+  auto issue = [&](int k0, int slot) {
+    const uint32_t base = lds_base + slot * TW_STAGE;
+    const int64_t eo = R0 * lde + k0;
+    const int64_t mo = (int64_t)(c0 + C0) * n + b0 + k0;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int64_t r = std::min<int64_t>(R0 + 32 * t + (lane & 31), rows - 1);
-    const int c = std::min(C0 + 32 * t + (lane & 31), N - 1);
-    const int64_t ao = r * 128 + kofs;
-    const int64_t bo = (int64_t)(c0 + c) * n + b0 + kofs;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      a[0][t][kk] = ld(E0 + ao + 16 * kk);
-      a[1][t][kk] = ld(E1 + ao + 16 * kk);
-      a[2][t][kk] = ld(E2 + ao + 16 * kk);
-      b[0][t][kk] = ld(Mt0 + bo + 16 * kk);
-      b[1][t][kk] = ld(Mt1 + bo + 16 * kk);
-      b[2][t][kk] = ld(Mt2 + bo + 16 * kk);
+    for (int i = 0; i < TW_DMA; ++i) {
+      const int q = wave + 4 * i;
+      const uint16_t* src = q < 8 ? E0 + eo : q < 16 ? E1 + eo : q < 24 ? E2 + eo
+                          : q < 32 ? Mt0 + mo : q < 40 ? Mt1 + mo : Mt2 + mo;
+      tw_dma16(src, voff[i], base + q * 1024);
     }
+  };
+  const int wr0 = 64 * (wave >> 1), wc0 = 64 * (wave & 1);
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
+  auto frag = [&](const tw_lds_char* st, int plane, int r, int q) {
+    const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(st + plane * TW_PLANE + tw_unit(r, q) * 16);
+    return as_bf16x8(v);
+  };
+  const int nst = K / TW_KC;  // >= 2
+  issue(0, 0);
+  issue(TW_KC, 1);
+  for (int stg = 0; stg < nst; ++stg) {
+    const int slot = stg % 3;
+    // the slot of stage stg + 2 held stage stg - 1, which every wave finished before the
+    // barrier that ended the previous iteration
+    if (stg + 2 < nst) {
+      issue(TW_KC * (stg + 2), (stg + 2) % 3);
+      tw_vm_wait<2 * TW_DMA>();
+    } else if (stg + 1 < nst) {
+      tw_vm_wait<TW_DMA>();
+    } else {
+      tw_vm_wait<0>();
+    }
+    tw_barrier();
+    const tw_lds_char* st = lds + slot * TW_STAGE;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int q = 2 * ks + (lane >> 5);
+      bf16x8 a[3][2], b[3][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+          a[p][t] = frag(st, p, wr0 + 32 * t + (lane & 31), q);
+          b[p][t] = frag(st, 3 + p, wc0 + 32 * t + (lane & 31), q);
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          f32x16 v = acc[x][y];
+          v = mfma32x32x16_bf16(a[2][x], b[0][y], v);  // smallest terms first
+          v = mfma32x32x16_bf16(a[1][x], b[1][y], v);
+          v = mfma32x32x16_bf16(a[0][x], b[2][y], v);
+          v = mfma32x32x16_bf16(a[1][x], b[0][y], v);
+          v = mfma32x32x16_bf16(a[0][x], b[1][y], v);
+          v = mfma32x32x16_bf16(a[0][x], b[0][y], v);
+          acc[x][y] = v;
+        }
+    }
+    tw_barrier();  // every wave is done with this slot before the next stage's DMA into it
   }
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
-      f32x16 v = {};
+      const int c = C0 + wc0 + 32 * y + (lane & 31);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        v = mfma32x32x16_bf16(a[2][x][kk], b[0][y][kk], v);  // smallest terms first
-        v = mfma32x32x16_bf16(a[1][x][kk], b[1][y][kk], v);
-        v = mfma32x32x16_bf16(a[0][x][kk], b[2][y][kk], v);
-        v = mfma32x32x16_bf16(a[1][x][kk], b[0][y][kk], v);
-        v = mfma32x32x16_bf16(a[0][x][kk], b[1][y][kk], v);
-        v = mfma32x32x16_bf16(a[0][x][kk], b[0][y][kk], v);
+      for (int v = 0; v < 16; ++v) {
+        const int64_t r = R0 + wr0 + 32 * x + acc_row(v, lane);
+        if (r < rows && c < N) C[r * n + c0 + c] += acc[x][y][v];
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) red[wave][32 * x + acc_row(i, lane)][32 * y + (lane & 31)] = v[i];
     }
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int e = tid + 256 * q, r = e >> 6, c = e & 63;
-    if (R0 + r < rows && C0 + c < N)
-      C[(R0 + r) * n + c0 + C0 + c] = cv[q] + (((red[0][r][c] + red[1][r][c]) + red[2][r][c]) + red[3][r][c]);
-  }
 }
 
 }  // namespace wr
@@ -316,6 +452,7 @@ __global__ __launch_bounds__(256, 2) void trail_s6_kernel(int64_t rows, int N, i
 using namespace wr;
 
 static constexpr int kBatch = 128;
+static constexpr int kSuper = 4 * kBatch;  // columns whose errors one wide trailing update applies
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -333,7 +470,7 @@ static GptqLayout gptq_layout(int64_t rows, int64_t n) {
   };
   l.M = take((size_t)n * n * 4);                                       // M, fp32
   l.C = take((size_t)rows * n * 4);                                    // corrections C
-  for (int i = 0; i < 3; ++i) l.E[i] = take((size_t)rows * kBatch * 2);  // batch errors, bf16 parts
+  for (int i = 0; i < 3; ++i) l.E[i] = take((size_t)rows * kSuper * 2);  // errors of 4 batches, bf16 parts
   for (int i = 0; i < 3; ++i) l.Mt[i] = take((size_t)n * n * 2);          // M transposed, bf16 parts
   l.total = off;
   return l;
@@ -343,21 +480,23 @@ size_t wr_gptq_ws_bytes(int64_t rows, int64_t n) { return gptq_layout(rows, n).t
 
 template <int P, int G>
 static void launch_panel(hipStream_t st, const void* W, int w_dtype, int64_t rows, int n, int64_t ldw, const float* Mm,
-                         const uint8_t* bits, int b0, int ncols, float* Cb, uint16_t* const* E, uint8_t* codes,
-                         uint16_t* scales, const int32_t* dev_info) {
+                         const uint8_t* bits, int b0, int ncols, float* Cb, uint16_t* const* E, uint16_t* const* Mt,
+                         uint8_t* codes, uint16_t* scales, const int32_t* dev_info) {
   const unsigned grid = (unsigned)((rows + (256 / P) - 1) / (256 / P));
+  const int eoff = b0 % kSuper;  // this batch's slot among the errors of its group of four
   hipLaunchKernelGGL((sweep_panel_kernel<P, kBatch, G>), dim3(grid), dim3(256), 0, st, W, w_dtype, rows, n, ldw, Mm,
-                     bits, b0, ncols, Cb, E[0], E[1], E[2], codes, scales, dev_info);
+                     bits, b0, ncols, Cb, kSuper, eoff, E[0] + eoff, E[1] + eoff, E[2] + eoff, Mt[0], Mt[1], Mt[2],
+                     codes, scales, dev_info);
 }
 
 template <int P>
 static int launch_panel_g(hipStream_t st, int G, const void* W, int w_dtype, int64_t rows, int n, int64_t ldw,
                           const float* Mm, const uint8_t* bits, int b0, int ncols, float* Cb, uint16_t* const* E,
-                          uint8_t* codes, uint16_t* scales, const int32_t* dev_info) {
+                          uint16_t* const* Mt, uint8_t* codes, uint16_t* scales, const int32_t* dev_info) {
   switch (G) {
-    case 32: launch_panel<P, 32>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, codes, scales, dev_info); break;
-    case 64: launch_panel<P, 64>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, codes, scales, dev_info); break;
-    case 128: launch_panel<P, 128>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, codes, scales, dev_info); break;
+    case 32: launch_panel<P, 32>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, Mt, codes, scales, dev_info); break;
+    case 64: launch_panel<P, 64>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, Mt, codes, scales, dev_info); break;
+    case 128: launch_panel<P, 128>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, Mt, codes, scales, dev_info); break;
     default: return WR_EUNSUPPORTED;
   }
   WR_CHECK_LAUNCH();
@@ -399,15 +538,27 @@ int wr_gptq_sweep_impl(wr_ctx* ctx, const void* W, int w_dtype, int64_t rows, in
     hipLaunchKernelGGL(split_mt_kernel, dim3(nt, nt), dim3(256), 0, st, Mm, n, Mt[0], Mt[1], Mt[2], dev_info);
     WR_CHECK_LAUNCH();
   }
+  // Batches go in groups of four (kSuper columns).  A batch's panel applies the errors of
+  // the earlier batches of its group to its own columns; after a group's last batch its
+  // errors reach every column after the group at once (K = 512), so the corrections C of
+  // the far columns are read and written once per group, not per batch.
   for (int b0 = 0; b0 < n; b0 += kBatch) {
     const int ncols = std::min(kBatch, n - b0);
-    rc = launch_panel_g<16>(st, group, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, codes, scales, dev_info);
+    rc = launch_panel_g<16>(st, group, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, Mt, codes, scales,
+                            dev_info);
     if (rc) return rc;
-    const int rest = n - b0 - ncols;
-    if (rest > 0) {  // ncols == kBatch here: only the last batch can be short
-      const dim3 grid((unsigned)((rest + 63) / 64), (unsigned)((rows + 63) / 64));
-      hipLaunchKernelGGL(trail_s6_kernel, grid, dim3(256), 0, st, rows, rest, n, b0, b0 + ncols, E[0], E[1], E[2],
-                         Mt[0], Mt[1], Mt[2], Cb, dev_info);
+    const int s0 = b0 - b0 % kSuper, s1 = std::min(s0 + kSuper, n);
+    if (b0 + ncols == s1 && s1 < n) {  // the group is complete and full (s1 - s0 == kSuper)
+      static bool lds_attr = false;
+      if (!lds_attr) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(trail_wide_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 3 * TW_STAGE) != hipSuccess)
+          return WR_EHIP;
+        lds_attr = true;
+      }
+      const dim3 grid((unsigned)((n - s1 + TW_T - 1) / TW_T), (unsigned)((rows + TW_T - 1) / TW_T));
+      hipLaunchKernelGGL(trail_wide_kernel, grid, dim3(256), 3 * TW_STAGE, st, rows, n - s1, n, kSuper, s0, s1, E[0],
+                         E[1], E[2], kSuper, Mt[0], Mt[1], Mt[2], Cb, dev_info);
       WR_CHECK_LAUNCH();
     }
   }

@@ -206,6 +206,30 @@ def test_gptq_mixed_bits_and_groups(wr, ctx, bits):
         assert scale_ulps(scales[ok], ref["scales"][ok]).max() <= 1
 
 
+def test_gptq_several_column_groups(wr, ctx):
+    """n = 1280: two full groups of four 128-column batches (the panels apply the earlier
+    batches of their group themselves, one wide update per group) and a short third group;
+    37 rows (a ragged last 16-row panel)."""
+    rng = np.random.default_rng(23)
+    rows, n = 37, 1280
+    A = rng.standard_normal((2 * n, n)) * np.sqrt(10.0 ** (-2 * np.arange(n) / (n - 1)))
+    A[:, :8] *= 10
+    H = A.T @ A / (2 * n)
+    H, _ = oracle.damp(H, 0.01)
+    H32 = H.astype(np.float32)
+    W = torch.from_numpy(0.02 * rng.standard_normal((rows, n))).to(torch.bfloat16)
+    bits_rows = np.where(np.arange(rows) % 4 == 0, 3, 2)
+    for g in (64, 32):
+        codes, scales, info = _sweep(wr, ctx, W, H32, bits_rows, g)
+        assert info == 0
+        ref = oracle.gptq_sweep(W.double().numpy(), H32.astype(np.float64), bits_rows, g)
+        cp = code_parity(codes, ref["codes"], ref["t"], oracle.levels_count(bits_rows))
+        # a row may leave the oracle's trajectory only at a near-tie (fp32 vs fp64 sweep)
+        assert len(cp["rows"]) <= 2 and cp["worst_first"] <= TIE, (g, cp)
+        ok = cp["identical_rows"]
+        assert scale_ulps(scales[ok], ref["scales"][ok]).max() <= 1
+
+
 def test_gptq_diagonal_H_is_plain_rounding(wr, ctx, toy):
     W = toy["W"]
     d = np.linspace(0.5, 2.0, 512)
