@@ -10,7 +10,8 @@ quantized per second.
 Also reported: the roofline of the dominant kernel (the bf16 SYRK that
 accumulates H: N n (n + 1) useful flops per call, timed live with HIP events on
 the stream it runs on) and the CPU oracle timed on a bounded sample of the same
-workload on the host cores.
+workload on the host cores, and, outside the timed step, the materializer (packed
+module -> bf16 weights) against the HBM peak.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -27,7 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-PEAK_HBM_GBS = 8000.0
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 WORKLOAD = {
     "workload": "q_proj 4096x2560 bf16 (Student-t nu=5, std 0.02), X 131072x2560 bf16 (spectral + 1% outlier "
@@ -110,6 +111,36 @@ def cpu_baseline(X_host, W_host, B_host, A_host, cfg, n_rows, n_calib):
                   f"{n_rows} of {cfg['rows']} weight rows, one factorisation; extrapolated linearly "
                   f"(measured {t_h + t_sweep + t_rest + t_fact:.1f} s)",
     }
+
+
+def time_materialize(wr, ctx, torch, reps=20):
+    """The materializer (packed module -> bf16 weights, inverse rotation) on one layer's 2560-wide
+    group of the 36-layer body: q, k, v, gate and up stacked, 25600 x 2560, 2-bit, group 64,
+    Hadamard blocks of 512.  HBM-bound: algorithmic bytes = packed codes and scales read + bf16
+    written, against the 8 TB/s peak."""
+    rows, n, bits, g, m = 25600, 2560, 2, 64, 512
+    code_bytes = rows * n * bits // 8
+    gen = torch.Generator(device="cuda").manual_seed(20261208)
+    buf = torch.randint(0, 256, (wr.packed_nbytes(rows, n, bits, g),), dtype=torch.uint8, device="cuda",
+                        generator=gen)
+    sc = (torch.rand(rows * (n // g), device="cuda", generator=gen) * 0.029 + 1e-3).to(torch.float16)
+    buf[code_bytes:] = sc.view(torch.uint8)
+    signs = (torch.randint(0, 2, (n,), device="cuda", generator=gen) * 2 - 1).to(torch.int8)
+    out = torch.empty(rows, n, dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        wr.wr_materialize(ctx, buf, rows, n, bits, g, out, had_block=m, signs=signs)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(ctx.stream)
+    for _ in range(reps):
+        wr.wr_materialize(ctx, buf, rows, n, bits, g, out, had_block=m, signs=signs)
+    e1.record(ctx.stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = buf.numel() + 2 * rows * n
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"{rows}x{n} 2-bit group {g}, inverse Hadamard blocks of {m}", "ms": ms,
+            "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+            "bytes_per_launch": nbytes}
 
 
 def progress(msg):
@@ -227,6 +258,8 @@ def main():
         },
         "stage_ms": per_stage,
     }
+    progress("timing the materializer")
+    line["materialize"] = time_materialize(wr, ctx, torch)
     if not args.no_cpu_baseline:
         progress("timing the oracle on a bounded sample")
         Xh = X[: args.cpu_calib].float().cpu().numpy()

@@ -188,6 +188,23 @@ int wr_pack(wr_ctx* ctx, const uint8_t* codes, const uint16_t* scales, int64_t r
 int wr_unpack(wr_ctx* ctx, const uint8_t* in, size_t in_bytes, int64_t rows, int64_t n, int32_t bits,
               int32_t group, uint8_t* codes, uint16_t* scales, uint16_t* dequant_bf16);
 
+/*
+ * (f) Materialize (Wringer model cards, "What is in this repo": the materializer turns
+ * the container into the fake-quant bf16 checkpoint that inference loads; "Honest
+ * caveats": materializing at ledger precision).
+ * For one packed module (wr_pack layout: rows x n_store codes of `bits` bits, fp16 scales
+ * per `group`), writes out (rows x n_out bf16 bit patterns, leading dimension ldo):
+ *   out[r][j] = bf16_RNE( (R^T v_r)_j ),  v_r = the dequantized row (2 c - L) s,  j < n_out,
+ * where R is the rotation of wr_hadamard_rotate with had_block and signs (device int8, +-1,
+ * length n_store); had_block 0 means R = I (signs may be null).  The dequantized values are
+ * exact in fp32, R^T is applied in fp32 and each weight is rounded to bf16 once; the last
+ * n_store - n_out columns (the zero padding of the input dim) are dropped.
+ * n_out <= n_store, ldo >= n_out, n_store % 8 == 0; with a rotation had_block is a power of
+ * two in 2..4096 dividing n_store.  in_bytes must equal the wr_pack size.  No workspace.
+ */
+int wr_materialize(wr_ctx* ctx, const uint8_t* in, size_t in_bytes, int64_t rows, int64_t n_store, int32_t bits,
+                   int32_t group, int32_t had_block, const int8_t* signs, int64_t n_out, uint16_t* out, int64_t ldo);
+
 /* Static description of a status code. */
 const char* wr_strerror(int status);
 

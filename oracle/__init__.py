@@ -38,6 +38,7 @@ from .wring import wring_target, wring
 from .pack import pack, unpack, packed_bytes, code_bytes_per_row
 from .metrics import proxy_loss, ledger_bits_per_weight, threshold_distance
 from .solve import solve_module, solve_rows
+from .materialize import bf16_rne_bits, bf16_bits_to_f64, materialize, materialize_exact
 
 __all__ = [
     "second_moment", "second_moment_chunks", "sum_of_products", "pad_square", "damp",
@@ -49,4 +50,5 @@ __all__ = [
     "pack", "unpack", "packed_bytes", "code_bytes_per_row",
     "proxy_loss", "ledger_bits_per_weight", "threshold_distance",
     "solve_module", "solve_rows",
+    "bf16_rne_bits", "bf16_bits_to_f64", "materialize", "materialize_exact",
 ]

@@ -24,7 +24,7 @@ WR_RECODE_NEAREST = 1
 EXPORTED = (
     "wr_create", "wr_destroy", "wr_workspace_bytes", "wr_set_workspace",
     "wr_hessian_accumulate", "wr_hessian_finalize", "wr_hadamard_rotate",
-    "wr_gptq_sweep", "wr_wring_solve", "wr_pack", "wr_unpack", "wr_strerror",
+    "wr_gptq_sweep", "wr_wring_solve", "wr_pack", "wr_unpack", "wr_materialize", "wr_strerror",
 )
 
 
@@ -63,6 +63,7 @@ def load():
         "wr_wring_solve": (I, [P, P, I, I64, P, P, c.c_int32, F, I, P, I64, I64, I64, P, c.c_int32, F, I, P, P, P]),
         "wr_pack": (I, [P, P, P, I64, I64, c.c_int32, c.c_int32, P, SZ]),
         "wr_unpack": (I, [P, P, SZ, I64, I64, c.c_int32, c.c_int32, P, P, P]),
+        "wr_materialize": (I, [P, P, SZ, I64, I64, c.c_int32, c.c_int32, c.c_int32, P, I64, P, I64]),
         "wr_strerror": (c.c_char_p, [I]),
     }
     for name, (res, args) in sig.items():
@@ -235,6 +236,19 @@ def wr_wring_solve(ctx, H, bits, group, lam, codes, scales, dev_info, target=Non
         ctx.handle, _ptr(target), _wdtype(target) if target is not None else WR_F32, ldt, _ptr(B), _ptr(A), rank,
         float(alpha), ab_dtype, _ptr(H), ldh, rows, n, _ptr(bits), int(group), float(lam),
         WR_RECODE_NEAREST if recode else 0, _ptr(codes), _ptr(scales), _ptr(dev_info)))
+
+
+def wr_materialize(ctx, buf, rows, n_store, bits, group, out, had_block=0, signs=None):
+    """bf16 weights (out: rows x n_out bf16, n_out <= n_store) from one packed module."""
+    _dev(buf, "buf", (torch.uint8,))
+    _dev(out, "out", (torch.bfloat16, torch.int16, torch.uint16))
+    _dev(signs, "signs", (torch.int8,))
+    if out.dim() != 2 or out.shape[0] != rows:
+        raise ValueError("out must be rows x n_out")
+    ldo = _rowmajor(out, "out")
+    _check("wr_materialize", load().wr_materialize(ctx.handle, _ptr(buf), buf.numel(), rows, n_store, int(bits),
+                                                   int(group), int(had_block), _ptr(signs), out.shape[1], _ptr(out),
+                                                   ldo))
 
 
 def packed_nbytes(rows, n, bits, group):

@@ -17,6 +17,8 @@ int wr_wring_solve_impl(wr_ctx*, const void*, int, int64_t, const void*, const v
                         int64_t, int64_t, int64_t, const uint8_t*, int32_t, float, int, uint8_t*, uint16_t*, int32_t*);
 int wr_pack_impl(wr_ctx*, const uint8_t*, const uint16_t*, int64_t, int64_t, int32_t, int32_t, uint8_t*);
 int wr_unpack_impl(wr_ctx*, const uint8_t*, int64_t, int64_t, int32_t, int32_t, uint8_t*, uint16_t*, uint16_t*);
+int wr_materialize_impl(wr_ctx*, const uint8_t*, int64_t, int64_t, int32_t, int32_t, int32_t, const int8_t*, int64_t,
+                        uint16_t*, int64_t);
 
 namespace {
 
@@ -187,6 +189,22 @@ int wr_unpack(wr_ctx* ctx, const uint8_t* in, size_t in_bytes, int64_t rows, int
   DeviceScope ds(ctx->device);
   if (!ds.ok) return WR_EHIP;
   return wr_unpack_impl(ctx, in, rows, n, bits, group, codes, scales, dequant_bf16);
+}
+
+int wr_materialize(wr_ctx* ctx, const uint8_t* in, size_t in_bytes, int64_t rows, int64_t n_store, int32_t bits,
+                   int32_t group, int32_t had_block, const int8_t* signs, int64_t n_out, uint16_t* out, int64_t ldo) {
+  if (!ctx || rows < 0 || n_store <= 0 || n_store > (1 << 24) || bits < 2 || bits > 4 || group <= 0 ||
+      n_store % group != 0 || n_store % 8 != 0 || n_out <= 0 || n_out > n_store || ldo < n_out)
+    return WR_EINVAL;
+  if (rows > 65535) return WR_EINVAL;
+  if (had_block != 0 && (!signs || !pow2(had_block) || had_block < 2 || had_block > 4096 || n_store % had_block != 0))
+    return WR_EINVAL;
+  if (rows > 0 && (!in || !out)) return WR_EINVAL;
+  const size_t need = (size_t)rows * n_store * bits / 8 + 2 * (size_t)rows * (n_store / group);
+  if (in_bytes != need) return WR_EINVAL;
+  DeviceScope ds(ctx->device);
+  if (!ds.ok) return WR_EHIP;
+  return wr_materialize_impl(ctx, in, rows, n_store, bits, group, had_block, signs, n_out, out, ldo);
 }
 
 const char* wr_strerror(int status) {

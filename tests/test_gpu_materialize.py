@@ -1,0 +1,69 @@
+"""GPU parity of wr_materialize against the oracle (packed module -> bf16 weights in the input basis)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def wr():
+    from post_bit_weight_amd import _lib
+    return _lib
+
+
+@pytest.fixture(scope="module")
+def ctx(wr):
+    return wr.Context(0)
+
+
+CASES = [  # rows, n_store, bits, group, had_block, n_out
+    (37, 1024, 2, 64, 0, 1000),
+    (37, 1024, 3, 32, 256, 1000),
+    (16, 2560, 2, 64, 512, 2560),
+    (5, 10240, 2, 64, 1024, 9728),  # the padded 9728-wide input dim, blocks of 1024
+    (4, 776, 3, 8, 0, 770),         # ragged last 512-column segment, 3-bit fields across bytes
+    (9, 160, 4, 32, 32, 150),       # blocks below one wave's 64 columns, ragged segment
+    (6, 200, 3, 8, 8, 197),
+    (3, 4096, 2, 128, 4096, 4096),  # the largest block: 64 columns per lane
+]
+
+
+@pytest.mark.parametrize("rows,n,bits,g,m,n_out", CASES)
+def test_materialize_matches_oracle(wr, ctx, rows, n, bits, g, m, n_out):
+    rng = np.random.default_rng(rows * 7 + n + m)
+    L = 2 ** bits - 1
+    codes = rng.integers(0, L + 1, size=(rows, n))
+    scales = oracle.fp16_rne(rng.uniform(1e-3, 3e-2, size=(rows, n // g)))
+    buf = oracle.pack(codes, scales, bits, g)
+    signs = rng.choice([-1, 1], size=n).astype(np.int8)
+    dbuf = torch.from_numpy(np.ascontiguousarray(buf)).cuda()
+    dsig = torch.from_numpy(signs).cuda()
+    out = torch.zeros(rows, n_out + 3, dtype=torch.bfloat16, device="cuda")[:, :n_out]  # ld > n_out
+    wr.wr_materialize(ctx, dbuf, rows, n, bits, g, out, had_block=m, signs=dsig if m else None)
+    torch.cuda.synchronize()
+    got = out.contiguous().view(torch.int16).cpu().numpy().astype(np.uint16)
+    ref = oracle.materialize(buf, rows, n, bits, g, m, signs.astype(np.float64), n_out)
+    if m == 0:
+        assert np.array_equal(got, ref)
+        return
+    # fp32 butterflies on the GPU: a bf16 rounding may differ only next to a midpoint
+    diff = got != ref
+    assert diff.mean() <= 1e-3, diff.mean()
+    exact = oracle.materialize_exact(buf, rows, n, bits, g, m, signs.astype(np.float64), n_out)
+    gv, rv = oracle.bf16_bits_to_f64(got[diff]), oracle.bf16_bits_to_f64(ref[diff])
+    mid = 0.5 * (gv + rv)
+    assert np.all(np.abs(exact[diff] - mid) <= 1e-6 * np.abs(exact[diff]))
+    _, e = np.frexp(np.maximum(np.abs(gv), np.abs(rv)))
+    assert np.all(np.abs(gv - rv) <= np.ldexp(1.0, e - 8))
+
+
+def test_materialize_rejects_bad_arguments(wr, ctx):
+    buf = torch.zeros(oracle.packed_bytes(2, 64, 2, 32), dtype=torch.uint8, device="cuda")
+    out = torch.zeros(2, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(RuntimeError):
+        wr.wr_materialize(ctx, buf[:-1], 2, 64, 2, 32, out)
+    with pytest.raises(RuntimeError):
+        wr.wr_materialize(ctx, buf, 2, 64, 2, 32, out, had_block=48, signs=torch.ones(64, dtype=torch.int8, device="cuda"))
