@@ -58,12 +58,13 @@ enum wr_op {             /* operations that need workspace, for wr_workspace_byt
   WR_OP_GPTQ = 1,        /* rows = weight rows, n = stored dim, group, lazy_batch */
   WR_OP_WRING = 2,       /* rows = weight rows, n = stored dim, group, rank */
   WR_OP_ROTATE = 3,      /* none needed; returns 0 */
-  WR_OP_FINALIZE = 4     /* n = n_store; needed by wr_hessian_finalize with a rotation */
+  WR_OP_FINALIZE = 4,    /* n = n_store; needed by wr_hessian_finalize with a rotation */
+  WR_OP_WRING_GPTQ = 5   /* rows, n, group, rank: wr_wring_solve with WR_RECODE_GPTQ */
 };
 
 enum wr_hessian_flags { WR_H_ZERO = 1 };               /* zero S before accumulating */
 enum wr_rotate_mode { WR_ROT_ROWS = 0, WR_ROT_ROWS_INVERSE = 1, WR_ROT_SYM = 2 };
-enum wr_wring_flags { WR_RECODE_NEAREST = 1 };
+enum wr_wring_flags { WR_RECODE_NEAREST = 1, WR_RECODE_GPTQ = 2 };
 
 typedef struct wr_ctx wr_ctx;
 
@@ -160,11 +161,18 @@ int wr_gptq_sweep(wr_ctx* ctx, const void* W, int w_dtype, int64_t rows, int64_t
  * dequant(codes, scales); plus (alpha / rank) * B A when B (rows x rank) and
  * A (rank x n) are both non-null (dtype ab_dtype, contiguous).
  * With WR_RECODE_NEAREST the codes are first replaced by the nearest level of
- * T / s on the current scales s.  Then every row's scales are re-solved:
+ * T / s on the current scales s (the v0.3 finisher of the Qwen3-4B card).  With
+ * WR_RECODE_GPTQ (the v0.2 finisher: "GPTQ codes + joint scales", same card,
+ * "Why the solver changed"; the Agents-A1 card's finisher) codes and scales
+ * are first replaced by those of the GPTQ sweep of T with H (as wr_gptq_sweep,
+ * lazy batch 128; n % 4 == 0), whose scales then serve as s0; a failure of the
+ * sweep is reported in dev_info and leaves codes and scales as the sweep does.
+ * The two flags exclude each other.  Then every row's scales are re-solved:
  *   s = argmin (t - Q s)^T H (t - Q s) + lambda mu ||s - s0||^2,
  *   mu = trace(Q^T H Q) / nb,  s0 = the scales passed in,
  * and projected to fp16 (round to nearest even).  codes and scales are
- * in/out.  H: damped, n x n fp32 (ld ldh).  Workspace: WR_OP_WRING.
+ * in/out.  H: damped, n x n fp32 (ld ldh).  Workspace: WR_OP_WRING, or
+ * WR_OP_WRING_GPTQ with WR_RECODE_GPTQ.
  */
 int wr_wring_solve(wr_ctx* ctx, const void* target, int t_dtype, int64_t ldt,
                    const void* B, const void* A, int32_t rank, float alpha, int ab_dtype,

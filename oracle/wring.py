@@ -9,10 +9,18 @@ solve with the watered weights as target.
 Readings: the adapter term is (alpha / r) B A (the usual LoRA scaling; with
 alpha = r it is B A); the "same grid" is the current fp16 scales; the prior of
 the scale solve is centred on those scales.
+
+The earlier finisher (v0.2 of the Qwen3-4B card, "GPTQ codes + joint scales"
+in its "Why the solver changed"; the Agents-A1 card's finisher) re-solves the
+codes of the watered target with the GPTQ sweep instead (``wring_gptq``).
+Reading: the sweep runs on W' with the damped H exactly as the first solve does
+(its own absmax block scales), and the joint solve's prior is centred on the
+sweep's scales, the ones its codes were rounded against.
 """
 
 import numpy as np
 
+from .gptq import gptq_sweep
 from .grid import dequant, levels_count, nearest_code
 from .joint import joint_scales
 
@@ -42,3 +50,15 @@ def wring(codes, scales, bits, group, B, A, alpha, H, lam):
     c_new = nearest_code(t, L)
     s_new, s_raw = joint_scales(c_new, bits, group, H, Wp, scales, lam)
     return {"codes": c_new, "scales": s_new, "scales_unrounded": s_raw, "target": Wp, "t": t}
+
+
+def wring_gptq(codes, scales, bits, group, B, A, alpha, H, lam):
+    """GPTQ sweep of W' with H, then joint scales against W' with the prior at the sweep's scales.
+
+    Returns dict(codes, scales, scales_unrounded, target, t, sweep_scales).
+    """
+    Wp = wring_target(codes, scales, bits, group, B, A, alpha)
+    g = gptq_sweep(Wp, H, bits, group)
+    s_new, s_raw = joint_scales(g["codes"], bits, group, H, Wp, g["scales"], lam)
+    return {"codes": g["codes"], "scales": s_new, "scales_unrounded": s_raw, "target": Wp, "t": g["t"],
+            "sweep_scales": g["scales"]}

@@ -16,10 +16,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwringer.
 
 WR_OK, WR_EINVAL, WR_EWORKSPACE, WR_EHIP, WR_EUNSUPPORTED = 0, 1, 2, 3, 4
 WR_F32, WR_BF16 = 0, 1
-WR_OP_HESSIAN, WR_OP_GPTQ, WR_OP_WRING, WR_OP_ROTATE, WR_OP_FINALIZE = 0, 1, 2, 3, 4
+WR_OP_HESSIAN, WR_OP_GPTQ, WR_OP_WRING, WR_OP_ROTATE, WR_OP_FINALIZE, WR_OP_WRING_GPTQ = 0, 1, 2, 3, 4, 5
 WR_H_ZERO = 1
 WR_ROT_ROWS, WR_ROT_ROWS_INVERSE, WR_ROT_SYM = 0, 1, 2
 WR_RECODE_NEAREST = 1
+WR_RECODE_GPTQ = 2
 
 EXPORTED = (
     "wr_create", "wr_destroy", "wr_workspace_bytes", "wr_set_workspace",
@@ -211,6 +212,10 @@ def wr_gptq_sweep(ctx, W, H, bits, group, lazy_batch, codes, scales, dev_info):
 
 def wr_wring_solve(ctx, H, bits, group, lam, codes, scales, dev_info, target=None, B=None, A=None, alpha=0.0,
                    recode=False):
+    """recode: False (joint scales only), True or "nearest" (WR_RECODE_NEAREST), "gptq" (WR_RECODE_GPTQ)."""
+    if recode not in (False, True, "nearest", "gptq"):
+        raise ValueError("recode must be False, True, 'nearest' or 'gptq'")
+    flags = WR_RECODE_GPTQ if recode == "gptq" else (WR_RECODE_NEAREST if recode else 0)
     _dev(target, "target", FLOATS)
     _dev(B, "B", FLOATS)
     _dev(A, "A", FLOATS)
@@ -231,11 +236,12 @@ def wr_wring_solve(ctx, H, bits, group, lam, codes, scales, dev_info, target=Non
         if tuple(B.shape) != (rows, rank) or tuple(A.shape) != (rank, n):
             raise ValueError("B must be rows x r and A r x n")
         ab_dtype = _wdtype(A)
-    ctx.ensure_workspace(wr_workspace_bytes(WR_OP_WRING, rows, n, group, rank, 0))
+    op = WR_OP_WRING_GPTQ if flags == WR_RECODE_GPTQ else WR_OP_WRING
+    ctx.ensure_workspace(wr_workspace_bytes(op, rows, n, group, rank, 0))
     _check("wr_wring_solve", load().wr_wring_solve(
         ctx.handle, _ptr(target), _wdtype(target) if target is not None else WR_F32, ldt, _ptr(B), _ptr(A), rank,
         float(alpha), ab_dtype, _ptr(H), ldh, rows, n, _ptr(bits), int(group), float(lam),
-        WR_RECODE_NEAREST if recode else 0, _ptr(codes), _ptr(scales), _ptr(dev_info)))
+        flags, _ptr(codes), _ptr(scales), _ptr(dev_info)))
 
 
 def wr_materialize(ctx, buf, rows, n_store, bits, group, out, had_block=0, signs=None):

@@ -6,6 +6,7 @@
 size_t wr_hessian_ws_bytes(int64_t rows, int64_t n, int x_dtype, int num_cu);
 size_t wr_gptq_ws_bytes(int64_t rows, int64_t n);
 size_t wr_wring_ws_bytes(int64_t rows, int64_t n, int32_t group, int32_t rank);
+size_t wr_wring_gptq_ws_bytes(int64_t rows, int64_t n, int32_t group, int32_t rank);
 int wr_hessian_accumulate_impl(wr_ctx*, const void*, int, int64_t, int64_t, int64_t, double*, int);
 int wr_hessian_finalize_impl(wr_ctx*, const double*, int64_t, int64_t, float, int64_t, float*, int64_t, float*, int32_t,
                              const int8_t*);
@@ -84,6 +85,7 @@ size_t wr_workspace_bytes(int op, int64_t rows, int64_t n, int32_t group, int32_
     case WR_OP_GPTQ: return wr_gptq_ws_bytes(rows, n);
     case WR_OP_FINALIZE: return wr_finalize_ws_bytes(n);
     case WR_OP_WRING: return group > 0 ? wr_wring_ws_bytes(rows, n, group, rank > 0 ? rank : 0) : 0;
+    case WR_OP_WRING_GPTQ: return group > 0 ? wr_wring_gptq_ws_bytes(rows, n, group, rank > 0 ? rank : 0) : 0;
     default: return 0;
   }
 }
@@ -155,8 +157,10 @@ int wr_wring_solve(wr_ctx* ctx, const void* target, int t_dtype, int64_t ldt, co
                    const uint8_t* bits, int32_t group, float lambda, int flags, uint8_t* codes, uint16_t* scales,
                    int32_t* dev_info) {
   if (!ctx || !H || !dev_info || rows < 0 || n <= 0 || n > 65536 || ldh < n || group <= 0 || n % group != 0 ||
-      group % 8 != 0 || !(lambda >= 0.0f) || (flags & ~WR_RECODE_NEAREST))
+      group % 8 != 0 || !(lambda >= 0.0f) || (flags & ~(WR_RECODE_NEAREST | WR_RECODE_GPTQ)) ||
+      (flags == (WR_RECODE_NEAREST | WR_RECODE_GPTQ)))
     return WR_EINVAL;
+  if ((flags & WR_RECODE_GPTQ) && n % 4 != 0) return WR_EINVAL;
   if (rows > 65535) return WR_EINVAL;
   if (target && (!valid_dtype(t_dtype) || ldt < n)) return WR_EINVAL;
   if ((B != nullptr) != (A != nullptr)) return WR_EINVAL;

@@ -639,19 +639,35 @@ size_t wr_wring_ws_bytes(int64_t rows, int64_t n, int32_t group, int32_t rank) {
   return wring_layout(rows, n, group, rank).total;
 }
 
-int wr_wring_solve_impl(wr_ctx* ctx, const void* target, int t_dtype, int64_t ldt, const void* B, const void* A,
-                        int32_t rank, float alpha, int ab_dtype, const float* H, int64_t ldh, int64_t rows, int64_t n64,
-                        const uint8_t* bits, int32_t group, float lambda, int flags, uint8_t* codes, uint16_t* scales,
-                        int32_t* dev_info) {
+size_t wr_gptq_ws_bytes(int64_t rows, int64_t n);
+int wr_gptq_sweep_impl(wr_ctx* ctx, const void* W, int w_dtype, int64_t rows, int64_t n64, int64_t ldw,
+                       const float* H, int64_t ldh, const uint8_t* bits, int32_t group, int32_t lazy_batch,
+                       uint8_t* codes, uint16_t* scales, int32_t* dev_info);
+
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Workspace of the wring with GPTQ codes: the target T (rows x n fp32) kept across the sweep,
+// then room for the larger of the sweep's and the joint solve's own workspaces.
+size_t wr_wring_gptq_ws_bytes(int64_t rows, int64_t n, int32_t group, int32_t rank) {
+  const size_t a = wr_gptq_ws_bytes(rows, n), b = wring_layout(rows, n, group, rank).total;
+  return align256((size_t)rows * n * 4) + (a > b ? a : b);
+}
+
+// The joint solve on workspace ws.  With T_only the target T is formed there (codes and
+// scales untouched) and nothing else is done; reset_info = false keeps a status already in
+// dev_info (the later kernels do nothing when it is nonzero).
+static int wring_core(wr_ctx* ctx, char* ws, size_t ws_bytes, const void* target, int t_dtype, int64_t ldt,
+                      const void* B, const void* A, int32_t rank, float alpha, int ab_dtype, const float* H,
+                      int64_t ldh, int64_t rows, int64_t n64, const uint8_t* bits, int32_t group, float lambda,
+                      int flags, bool reset_info, float* T_only, uint8_t* codes, uint16_t* scales, int32_t* dev_info) {
   if (group != 32 && group != 64 && group != 128) return WR_EUNSUPPORTED;
   const bool adapter = B && A && rank > 0;
   const WringLayout lay = wring_layout(rows, n64, group, adapter ? rank : 0);
-  if (ctx->ws_bytes < lay.total) return WR_EWORKSPACE;
+  if (ws_bytes < lay.total) return WR_EWORKSPACE;
   const int n = (int)n64;
   const int nb = n / group;
   hipStream_t st = ctx->stream;
-  char* ws = static_cast<char*>(ctx->ws);
-  float* T = reinterpret_cast<float*>(ws + lay.T);
+  float* T = T_only ? T_only : reinterpret_cast<float*>(ws + lay.T);
   uint16_t* Lev = reinterpret_cast<uint16_t*>(ws + lay.Lev);
   const bool lh = group == 64;
   uint16_t* T0 = lh ? nullptr : reinterpret_cast<uint16_t*>(ws + lay.T0);
@@ -663,8 +679,10 @@ int wr_wring_solve_impl(wr_ctx* ctx, const void* target, int t_dtype, int64_t ld
   float* Gm = reinterpret_cast<float*>(ws + lay.Gm);
   float* rh = reinterpret_cast<float*>(ws + lay.rhs);
 
-  hipLaunchKernelGGL(set_int_kernel, dim3(1), dim3(1), 0, st, dev_info, 0);
-  WR_CHECK_LAUNCH();
+  if (reset_info) {
+    hipLaunchKernelGGL(set_int_kernel, dim3(1), dim3(1), 0, st, dev_info, 0);
+    WR_CHECK_LAUNCH();
+  }
   if (rows == 0) return WR_OK;
   const unsigned gx = (unsigned)std::min<int64_t>((n + 255) / 256, 16);
   const bool fused = lh && (!adapter || (ab_dtype == WR_BF16 && rank % 16 == 0 &&
@@ -700,6 +718,7 @@ int wr_wring_solve_impl(wr_ctx* ctx, const void* target, int t_dtype, int64_t ld
                        n, group, (flags & WR_RECODE_NEAREST) ? 1 : 0, Lev, T0, T1, T2, dev_info);
     WR_CHECK_LAUNCH();
   }
+  if (T_only) return WR_OK;
   hipLaunchKernelGGL(split_h_kernel, dim3(gx, (unsigned)n), dim3(256), 0, st, H, ldh, n, H0, H1, H2);
   WR_CHECK_LAUNCH();
   dim3 ggrid((unsigned)((rows + 127) / 128), (unsigned)nb);
@@ -745,4 +764,51 @@ int wr_wring_solve_impl(wr_ctx* ctx, const void* target, int t_dtype, int64_t ld
                      dev_info);
   WR_CHECK_LAUNCH();
   return WR_OK;
+}
+
+namespace {
+// Points the context's workspace at a sub-range for the duration of a call.
+struct WorkspaceView {
+  wr_ctx* c;
+  void* ws;
+  size_t bytes;
+  WorkspaceView(wr_ctx* ctx, void* sub, size_t sub_bytes) : c(ctx), ws(ctx->ws), bytes(ctx->ws_bytes) {
+    c->ws = sub;
+    c->ws_bytes = sub_bytes;
+  }
+  ~WorkspaceView() {
+    c->ws = ws;
+    c->ws_bytes = bytes;
+  }
+};
+}  // namespace
+
+int wr_wring_solve_impl(wr_ctx* ctx, const void* target, int t_dtype, int64_t ldt, const void* B, const void* A,
+                        int32_t rank, float alpha, int ab_dtype, const float* H, int64_t ldh, int64_t rows, int64_t n,
+                        const uint8_t* bits, int32_t group, float lambda, int flags, uint8_t* codes, uint16_t* scales,
+                        int32_t* dev_info) {
+  if (!(flags & WR_RECODE_GPTQ))
+    return wring_core(ctx, static_cast<char*>(ctx->ws), ctx->ws_bytes, target, t_dtype, ldt, B, A, rank, alpha,
+                      ab_dtype, H, ldh, rows, n, bits, group, lambda, flags, true, nullptr, codes, scales, dev_info);
+  // GPTQ codes on the watered target: T = target or dequant, plus the adapter; the sweep of T
+  // with H gives codes and scales; then the joint scales against T, the prior centred on the
+  // sweep's scales.
+  const bool adapter = B && A && rank > 0;
+  if (ctx->ws_bytes < wr_wring_gptq_ws_bytes(rows, n, group, adapter ? rank : 0)) return WR_EWORKSPACE;
+  char* ws = static_cast<char*>(ctx->ws);
+  float* Tk = reinterpret_cast<float*>(ws);
+  const size_t tb = align256((size_t)rows * n * 4);
+  char* rest = ws + tb;
+  const size_t rest_bytes = ctx->ws_bytes - tb;
+  int rc = wring_core(ctx, rest, rest_bytes, target, t_dtype, ldt, B, A, rank, alpha, ab_dtype, H, ldh, rows, n, bits,
+                      group, lambda, 0, true, Tk, codes, scales, dev_info);
+  if (rc) return rc;
+  if (rows == 0) return WR_OK;
+  {
+    WorkspaceView view(ctx, rest, rest_bytes);
+    rc = wr_gptq_sweep_impl(ctx, Tk, WR_F32, rows, n, n, H, ldh, bits, group, 128, codes, scales, dev_info);
+  }
+  if (rc) return rc;
+  return wring_core(ctx, rest, rest_bytes, Tk, WR_F32, n, nullptr, nullptr, 0, 0.0f, WR_F32, H, ldh, rows, n, bits,
+                    group, lambda, 0, false, nullptr, codes, scales, dev_info);
 }

@@ -1,0 +1,128 @@
+"""GPU parity of the GPTQ-codes finisher (wr_wring_solve with WR_RECODE_GPTQ) against the oracle.
+
+The v0.2 finisher of the Qwen3-4B card ("GPTQ codes + joint scales", section "Why the solver
+changed") and the Agents-A1 card's finisher: the GPTQ sweep of the watered target
+W' = dequant(codes, scales) + (alpha / r) B A with the damped H, then the joint scales against
+W' with the prior at the sweep's scales.  Both sides use the same fp32 H, so codes may differ
+only where the oracle's pre-rounding value sits within TIE of a decision threshold (the rest of
+such a row is a different valid rounding), scales agree within one fp16 ulp on rows whose codes
+agree, and the proxy losses within 1e-4.
+"""
+import ctypes as c
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import code_parity, f16_bits, scale_ulps
+
+pytestmark = pytest.mark.gpu
+
+TIE = 5e-3
+
+
+@pytest.fixture(scope="module")
+def wr():
+    from post_bit_weight_amd import _lib
+    return _lib
+
+
+@pytest.fixture(scope="module")
+def ctx(wr):
+    return wr.Context(0)
+
+
+def _run(wr, ctx, H32, codes, scales, bits, g, lam, B, A, alpha):
+    rows, n = codes.shape
+    c_t = torch.from_numpy(codes.astype(np.uint8)).cuda()
+    s_t = torch.from_numpy(scales.astype(np.float16)).cuda()
+    info = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bits_t = torch.full((rows,), bits, dtype=torch.uint8, device="cuda")
+    wr.wr_wring_solve(ctx, torch.from_numpy(H32).cuda(), bits_t, g, lam, c_t, s_t, info,
+                      B=B.contiguous().cuda(), A=A.contiguous().cuda(), alpha=alpha, recode="gptq")
+    return c_t.cpu().numpy().astype(np.int64), s_t.cpu().numpy().astype(np.float64), int(info.item())
+
+
+def _compare(codes, scales, ref, H0, bits, g):
+    L = 2 ** bits - 1
+    cp = code_parity(codes, ref["codes"], ref["t"], L)
+    assert cp["frac"] <= 1e-3 and cp["worst_first"] <= TIE, cp
+    ok = cp["identical_rows"]
+    assert scale_ulps(scales[ok], ref["scales"][ok]).max(initial=0) <= 1
+    same = ok & (scale_ulps(scales, ref["scales"]).max(axis=1) == 0)
+    lg = oracle.proxy_loss(ref["target"][same], oracle.dequant(codes, scales, bits, g)[same], H0)
+    lr = oracle.proxy_loss(ref["target"][same], oracle.dequant(ref["codes"], ref["scales"], bits, g)[same], H0)
+    assert abs(lg - lr) <= 1e-4 * lr
+    return cp
+
+
+def _first_solve(W, H, bits, g, lam):
+    g0 = oracle.gptq_sweep(W, H, bits, g)
+    s1, _ = oracle.joint_scales(g0["codes"], bits, g, H, W, g0["scales"], lam)
+    return g0["codes"], s1
+
+
+def test_gptq_finisher_toy(wr, ctx):
+    """The toy layer: W 256 x 512 fp32, H from 4096 fp32 rows, group 32, rank-8 fp32 adapter."""
+    from post_bit_weight_amd import synth
+    W = synth.gaussian((256, 512), 0.02, seed=101)
+    X = synth.SpectralSource(512, seed=102, n_outliers=5).chunk(0, 4096, dtype=torch.float32)
+    B = synth.gaussian((256, 8), 0.01, seed=103)
+    A = synth.gaussian((8, 512), 0.01, seed=104)
+    H0 = oracle.second_moment(X.double().numpy())
+    H32 = oracle.damp(H0, 0.01)[0].astype(np.float32)
+    Hd = H32.astype(np.float64)
+    codes0, s1 = _first_solve(W.double().numpy(), Hd, 2, 32, 0.01)
+    codes, scales, info = _run(wr, ctx, H32, codes0, s1, 2, 32, 0.01, B, A, 8.0)
+    assert info == 0
+    ref = oracle.wring_gptq(codes0, s1, 2, 32, B.double().numpy(), A.double().numpy(), 8.0, Hd, 0.01)
+    _compare(codes, scales, ref, H0, 2, 32)
+
+
+def test_gptq_finisher_q_proj_slice(wr, ctx):
+    """128 rows of the q_proj shape: n 2560, bf16 W and rank-128 bf16 adapter (alpha 128),
+    group 64, H from 16384 spectral calibration rows."""
+    from post_bit_weight_amd import synth
+    rows, n, g, r = 128, 2560, 64, 128
+    X = synth.SpectralSource(n, seed=20261210, outlier_frac=0.01).chunk(0, 16384, dtype=torch.bfloat16)
+    W = synth.student_t((rows, n), seed=20261211, dtype=torch.bfloat16)
+    B = synth.gaussian((rows, r), 0.01, seed=20261212, dtype=torch.bfloat16)
+    A = synth.gaussian((r, n), 0.01, seed=20261213, dtype=torch.bfloat16)
+    H0 = oracle.second_moment(X.double().numpy())
+    H32 = oracle.damp(H0, 0.01)[0].astype(np.float32)
+    Hd = H32.astype(np.float64)
+    codes0, s1 = _first_solve(W.double().numpy(), Hd, 2, g, 0.01)
+    codes, scales, info = _run(wr, ctx, H32, codes0, s1, 2, g, 0.01, B, A, float(r))
+    assert info == 0
+    ref = oracle.wring_gptq(codes0, s1, 2, g, B.double().numpy(), A.double().numpy(), float(r), Hd, 0.01)
+    cp = _compare(codes, scales, ref, H0, 2, g)
+    print(f"codes differing {cp['frac']:.2e}, rows with a tie {len(cp['rows'])}")
+
+
+def test_gptq_finisher_grid_point_is_fixed(wr, ctx):
+    """A grid point whose blocks each hold a level +-L, zero adapter: exact fixed point."""
+    rng = np.random.default_rng(36)
+    rows, n, g = 64, 512, 64
+    Xr = rng.standard_normal((2048, n))
+    H32 = (Xr.T @ Xr / 2048 + 0.05 * np.eye(n)).astype(np.float32)
+    codes0 = rng.integers(0, 4, size=(rows, n))
+    codes0[:, ::g] = rng.choice([0, 3], size=(rows, n // g))
+    s0 = oracle.fp16_rne(rng.uniform(0.005, 0.02, size=(rows, n // g)))
+    codes, scales, info = _run(wr, ctx, H32, codes0, s0, 2, g, 0.01, torch.zeros(rows, 16, dtype=torch.bfloat16),
+                               torch.zeros(16, n, dtype=torch.bfloat16), 16.0)
+    assert info == 0 and np.array_equal(codes, codes0) and np.array_equal(f16_bits(scales), f16_bits(s0))
+
+
+def test_gptq_and_nearest_flags_exclude_each_other(wr, ctx):
+    rows, n, g = 8, 128, 64
+    H = torch.eye(n, dtype=torch.float32, device="cuda")
+    codes = torch.zeros(rows, n, dtype=torch.uint8, device="cuda")
+    scales = torch.ones(rows, n // g, dtype=torch.float16, device="cuda")
+    bits = torch.full((rows,), 2, dtype=torch.uint8, device="cuda")
+    info = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lib = wr.load()
+    p = lambda t: c.c_void_p(t.data_ptr())
+    rc = lib.wr_wring_solve(ctx.handle, None, wr.WR_F32, 0, None, None, 0, 0.0, wr.WR_F32, p(H), n, rows, n, p(bits),
+                            g, 0.01, wr.WR_RECODE_NEAREST | wr.WR_RECODE_GPTQ, p(codes), p(scales), p(info))
+    assert rc == wr.WR_EINVAL

@@ -57,3 +57,49 @@ def test_wring_fits_the_watered_target_better_than_the_old_point():
     new = oracle.proxy_loss(out["target"], oracle.dequant(out["codes"], out["scales"], 2, 8), H)
     old = oracle.proxy_loss(out["target"], oracle.dequant(codes, scales, 2, 8), H)
     assert new < old
+
+
+def test_gptq_finisher_with_identity_h_is_absmax_rounding_then_block_ridge():
+    """H = I: no error feedback, so the sweep rounds each weight to the nearest level on the
+    block's absmax fp16 scale; the joint solve separates into one ridge problem per block,
+    s_b = (q_b . t_b + lam mu s0_b) / (q_b . q_b + lam mu), mu = sum_b q_b . q_b / nb."""
+    rng = np.random.default_rng(34)
+    rows, n, g, bits, lam = 5, 24, 8, 2, 0.01
+    L = 2 ** bits - 1
+    codes0 = rng.integers(0, L + 1, size=(rows, n))
+    s_in = oracle.fp16_rne(rng.uniform(0.1, 0.5, size=(rows, n // g)))
+    B = 0.3 * rng.standard_normal((rows, 3))
+    A = 0.3 * rng.standard_normal((3, n))
+    out = oracle.wring_gptq(codes0, s_in, bits, g, B, A, 3.0, np.eye(n), lam)
+    Wp = out["target"]
+    for i in range(rows):
+        q = np.zeros(n)
+        s0 = np.zeros(n // g)
+        for b in range(n // g):
+            s0[b] = float(np.float16(max(abs(Wp[i, j]) for j in range(b * g, b * g + g)) / L))
+            for j in range(b * g, b * g + g):
+                c = min(max(int(np.floor((Wp[i, j] / s0[b] + L) / 2 + 0.5)), 0), L)
+                assert out["codes"][i, j] == c
+                q[j] = 2 * c - L
+        assert np.array_equal(out["sweep_scales"][i], s0)
+        qq = [sum(q[j] ** 2 for j in range(b * g, b * g + g)) for b in range(n // g)]
+        qt = [sum(q[j] * Wp[i, j] for j in range(b * g, b * g + g)) for b in range(n // g)]
+        mu = sum(qq) / (n // g)
+        for b in range(n // g):
+            ridge = (qt[b] + lam * mu * s0[b]) / (qq[b] + lam * mu)
+            assert np.isclose(out["scales_unrounded"][i, b], ridge, rtol=1e-12)
+            assert out["scales"][i, b] == float(np.float16(ridge))
+
+
+def test_gptq_finisher_keeps_a_grid_point_with_extreme_levels():
+    """W' = Q s0 exactly and every block holds a level +-L: the sweep makes no error (so no
+    feedback) and reproduces the absmax scales s0; the joint residual vanishes at s0, where
+    the prior is centred, so codes and scales come back unchanged for any SPD H."""
+    rng = np.random.default_rng(35)
+    for bits in (2, 3):
+        H, codes, scales, L = _setup(rng, rows=6, n=32, g=8, bits=bits)
+        codes[:, ::8] = rng.choice([0, L], size=(6, 4))
+        out = oracle.wring_gptq(codes, scales, bits, 8, np.zeros((6, 2)), np.zeros((2, 32)), 2.0, H, 0.01)
+        assert np.array_equal(out["codes"], codes)
+        assert np.array_equal(out["sweep_scales"], scales)
+        assert np.array_equal(out["scales"], scales)
