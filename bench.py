@@ -11,7 +11,9 @@ Also reported: the roofline of the dominant kernel (the bf16 SYRK that
 accumulates H: N n (n + 1) useful flops per call, timed live with HIP events on
 the stream it runs on) and the CPU oracle timed on a bounded sample of the same
 workload on the host cores, and, outside the timed step, the materializer (packed
-module -> bf16 weights) against the HBM peak.
+module -> bf16 weights) against the HBM peak and the finisher variant with GPTQ
+codes (wring by a GPTQ sweep of the watered target instead of nearest-point
+codes).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -143,6 +145,35 @@ def time_materialize(wr, ctx, torch, reps=20):
             "bytes_per_launch": nbytes}
 
 
+def time_finisher_gptq(wr, ctx, torch, H, W, B, A, bits_t, cfg, reps=5):
+    """The GPTQ-codes finisher (wr_wring_solve with WR_RECODE_GPTQ: watered target, GPTQ sweep of
+    it, joint scales) on the step's workload, starting from the first solve's codes and scales.
+    Each call is timed alone with HIP events on the library's stream."""
+    rows, n, g, rank = cfg["rows"], cfg["n"], cfg["group"], cfg["rank"]
+    c1 = torch.empty(rows, n, dtype=torch.uint8, device="cuda")
+    s1 = torch.empty(rows, n // g, dtype=torch.float16, device="cuda")
+    info = torch.zeros(3, dtype=torch.int32, device="cuda")
+    wr.wr_gptq_sweep(ctx, W, H, bits_t, g, 128, c1, s1, info[0:1])
+    wr.wr_wring_solve(ctx, H, bits_t, g, 0.01, c1, s1, info[1:2], target=W)
+    codes, scales = torch.empty_like(c1), torch.empty_like(s1)
+    times = []
+    for k in range(reps + 2):
+        codes.copy_(c1)
+        scales.copy_(s1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(ctx.stream)
+        wr.wr_wring_solve(ctx, H, bits_t, g, 0.01, codes, scales, info[2:3], B=B, A=A, alpha=float(rank), recode="gptq")
+        e1.record(ctx.stream)
+        torch.cuda.synchronize()
+        if k >= 2:
+            times.append(e0.elapsed_time(e1))
+    if int(info.abs().sum().item()) != 0:
+        raise RuntimeError(f"dev_info reports a failure in the GPTQ finisher: {info.tolist()}")
+    ms = sum(times) / len(times)
+    return {"workload": f"wring with GPTQ codes, {rows}x{n}, rank {rank}", "ms": ms,
+            "weights_per_s": rows * n / (ms * 1e-3)}
+
+
 def progress(msg):
     print(f"bench.py: {msg}", file=sys.stderr, flush=True)
 
@@ -260,6 +291,8 @@ def main():
     }
     progress("timing the materializer")
     line["materialize"] = time_materialize(wr, ctx, torch)
+    progress("timing the GPTQ-codes finisher")
+    line["finisher_gptq"] = time_finisher_gptq(wr, ctx, torch, H, W, B, A, bits_t, cfg)
     if not args.no_cpu_baseline:
         progress("timing the oracle on a bounded sample")
         Xh = X[: args.cpu_calib].float().cpu().numpy()

@@ -47,8 +47,13 @@ def prepare_weights(ctx, W, n_store, had_block=None, signs=None):
     return Wp
 
 
-def quantize(ctx, Wst, H, bits, group, lam=0.01, B=None, A=None, alpha=None, lazy_batch=128, keep_stages=False):
-    """GPTQ sweep, joint scales, wring.  bits: int or a per-row uint8 tensor.  Returns a dict of tensors."""
+def quantize(ctx, Wst, H, bits, group, lam=0.01, B=None, A=None, alpha=None, lazy_batch=128, keep_stages=False,
+             finisher="nearest"):
+    """GPTQ sweep, joint scales, wring.  bits: int or a per-row uint8 tensor.  finisher: "nearest"
+    (nearest-point codes on the current scales) or "gptq" (a GPTQ sweep of the watered target).
+    Returns a dict of tensors."""
+    if finisher not in ("nearest", "gptq"):
+        raise ValueError("finisher must be 'nearest' or 'gptq'")
     rows, n = Wst.shape
     if isinstance(bits, int):
         bits_t = torch.full((rows,), bits, dtype=torch.uint8, device=ctx.device)
@@ -66,7 +71,8 @@ def quantize(ctx, Wst, H, bits, group, lam=0.01, B=None, A=None, alpha=None, laz
         out["joint_scales"] = scales.clone()
     if B is not None:
         wr.wr_wring_solve(ctx, H, bits_t, group, lam, codes, scales, info[2:3], B=B, A=A,
-                          alpha=alpha if alpha is not None else A.shape[0], recode=True)
+                          alpha=alpha if alpha is not None else A.shape[0],
+                          recode="gptq" if finisher == "gptq" else True)
     out.update(codes=codes, scales=scales, dev_info=info, bits=bits_t)
     return out
 
