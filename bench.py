@@ -15,7 +15,7 @@ module -> bf16 weights) against the HBM peak and the finisher variant with GPTQ
 codes (wring by a GPTQ sweep of the watered target instead of nearest-point
 codes).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras | --extras-only]
 """
 
 import argparse
@@ -51,6 +51,10 @@ def parse():
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="before the warmup, copy MIB mebibytes device to device once (a plain copy kernel of known "
                         "size, the yardstick for the FETCH_SIZE / WRITE_SIZE counters)")
+    p.add_argument("--no-extras", action="store_true",
+                   help="time the solve step only (no materializer or finisher-variant timing)")
+    p.add_argument("--extras-only", action="store_true",
+                   help="one untimed step (for H), then only the materializer and the finisher-variant timings")
     return p.parse_args()
 
 
@@ -245,11 +249,16 @@ def main():
         mark(6)
 
     progress("warmup")
-    for _ in range(args.warmup):
+    for _ in range(1 if args.extras_only else args.warmup):
         step()
     torch.cuda.synchronize()
     if int(info.abs().sum().item()) != 0:
         raise RuntimeError(f"dev_info reports a failure: {info.tolist()}")
+    if args.extras_only:
+        progress("timing the materializer and the GPTQ-codes finisher")
+        print(json.dumps({"materialize": time_materialize(wr, ctx, torch),
+                          "finisher_gptq": time_finisher_gptq(wr, ctx, torch, H, W, B, A, bits_t, cfg)}), flush=True)
+        return
 
     progress(f"timing {args.steps} steps")
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
@@ -289,10 +298,11 @@ def main():
         },
         "stage_ms": per_stage,
     }
-    progress("timing the materializer")
-    line["materialize"] = time_materialize(wr, ctx, torch)
-    progress("timing the GPTQ-codes finisher")
-    line["finisher_gptq"] = time_finisher_gptq(wr, ctx, torch, H, W, B, A, bits_t, cfg)
+    if not args.no_extras:
+        progress("timing the materializer")
+        line["materialize"] = time_materialize(wr, ctx, torch)
+        progress("timing the GPTQ-codes finisher")
+        line["finisher_gptq"] = time_finisher_gptq(wr, ctx, torch, H, W, B, A, bits_t, cfg)
     if not args.no_cpu_baseline:
         progress("timing the oracle on a bounded sample")
         Xh = X[: args.cpu_calib].float().cpu().numpy()
