@@ -48,12 +48,17 @@ def prepare_weights(ctx, W, n_store, had_block=None, signs=None):
 
 
 def quantize(ctx, Wst, H, bits, group, lam=0.01, B=None, A=None, alpha=None, lazy_batch=128, keep_stages=False,
-             finisher="nearest"):
+             finisher="nearest", adapters=None):
     """GPTQ sweep, joint scales, wring.  bits: int or a per-row uint8 tensor.  finisher: "nearest"
     (nearest-point codes on the current scales) or "gptq" (a GPTQ sweep of the watered target).
-    Returns a dict of tensors."""
+    adapters: a sequence of (B, A) pairs for several fill-and-wring rounds, each wring starting
+    from the previous one's codes and scales (instead of B and A).  Returns a dict of tensors."""
     if finisher not in ("nearest", "gptq"):
         raise ValueError("finisher must be 'nearest' or 'gptq'")
+    if adapters is not None and B is not None:
+        raise ValueError("pass either B and A or adapters")
+    if adapters is None:
+        adapters = [] if B is None else [(B, A)]
     rows, n = Wst.shape
     if isinstance(bits, int):
         bits_t = torch.full((rows,), bits, dtype=torch.uint8, device=ctx.device)
@@ -61,7 +66,7 @@ def quantize(ctx, Wst, H, bits, group, lam=0.01, B=None, A=None, alpha=None, laz
         bits_t = bits
     codes = torch.empty(rows, n, dtype=torch.uint8, device=ctx.device)
     scales = torch.empty(rows, n // group, dtype=torch.float16, device=ctx.device)
-    info = torch.zeros(3, dtype=torch.int32, device=ctx.device)
+    info = torch.zeros(2 + max(1, len(adapters)), dtype=torch.int32, device=ctx.device)
     out = {}
     wr.wr_gptq_sweep(ctx, Wst, H, bits_t, group, lazy_batch, codes, scales, info[0:1])
     if keep_stages:
@@ -69,10 +74,12 @@ def quantize(ctx, Wst, H, bits, group, lam=0.01, B=None, A=None, alpha=None, laz
     wr.wr_wring_solve(ctx, H, bits_t, group, lam, codes, scales, info[1:2], target=Wst)
     if keep_stages:
         out["joint_scales"] = scales.clone()
-    if B is not None:
-        wr.wr_wring_solve(ctx, H, bits_t, group, lam, codes, scales, info[2:3], B=B, A=A,
-                          alpha=alpha if alpha is not None else A.shape[0],
+    for k, (Bk, Ak) in enumerate(adapters):
+        wr.wr_wring_solve(ctx, H, bits_t, group, lam, codes, scales, info[2 + k:3 + k], B=Bk, A=Ak,
+                          alpha=alpha if alpha is not None else Ak.shape[0],
                           recode="gptq" if finisher == "gptq" else True)
+        if keep_stages and k + 1 < len(adapters):
+            out[f"round{k + 1}_codes"], out[f"round{k + 1}_scales"] = codes.clone(), scales.clone()
     out.update(codes=codes, scales=scales, dev_info=info, bits=bits_t)
     return out
 

@@ -126,3 +126,33 @@ def test_gptq_and_nearest_flags_exclude_each_other(wr, ctx):
     rc = lib.wr_wring_solve(ctx.handle, None, wr.WR_F32, 0, None, None, 0, 0.0, wr.WR_F32, p(H), n, rows, n, p(bits),
                             g, 0.01, wr.WR_RECODE_NEAREST | wr.WR_RECODE_GPTQ, p(codes), p(scales), p(info))
     assert rc == wr.WR_EINVAL
+
+
+@pytest.mark.parametrize("finisher", ["nearest", "gptq"])
+def test_two_fill_and_wring_rounds(wr, ctx, finisher):
+    """Two rounds (the Agents-A1 card ran two fill-and-wring rounds): the second wring starts from
+    the first one's codes and scales with a second adapter.  pipeline.quantize chains them; each
+    round is compared with the oracle started from the GPU's own input to that round."""
+    from post_bit_weight_amd import pipeline, synth
+    rows, n, g, r = 96, 1024, 64, 64
+    X = synth.SpectralSource(n, seed=20261220, outlier_frac=0.01).chunk(0, 8192, dtype=torch.bfloat16)
+    W = synth.student_t((rows, n), seed=20261221, dtype=torch.bfloat16)
+    ad = [(synth.gaussian((rows, r), 0.01, seed=20261222 + 2 * k, dtype=torch.bfloat16),
+           synth.gaussian((r, n), 0.01, seed=20261223 + 2 * k, dtype=torch.bfloat16)) for k in range(2)]
+    H0 = oracle.second_moment(X.double().numpy())
+    H32 = oracle.damp(H0, 0.01)[0].astype(np.float32)
+    Hd = H32.astype(np.float64)
+    out = pipeline.quantize(ctx, W.cuda(), torch.from_numpy(H32).cuda(), 2, g, 0.01,
+                            adapters=[(B.cuda(), A.cuda()) for B, A in ad], keep_stages=True, finisher=finisher)
+    torch.cuda.synchronize()
+    assert (out["dev_info"].cpu().numpy() == 0).all()
+    inputs = [(out["gptq_codes"], out["joint_scales"]), (out["round1_codes"], out["round1_scales"])]
+    results = [(out["round1_codes"], out["round1_scales"]), (out["codes"], out["scales"])]
+    fn = oracle.wring_gptq if finisher == "gptq" else oracle.wring
+    for k in range(2):
+        c_in = inputs[k][0].cpu().numpy().astype(np.int64)
+        s_in = inputs[k][1].cpu().numpy().astype(np.float64)
+        ref = fn(c_in, s_in, 2, g, ad[k][0].double().numpy(), ad[k][1].double().numpy(), float(r), Hd, 0.01)
+        got_c = results[k][0].cpu().numpy().astype(np.int64)
+        got_s = results[k][1].cpu().numpy().astype(np.float64)
+        _compare(got_c, got_s, ref, H0, 2, g)
