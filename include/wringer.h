@@ -59,7 +59,8 @@ enum wr_op {             /* operations that need workspace, for wr_workspace_byt
   WR_OP_WRING = 2,       /* rows = weight rows, n = stored dim, group, rank */
   WR_OP_ROTATE = 3,      /* none needed; returns 0 */
   WR_OP_FINALIZE = 4,    /* n = n_store; needed by wr_hessian_finalize with a rotation */
-  WR_OP_WRING_GPTQ = 5   /* rows, n, group, rank: wr_wring_solve with WR_RECODE_GPTQ */
+  WR_OP_WRING_GPTQ = 5,  /* rows, n, group, rank: wr_wring_solve with WR_RECODE_GPTQ */
+  WR_OP_TRELLIS = 6      /* rows, n, group = number of trellis states: wr_trellis_quantize */
 };
 
 enum wr_hessian_flags { WR_H_ZERO = 1 };               /* zero S before accumulating */
@@ -212,6 +213,27 @@ int wr_unpack(wr_ctx* ctx, const uint8_t* in, size_t in_bytes, int64_t rows, int
  */
 int wr_materialize(wr_ctx* ctx, const uint8_t* in, size_t in_bytes, int64_t rows, int64_t n_store, int32_t bits,
                    int32_t group, int32_t had_block, const int8_t* signs, int64_t n_out, uint16_t* out, int64_t ldo);
+
+/*
+ * (f) Trellis-coded quantization with a Viterbi search (Pingala-8 post, "Trick 3: trellis
+ * coding": a state carried from step to step selects the coset of values a step may use, the
+ * bits written pick the value and the next state, and the Viterbi algorithm finds the
+ * cheapest path).  One weight per step on a shift-register trellis of S = 2^log2_states
+ * states (1 <= log2_states <= 4): branch bit u leads from state s to ((s << 1) | u) mod S
+ * (the post's toy is S = 2, where the bit written becomes the next state); branch (s, u)
+ * carries the coset values[(s * 2 + u) * coset_size + v], v < coset_size (1, 2 or 4),
+ * fp32, device memory.  For each row of T (rows x n fp32, ld ldt, a multiple of 4, T
+ * 16-byte aligned), starting in start_state, finds the path minimising the sum of squared
+ * errors (per step the nearest value of the branch's coset); ties go to the smaller
+ * predecessor state, the smaller end state, the smaller coset index.  Writes codes (rows x n
+ * uint8, ld ldc: u | v << 1), optionally recon (rows x n fp32, ld ldr: the decoded values)
+ * and cost (rows fp64: the path's sum of squared errors, summed in fp64).  The search runs in
+ * fp32 with the costs renormalised every 16 steps; targets must be finite.
+ * Workspace: WR_OP_TRELLIS (rows, n, group = S).
+ */
+int wr_trellis_quantize(wr_ctx* ctx, const float* T, int64_t ldt, int64_t rows, int64_t n, int32_t log2_states,
+                        int32_t coset_size, const float* values, int32_t start_state, uint8_t* codes, int64_t ldc,
+                        float* recon, int64_t ldr, double* cost);
 
 /* Static description of a status code. */
 const char* wr_strerror(int status);

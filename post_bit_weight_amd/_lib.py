@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwringer.
 
 WR_OK, WR_EINVAL, WR_EWORKSPACE, WR_EHIP, WR_EUNSUPPORTED = 0, 1, 2, 3, 4
 WR_F32, WR_BF16 = 0, 1
-WR_OP_HESSIAN, WR_OP_GPTQ, WR_OP_WRING, WR_OP_ROTATE, WR_OP_FINALIZE, WR_OP_WRING_GPTQ = 0, 1, 2, 3, 4, 5
+WR_OP_HESSIAN, WR_OP_GPTQ, WR_OP_WRING, WR_OP_ROTATE, WR_OP_FINALIZE, WR_OP_WRING_GPTQ, WR_OP_TRELLIS = range(7)
 WR_H_ZERO = 1
 WR_ROT_ROWS, WR_ROT_ROWS_INVERSE, WR_ROT_SYM = 0, 1, 2
 WR_RECODE_NEAREST = 1
@@ -25,7 +25,8 @@ WR_RECODE_GPTQ = 2
 EXPORTED = (
     "wr_create", "wr_destroy", "wr_workspace_bytes", "wr_set_workspace",
     "wr_hessian_accumulate", "wr_hessian_finalize", "wr_hadamard_rotate",
-    "wr_gptq_sweep", "wr_wring_solve", "wr_pack", "wr_unpack", "wr_materialize", "wr_strerror",
+    "wr_gptq_sweep", "wr_wring_solve", "wr_pack", "wr_unpack", "wr_materialize", "wr_trellis_quantize",
+    "wr_strerror",
 )
 
 
@@ -65,6 +66,7 @@ def load():
         "wr_pack": (I, [P, P, P, I64, I64, c.c_int32, c.c_int32, P, SZ]),
         "wr_unpack": (I, [P, P, SZ, I64, I64, c.c_int32, c.c_int32, P, P, P]),
         "wr_materialize": (I, [P, P, SZ, I64, I64, c.c_int32, c.c_int32, c.c_int32, P, I64, P, I64]),
+        "wr_trellis_quantize": (I, [P, P, I64, I64, I64, c.c_int32, c.c_int32, P, c.c_int32, P, I64, P, I64, P]),
         "wr_strerror": (c.c_char_p, [I]),
     }
     for name, (res, args) in sig.items():
@@ -279,3 +281,28 @@ def wr_unpack(ctx, buf, rows, n, bits, group, codes=None, scales=None, dequant=N
     _dev(dequant, "dequant", (torch.bfloat16,))
     _check("wr_unpack", load().wr_unpack(ctx.handle, _ptr(buf), buf.numel(), rows, n, int(bits), int(group),
                                          _ptr(codes), _ptr(scales), _ptr(dequant)))
+
+
+def wr_trellis_quantize(ctx, T, log2_states, values, codes, recon=None, cost=None, start_state=0):
+    """Viterbi search of a shift-register trellis for each row of T (rows x n fp32).
+
+    values: S x 2 x C fp32 device tensor (the coset of each branch); codes: rows x n uint8;
+    recon: optional rows x n fp32; cost: optional rows fp64."""
+    _dev(T, "T", (torch.float32,))
+    _dev(values, "values", (torch.float32,))
+    _dev(codes, "codes", (torch.uint8,))
+    _dev(recon, "recon", (torch.float32,))
+    _dev(cost, "cost", (torch.float64,))
+    rows, n = T.shape
+    S = 1 << int(log2_states)
+    if values.dim() != 3 or values.shape[0] != S or values.shape[1] != 2 or not values.is_contiguous():
+        raise ValueError("values must be a contiguous S x 2 x C tensor")
+    if tuple(codes.shape) != (rows, n) or (recon is not None and tuple(recon.shape) != (rows, n)):
+        raise ValueError("codes and recon must be rows x n")
+    if cost is not None and (cost.numel() != rows or not cost.is_contiguous()):
+        raise ValueError("cost must hold one value per row")
+    ctx.ensure_workspace(wr_workspace_bytes(WR_OP_TRELLIS, rows, n, S))
+    _check("wr_trellis_quantize", load().wr_trellis_quantize(
+        ctx.handle, _ptr(T), _rowmajor(T, "T"), rows, n, int(log2_states), values.shape[2], _ptr(values),
+        int(start_state), _ptr(codes), _rowmajor(codes, "codes"), _ptr(recon),
+        _rowmajor(recon, "recon") if recon is not None else 0, _ptr(cost)))

@@ -18,6 +18,9 @@ int wr_wring_solve_impl(wr_ctx*, const void*, int, int64_t, const void*, const v
                         int64_t, int64_t, int64_t, const uint8_t*, int32_t, float, int, uint8_t*, uint16_t*, int32_t*);
 int wr_pack_impl(wr_ctx*, const uint8_t*, const uint16_t*, int64_t, int64_t, int32_t, int32_t, uint8_t*);
 int wr_unpack_impl(wr_ctx*, const uint8_t*, int64_t, int64_t, int32_t, int32_t, uint8_t*, uint16_t*, uint16_t*);
+size_t wr_trellis_ws_bytes(int64_t rows, int64_t n, int32_t states);
+int wr_trellis_quantize_impl(wr_ctx*, const float*, int64_t, int64_t, int64_t, int32_t, int32_t, const float*, int32_t,
+                             uint8_t*, int64_t, float*, int64_t, double*);
 int wr_materialize_impl(wr_ctx*, const uint8_t*, int64_t, int64_t, int32_t, int32_t, int32_t, const int8_t*, int64_t,
                         uint16_t*, int64_t);
 
@@ -86,6 +89,7 @@ size_t wr_workspace_bytes(int op, int64_t rows, int64_t n, int32_t group, int32_
     case WR_OP_FINALIZE: return wr_finalize_ws_bytes(n);
     case WR_OP_WRING: return group > 0 ? wr_wring_ws_bytes(rows, n, group, rank > 0 ? rank : 0) : 0;
     case WR_OP_WRING_GPTQ: return group > 0 ? wr_wring_gptq_ws_bytes(rows, n, group, rank > 0 ? rank : 0) : 0;
+    case WR_OP_TRELLIS: return group >= 2 && group <= 16 ? wr_trellis_ws_bytes(rows, n, group) : 0;
     default: return 0;
   }
 }
@@ -209,6 +213,22 @@ int wr_materialize(wr_ctx* ctx, const uint8_t* in, size_t in_bytes, int64_t rows
   DeviceScope ds(ctx->device);
   if (!ds.ok) return WR_EHIP;
   return wr_materialize_impl(ctx, in, rows, n_store, bits, group, had_block, signs, n_out, out, ldo);
+}
+
+int wr_trellis_quantize(wr_ctx* ctx, const float* T, int64_t ldt, int64_t rows, int64_t n, int32_t log2_states,
+                        int32_t coset_size, const float* values, int32_t start_state, uint8_t* codes, int64_t ldc,
+                        float* recon, int64_t ldr, double* cost) {
+  if (!ctx || rows < 0 || n <= 0 || n > (1 << 24) || log2_states < 1 || log2_states > 4 ||
+      !(coset_size == 1 || coset_size == 2 || coset_size == 4) || start_state < 0 || start_state >= (1 << log2_states))
+    return WR_EINVAL;
+  if (rows > 0 && (!T || !values || !codes || ldt < n || ldt % 4 != 0 || !aligned(T, 16) || ldc < n ||
+                   (recon && ldr < n)))
+    return WR_EINVAL;
+  if (rows > ((int64_t)1 << 31) / 16) return WR_EINVAL;
+  DeviceScope ds(ctx->device);
+  if (!ds.ok) return WR_EHIP;
+  return wr_trellis_quantize_impl(ctx, T, ldt, rows, n, log2_states, coset_size, values, start_state, codes, ldc, recon,
+                                  ldr, cost);
 }
 
 const char* wr_strerror(int status) {

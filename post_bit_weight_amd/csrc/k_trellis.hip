@@ -1,0 +1,219 @@
+// Trellis-coded quantization with a Viterbi search (Pingala-8 post, "Trick 3: trellis coding"):
+// the state carried from one step to the next picks the coset of values the step may use; the
+// bits written pick the value and the next state; the Viterbi algorithm keeps, for every
+// state, the cheapest path ending there.  Scalar steps on a shift-register trellis of S = 2^m
+// states: branch bit u leads from s to ((s << 1) | u) mod S, so the predecessors of s are
+// s >> 1 and (s >> 1) + S/2 with branch bit s & 1; branch (p, u) carries a coset of C values,
+// of which the nearest is taken.
+//
+// Layout of the work: S consecutive lanes per row, lane s holding the cost of the cheapest path
+// that ends in state s.  A step computes the two branch metrics into s (the coset values of
+// both incoming branches sit in the lane's registers), reads the two predecessors' costs across
+// lanes and keeps the cheaper (the smaller predecessor on a tie); the decision bit goes into a
+// word written every 32 steps to a step-major workspace (coalesced).  Costs are renormalised by
+// the row's minimum every 16 steps, so fp32 keeps the differences that decide the path.  The
+// traceback runs on every lane of the row (the same path), reading the S decision words of a
+// 32-step chunk at a time; lane j writes the codes of the steps with k % S == j.
+#include "common.hpp"
+
+namespace wr {
+
+// Cost of the predecessor p0 = s >> 1 (J = 0) or p1 = p0 + S/2 (J = 1) of this lane's state:
+// quad_perm patterns for S = 2 ([0,0,2,2], [1,1,3,3]) and S = 4 ([0,0,1,1], [2,2,3,3]), a lane
+// permute for larger S.
+template <int S, int J>
+__device__ __forceinline__ float pred_cost(float x, int src_lane) {
+  const int i = __float_as_int(x);
+  if constexpr (S == 2) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(i, J ? 0xF5 : 0xA0, 0xF, 0xF, true));
+  } else if constexpr (S == 4) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(i, J ? 0xFA : 0x50, 0xF, 0xF, true));
+  } else {
+    return __shfl(x, src_lane);
+  }
+}
+
+// the 32 targets of chunk ch of a row (zeros past n)
+__device__ __forceinline__ void load_chunk(const float* __restrict__ t, int ch, int n, float (&x)[32]) {
+  const int k0 = ch * 32;
+  if (k0 + 32 <= n) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(t + k0 + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * q + e] = v[e];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) x[j] = k0 + j < n ? t[k0 + j] : 0.0f;
+  }
+}
+
+template <int LOGS, int C>
+__global__ __launch_bounds__(256) void trellis_viterbi_kernel(const float* __restrict__ T, int64_t ldt, int64_t rows,
+                                                              int n, const float* __restrict__ values, int start,
+                                                              uint32_t* __restrict__ bp, uint8_t* __restrict__ codes,
+                                                              int64_t ldc, float* __restrict__ recon, int64_t ldr,
+                                                              double* __restrict__ cost_out) {
+  constexpr int S = 1 << LOGS;
+  __shared__ float tab[S * 2 * C];
+  for (int i = threadIdx.x; i < S * 2 * C; i += blockDim.x) tab[i] = values[i];
+  __syncthreads();
+  const int s = threadIdx.x & (S - 1);
+  const int gbase = (threadIdx.x & 63) & ~(S - 1);
+  const int64_t row0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> LOGS;
+  const bool live = row0 < rows;
+  const int64_t row = live ? row0 : rows - 1;  // every lane takes part in the exchanges
+  const float* t = T + row * ldt;
+  const int p0 = s >> 1, p1 = p0 + S / 2, u = s & 1;
+  const int lane0 = gbase + p0, lane1 = gbase + p1;
+  float v0[C], v1[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    v0[c] = tab[(p0 * 2 + u) * C + c];
+    v1[c] = tab[(p1 * 2 + u) * C + c];
+  }
+  const int64_t stride = rows * S;  // words per 32-step chunk
+  const int nchunk = (n + 31) >> 5;
+  float cost = s == start ? 0.0f : INFINITY;
+  float xs[32], nx[32];
+  load_chunk(t, 0, n, xs);
+  for (int ch = 0; ch < nchunk; ++ch) {
+    if (ch + 1 < nchunk) load_chunk(t, ch + 1, n, nx);
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if (ch * 32 + j < n) {
+        const float x = xs[j];
+        float b0 = INFINITY, b1 = INFINITY;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          const float d0 = x - v0[c], d1 = x - v1[c];
+          b0 = fminf(b0, d0 * d0);
+          b1 = fminf(b1, d1 * d1);
+        }
+        const float c0 = pred_cost<S, 0>(cost, lane0) + b0;
+        const float c1 = pred_cost<S, 1>(cost, lane1) + b1;
+        const bool up = c1 < c0;  // a tie keeps the smaller predecessor
+        cost = up ? c1 : c0;
+        word |= (uint32_t)up << j;
+        if ((j & 15) == 15) {
+          float m = cost;
+#pragma unroll
+          for (int o = 1; o < S; o <<= 1) m = fminf(m, __shfl_xor(m, o));
+          cost -= m;
+        }
+      }
+    }
+    if (live) bp[(int64_t)ch * stride + row * S + s] = word;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) xs[j] = nx[j];
+  }
+  // cheapest end state (the smaller state on a tie)
+  float bc = cost;
+  int bs = s;
+#pragma unroll
+  for (int o = 1; o < S; o <<= 1) {
+    const float oc = __shfl_xor(bc, o);
+    const int os = __shfl_xor(bs, o);
+    if (oc < bc || (oc == bc && os < bs)) {
+      bc = oc;
+      bs = os;
+    }
+  }
+  __syncthreads();  // the row's decision words (written by its S lanes) are visible
+  // traceback, the same path on every lane of the row
+  int cur = bs;
+  double acc = 0.0;
+  uint32_t w[S], nw[S];
+  const uint32_t* src = bp + (int64_t)(nchunk - 1) * stride + row * S;
+#pragma unroll
+  for (int j = 0; j < S; ++j) w[j] = src[j];
+  load_chunk(t, nchunk - 1, n, xs);
+  for (int ch = nchunk - 1; ch >= 0; --ch) {
+    if (ch > 0) {
+      const uint32_t* ps = bp + (int64_t)(ch - 1) * stride + row * S;
+#pragma unroll
+      for (int j = 0; j < S; ++j) nw[j] = ps[j];
+      load_chunk(t, ch - 1, n, nx);
+    }
+#pragma unroll
+    for (int j = 31; j >= 0; --j) {
+      const int k = ch * 32 + j;
+      if (k < n) {
+        uint32_t wd = w[0];
+#pragma unroll
+        for (int q = 1; q < S; ++q) wd = cur == q ? w[q] : wd;
+        const int upb = (wd >> j) & 1;
+        const int p = (cur >> 1) + upb * (S / 2);
+        const int uu = cur & 1;
+        const float x = xs[j];
+        const float* cs = tab + (p * 2 + uu) * C;
+        int vb = 0;
+        float rb = cs[0];
+        float db = (x - rb) * (x - rb);
+#pragma unroll
+        for (int c = 1; c < C; ++c) {
+          const float val = cs[c];
+          const float d = (x - val) * (x - val);
+          if (d < db) {  // a tie keeps the smaller index
+            db = d;
+            rb = val;
+            vb = c;
+          }
+        }
+        const double dd = (double)x - (double)rb;
+        acc = fma(dd, dd, acc);
+        if (live && (k & (S - 1)) == s) {
+          codes[row * ldc + k] = (uint8_t)(uu | (vb << 1));
+          if (recon) recon[row * ldr + k] = rb;
+        }
+        cur = p;
+      }
+    }
+    if (ch > 0) {
+#pragma unroll
+      for (int j = 0; j < S; ++j) w[j] = nw[j];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) xs[j] = nx[j];
+    }
+  }
+  if (live && s == 0 && cost_out) cost_out[row] = acc;
+}
+
+}  // namespace wr
+
+using namespace wr;
+
+size_t wr_trellis_ws_bytes(int64_t rows, int64_t n, int32_t states) {
+  return (size_t)((n + 31) / 32) * (size_t)rows * (size_t)states * 4;
+}
+
+int wr_trellis_quantize_impl(wr_ctx* ctx, const float* T, int64_t ldt, int64_t rows, int64_t n, int32_t log2_states,
+                             int32_t coset_size, const float* values, int32_t start_state, uint8_t* codes, int64_t ldc,
+                             float* recon, int64_t ldr, double* cost) {
+  if (rows == 0) return WR_OK;
+  const int S = 1 << log2_states;
+  if (ctx->ws_bytes < wr_trellis_ws_bytes(rows, n, S)) return WR_EWORKSPACE;
+  uint32_t* bp = static_cast<uint32_t*>(ctx->ws);
+  const dim3 grid((unsigned)((rows * S + 255) / 256));
+#define WR_TRL(LS, CC)                                                                                             \
+  hipLaunchKernelGGL((trellis_viterbi_kernel<LS, CC>), grid, dim3(256), 0, ctx->stream, T, ldt, rows, (int)n, values, \
+                     start_state, bp, codes, ldc, recon, ldr, cost)
+#define WR_TRL_C(LS)               \
+  switch (coset_size) {            \
+    case 1: WR_TRL(LS, 1); break;  \
+    case 2: WR_TRL(LS, 2); break;  \
+    default: WR_TRL(LS, 4); break; \
+  }
+  switch (log2_states) {
+    case 1: WR_TRL_C(1); break;
+    case 2: WR_TRL_C(2); break;
+    case 3: WR_TRL_C(3); break;
+    default: WR_TRL_C(4); break;
+  }
+#undef WR_TRL_C
+#undef WR_TRL
+  WR_CHECK_LAUNCH();
+  return WR_OK;
+}

@@ -97,3 +97,15 @@ def signs(n, seed, device="cpu"):
     g = _gen(seed, "cpu")
     s = torch.randint(0, 2, (n,), generator=g, dtype=torch.int8) * 2 - 1
     return s.to(device)
+
+
+def trellis8_values(device="cpu"):
+    """The 8-state trellis of the trellis workload, 2 bits per weight (the Pingala-8 post names
+    an 8-state set-partitioned trellis without giving it): eight levels -3.5 .. 3.5 in steps of
+    1, split into four cosets D_j = {level j, level j + 4}; branch u of state s carries
+    D_{(s & 1) + 2u}, so the two branches of a state use the cosets of one parent subset (even
+    states the even levels, odd states the odd ones), as in the post's 2-state toy.
+    Returns an 8 x 2 x 2 fp32 tensor."""
+    levels = [-3.5 + i for i in range(8)]
+    vals = [[[levels[(s & 1) + 2 * u], levels[(s & 1) + 2 * u + 4]] for u in range(2)] for s in range(8)]
+    return torch.tensor(vals, dtype=torch.float32, device=device)
