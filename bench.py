@@ -11,9 +11,9 @@ Also reported: the roofline of the dominant kernel (the bf16 SYRK that
 accumulates H: N n (n + 1) useful flops per call, timed live with HIP events on
 the stream it runs on) and the CPU oracle timed on a bounded sample of the same
 workload on the host cores, and, outside the timed step, the materializer (packed
-module -> bf16 weights) against the HBM peak and the finisher variant with GPTQ
+module -> bf16 weights) against the HBM peak, the finisher variant with GPTQ
 codes (wring by a GPTQ sweep of the watered target instead of nearest-point
-codes).
+codes), and the trellis-coded quantizer (Viterbi search) against the VALU peak.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras | --extras-only]
 """
@@ -178,6 +178,38 @@ def time_finisher_gptq(wr, ctx, torch, H, W, B, A, bits_t, cfg, reps=5):
             "weights_per_s": rows * n / (ms * 1e-3)}
 
 
+PEAK_VALU_OPS = 256 * 64 * 2.4e9  # fp32 lane operations per second without packing: 256 CUs x 64 lanes x 2.4 GHz
+
+
+def time_trellis(wr, ctx, torch, reps=5):
+    """Trellis-coded quantization (Viterbi search) of one layer's 2560-wide group, 25600 x 2560
+    targets in level units (Student-t, std 1.5), 8-state trellis, cosets of 2 (2 bits/weight).
+    Bound by VALU issue: per weight and state the forward pass evaluates 2 branches x 2 coset
+    values (subtract, multiply, min: 3 ops each) and keeps the cheaper of 2 candidates (2 adds,
+    compare, select), 16 ops, i.e. 128 per weight; the traceback adds about 12 per weight."""
+    from post_bit_weight_amd import synth
+    rows, n, log2s = 25600, 2560, 3
+    T = synth.student_t((rows, n), seed=20261230, std=1.5, device="cuda")
+    vals = synth.trellis8_values(device="cuda")
+    codes = torch.empty(rows, n, dtype=torch.uint8, device="cuda")
+    cost = torch.empty(rows, dtype=torch.float64, device="cuda")
+    for _ in range(2):
+        wr.wr_trellis_quantize(ctx, T, log2s, vals, codes, None, cost)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(ctx.stream)
+    for _ in range(reps):
+        wr.wr_trellis_quantize(ctx, T, log2s, vals, codes, None, cost)
+    e1.record(ctx.stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    ops = 140.0 * rows * n
+    achieved = ops / (ms * 1e-3)
+    return {"workload": f"trellis {rows}x{n}, 8 states, cosets of 2 (2 bits/weight)", "ms": ms,
+            "weights_per_s": rows * n / (ms * 1e-3), "bound": "alu", "achieved": achieved / 1e12,
+            "peak": PEAK_VALU_OPS / 1e12, "unit": "Tops/s", "frac": achieved / PEAK_VALU_OPS,
+            "algorithmic_ops_per_weight": 140}
+
+
 def progress(msg):
     print(f"bench.py: {msg}", file=sys.stderr, flush=True)
 
@@ -257,7 +289,8 @@ def main():
     if args.extras_only:
         progress("timing the materializer and the GPTQ-codes finisher")
         print(json.dumps({"materialize": time_materialize(wr, ctx, torch),
-                          "finisher_gptq": time_finisher_gptq(wr, ctx, torch, H, W, B, A, bits_t, cfg)}), flush=True)
+                          "finisher_gptq": time_finisher_gptq(wr, ctx, torch, H, W, B, A, bits_t, cfg),
+                          "trellis": time_trellis(wr, ctx, torch)}), flush=True)
         return
 
     progress(f"timing {args.steps} steps")
@@ -303,6 +336,8 @@ def main():
         line["materialize"] = time_materialize(wr, ctx, torch)
         progress("timing the GPTQ-codes finisher")
         line["finisher_gptq"] = time_finisher_gptq(wr, ctx, torch, H, W, B, A, bits_t, cfg)
+        progress("timing the trellis quantizer")
+        line["trellis"] = time_trellis(wr, ctx, torch)
     if not args.no_cpu_baseline:
         progress("timing the oracle on a bounded sample")
         Xh = X[: args.cpu_calib].float().cpu().numpy()
