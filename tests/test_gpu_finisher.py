@@ -156,3 +156,37 @@ def test_two_fill_and_wring_rounds(wr, ctx, finisher):
         got_c = results[k][0].cpu().numpy().astype(np.int64)
         got_s = results[k][1].cpu().numpy().astype(np.float64)
         _compare(got_c, got_s, ref, H0, 2, g)
+
+
+def test_gptq_finisher_q_proj_full_size_sampled_rows(wr, ctx):
+    """The bench workload end to end on the GPU (H from 131072 calibration rows by the library,
+    first solve, then the GPTQ-codes finisher on all 4096 rows); the oracle's finisher on 48
+    sampled rows from the GPU's first-solve codes and scales with the same H (rows are
+    independent given H)."""
+    from post_bit_weight_amd import pipeline, synth
+    rows, n, N, g, r = 4096, 2560, 131072, 64, 128
+    src = synth.SpectralSource(n, seed=20261204, device="cuda", outlier_frac=0.01)
+    X = torch.cat([src.chunk(k, 16384) for k in range(N // 16384)])
+    W = synth.student_t((rows, n), seed=20261205, device="cuda", dtype=torch.bfloat16)
+    B = synth.gaussian((rows, r), 0.01, seed=20261206, device="cuda", dtype=torch.bfloat16)
+    A = synth.gaussian((r, n), 0.01, seed=20261207, device="cuda", dtype=torch.bfloat16)
+    S, total = pipeline.accumulate_hessian(ctx, [X], n)
+    H, _ = pipeline.finalize_hessian(ctx, S, total, 0.01, n)
+    del X
+    bits_t = torch.full((rows,), 2, dtype=torch.uint8, device="cuda")
+    c1 = torch.empty(rows, n, dtype=torch.uint8, device="cuda")
+    s1 = torch.empty(rows, n // g, dtype=torch.float16, device="cuda")
+    info = torch.zeros(3, dtype=torch.int32, device="cuda")
+    wr.wr_gptq_sweep(ctx, W, H, bits_t, g, 128, c1, s1, info[0:1])
+    wr.wr_wring_solve(ctx, H, bits_t, g, 0.01, c1, s1, info[1:2], target=W)
+    c2, s2 = c1.clone(), s1.clone()
+    wr.wr_wring_solve(ctx, H, bits_t, g, 0.01, c2, s2, info[2:3], B=B, A=A, alpha=float(r), recode="gptq")
+    torch.cuda.synchronize()
+    assert (info.cpu().numpy() == 0).all()
+    sel = np.sort(np.r_[0, rows - 1, np.random.default_rng(11).choice(np.arange(1, rows - 1), 46, replace=False)])
+    t = torch.as_tensor(sel, device="cuda")
+    Hd = H.cpu().double().numpy()
+    ref = oracle.wring_gptq(c1[t].cpu().numpy().astype(np.int64), s1[t].cpu().numpy().astype(np.float64), 2, g,
+                            B[t].double().cpu().numpy(), A.double().cpu().numpy(), float(r), Hd, 0.01)
+    cp = _compare(c2[t].cpu().numpy().astype(np.int64), s2[t].cpu().numpy().astype(np.float64), ref, Hd, 2, g)
+    print(f"codes differing {cp['frac']:.2e}, rows with a tie {len(cp['rows'])}")

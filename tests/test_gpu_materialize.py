@@ -82,3 +82,40 @@ def test_materialize_rejects_bad_arguments(wr, ctx):
         wr.wr_materialize(ctx, buf[:-1], 2, 64, 2, 32, out)
     with pytest.raises(RuntimeError):
         wr.wr_materialize(ctx, buf, 2, 64, 2, 32, out, had_block=48, signs=torch.ones(64, dtype=torch.int8, device="cuda"))
+
+
+def _sub_container(buf, rows, n, bits, g, sel):
+    """The container of the selected rows alone (codes of those rows, then their scales)."""
+    rb, sb = n * bits // 8, 2 * (n // g)
+    codes = buf[:rows * rb].reshape(rows, rb)[sel]
+    scales = buf[rows * rb:].reshape(rows, sb)[sel]
+    return np.concatenate([codes.ravel(), scales.ravel()])
+
+
+def test_materialize_bench_size_sampled_rows(wr, ctx):
+    """The bench launch: 25600 x 2560, 2-bit, group 64, blocks of 512, aligned output; the oracle
+    on 48 sampled rows (rows are independent), to the same bar as above."""
+    rows, n, bits, g, m = 25600, 2560, 2, 64, 512
+    gen = torch.Generator(device="cuda").manual_seed(20261208)
+    code_bytes = rows * n * bits // 8
+    buf = torch.randint(0, 256, (wr.packed_nbytes(rows, n, bits, g),), dtype=torch.uint8, device="cuda", generator=gen)
+    sc = (torch.rand(rows * (n // g), device="cuda", generator=gen) * 0.029 + 1e-3).to(torch.float16)
+    buf[code_bytes:] = sc.view(torch.uint8)
+    signs = (torch.randint(0, 2, (n,), device="cuda", generator=gen) * 2 - 1).to(torch.int8)
+    out = torch.empty(rows, n, dtype=torch.bfloat16, device="cuda")
+    wr.wr_materialize(ctx, buf, rows, n, bits, g, out, had_block=m, signs=signs)
+    torch.cuda.synchronize()
+    sel = np.sort(np.r_[0, rows - 1, np.random.default_rng(9).choice(np.arange(1, rows - 1), 46, replace=False)])
+    sub = _sub_container(buf.cpu().numpy(), rows, n, bits, g, sel)
+    sg = signs.cpu().numpy().astype(np.float64)
+    ref = oracle.materialize(sub, sel.size, n, bits, g, m, sg, n)
+    got = out[torch.as_tensor(sel, device="cuda")].view(torch.int16).cpu().numpy().astype(np.uint16)
+    diff = got != ref
+    assert diff.mean() <= 1e-3, diff.mean()
+    exact = oracle.materialize_exact(sub, sel.size, n, bits, g, m, sg, n)
+    codes_d, scales_d = oracle.unpack(sub, sel.size, n, bits, g)
+    absv = np.abs(oracle.dequant(codes_d, scales_d, bits, g)).reshape(sel.size, n // m, m).sum(axis=2) / np.sqrt(m)
+    bound = (np.log2(m) + 4) * 2.0 ** -24 * np.repeat(absv, m, axis=1)
+    gv, ex = oracle.bf16_bits_to_f64(got[diff]), exact[diff]
+    _, e = np.frexp(np.maximum(np.abs(gv), np.abs(ex)))
+    assert np.all(np.abs(gv - ex) <= np.ldexp(1.0, e - 9) + bound[diff])
