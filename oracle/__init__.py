@@ -34,7 +34,7 @@ from .rotation import sylvester, rotation_matrix, rotate_rows, rotate_rows_inver
 from .grid import fp16_rne, levels_count, nearest_code, level_of, dequant
 from .gptq import upper_cholesky_of_inverse, feedback_sweep, gptq_sweep, integer_feedback_round
 from .joint import joint_scales, row_gram
-from .wring import wring_target, wring, wring_gptq
+from .wring import wring_target, wring, wring_gptq, wring_scale_search, scale_search_block
 from .pack import pack, unpack, packed_bytes, code_bytes_per_row
 from .metrics import proxy_loss, ledger_bits_per_weight, threshold_distance
 from .solve import solve_module, solve_rows
@@ -47,7 +47,7 @@ __all__ = [
     "fp16_rne", "levels_count", "nearest_code", "level_of", "dequant",
     "upper_cholesky_of_inverse", "feedback_sweep", "gptq_sweep", "integer_feedback_round",
     "joint_scales", "row_gram",
-    "wring_target", "wring", "wring_gptq",
+    "wring_target", "wring", "wring_gptq", "wring_scale_search", "scale_search_block",
     "pack", "unpack", "packed_bytes", "code_bytes_per_row",
     "proxy_loss", "ledger_bits_per_weight", "threshold_distance",
     "solve_module", "solve_rows",

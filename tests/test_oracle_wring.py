@@ -103,3 +103,35 @@ def test_gptq_finisher_keeps_a_grid_point_with_extreme_levels():
         assert np.array_equal(out["codes"], codes)
         assert np.array_equal(out["sweep_scales"], scales)
         assert np.array_equal(out["scales"], scales)
+
+
+def test_scale_search_is_the_best_candidate_by_enumeration():
+    """Each block's result is the candidate with the least squared error over all 32 candidate
+    scales and, for that scale, over every code vector (brute force on 4-weight blocks: the
+    nearest level per weight is the error-minimising code for a fixed scale)."""
+    import itertools
+    rng = np.random.default_rng(37)
+    for bits in (2, 3):
+        L = 2 ** bits - 1
+        for _ in range(6):
+            w = rng.normal(0, 1, size=4)
+            s, c, e, k = oracle.scale_search_block(w, L)
+            amax = np.max(np.abs(w))
+            best = np.inf
+            for kk in range(32):
+                sk = float(np.float16((1 - kk / 64) * amax / L))
+                for cc in itertools.product(range(L + 1), repeat=4):
+                    best = min(best, float(np.sum((w - sk * (2 * np.array(cc) - L)) ** 2)))
+            assert np.isclose(e, best, rtol=1e-12, atol=1e-15)
+            assert np.isclose(np.sum((w - s * (2 * c - L)) ** 2), e, rtol=1e-12)
+
+
+def test_scale_search_keeps_the_absmax_scale_when_it_is_exact():
+    """A block already on the grid at its absmax scale (a level +-L present) has zero error at
+    k = 0, the first candidate, which a tie keeps."""
+    rng = np.random.default_rng(38)
+    H, codes, scales, L = _setup(rng, rows=3, n=24, g=8)
+    codes[:, ::8] = L
+    out = oracle.wring_scale_search(codes, scales, 2, 8, np.zeros((3, 2)), np.zeros((2, 24)), 2.0)
+    assert np.array_equal(out["codes"], codes) and np.array_equal(out["scales"], scales)
+    assert np.all(out["k"] == 0) and np.all(out["errors"] == 0)
