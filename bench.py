@@ -150,8 +150,9 @@ def time_materialize(wr, ctx, torch, reps=20):
 
 
 def time_finisher_gptq(wr, ctx, torch, H, W, B, A, bits_t, cfg, reps=5):
-    """The GPTQ-codes finisher (wr_wring_solve with WR_RECODE_GPTQ: watered target, GPTQ sweep of
-    it, joint scales) on the step's workload, starting from the first solve's codes and scales.
+    """The finisher variants on the step's workload, from the first solve's codes and scales: GPTQ
+    codes (wr_wring_solve with WR_RECODE_GPTQ: watered target, GPTQ sweep of it, joint scales) and
+    searched block scales (WR_RECODE_SEARCH: watered target, 32 candidate scales per block).
     Each call is timed alone with HIP events on the library's stream."""
     rows, n, g, rank = cfg["rows"], cfg["n"], cfg["group"], cfg["rank"]
     c1 = torch.empty(rows, n, dtype=torch.uint8, device="cuda")
@@ -160,22 +161,26 @@ def time_finisher_gptq(wr, ctx, torch, H, W, B, A, bits_t, cfg, reps=5):
     wr.wr_gptq_sweep(ctx, W, H, bits_t, g, 128, c1, s1, info[0:1])
     wr.wr_wring_solve(ctx, H, bits_t, g, 0.01, c1, s1, info[1:2], target=W)
     codes, scales = torch.empty_like(c1), torch.empty_like(s1)
-    times = []
-    for k in range(reps + 2):
-        codes.copy_(c1)
-        scales.copy_(s1)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(ctx.stream)
-        wr.wr_wring_solve(ctx, H, bits_t, g, 0.01, codes, scales, info[2:3], B=B, A=A, alpha=float(rank), recode="gptq")
-        e1.record(ctx.stream)
-        torch.cuda.synchronize()
-        if k >= 2:
-            times.append(e0.elapsed_time(e1))
-    if int(info.abs().sum().item()) != 0:
-        raise RuntimeError(f"dev_info reports a failure in the GPTQ finisher: {info.tolist()}")
-    ms = sum(times) / len(times)
-    return {"workload": f"wring with GPTQ codes, {rows}x{n}, rank {rank}", "ms": ms,
-            "weights_per_s": rows * n / (ms * 1e-3)}
+    out = {}
+    for kind in ("gptq", "search"):
+        times = []
+        for k in range(reps + 2):
+            codes.copy_(c1)
+            scales.copy_(s1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(ctx.stream)
+            wr.wr_wring_solve(ctx, H, bits_t, g, 0.01, codes, scales, info[2:3], B=B, A=A, alpha=float(rank),
+                              recode=kind)
+            e1.record(ctx.stream)
+            torch.cuda.synchronize()
+            if k >= 2:
+                times.append(e0.elapsed_time(e1))
+        if int(info.abs().sum().item()) != 0:
+            raise RuntimeError(f"dev_info reports a failure in the {kind} finisher: {info.tolist()}")
+        ms = sum(times) / len(times)
+        out[kind] = {"ms": ms, "weights_per_s": rows * n / (ms * 1e-3)}
+    return {"workload": f"wring with GPTQ codes / with searched block scales, {rows}x{n}, rank {rank}",
+            "ms": out["gptq"]["ms"], "weights_per_s": out["gptq"]["weights_per_s"], "scale_search": out["search"]}
 
 
 PEAK_VALU_OPS = 256 * 64 * 2.4e9  # fp32 lane operations per second without packing: 256 CUs x 64 lanes x 2.4 GHz

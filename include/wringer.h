@@ -65,7 +65,7 @@ enum wr_op {             /* operations that need workspace, for wr_workspace_byt
 
 enum wr_hessian_flags { WR_H_ZERO = 1 };               /* zero S before accumulating */
 enum wr_rotate_mode { WR_ROT_ROWS = 0, WR_ROT_ROWS_INVERSE = 1, WR_ROT_SYM = 2 };
-enum wr_wring_flags { WR_RECODE_NEAREST = 1, WR_RECODE_GPTQ = 2 };
+enum wr_wring_flags { WR_RECODE_NEAREST = 1, WR_RECODE_GPTQ = 2, WR_RECODE_SEARCH = 4 };
 
 typedef struct wr_ctx wr_ctx;
 
@@ -168,7 +168,12 @@ int wr_gptq_sweep(wr_ctx* ctx, const void* W, int w_dtype, int64_t rows, int64_t
  * are first replaced by those of the GPTQ sweep of T with H (as wr_gptq_sweep,
  * lazy batch 128; n % 4 == 0), whose scales then serve as s0; a failure of the
  * sweep is reported in dev_info and leaves codes and scales as the sweep does.
- * The two flags exclude each other.  Then every row's scales are re-solved:
+ * With WR_RECODE_SEARCH (the finisher "nearest-point codes + block scale search" of
+ * the same comparison) each block's scale is searched instead of solved: candidates
+ * s_k = fp16((1 - k/64) max|t| / L), k = 0..31, each with the nearest codes of t / s_k;
+ * the candidate with the least squared error of the block is kept (the smaller k on a
+ * tie) and no joint solve follows (H and lambda are unused; H may be null).
+ * At most one of the three flags.  Otherwise every row's scales are re-solved:
  *   s = argmin (t - Q s)^T H (t - Q s) + lambda mu ||s - s0||^2,
  *   mu = trace(Q^T H Q) / nb,  s0 = the scales passed in,
  * and projected to fp16 (round to nearest even).  codes and scales are

@@ -21,6 +21,7 @@ WR_H_ZERO = 1
 WR_ROT_ROWS, WR_ROT_ROWS_INVERSE, WR_ROT_SYM = 0, 1, 2
 WR_RECODE_NEAREST = 1
 WR_RECODE_GPTQ = 2
+WR_RECODE_SEARCH = 4
 
 EXPORTED = (
     "wr_create", "wr_destroy", "wr_workspace_bytes", "wr_set_workspace",
@@ -214,10 +215,11 @@ def wr_gptq_sweep(ctx, W, H, bits, group, lazy_batch, codes, scales, dev_info):
 
 def wr_wring_solve(ctx, H, bits, group, lam, codes, scales, dev_info, target=None, B=None, A=None, alpha=0.0,
                    recode=False):
-    """recode: False (joint scales only), True or "nearest" (WR_RECODE_NEAREST), "gptq" (WR_RECODE_GPTQ)."""
-    if recode not in (False, True, "nearest", "gptq"):
-        raise ValueError("recode must be False, True, 'nearest' or 'gptq'")
-    flags = WR_RECODE_GPTQ if recode == "gptq" else (WR_RECODE_NEAREST if recode else 0)
+    """recode: False (joint scales only), True or "nearest" (WR_RECODE_NEAREST), "gptq" (WR_RECODE_GPTQ),
+    "search" (WR_RECODE_SEARCH: searched block scales, no joint solve; H may be None)."""
+    if recode not in (False, True, "nearest", "gptq", "search"):
+        raise ValueError("recode must be False, True, 'nearest', 'gptq' or 'search'")
+    flags = {"gptq": WR_RECODE_GPTQ, "search": WR_RECODE_SEARCH}.get(recode, WR_RECODE_NEAREST if recode else 0)
     _dev(target, "target", FLOATS)
     _dev(B, "B", FLOATS)
     _dev(A, "A", FLOATS)
@@ -227,7 +229,7 @@ def wr_wring_solve(ctx, H, bits, group, lam, codes, scales, dev_info, target=Non
     _dev(scales, "scales", (torch.float16, torch.int16, torch.uint16))
     _dev(dev_info, "dev_info", (torch.int32,))
     rows, n = codes.shape
-    ldh = _rowmajor(H, "H")
+    ldh = _rowmajor(H, "H") if H is not None else 0
     ldt = _rowmajor(target, "target") if target is not None else 0
     rank = 0
     ab_dtype = WR_F32

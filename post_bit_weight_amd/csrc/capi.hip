@@ -160,17 +160,19 @@ int wr_wring_solve(wr_ctx* ctx, const void* target, int t_dtype, int64_t ldt, co
                    int32_t rank, float alpha, int ab_dtype, const float* H, int64_t ldh, int64_t rows, int64_t n,
                    const uint8_t* bits, int32_t group, float lambda, int flags, uint8_t* codes, uint16_t* scales,
                    int32_t* dev_info) {
-  if (!ctx || !H || !dev_info || rows < 0 || n <= 0 || n > 65536 || ldh < n || group <= 0 || n % group != 0 ||
-      group % 8 != 0 || !(lambda >= 0.0f) || (flags & ~(WR_RECODE_NEAREST | WR_RECODE_GPTQ)) ||
-      (flags == (WR_RECODE_NEAREST | WR_RECODE_GPTQ)))
+  const int mode = flags & (WR_RECODE_NEAREST | WR_RECODE_GPTQ | WR_RECODE_SEARCH);
+  const bool search = flags == WR_RECODE_SEARCH;  // H and lambda unused
+  if (!ctx || !dev_info || rows < 0 || n <= 0 || n > 65536 || group <= 0 || n % group != 0 || group % 8 != 0 ||
+      (flags & ~(WR_RECODE_NEAREST | WR_RECODE_GPTQ | WR_RECODE_SEARCH)) || (mode & (mode - 1)) != 0)
     return WR_EINVAL;
+  if (!search && (!H || ldh < n || !(lambda >= 0.0f))) return WR_EINVAL;
   if ((flags & WR_RECODE_GPTQ) && n % 4 != 0) return WR_EINVAL;
   if (rows > 65535) return WR_EINVAL;
   if (target && (!valid_dtype(t_dtype) || ldt < n)) return WR_EINVAL;
   if ((B != nullptr) != (A != nullptr)) return WR_EINVAL;
   if (B && (rank <= 0 || rank % 4 != 0 || !valid_dtype(ab_dtype))) return WR_EINVAL;
   if (rows > 0 && (!bits || !codes || !scales)) return WR_EINVAL;
-  if (!aligned(H, 16) || !aligned(codes, 16) || ldh % 4 != 0) return WR_EINVAL;
+  if ((!search && (!aligned(H, 16) || ldh % 4 != 0)) || !aligned(codes, 16)) return WR_EINVAL;
   DeviceScope ds(ctx->device);
   if (!ds.ok) return WR_EHIP;
   return wr_wring_solve_impl(ctx, target, t_dtype, ldt, B, A, rank, alpha, ab_dtype, H, ldh, rows, n, bits, group,

@@ -600,6 +600,74 @@ __global__ __launch_bounds__(64) void row_solve_kernel(const float* __restrict__
   for (int i = lane; i < nb; i += 64) scales[(size_t)row * nb + i] = f64_to_f16_bits_clamped(y[i]);
 }
 
+// Block scale search (the finisher "nearest-point codes + block scale search"): for each block
+// of G weights of T, the candidate scales s_k = fp16((1 - k/64) max|t| / L), k = 0..31, each with
+// the nearest codes of t / s_k (IEEE division, as in the recode); the candidate with the least
+// squared error of the block wins, the smaller k on a tie.  One half-wave (32 lanes, lane = k)
+// per block, eight blocks per workgroup, the block's targets staged in LDS; the scale is
+// formed in fp64 and rounded once to fp16; the error is summed in fp64.  Nothing is written
+// when dev_info is already set (a non-finite target).
+template <int G>
+__global__ __launch_bounds__(256) void scale_search_kernel(const float* __restrict__ T, int64_t rows, int n,
+                                                           const uint8_t* __restrict__ bits, uint8_t* __restrict__ codes,
+                                                           uint16_t* __restrict__ scales,
+                                                           const int32_t* __restrict__ dev_info) {
+  if (*dev_info != 0) return;
+  __shared__ float sT[8][G];
+  const int nb = n / G;
+  const int64_t blocks = rows * nb;
+  const int tid = threadIdx.x, k = tid & 31, bl = tid >> 5;
+  const int64_t blk0 = (int64_t)blockIdx.x * 8;
+  for (int i = tid; i < 8 * G; i += 256) {
+    const int bb = i / G, j = i % G;
+    const int64_t blk = blk0 + bb;
+    float v = 0.0f;
+    if (blk < blocks) {
+      const int64_t r = blk / nb;
+      v = T[r * n + (blk - r * nb) * G + j];
+    }
+    sT[bb][j] = v;
+  }
+  __syncthreads();
+  const int64_t blk = blk0 + bl;
+  const bool live = blk < blocks;
+  const int64_t r = live ? blk / nb : 0;
+  const int b = live ? (int)(blk - r * nb) : 0;
+  const int L = (1 << bits[r]) - 1;
+  float amax = 0.0f;
+  for (int j = 0; j < G; ++j) amax = fmaxf(amax, fabsf(sT[bl][j]));
+  auto cand = [&](int kk) { return f16_bits_to_f32(f64_to_f16_bits_clamped((1.0 - kk / 64.0) * (double)amax / L)); };
+  const float s = cand(k);
+  double err = 0.0;
+  for (int j = 0; j < G; ++j) {
+    const float w = sT[bl][j];
+    const int c = nearest_code(s > 0.0f ? w / s : 0.0f, L);
+    const double d = (double)w - (double)s * (double)(2 * c - L);
+    err = fma(d, d, err);
+  }
+  double be = err;
+  int bk = k;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) {
+    const double oe = __shfl_xor(be, o);
+    const int ok = __shfl_xor(bk, o);
+    if (oe < be || (oe == be && ok < bk)) {
+      be = oe;
+      bk = ok;
+    }
+  }
+  if (!live) return;
+  const float sb = cand(bk);
+  constexpr int PER = G / 32;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int j = k * PER + q;
+    const float w = sT[bl][j];
+    codes[r * n + (int64_t)b * G + j] = (uint8_t)nearest_code(sb > 0.0f ? w / sb : 0.0f, L);
+  }
+  if (k == 0) scales[r * nb + b] = f64_to_f16_bits_clamped((double)sb);
+}
+
 }  // namespace wr
 
 using namespace wr;
@@ -787,6 +855,30 @@ int wr_wring_solve_impl(wr_ctx* ctx, const void* target, int t_dtype, int64_t ld
                         int32_t rank, float alpha, int ab_dtype, const float* H, int64_t ldh, int64_t rows, int64_t n,
                         const uint8_t* bits, int32_t group, float lambda, int flags, uint8_t* codes, uint16_t* scales,
                         int32_t* dev_info) {
+  if (flags & WR_RECODE_SEARCH) {
+    // the watered target into the joint solve's T slot, then the search (no joint solve)
+    if (group != 32 && group != 64 && group != 128) return WR_EUNSUPPORTED;
+    const bool adapter = B && A && rank > 0;
+    const WringLayout lay = wring_layout(rows, n, group, adapter ? rank : 0);
+    if (ctx->ws_bytes < lay.total) return WR_EWORKSPACE;
+    char* ws = static_cast<char*>(ctx->ws);
+    float* T = reinterpret_cast<float*>(ws + lay.T);
+    int rc = wring_core(ctx, ws, ctx->ws_bytes, target, t_dtype, ldt, B, A, rank, alpha, ab_dtype, H, ldh, rows, n,
+                        bits, group, lambda, 0, true, T, codes, scales, dev_info);
+    if (rc || rows == 0) return rc;
+    const dim3 grid((unsigned)((rows * (n / group) + 7) / 8));
+    if (group == 32)
+      hipLaunchKernelGGL(scale_search_kernel<32>, grid, dim3(256), 0, ctx->stream, T, rows, (int)n, bits, codes, scales,
+                         dev_info);
+    else if (group == 64)
+      hipLaunchKernelGGL(scale_search_kernel<64>, grid, dim3(256), 0, ctx->stream, T, rows, (int)n, bits, codes, scales,
+                         dev_info);
+    else
+      hipLaunchKernelGGL(scale_search_kernel<128>, grid, dim3(256), 0, ctx->stream, T, rows, (int)n, bits, codes,
+                         scales, dev_info);
+    WR_CHECK_LAUNCH();
+    return WR_OK;
+  }
   if (!(flags & WR_RECODE_GPTQ))
     return wring_core(ctx, static_cast<char*>(ctx->ws), ctx->ws_bytes, target, t_dtype, ldt, B, A, rank, alpha,
                       ab_dtype, H, ldh, rows, n, bits, group, lambda, flags, true, nullptr, codes, scales, dev_info);

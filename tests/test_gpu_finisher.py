@@ -190,3 +190,61 @@ def test_gptq_finisher_q_proj_full_size_sampled_rows(wr, ctx):
                             B[t].double().cpu().numpy(), A.double().cpu().numpy(), float(r), Hd, 0.01)
     cp = _compare(c2[t].cpu().numpy().astype(np.int64), s2[t].cpu().numpy().astype(np.float64), ref, Hd, 2, g)
     print(f"codes differing {cp['frac']:.2e}, rows with a tie {len(cp['rows'])}")
+
+
+def _search_check(codes, scales, ref, bits, g):
+    """The searched finisher: each block's GPU scale gives an error within rounding of the oracle's
+    least one (both evaluated in fp64 on the oracle's W'), the GPU's codes are the nearest levels
+    at that scale except within 1e-4 level units of a threshold, and at least 99 % of scales equal
+    the oracle's."""
+    L = 2 ** bits - 1
+    Wp = ref["target"]
+    rows, n = Wp.shape
+    nb = n // g
+    s_rep = np.repeat(scales, g, axis=1)
+    lev = 2 * codes - L
+    err = ((Wp - s_rep * lev) ** 2).reshape(rows, nb, g).sum(axis=2)
+    best = ref["errors"]
+    assert np.all(err <= best * (1 + 1e-5) + 1e-18), np.max(err / np.maximum(best, 1e-30))
+    t = np.divide(Wp, s_rep, out=np.zeros_like(Wp), where=s_rep > 0)
+    near = oracle.nearest_code(t, L)
+    bad = (near != codes) & (oracle.threshold_distance(t, L) > 1e-4)
+    assert not bad.any(), int(bad.sum())
+    same = np.mean(f16_bits(scales) == f16_bits(ref["scales"]))
+    assert same >= 0.99, same
+    return same
+
+
+def _run_search(wr, ctx, codes, scales, bits, g, B, A, alpha):
+    rows, n = codes.shape
+    c_t = torch.from_numpy(codes.astype(np.uint8)).cuda()
+    s_t = torch.from_numpy(scales.astype(np.float16)).cuda()
+    info = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bits_t = torch.full((rows,), bits, dtype=torch.uint8, device="cuda")
+    wr.wr_wring_solve(ctx, None, bits_t, g, 0.0, c_t, s_t, info, B=B.contiguous().cuda(), A=A.contiguous().cuda(),
+                      alpha=alpha, recode="search")
+    return c_t.cpu().numpy().astype(np.int64), s_t.cpu().numpy().astype(np.float64), int(info.item())
+
+
+@pytest.mark.parametrize("shape", ["toy", "q_proj_slice"])
+def test_scale_search_finisher(wr, ctx, shape):
+    """The toy layer (fp32, group 32, rank 8) and a q_proj-shaped slice (bf16, group 64, rank 128),
+    from the oracle's first-solve codes and scales."""
+    from post_bit_weight_amd import synth
+    if shape == "toy":
+        rows, n, g, r, dt = 256, 512, 32, 8, torch.float32
+        W = synth.gaussian((rows, n), 0.02, seed=101)
+        X = synth.SpectralSource(n, seed=102, n_outliers=5).chunk(0, 4096, dtype=torch.float32)
+    else:
+        rows, n, g, r, dt = 128, 2560, 64, 128, torch.bfloat16
+        W = synth.student_t((rows, n), seed=20261211, dtype=dt)
+        X = synth.SpectralSource(n, seed=20261210, outlier_frac=0.01).chunk(0, 16384, dtype=dt)
+    B = synth.gaussian((rows, r), 0.01, seed=103, dtype=dt)
+    A = synth.gaussian((r, n), 0.01, seed=104, dtype=dt)
+    Hd = oracle.damp(oracle.second_moment(X.double().numpy()), 0.01)[0].astype(np.float32).astype(np.float64)
+    codes0, s1 = _first_solve(W.double().numpy(), Hd, 2, g, 0.01)
+    codes, scales, info = _run_search(wr, ctx, codes0, s1, 2, g, B, A, float(r))
+    assert info == 0
+    ref = oracle.wring_scale_search(codes0, s1, 2, g, B.double().numpy(), A.double().numpy(), float(r))
+    same = _search_check(codes, scales, ref, 2, g)
+    print(f"scales equal to the oracle's: {same:.4f}")
