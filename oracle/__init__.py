@@ -40,6 +40,7 @@ from .metrics import proxy_loss, ledger_bits_per_weight, threshold_distance
 from .solve import solve_module, solve_rows
 from .materialize import bf16_rne_bits, bf16_bits_to_f64, materialize, materialize_exact
 from .trellis import viterbi as trellis_viterbi, greedy as trellis_greedy, decode as trellis_decode
+from .gemv import packed_gemv
 
 __all__ = [
     "second_moment", "second_moment_chunks", "sum_of_products", "pad_square", "damp",
@@ -53,4 +54,5 @@ __all__ = [
     "solve_module", "solve_rows",
     "bf16_rne_bits", "bf16_bits_to_f64", "materialize", "materialize_exact",
     "trellis_viterbi", "trellis_greedy", "trellis_decode",
+    "packed_gemv",
 ]
