@@ -60,7 +60,8 @@ enum wr_op {             /* operations that need workspace, for wr_workspace_byt
   WR_OP_ROTATE = 3,      /* none needed; returns 0 */
   WR_OP_FINALIZE = 4,    /* n = n_store; needed by wr_hessian_finalize with a rotation */
   WR_OP_WRING_GPTQ = 5,  /* rows, n, group, rank: wr_wring_solve with WR_RECODE_GPTQ */
-  WR_OP_TRELLIS = 6      /* rows, n, group = number of trellis states: wr_trellis_quantize */
+  WR_OP_TRELLIS = 6,     /* rows, n, group = number of trellis states: wr_trellis_quantize */
+  WR_OP_GEMV = 7         /* rows = number of input vectors, n = n_store: wr_packed_gemv */
 };
 
 enum wr_hessian_flags { WR_H_ZERO = 1 };               /* zero S before accumulating */
@@ -239,6 +240,25 @@ int wr_materialize(wr_ctx* ctx, const uint8_t* in, size_t in_bytes, int64_t rows
 int wr_trellis_quantize(wr_ctx* ctx, const float* T, int64_t ldt, int64_t rows, int64_t n, int32_t log2_states,
                         int32_t coset_size, const float* values, int32_t start_state, uint8_t* codes, int64_t ldc,
                         float* recon, int64_t ldr, double* cost);
+
+/*
+ * (f) Product of a packed module with input vectors (Wringer model cards, "What is in this
+ * repo": the container of packed codes and fp16 block scales, stored in the rotated and
+ * zero-padded basis; the cards name the multiplication of packed codes with the activations
+ * as what decoding from the container needs).  For the module in `in` (wr_pack layout,
+ * in_bytes its size; rows x n_store codes of `bits` bits, group a multiple of 32, n_store a
+ * multiple of 32, `in` 16-byte aligned) and batch input vectors x (batch x n_in fp32, ld ldx,
+ * n_in <= n_store, 1 <= batch <= 8):
+ *   y[b][r] = sum_j (2 c_rj - L) s_r,j/group (R x_pad)_j
+ * with x_pad the vector zero-padded to n_store and R the rotation of wr_hadamard_rotate
+ * (had_block, signs: device int8 +-1 of length n_store; had_block 0: R = I), i.e. the
+ * module's weights in the input basis times x.  x' = R x_pad is formed in fp32 in the
+ * workspace, the products and sums run in fp32.  y: batch x rows fp32, ld ldy >= rows.
+ * Workspace: WR_OP_GEMV (rows = batch, n = n_store).
+ */
+int wr_packed_gemv(wr_ctx* ctx, const uint8_t* in, size_t in_bytes, int64_t rows, int64_t n_store, int32_t bits,
+                   int32_t group, int32_t had_block, const int8_t* signs, const float* x, int64_t n_in, int64_t ldx,
+                   int32_t batch, float* y, int64_t ldy);
 
 /* Static description of a status code. */
 const char* wr_strerror(int status);

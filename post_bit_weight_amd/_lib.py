@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwringer.
 
 WR_OK, WR_EINVAL, WR_EWORKSPACE, WR_EHIP, WR_EUNSUPPORTED = 0, 1, 2, 3, 4
 WR_F32, WR_BF16 = 0, 1
-WR_OP_HESSIAN, WR_OP_GPTQ, WR_OP_WRING, WR_OP_ROTATE, WR_OP_FINALIZE, WR_OP_WRING_GPTQ, WR_OP_TRELLIS = range(7)
+(WR_OP_HESSIAN, WR_OP_GPTQ, WR_OP_WRING, WR_OP_ROTATE, WR_OP_FINALIZE, WR_OP_WRING_GPTQ, WR_OP_TRELLIS,
+ WR_OP_GEMV) = range(8)
 WR_H_ZERO = 1
 WR_ROT_ROWS, WR_ROT_ROWS_INVERSE, WR_ROT_SYM = 0, 1, 2
 WR_RECODE_NEAREST = 1
@@ -27,7 +28,7 @@ EXPORTED = (
     "wr_create", "wr_destroy", "wr_workspace_bytes", "wr_set_workspace",
     "wr_hessian_accumulate", "wr_hessian_finalize", "wr_hadamard_rotate",
     "wr_gptq_sweep", "wr_wring_solve", "wr_pack", "wr_unpack", "wr_materialize", "wr_trellis_quantize",
-    "wr_strerror",
+    "wr_packed_gemv", "wr_strerror",
 )
 
 
@@ -68,6 +69,8 @@ def load():
         "wr_unpack": (I, [P, P, SZ, I64, I64, c.c_int32, c.c_int32, P, P, P]),
         "wr_materialize": (I, [P, P, SZ, I64, I64, c.c_int32, c.c_int32, c.c_int32, P, I64, P, I64]),
         "wr_trellis_quantize": (I, [P, P, I64, I64, I64, c.c_int32, c.c_int32, P, c.c_int32, P, I64, P, I64, P]),
+        "wr_packed_gemv": (I, [P, P, SZ, I64, I64, c.c_int32, c.c_int32, c.c_int32, P, P, I64, I64, c.c_int32, P,
+                               I64]),
         "wr_strerror": (c.c_char_p, [I]),
     }
     for name, (res, args) in sig.items():
@@ -308,3 +311,19 @@ def wr_trellis_quantize(ctx, T, log2_states, values, codes, recon=None, cost=Non
         ctx.handle, _ptr(T), _rowmajor(T, "T"), rows, n, int(log2_states), values.shape[2], _ptr(values),
         int(start_state), _ptr(codes), _rowmajor(codes, "codes"), _ptr(recon),
         _rowmajor(recon, "recon") if recon is not None else 0, _ptr(cost)))
+
+
+def wr_packed_gemv(ctx, buf, rows, n_store, bits, group, x, y, had_block=0, signs=None):
+    """y (batch x rows fp32) = the packed module's weights in the input basis times each row of x
+    (batch x n_in fp32, n_in <= n_store)."""
+    _dev(buf, "buf", (torch.uint8,))
+    _dev(x, "x", (torch.float32,))
+    _dev(y, "y", (torch.float32,))
+    _dev(signs, "signs", (torch.int8,))
+    if x.dim() != 2 or y.dim() != 2 or y.shape[0] != x.shape[0] or y.shape[1] != rows:
+        raise ValueError("x must be batch x n_in and y batch x rows")
+    batch = x.shape[0]
+    ctx.ensure_workspace(wr_workspace_bytes(WR_OP_GEMV, batch, n_store))
+    _check("wr_packed_gemv", load().wr_packed_gemv(ctx.handle, _ptr(buf), buf.numel(), rows, n_store, int(bits),
+                                                   int(group), int(had_block), _ptr(signs), _ptr(x), x.shape[1],
+                                                   _rowmajor(x, "x"), batch, _ptr(y), _rowmajor(y, "y")))

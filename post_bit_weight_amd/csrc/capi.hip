@@ -19,6 +19,9 @@ int wr_wring_solve_impl(wr_ctx*, const void*, int, int64_t, const void*, const v
 int wr_pack_impl(wr_ctx*, const uint8_t*, const uint16_t*, int64_t, int64_t, int32_t, int32_t, uint8_t*);
 int wr_unpack_impl(wr_ctx*, const uint8_t*, int64_t, int64_t, int32_t, int32_t, uint8_t*, uint16_t*, uint16_t*);
 size_t wr_trellis_ws_bytes(int64_t rows, int64_t n, int32_t states);
+size_t wr_gemv_ws_bytes(int64_t n_store, int32_t batch);
+int wr_packed_gemv_impl(wr_ctx*, const uint8_t*, int64_t, int64_t, int32_t, int32_t, int32_t, const int8_t*, const float*,
+                        int64_t, int64_t, int32_t, float*, int64_t);
 int wr_trellis_quantize_impl(wr_ctx*, const float*, int64_t, int64_t, int64_t, int32_t, int32_t, const float*, int32_t,
                              uint8_t*, int64_t, float*, int64_t, double*);
 int wr_materialize_impl(wr_ctx*, const uint8_t*, int64_t, int64_t, int32_t, int32_t, int32_t, const int8_t*, int64_t,
@@ -90,6 +93,7 @@ size_t wr_workspace_bytes(int op, int64_t rows, int64_t n, int32_t group, int32_
     case WR_OP_WRING: return group > 0 ? wr_wring_ws_bytes(rows, n, group, rank > 0 ? rank : 0) : 0;
     case WR_OP_WRING_GPTQ: return group > 0 ? wr_wring_gptq_ws_bytes(rows, n, group, rank > 0 ? rank : 0) : 0;
     case WR_OP_TRELLIS: return group >= 2 && group <= 16 ? wr_trellis_ws_bytes(rows, n, group) : 0;
+    case WR_OP_GEMV: return rows >= 1 && rows <= 8 ? wr_gemv_ws_bytes(n, (int32_t)rows) : 0;
     default: return 0;
   }
 }
@@ -231,6 +235,24 @@ int wr_trellis_quantize(wr_ctx* ctx, const float* T, int64_t ldt, int64_t rows, 
   if (!ds.ok) return WR_EHIP;
   return wr_trellis_quantize_impl(ctx, T, ldt, rows, n, log2_states, coset_size, values, start_state, codes, ldc, recon,
                                   ldr, cost);
+}
+
+int wr_packed_gemv(wr_ctx* ctx, const uint8_t* in, size_t in_bytes, int64_t rows, int64_t n_store, int32_t bits,
+                   int32_t group, int32_t had_block, const int8_t* signs, const float* x, int64_t n_in, int64_t ldx,
+                   int32_t batch, float* y, int64_t ldy) {
+  if (!ctx || rows < 0 || n_store <= 0 || n_store > (1 << 24) || n_store % 32 != 0 || bits < 2 || bits > 4 ||
+      group <= 0 || group % 32 != 0 || n_store % group != 0 || batch < 1 || batch > 8 || n_in <= 0 || n_in > n_store ||
+      ldx < n_in || !x || !y || ldy < rows)
+    return WR_EINVAL;
+  if (rows > 2147483647 / 16) return WR_EINVAL;
+  if (had_block != 0 && (!signs || !pow2(had_block) || had_block < 2 || had_block > 4096 || n_store % had_block != 0))
+    return WR_EINVAL;
+  if (rows > 0 && (!in || !aligned(in, 16))) return WR_EINVAL;
+  const size_t need = (size_t)rows * n_store * bits / 8 + 2 * (size_t)rows * (n_store / group);
+  if (in_bytes != need) return WR_EINVAL;
+  DeviceScope ds(ctx->device);
+  if (!ds.ok) return WR_EHIP;
+  return wr_packed_gemv_impl(ctx, in, rows, n_store, bits, group, had_block, signs, x, n_in, ldx, batch, y, ldy);
 }
 
 const char* wr_strerror(int status) {
