@@ -13,7 +13,9 @@ the stream it runs on) and the CPU oracle timed on a bounded sample of the same
 workload on the host cores, and, outside the timed step, the materializer (packed
 module -> bf16 weights) against the HBM peak, the finisher variant with GPTQ
 codes (wring by a GPTQ sweep of the watered target instead of nearest-point
-codes), and the trellis-coded quantizer (Viterbi search) against the VALU peak.
+codes), the trellis-coded quantizer (Viterbi search) against the VALU peak, and
+the packed-module product (decode-time GEMV from the container) against the HBM
+peak.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras | --extras-only]
 """
@@ -215,6 +217,58 @@ def time_trellis(wr, ctx, torch, reps=5):
             "algorithmic_ops_per_weight": 140}
 
 
+def queued_ms(torch, ctx, fn, reps):
+    """GPU time per call of fn with the calls queued back to back: a spin kernel holds the stream
+    while the host enqueues the calls (so host-side overhead, larger than a few-microsecond call,
+    does not show as idle GPU time); checks that the spin outlasted the enqueueing."""
+    cycles = 20_000_000
+    for _ in range(6):
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s0.record(ctx.stream)
+        torch.cuda._sleep(cycles)
+        s1.record(ctx.stream)
+        e0.record(ctx.stream)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        host_ms = (time.perf_counter() - t0) * 1e3
+        e1.record(ctx.stream)
+        torch.cuda.synchronize()
+        if s0.elapsed_time(s1) > 1.2 * host_ms:
+            return e0.elapsed_time(e1) / reps
+        cycles *= 2
+    raise RuntimeError("the spin kernel did not cover the host's enqueueing")
+
+
+def time_gemv(wr, ctx, torch, reps=50):
+    """The packed-module product (decode-time use of the container) on one layer's 2560-wide group,
+    25600 x 2560, 2-bit, group 64, blocks of 512, one input vector.  HBM-bound: algorithmic bytes
+    = the packed codes and scales read once (the vector and the outputs are 0.6 % more).  Timed
+    with HIP events over `reps` calls queued back to back (each call: the input rotation and the
+    product)."""
+    rows, n, bits, g, m = 25600, 2560, 2, 64, 512
+    gen = torch.Generator(device="cuda").manual_seed(20261240)
+    code_bytes = rows * n * bits // 8
+    buf = torch.randint(0, 256, (wr.packed_nbytes(rows, n, bits, g),), dtype=torch.uint8, device="cuda", generator=gen)
+    sc = (torch.rand(rows * (n // g), device="cuda", generator=gen) * 0.029 + 1e-3).to(torch.float16)
+    buf[code_bytes:] = sc.view(torch.uint8)
+    signs = (torch.randint(0, 2, (n,), device="cuda", generator=gen) * 2 - 1).to(torch.int8)
+    x = torch.randn(1, n, device="cuda", generator=gen)
+    y = torch.empty(1, rows, dtype=torch.float32, device="cuda")
+    def call():
+        wr.wr_packed_gemv(ctx, buf, rows, n, bits, g, x, y, had_block=m, signs=signs)
+    for _ in range(3):
+        call()
+    ms = queued_ms(torch, ctx, call, reps)
+    nbytes = buf.numel()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"packed product {rows}x{n} 2-bit group {g}, blocks of {m}, 1 vector", "ms_per_call": ms,
+            "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+            "bytes_per_call": nbytes}
+
+
 def progress(msg):
     print(f"bench.py: {msg}", file=sys.stderr, flush=True)
 
@@ -295,7 +349,7 @@ def main():
         progress("timing the materializer and the GPTQ-codes finisher")
         print(json.dumps({"materialize": time_materialize(wr, ctx, torch),
                           "finisher_gptq": time_finisher_gptq(wr, ctx, torch, H, W, B, A, bits_t, cfg),
-                          "trellis": time_trellis(wr, ctx, torch)}), flush=True)
+                          "trellis": time_trellis(wr, ctx, torch), "gemv": time_gemv(wr, ctx, torch)}), flush=True)
         return
 
     progress(f"timing {args.steps} steps")
@@ -343,6 +397,8 @@ def main():
         line["finisher_gptq"] = time_finisher_gptq(wr, ctx, torch, H, W, B, A, bits_t, cfg)
         progress("timing the trellis quantizer")
         line["trellis"] = time_trellis(wr, ctx, torch)
+        progress("timing the packed-module product")
+        line["gemv"] = time_gemv(wr, ctx, torch)
     if not args.no_cpu_baseline:
         progress("timing the oracle on a bounded sample")
         Xh = X[: args.cpu_calib].float().cpu().numpy()

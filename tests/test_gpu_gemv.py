@@ -50,6 +50,7 @@ CASES = [  # rows, n_store, n_in, bits, group, had_block, batch
     (3, 4096, 4096, 2, 64, 4096, 2),
     (9, 96, 90, 2, 32, 32, 1),
     (40, 2560, 2560, 3, 64, 512, 5),
+    (20, 4096, 4096, 2, 64, 256, 6),  # x' too large for LDS: rotation kernel + product from global memory
 ]
 
 
