@@ -276,9 +276,32 @@ __device__ __forceinline__ void store_block64(const double* sM, double* __restri
   }
 }
 
+// The block column kb of the factor below the diagonal, L_ik = A_ik L_kk^-T for every block row
+// i > k, one workgroup per block row, written to L: the first phase of a step whose trailing
+// matrix has many tiles (then chol_step_kernel reads the panels instead of solving them in
+// every tile).
+__global__ __launch_bounds__(256) void chol_panel_kernel(const double* __restrict__ A, double* __restrict__ L,
+                                                         const double* __restrict__ Xin, int n, int kb,
+                                                         const int32_t* __restrict__ dev_info) {
+  if (*dev_info != 0) return;
+  __shared__ double sL[CB * CP];
+  __shared__ double sX[CB * CP];
+  __shared__ double sP[CB * CP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i0 = kb + CB + CB * blockIdx.x;
+  load_xd(Xin, sX, tid);
+  load_block64(L, n, kb, kb, n, n, sL, tid);
+  load_block64(A, n, i0, kb, n, n, sP, tid);
+  lds_sync();
+  panel_rows(sP, sL, sX, wave, lane);
+  lds_sync();
+  store_block64(sP, L, n, i0, kb, tid);
+}
+
 // Step kb, after the diagonal block kb is factored (L_kk in L, its inverted 16 x 16
 // diagonal blocks in Xin).  Every workgroup solves for the factor's blocks that it needs
-// from the block column A[.., kb..kb+63] itself, so no workgroup waits for another.
+// from the block column A[.., kb..kb+63] itself, so no workgroup waits for another; with
+// panels_ready those blocks are already in L (chol_panel_kernel) and are read instead.
 //   workgroup 0:   L_{k+1,k}, then the next diagonal block A_{k+1,k+1} - L_{k+1,k} L_{k+1,k}^T,
 //                  factored and inverted (to L and Xout), then L_{k+1,k} to L;
 //   workgroup t:   trailing lower tile (ti, tj) != (0, 0): L_ik, L_jk, A_ij -= L_ik L_jk^T;
@@ -286,7 +309,7 @@ __device__ __forceinline__ void store_block64(const double* sM, double* __restri
 // Xin and Xout are different buffers (workgroup 0 writes Xout while the others read Xin).
 __global__ __launch_bounds__(256) void chol_step_kernel(double* __restrict__ A, double* __restrict__ L,
                                                         const double* __restrict__ Xin, double* __restrict__ Xout,
-                                                        int n, int kb, int32_t* __restrict__ dev_info) {
+                                                        int n, int kb, int panels_ready, int32_t* __restrict__ dev_info) {
   if (*dev_info != 0) return;
   __shared__ double sL[CB * CP];
   __shared__ double sX[CB * CP];
@@ -296,15 +319,22 @@ __global__ __launch_bounds__(256) void chol_step_kernel(double* __restrict__ A, 
   const int base = kb + CB;
   const f64x4 zero = {0.0, 0.0, 0.0, 0.0};
   if (blockIdx.x == 0) {
-    load_xd(Xin, sX, tid);
-    load_block64(L, n, kb, kb, n, n, sL, tid);
-    load_block64(A, n, base, kb, n, n, sP, tid);
-    load_block64(A, n, base, base, n, n, sQ, tid);
-    lds_sync();
-    pad_diag(sQ, n, base, tid);
-    panel_rows(sP, sL, sX, wave, lane);
-    lds_sync();
-    store_block64(sP, L, n, base, kb, tid);  // L_{k+1,k}; nothing in this kernel reads it back
+    if (panels_ready) {
+      load_block64(L, n, base, kb, n, n, sP, tid);
+      load_block64(A, n, base, base, n, n, sQ, tid);
+      lds_sync();
+      pad_diag(sQ, n, base, tid);
+    } else {
+      load_xd(Xin, sX, tid);
+      load_block64(L, n, kb, kb, n, n, sL, tid);
+      load_block64(A, n, base, kb, n, n, sP, tid);
+      load_block64(A, n, base, base, n, n, sQ, tid);
+      lds_sync();
+      pad_diag(sQ, n, base, tid);
+      panel_rows(sP, sL, sX, wave, lane);
+      lds_sync();
+      store_block64(sP, L, n, base, kb, tid);  // L_{k+1,k}; nothing in this kernel reads it back
+    }
     // next diagonal block sQ -= sP sP^T: wave 0 takes the first 16 x 16 block and factors it
     // at once, waves 1-3 take the other nine lower blocks
     int bad0 = -1;
@@ -351,15 +381,21 @@ __global__ __launch_bounds__(256) void chol_step_kernel(double* __restrict__ A, 
         const int gj = j0 + 32 * wj + 16 * y + (lane & 15);
         cur[x][y][v] = active && gi < n && gj < n ? A[(int64_t)gi * n + gj] : 0.0;
       }
-  load_xd(Xin, sX, tid);
-  load_block64(L, n, kb, kb, n, n, sL, tid);
-  load_block64(A, n, i0, kb, n, n, sP, tid);
-  if (!diag) load_block64(A, n, j0, kb, n, n, sQ, tid);
-  lds_sync();
-  panel_rows(sP, sL, sX, wave, lane);
-  if (!diag) panel_rows(sQ, sL, sX, wave, lane);
-  lds_sync();
-  if (tj == 0) store_block64(sP, L, n, i0, kb, tid);
+  if (panels_ready) {
+    load_block64(L, n, i0, kb, n, n, sP, tid);
+    if (!diag) load_block64(L, n, j0, kb, n, n, sQ, tid);
+    lds_sync();
+  } else {
+    load_xd(Xin, sX, tid);
+    load_block64(L, n, kb, kb, n, n, sL, tid);
+    load_block64(A, n, i0, kb, n, n, sP, tid);
+    if (!diag) load_block64(A, n, j0, kb, n, n, sQ, tid);
+    lds_sync();
+    panel_rows(sP, sL, sX, wave, lane);
+    if (!diag) panel_rows(sQ, sL, sX, wave, lane);
+    lds_sync();
+    if (tj == 0) store_block64(sP, L, n, i0, kb, tid);
+  }
   if (!active) return;
   const double* Pj = diag ? sP : sQ;
 #pragma unroll
@@ -375,6 +411,10 @@ __global__ __launch_bounds__(256) void chol_step_kernel(double* __restrict__ A, 
       }
     }
 }
+
+// Block rows of the trailing matrix from which a step solves its panel blocks in a phase of
+// their own (measured at n = 2560: 1.006 ms with 24, 1.069 ms with the single phase throughout).
+static const int kTwoPhaseTiles = 24;
 
 // A = J H J (lower triangle), widened to fp64.
 __global__ void reverse_copy_kernel(const float* __restrict__ H, int64_t ldh, int n, double* __restrict__ A) {
@@ -419,8 +459,14 @@ int wr_factor_m(hipStream_t st, const float* H, int64_t ldh, int n, void* ws, fl
   WR_CHECK_LAUNCH();
   for (int kb = 0, s = 0; kb + CB < n; kb += CB, ++s) {
     const int nt = (n - kb - CB + CB - 1) / CB;
+    // many trailing tiles: solve each panel block once first instead of in every tile
+    const int two_phase = nt >= kTwoPhaseTiles ? 1 : 0;
+    if (two_phase) {
+      hipLaunchKernelGGL(chol_panel_kernel, dim3(nt), dim3(256), 0, st, A, Lf, Xinv[s & 1], n, kb, dev_info);
+      WR_CHECK_LAUNCH();
+    }
     hipLaunchKernelGGL(chol_step_kernel, dim3(nt * (nt + 1) / 2), dim3(256), 0, st, A, Lf, Xinv[s & 1],
-                       Xinv[(s + 1) & 1], n, kb, dev_info);
+                       Xinv[(s + 1) & 1], n, kb, two_phase, dev_info);
     WR_CHECK_LAUNCH();
   }
   hipLaunchKernelGGL(build_m_kernel, dim3(n), dim3(256), 0, st, Lf, n, M, dev_info);
