@@ -12,8 +12,7 @@
 // lanes and keeps the cheaper (the smaller predecessor on a tie); the decision bit goes into a
 // word written every 32 steps to a step-major workspace (coalesced).  Costs are renormalised by
 // the row's minimum every 16 steps, so fp32 keeps the differences that decide the path.  The
-// traceback runs on every lane of the row (the same path), reading the S decision words of a
-// 32-step chunk at a time; lane j writes the codes of the steps with k % S == j.
+// traceback is a second kernel with one lane per row.
 #include "common.hpp"
 
 namespace wr {
@@ -52,9 +51,7 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ t, int ch, 
 template <int LOGS, int C>
 __global__ __launch_bounds__(256) void trellis_viterbi_kernel(const float* __restrict__ T, int64_t ldt, int64_t rows,
                                                               int n, const float* __restrict__ values, int start,
-                                                              uint32_t* __restrict__ bp, uint8_t* __restrict__ codes,
-                                                              int64_t ldc, float* __restrict__ recon, int64_t ldr,
-                                                              double* __restrict__ cost_out) {
+                                                              uint32_t* __restrict__ bp, int32_t* __restrict__ end_state) {
   constexpr int S = 1 << LOGS;
   __shared__ float tab[S * 2 * C];
   for (int i = threadIdx.x; i < S * 2 * C; i += blockDim.x) tab[i] = values[i];
@@ -121,10 +118,39 @@ __global__ __launch_bounds__(256) void trellis_viterbi_kernel(const float* __res
       bs = os;
     }
   }
-  __syncthreads();  // the row's decision words (written by its S lanes) are visible
-  // traceback, the same path on every lane of the row
-  int cur = bs;
+  if (live && s == 0) end_state[row] = bs;
+}
+
+// Traceback, one lane per row: from the cheapest end state back through the decision words
+// (the S words of a 32-step chunk read together, the next chunk's words and targets requested
+// before the current chunk is walked); writes codes u | v << 1, the decoded values and the
+// path's fp64 cost.
+template <int LOGS, int C>
+__global__ __launch_bounds__(256) void trellis_traceback_kernel(const float* __restrict__ T, int64_t ldt, int64_t rows,
+                                                                int n, const float* __restrict__ values,
+                                                                const uint32_t* __restrict__ bp,
+                                                                const int32_t* __restrict__ end_state,
+                                                                uint8_t* __restrict__ codes, int64_t ldc,
+                                                                float* __restrict__ recon, int64_t ldr,
+                                                                double* __restrict__ cost_out) {
+  constexpr int S = 1 << LOGS;
+  __shared__ float tab[S * 2 * C];
+  for (int i = threadIdx.x; i < S * 2 * C; i += blockDim.x) tab[i] = values[i];
+  __syncthreads();
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= rows) return;
+  const float* t = T + row * ldt;
+  const int64_t stride = rows * S;
+  const int nchunk = (n + 31) >> 5;
+  float xs[32], nx[32];
+  int cur = end_state[row];
   double acc = 0.0;
+  // codes and values of a 16-step block collect in registers and go out in one 16-byte (or four)
+  // stores when the block is whole and the rows aligned
+  const bool vec = ldc % 16 == 0 && (reinterpret_cast<uintptr_t>(codes) & 15) == 0 &&
+                   (!recon || (ldr % 4 == 0 && (reinterpret_cast<uintptr_t>(recon) & 15) == 0));
+  uint32_t cw[4] = {0u, 0u, 0u, 0u};
+  float rv[16];
   uint32_t w[S], nw[S];
   const uint32_t* src = bp + (int64_t)(nchunk - 1) * stride + row * S;
 #pragma unroll
@@ -164,11 +190,30 @@ __global__ __launch_bounds__(256) void trellis_viterbi_kernel(const float* __res
         }
         const double dd = (double)x - (double)rb;
         acc = fma(dd, dd, acc);
-        if (live && (k & (S - 1)) == s) {
-          codes[row * ldc + k] = (uint8_t)(uu | (vb << 1));
-          if (recon) recon[row * ldr + k] = rb;
-        }
+        cw[(j >> 2) & 3] |= (uint32_t)(uu | (vb << 1)) << (8 * (j & 3));
+        rv[j & 15] = rb;
         cur = p;
+      }
+      if ((j & 15) == 0) {  // the block of steps [k, k + 16) is done
+        uint8_t* cd = codes + row * ldc + k;
+        float* rd = recon ? recon + row * ldr + k : nullptr;
+        if (vec && k + 16 <= n) {
+          *reinterpret_cast<u32x4*>(cd) = u32x4{cw[0], cw[1], cw[2], cw[3]};
+          if (rd) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<f32x4*>(rd + 4 * q) = f32x4{rv[4 * q], rv[4 * q + 1], rv[4 * q + 2], rv[4 * q + 3]};
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (k + e < n) {
+              cd[e] = (uint8_t)(cw[e >> 2] >> (8 * (e & 3)));
+              if (rd) rd[e] = rv[e];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cw[q] = 0u;
       }
     }
     if (ch > 0) {
@@ -178,7 +223,7 @@ __global__ __launch_bounds__(256) void trellis_viterbi_kernel(const float* __res
       for (int j = 0; j < 32; ++j) xs[j] = nx[j];
     }
   }
-  if (live && s == 0 && cost_out) cost_out[row] = acc;
+  if (cost_out) cost_out[row] = acc;
 }
 
 }  // namespace wr
@@ -186,7 +231,7 @@ __global__ __launch_bounds__(256) void trellis_viterbi_kernel(const float* __res
 using namespace wr;
 
 size_t wr_trellis_ws_bytes(int64_t rows, int64_t n, int32_t states) {
-  return (size_t)((n + 31) / 32) * (size_t)rows * (size_t)states * 4;
+  return (((size_t)((n + 31) / 32) * (size_t)rows * (size_t)states * 4 + 255) & ~(size_t)255) + (size_t)rows * 4;
 }
 
 int wr_trellis_quantize_impl(wr_ctx* ctx, const float* T, int64_t ldt, int64_t rows, int64_t n, int32_t log2_states,
@@ -196,10 +241,15 @@ int wr_trellis_quantize_impl(wr_ctx* ctx, const float* T, int64_t ldt, int64_t r
   const int S = 1 << log2_states;
   if (ctx->ws_bytes < wr_trellis_ws_bytes(rows, n, S)) return WR_EWORKSPACE;
   uint32_t* bp = static_cast<uint32_t*>(ctx->ws);
+  int32_t* end_state = reinterpret_cast<int32_t*>(
+      static_cast<char*>(ctx->ws) + (((size_t)((n + 31) / 32) * (size_t)rows * S * 4 + 255) & ~(size_t)255));
   const dim3 grid((unsigned)((rows * S + 255) / 256));
-#define WR_TRL(LS, CC)                                                                                             \
-  hipLaunchKernelGGL((trellis_viterbi_kernel<LS, CC>), grid, dim3(256), 0, ctx->stream, T, ldt, rows, (int)n, values, \
-                     start_state, bp, codes, ldc, recon, ldr, cost)
+  const dim3 tgrid((unsigned)((rows + 255) / 256));
+#define WR_TRL(LS, CC)                                                                                                \
+  hipLaunchKernelGGL((trellis_viterbi_kernel<LS, CC>), grid, dim3(256), 0, ctx->stream, T, ldt, rows, (int)n, values,    \
+                     start_state, bp, end_state);                                                                       \
+  hipLaunchKernelGGL((trellis_traceback_kernel<LS, CC>), tgrid, dim3(256), 0, ctx->stream, T, ldt, rows, (int)n, values, \
+                     bp, end_state, codes, ldc, recon, ldr, cost)
 #define WR_TRL_C(LS)               \
   switch (coset_size) {            \
     case 1: WR_TRL(LS, 1); break;  \
