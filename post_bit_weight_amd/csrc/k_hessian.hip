@@ -107,8 +107,6 @@ __global__ __launch_bounds__(SY_THREADS, 1) void syrk_bf16_kernel(const uint16_t
   }
   int I, J;
   tri_tile(tile, I, J);
-  // a diagonal tile of XA^T XA takes both operands from one panel: half the DMAs per stage
-  const bool one_panel = I == J && XA == XB;
   const int64_t r0 = (int64_t)split * rows_per_split;
   const int64_t r1 = r0 + rows_per_split < rows ? r0 + rows_per_split : rows;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -133,10 +131,8 @@ __global__ __launch_bounds__(SY_THREADS, 1) void syrk_bf16_kernel(const uint16_t
       const uint16_t* gb = XB + k0 * ldx;
 #pragma unroll
       for (int u = 0; u < 2; ++u) lds_dma16(ga, offA[u], sbase + (2 * wave + u) * 1024);
-      if (!one_panel) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) lds_dma16(gb, offB[u], sbase + SY_PANEL + (2 * wave + u) * 1024);
-      }
+      for (int u = 0; u < 2; ++u) lds_dma16(gb, offB[u], sbase + SY_PANEL + (2 * wave + u) * 1024);
     } else {
       // ragged last stage: bounds-checked loads through registers, zeros past r1
       lds_char* dst = lds + slot * SY_STAGE_BYTES;
@@ -149,7 +145,7 @@ __global__ __launch_bounds__(SY_THREADS, 1) void syrk_bf16_kernel(const uint16_t
           vb = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(XB + k0 * ldx) + offB[u]);
         }
         *(__attribute__((address_space(3))) u32x4*)(dst + ldsoff[u]) = va;
-        if (!one_panel) *(__attribute__((address_space(3))) u32x4*)(dst + SY_PANEL + ldsoff[u]) = vb;
+        *(__attribute__((address_space(3))) u32x4*)(dst + SY_PANEL + ldsoff[u]) = vb;
       }
     }
   };
@@ -168,7 +164,7 @@ __global__ __launch_bounds__(SY_THREADS, 1) void syrk_bf16_kernel(const uint16_t
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
       const int f = 64 * wj + 32 * y + 16 * (g & 1) + 4 * q;
-      rdB[y] = (one_panel ? 0 : SY_PANEL) + krow * (SY_T * 2) + (((f >> 3) ^ (4 * t)) << 4) + (f & 7) * 2;
+      rdB[y] = SY_PANEL + krow * (SY_T * 2) + (((f >> 3) ^ (4 * t)) << 4) + (f & 7) * 2;
     }
   }
 
@@ -202,10 +198,7 @@ __global__ __launch_bounds__(SY_THREADS, 1) void syrk_bf16_kernel(const uint16_t
   for (int64_t p = 0; p < SY_PF && p < nst; ++p) issue(p, (int)p);
   if (nst > 0) {
     if (nst - 1 > SY_PF - 1) {
-      if (one_panel)
-        vm_wait<SY_DMA_PER_WAVE / 2 * (SY_PF - 1)>();
-      else
-        vm_wait<SY_DMA_PER_WAVE * (SY_PF - 1)>();
+      vm_wait<SY_DMA_PER_WAVE * (SY_PF - 1)>();
     } else {
       vm_wait<0>();
     }
@@ -222,10 +215,7 @@ __global__ __launch_bounds__(SY_THREADS, 1) void syrk_bf16_kernel(const uint16_t
       // are outstanding; those are all full DMA stages unless the ragged last one
       // (or a stage past the end) is among them.
       if (s + SY_PF - 1 <= nst - 2) {
-        if (one_panel)
-          vm_wait<SY_DMA_PER_WAVE / 2 * (SY_PF - 2)>();
-        else
-          vm_wait<SY_DMA_PER_WAVE * (SY_PF - 2)>();
+        vm_wait<SY_DMA_PER_WAVE * (SY_PF - 2)>();
       } else {
         vm_wait<0>();
       }
@@ -279,8 +269,6 @@ __global__ void syrk_reduce_kernel(const float* __restrict__ partial, int ksplit
   const int tile = blockIdx.y;
   int I, J;
   tri_tile(tile, I, J);
-  // a diagonal tile of XA^T XA takes both operands from one panel: half the DMAs per stage
-  const bool one_panel = I == J && XA == XB;
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= SY_T * SY_T) return;
   const int ii = e / SY_T, jj = e - ii * SY_T;

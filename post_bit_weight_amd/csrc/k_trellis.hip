@@ -226,6 +226,231 @@ __global__ __launch_bounds__(256) void trellis_traceback_kernel(const float* __r
   if (cost_out) cost_out[row] = acc;
 }
 
+// Two steps per exchange (S >= 4).  After two steps state s'' = (4 p + 2 u1 + u2) mod S comes
+// from one of four states two steps back, p_j = (s'' >> 2) + j S/4, through the middle state
+// mid_a = s'' >> 1 (from p_0 or p_2) or mid_b = mid_a + S/2 (from p_1 or p_3).  Taking the
+// cheaper of each pair (the smaller state on a tie), then the cheaper middle state (mid_a on a
+// tie), with the costs added in the same order, is the one-step algorithm's decisions and
+// fp32 rounding exactly, with one round of lane exchanges per two steps.  Decision: 2 bits per
+// state and pair of steps (bit 0: mid_b taken; bit 1: the chosen middle state came from its
+// larger predecessor).  An odd last step is paired with a step of zero cost.
+template <int LOGS, int C>
+__global__ __launch_bounds__(256) void trellis_viterbi2_kernel(const float* __restrict__ T, int64_t ldt, int64_t rows,
+                                                               int n, const float* __restrict__ values, int start,
+                                                               uint32_t* __restrict__ bp, int32_t* __restrict__ end_state) {
+  constexpr int S = 1 << LOGS;
+  static_assert(S >= 4, "two steps per exchange need four predecessors");
+  __shared__ float tab[S * 2 * C];
+  for (int i = threadIdx.x; i < S * 2 * C; i += blockDim.x) tab[i] = values[i];
+  __syncthreads();
+  const int s = threadIdx.x & (S - 1);
+  const int gbase = (threadIdx.x & 63) & ~(S - 1);
+  const int64_t row0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> LOGS;
+  const bool live = row0 < rows;
+  const int64_t row = live ? row0 : rows - 1;  // every lane takes part in the exchanges
+  const float* t = T + row * ldt;
+  const int q = s >> 2, u1 = (s >> 1) & 1, u2 = s & 1;
+  const int ma = s >> 1, mb = ma + S / 2;
+  int plane[4];
+  float va[4][C], vma[C], vmb[C];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int pj = q + j * (S / 4);
+    plane[j] = gbase + pj;
+#pragma unroll
+    for (int c = 0; c < C; ++c) va[j][c] = tab[(pj * 2 + u1) * C + c];
+  }
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    vma[c] = tab[(ma * 2 + u2) * C + c];
+    vmb[c] = tab[(mb * 2 + u2) * C + c];
+  }
+  const int64_t stride = rows * S;  // words per 32-step chunk
+  const int nchunk = (n + 31) >> 5;
+  float cost = s == start ? 0.0f : INFINITY;
+  float xs[32], nx[32];
+  load_chunk(t, 0, n, xs);
+  for (int ch = 0; ch < nchunk; ++ch) {
+    if (ch + 1 < nchunk) load_chunk(t, ch + 1, n, nx);
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int k = ch * 32 + 2 * i;
+      if (k < n) {
+        const float x1 = xs[2 * i], x2 = xs[2 * i + 1];
+        float pc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pc[j] = __shfl(cost, plane[j]);
+        float b1[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          b1[j] = INFINITY;
+#pragma unroll
+          for (int c = 0; c < C; ++c) {
+            const float d = x1 - va[j][c];
+            b1[j] = fminf(b1[j], d * d);
+          }
+        }
+        const float ca0 = pc[0] + b1[0], ca1 = pc[2] + b1[2];
+        const float cb0 = pc[1] + b1[1], cb1 = pc[3] + b1[3];
+        const bool upa = ca1 < ca0, upb = cb1 < cb0;  // a tie keeps the smaller state
+        const float cA = upa ? ca1 : ca0, cB = upb ? cb1 : cb0;
+        float ba = 0.0f, bb = 0.0f;  // an odd last step is paired with a step of zero cost
+        if (k + 1 < n) {
+          ba = INFINITY;
+          bb = INFINITY;
+#pragma unroll
+          for (int c = 0; c < C; ++c) {
+            const float da = x2 - vma[c], db = x2 - vmb[c];
+            ba = fminf(ba, da * da);
+            bb = fminf(bb, db * db);
+          }
+        }
+        const float fa = cA + ba, fb = cB + bb;
+        const bool up2 = fb < fa;
+        cost = up2 ? fb : fa;
+        word |= ((uint32_t)up2 | ((uint32_t)(up2 ? upb : upa) << 1)) << (2 * i);
+        if ((i & 7) == 7) {
+          float m = cost;
+#pragma unroll
+          for (int o = 1; o < S; o <<= 1) m = fminf(m, __shfl_xor(m, o));
+          cost -= m;
+        }
+      }
+    }
+    if (live) bp[(int64_t)ch * stride + row * S + s] = word;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) xs[j] = nx[j];
+  }
+  float bc = cost;
+  int bs = s;
+#pragma unroll
+  for (int o = 1; o < S; o <<= 1) {
+    const float oc = __shfl_xor(bc, o);
+    const int os = __shfl_xor(bs, o);
+    if (oc < bc || (oc == bc && os < bs)) {
+      bc = oc;
+      bs = os;
+    }
+  }
+  if (live && s == 0) end_state[row] = bs;
+}
+
+// Traceback of trellis_viterbi2_kernel, one lane per row, two steps per decision.
+template <int LOGS, int C>
+__global__ __launch_bounds__(256) void trellis_traceback2_kernel(const float* __restrict__ T, int64_t ldt, int64_t rows,
+                                                                 int n, const float* __restrict__ values,
+                                                                 const uint32_t* __restrict__ bp,
+                                                                 const int32_t* __restrict__ end_state,
+                                                                 uint8_t* __restrict__ codes, int64_t ldc,
+                                                                 float* __restrict__ recon, int64_t ldr,
+                                                                 double* __restrict__ cost_out) {
+  constexpr int S = 1 << LOGS;
+  __shared__ float tab[S * 2 * C];
+  for (int i = threadIdx.x; i < S * 2 * C; i += blockDim.x) tab[i] = values[i];
+  __syncthreads();
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= rows) return;
+  const float* t = T + row * ldt;
+  const int64_t stride = rows * S;
+  const int nchunk = (n + 31) >> 5;
+  const bool vec = ldc % 16 == 0 && (reinterpret_cast<uintptr_t>(codes) & 15) == 0 &&
+                   (!recon || (ldr % 4 == 0 && (reinterpret_cast<uintptr_t>(recon) & 15) == 0));
+  float xs[32], nx[32];
+  int cur = end_state[row];
+  double acc = 0.0;
+  uint32_t cw[4] = {0u, 0u, 0u, 0u};
+  float rv[16];
+  uint32_t w[S], nw[S];
+  const uint32_t* src = bp + (int64_t)(nchunk - 1) * stride + row * S;
+#pragma unroll
+  for (int j = 0; j < S; ++j) w[j] = src[j];
+  load_chunk(t, nchunk - 1, n, xs);
+  // nearest value of the coset of branch (p, u) to x: code u | v << 1 and the value
+  auto choose = [&](int p, int u, float x, uint32_t& code, float& val) {
+    const float* cs = tab + (p * 2 + u) * C;
+    int vb = 0;
+    float rb = cs[0];
+    float db = (x - rb) * (x - rb);
+#pragma unroll
+    for (int c = 1; c < C; ++c) {
+      const float v = cs[c];
+      const float d = (x - v) * (x - v);
+      if (d < db) {  // a tie keeps the smaller index
+        db = d;
+        rb = v;
+        vb = c;
+      }
+    }
+    code = (uint32_t)(u | (vb << 1));
+    val = rb;
+  };
+  for (int ch = nchunk - 1; ch >= 0; --ch) {
+    if (ch > 0) {
+      const uint32_t* ps = bp + (int64_t)(ch - 1) * stride + row * S;
+#pragma unroll
+      for (int j = 0; j < S; ++j) nw[j] = ps[j];
+      load_chunk(t, ch - 1, n, nx);
+    }
+#pragma unroll
+    for (int i = 15; i >= 0; --i) {
+      const int k = ch * 32 + 2 * i;
+      if (k < n) {
+        uint32_t wd = w[0];
+#pragma unroll
+        for (int q = 1; q < S; ++q) wd = cur == q ? w[q] : wd;
+        const uint32_t d = (wd >> (2 * i)) & 3u;
+        const int mid = (cur >> 1) + (int)(d & 1u) * (S / 2);
+        const int p = (mid >> 1) + (int)(d >> 1) * (S / 2);
+        uint32_t code;
+        float val;
+        if (k + 1 < n) {
+          choose(mid, cur & 1, xs[2 * i + 1], code, val);
+          const double dd = (double)xs[2 * i + 1] - (double)val;
+          acc = fma(dd, dd, acc);
+          cw[((2 * i + 1) >> 2) & 3] |= code << (8 * ((2 * i + 1) & 3));
+          rv[(2 * i + 1) & 15] = val;
+        }
+        choose(p, mid & 1, xs[2 * i], code, val);
+        const double dd = (double)xs[2 * i] - (double)val;
+        acc = fma(dd, dd, acc);
+        cw[((2 * i) >> 2) & 3] |= code << (8 * ((2 * i) & 3));
+        rv[(2 * i) & 15] = val;
+        cur = p;
+      }
+      if ((i & 7) == 0) {  // the block of steps [k, k + 16) is done
+        uint8_t* cd = codes + row * ldc + k;
+        float* rd = recon ? recon + row * ldr + k : nullptr;
+        if (vec && k + 16 <= n) {
+          *reinterpret_cast<u32x4*>(cd) = u32x4{cw[0], cw[1], cw[2], cw[3]};
+          if (rd) {
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+              *reinterpret_cast<f32x4*>(rd + 4 * qq) =
+                  f32x4{rv[4 * qq], rv[4 * qq + 1], rv[4 * qq + 2], rv[4 * qq + 3]};
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (k + e < n) {
+              cd[e] = (uint8_t)(cw[e >> 2] >> (8 * (e & 3)));
+              if (rd) rd[e] = rv[e];
+            }
+        }
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) cw[qq] = 0u;
+      }
+    }
+    if (ch > 0) {
+#pragma unroll
+      for (int j = 0; j < S; ++j) w[j] = nw[j];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) xs[j] = nx[j];
+    }
+  }
+  if (cost_out) cost_out[row] = acc;
+}
+
 }  // namespace wr
 
 using namespace wr;
@@ -250,19 +475,26 @@ int wr_trellis_quantize_impl(wr_ctx* ctx, const float* T, int64_t ldt, int64_t r
                      start_state, bp, end_state);                                                                       \
   hipLaunchKernelGGL((trellis_traceback_kernel<LS, CC>), tgrid, dim3(256), 0, ctx->stream, T, ldt, rows, (int)n, values, \
                      bp, end_state, codes, ldc, recon, ldr, cost)
-#define WR_TRL_C(LS)               \
-  switch (coset_size) {            \
-    case 1: WR_TRL(LS, 1); break;  \
-    case 2: WR_TRL(LS, 2); break;  \
-    default: WR_TRL(LS, 4); break; \
+#define WR_TRL2(LS, CC)                                                                                               \
+  hipLaunchKernelGGL((trellis_viterbi2_kernel<LS, CC>), grid, dim3(256), 0, ctx->stream, T, ldt, rows, (int)n, values,    \
+                     start_state, bp, end_state);                                                                        \
+  hipLaunchKernelGGL((trellis_traceback2_kernel<LS, CC>), tgrid, dim3(256), 0, ctx->stream, T, ldt, rows, (int)n, values, \
+                     bp, end_state, codes, ldc, recon, ldr, cost)
+#define WR_TRL_C(M, LS)                \
+  switch (coset_size) {                \
+    case 1: M(LS, 1); break;           \
+    case 2: M(LS, 2); break;           \
+    default: M(LS, 4); break;          \
   }
+  // one step per exchange for 2 states, two steps per exchange from 4 states on
   switch (log2_states) {
-    case 1: WR_TRL_C(1); break;
-    case 2: WR_TRL_C(2); break;
-    case 3: WR_TRL_C(3); break;
-    default: WR_TRL_C(4); break;
+    case 1: WR_TRL_C(WR_TRL, 1); break;
+    case 2: WR_TRL_C(WR_TRL2, 2); break;
+    case 3: WR_TRL_C(WR_TRL2, 3); break;
+    default: WR_TRL_C(WR_TRL2, 4); break;
   }
 #undef WR_TRL_C
+#undef WR_TRL2
 #undef WR_TRL
   WR_CHECK_LAUNCH();
   return WR_OK;
