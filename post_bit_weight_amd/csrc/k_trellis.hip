@@ -12,10 +12,12 @@
 // lanes and keeps the cheaper (the smaller predecessor on a tie); the decision bit goes into a
 // word written every 32 steps to a step-major workspace (coalesced).  Costs are renormalised by
 // the row's minimum every 16 steps, so fp32 keeps the differences that decide the path.  The
-// traceback is a second kernel with one lane per row.
+// traceback is a second kernel.
 #include "common.hpp"
 
 namespace wr {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Cost of the predecessor p0 = s >> 1 (J = 0) or p1 = p0 + S/2 (J = 1) of this lane's state:
 // quad_perm patterns for S = 2 ([0,0,2,2], [1,1,3,3]) and S = 4 ([0,0,1,1], [2,2,3,3]), a lane
@@ -281,15 +283,15 @@ __global__ __launch_bounds__(256) void trellis_viterbi2_kernel(const float* __re
         float pc[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) pc[j] = __shfl(cost, plane[j]);
+        // the smallest squared distance to a coset is the square of the smallest distance
+        // (squaring and its rounding are monotone): one min with |.| operands per value
         float b1[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          b1[j] = INFINITY;
+          float m = fabsf(x1 - va[j][0]);
 #pragma unroll
-          for (int c = 0; c < C; ++c) {
-            const float d = x1 - va[j][c];
-            b1[j] = fminf(b1[j], d * d);
-          }
+          for (int c = 1; c < C; ++c) m = fminf(m, fabsf(x1 - va[j][c]));
+          b1[j] = m * m;
         }
         const float ca0 = pc[0] + b1[0], ca1 = pc[2] + b1[2];
         const float cb0 = pc[1] + b1[1], cb1 = pc[3] + b1[3];
@@ -297,14 +299,14 @@ __global__ __launch_bounds__(256) void trellis_viterbi2_kernel(const float* __re
         const float cA = upa ? ca1 : ca0, cB = upb ? cb1 : cb0;
         float ba = 0.0f, bb = 0.0f;  // an odd last step is paired with a step of zero cost
         if (k + 1 < n) {
-          ba = INFINITY;
-          bb = INFINITY;
+          float ma2 = fabsf(x2 - vma[0]), mb2 = fabsf(x2 - vmb[0]);
 #pragma unroll
-          for (int c = 0; c < C; ++c) {
-            const float da = x2 - vma[c], db = x2 - vmb[c];
-            ba = fminf(ba, da * da);
-            bb = fminf(bb, db * db);
+          for (int c = 1; c < C; ++c) {
+            ma2 = fminf(ma2, fabsf(x2 - vma[c]));
+            mb2 = fminf(mb2, fabsf(x2 - vmb[c]));
           }
+          ba = ma2 * ma2;
+          bb = mb2 * mb2;
         }
         const float fa = cA + ba, fb = cB + bb;
         const bool up2 = fb < fa;
@@ -317,6 +319,20 @@ __global__ __launch_bounds__(256) void trellis_viterbi2_kernel(const float* __re
           cost -= m;
         }
       }
+    }
+    // transpose the row's S words so that the traceback finds a state's decision with one
+    // bit-field read: split each word into S fields of E = 32/S bits (P = 16/S steps pairs each);
+    // afterwards word j holds field j of every state, state r's at bits E r.  One exchange per
+    // bit of the lane index swaps that bit between the lane and field indices.
+    constexpr int E = 32 / S;
+#pragma unroll
+    for (int o = 1; o < S; o <<= 1) {
+      uint32_t mo = 0u;
+#pragma unroll
+      for (int e = 0; e < S; ++e)
+        if (e & o) mo |= ((1u << E) - 1u) << (E * e);
+      const uint32_t other = (uint32_t)__shfl_xor((int)word, o);
+      word = (s & o) ? (word & mo) | ((other >> (E * o)) & ~mo) : (word & ~mo) | ((other << (E * o)) & mo);
     }
     if (live) bp[(int64_t)ch * stride + row * S + s] = word;
 #pragma unroll
@@ -336,7 +352,12 @@ __global__ __launch_bounds__(256) void trellis_viterbi2_kernel(const float* __re
   if (live && s == 0) end_state[row] = bs;
 }
 
-// Traceback of trellis_viterbi2_kernel, one lane per row, two steps per decision.
+// Traceback of trellis_viterbi2_kernel, two lanes per row: both walk the row's states through
+// every chunk of 32 steps (one bit-field read of the transposed decision words per pair of
+// steps), and lane h then decodes steps [16 h, 16 h + 16) of the chunk: the coset values of its
+// 16 branches are read from LDS together, the nearest value of each taken (the smaller index on
+// a tie), and its codes and values are written as whole 16-byte vectors.  The path's squared
+// error is summed in fp64 per lane, the two halves added at the end.
 template <int LOGS, int C>
 __global__ __launch_bounds__(256) void trellis_traceback2_kernel(const float* __restrict__ T, int64_t ldt, int64_t rows,
                                                                  int n, const float* __restrict__ values,
@@ -346,109 +367,147 @@ __global__ __launch_bounds__(256) void trellis_traceback2_kernel(const float* __
                                                                  float* __restrict__ recon, int64_t ldr,
                                                                  double* __restrict__ cost_out) {
   constexpr int S = 1 << LOGS;
-  __shared__ float tab[S * 2 * C];
+  constexpr int E = 32 / S, P = 16 / S;  // bits per state field of a word, step pairs per field
+  __shared__ __align__(16) float tab[S * 2 * C];
   for (int i = threadIdx.x; i < S * 2 * C; i += blockDim.x) tab[i] = values[i];
   __syncthreads();
-  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (row >= rows) return;
-  const float* t = T + row * ldt;
+  const int h = threadIdx.x & 1;
+  const int64_t row0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 1;
+  const bool live = row0 < rows;
+  const int64_t row = live ? row0 : rows - 1;
+  const float* t = T + row * ldt + 16 * h;
   const int64_t stride = rows * S;
   const int nchunk = (n + 31) >> 5;
   const bool vec = ldc % 16 == 0 && (reinterpret_cast<uintptr_t>(codes) & 15) == 0 &&
                    (!recon || (ldr % 4 == 0 && (reinterpret_cast<uintptr_t>(recon) & 15) == 0));
-  float xs[32], nx[32];
+  // this lane's 16 targets of chunk ch (zeros past n)
+  auto load_half = [&](int ch, float (&x)[16]) {
+    const int k0 = ch * 32 + 16 * h;
+    if (k0 + 16 <= n) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(t + ch * 32 + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * q + e] = v[e];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x[j] = k0 + j < n ? t[ch * 32 + j] : 0.0f;
+    }
+  };
+  float xs[16], nx[16];
+  uint32_t w[S], nw[S];
   int cur = end_state[row];
   double acc = 0.0;
-  uint32_t cw[4] = {0u, 0u, 0u, 0u};
-  float rv[16];
-  uint32_t w[S], nw[S];
-  const uint32_t* src = bp + (int64_t)(nchunk - 1) * stride + row * S;
+  {
+    const uint32_t* src = bp + (int64_t)(nchunk - 1) * stride + row * S;
 #pragma unroll
-  for (int j = 0; j < S; ++j) w[j] = src[j];
-  load_chunk(t, nchunk - 1, n, xs);
-  // nearest value of the coset of branch (p, u) to x: code u | v << 1 and the value
-  auto choose = [&](int p, int u, float x, uint32_t& code, float& val) {
-    const float* cs = tab + (p * 2 + u) * C;
-    int vb = 0;
-    float rb = cs[0];
-    float db = (x - rb) * (x - rb);
-#pragma unroll
-    for (int c = 1; c < C; ++c) {
-      const float v = cs[c];
-      const float d = (x - v) * (x - v);
-      if (d < db) {  // a tie keeps the smaller index
-        db = d;
-        rb = v;
-        vb = c;
-      }
-    }
-    code = (uint32_t)(u | (vb << 1));
-    val = rb;
-  };
+    for (int j = 0; j < S; ++j) w[j] = src[j];
+  }
+  load_half(nchunk - 1, xs);
   for (int ch = nchunk - 1; ch >= 0; --ch) {
     if (ch > 0) {
       const uint32_t* ps = bp + (int64_t)(ch - 1) * stride + row * S;
 #pragma unroll
       for (int j = 0; j < S; ++j) nw[j] = ps[j];
-      load_chunk(t, ch - 1, n, nx);
+      load_half(ch - 1, nx);
     }
+    // walk the chunk's pairs of steps; br[2m + e] = the branch (2 p + u) taken into step
+    // 16 h + 2 m + e: lane 1 keeps pairs 8..15, lane 0 pairs 0..7
+    int br[16];
 #pragma unroll
     for (int i = 15; i >= 0; --i) {
-      const int k = ch * 32 + 2 * i;
-      if (k < n) {
-        uint32_t wd = w[0];
-#pragma unroll
-        for (int q = 1; q < S; ++q) wd = cur == q ? w[q] : wd;
-        const uint32_t d = (wd >> (2 * i)) & 3u;
+      if (ch * 32 + 2 * i < n) {
+        const uint32_t d = __builtin_amdgcn_ubfe(w[i / P], (uint32_t)(E * cur + 2 * (i % P)), 2u);
         const int mid = (cur >> 1) + (int)(d & 1u) * (S / 2);
         const int p = (mid >> 1) + (int)(d >> 1) * (S / 2);
-        uint32_t code;
-        float val;
-        if (k + 1 < n) {
-          choose(mid, cur & 1, xs[2 * i + 1], code, val);
-          const double dd = (double)xs[2 * i + 1] - (double)val;
-          acc = fma(dd, dd, acc);
-          cw[((2 * i + 1) >> 2) & 3] |= code << (8 * ((2 * i + 1) & 3));
-          rv[(2 * i + 1) & 15] = val;
-        }
-        choose(p, mid & 1, xs[2 * i], code, val);
-        const double dd = (double)xs[2 * i] - (double)val;
-        acc = fma(dd, dd, acc);
-        cw[((2 * i) >> 2) & 3] |= code << (8 * ((2 * i) & 3));
-        rv[(2 * i) & 15] = val;
-        cur = p;
-      }
-      if ((i & 7) == 0) {  // the block of steps [k, k + 16) is done
-        uint8_t* cd = codes + row * ldc + k;
-        float* rd = recon ? recon + row * ldr + k : nullptr;
-        if (vec && k + 16 <= n) {
-          *reinterpret_cast<u32x4*>(cd) = u32x4{cw[0], cw[1], cw[2], cw[3]};
-          if (rd) {
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq)
-              *reinterpret_cast<f32x4*>(rd + 4 * qq) =
-                  f32x4{rv[4 * qq], rv[4 * qq + 1], rv[4 * qq + 2], rv[4 * qq + 3]};
-          }
+        const int bhi = 2 * mid + (cur & 1), blo = 2 * p + (mid & 1);
+        if (i >= 8) {
+          br[2 * (i - 8)] = blo;
+          br[2 * (i - 8) + 1] = bhi;
         } else {
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (k + e < n) {
-              cd[e] = (uint8_t)(cw[e >> 2] >> (8 * (e & 3)));
-              if (rd) rd[e] = rv[e];
-            }
+          br[2 * i] = h ? br[2 * i] : blo;
+          br[2 * i + 1] = h ? br[2 * i + 1] : bhi;
         }
+        cur = p;
+      } else if (i >= 8) {
+        br[2 * (i - 8)] = 0;
+        br[2 * (i - 8) + 1] = 0;
+      } else if (!h) {
+        br[2 * i] = 0;
+        br[2 * i + 1] = 0;
+      }
+    }
+    float cv[16][C];
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) cw[qq] = 0u;
+    for (int e = 0; e < 16; ++e) {
+      const float* cs = tab + br[e] * C;
+      if constexpr (C == 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(cs);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) cv[e][c] = v[c];
+      } else if constexpr (C == 2) {
+        const f32x2 v = *reinterpret_cast<const f32x2*>(cs);
+        cv[e][0] = v[0];
+        cv[e][1] = v[1];
+      } else {
+        cv[e][0] = cs[0];
+      }
+    }
+    const int k0 = ch * 32 + 16 * h;
+    uint32_t cw[4] = {0u, 0u, 0u, 0u};
+    float rv[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float x = xs[e];
+      int vb = 0;
+      float rb = cv[e][0];
+      float db = (x - rb) * (x - rb);
+#pragma unroll
+      for (int c = 1; c < C; ++c) {
+        const float d = (x - cv[e][c]) * (x - cv[e][c]);
+        if (d < db) {  // a tie keeps the smaller index
+          db = d;
+          rb = cv[e][c];
+          vb = c;
+        }
+      }
+      rv[e] = rb;
+      cw[e >> 2] |= (uint32_t)((br[e] & 1) | (vb << 1)) << (8 * (e & 3));
+      if (k0 + e < n) {
+        const double dd = (double)x - (double)rb;
+        acc = fma(dd, dd, acc);
+      }
+    }
+    if (live && k0 < n) {
+      uint8_t* cd = codes + row * ldc + k0;
+      float* rd = recon ? recon + row * ldr + k0 : nullptr;
+      if (vec && k0 + 16 <= n) {
+        *reinterpret_cast<u32x4*>(cd) = u32x4{cw[0], cw[1], cw[2], cw[3]};
+        if (rd) {
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq)
+            *reinterpret_cast<f32x4*>(rd + 4 * qq) = f32x4{rv[4 * qq], rv[4 * qq + 1], rv[4 * qq + 2], rv[4 * qq + 3]};
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (k0 + e < n) {
+            cd[e] = (uint8_t)(cw[e >> 2] >> (8 * (e & 3)));
+            if (rd) rd[e] = rv[e];
+          }
       }
     }
     if (ch > 0) {
 #pragma unroll
       for (int j = 0; j < S; ++j) w[j] = nw[j];
 #pragma unroll
-      for (int j = 0; j < 32; ++j) xs[j] = nx[j];
+      for (int j = 0; j < 16; ++j) xs[j] = nx[j];
     }
   }
-  if (cost_out) cost_out[row] = acc;
+  const int lo = __shfl_xor(__double2loint(acc), 1), hi = __shfl_xor(__double2hiint(acc), 1);
+  const double other = __hiloint2double(hi, lo);
+  if (live && h == 0 && cost_out) cost_out[row] = acc + other;
 }
 
 }  // namespace wr
@@ -470,6 +529,7 @@ int wr_trellis_quantize_impl(wr_ctx* ctx, const float* T, int64_t ldt, int64_t r
       static_cast<char*>(ctx->ws) + (((size_t)((n + 31) / 32) * (size_t)rows * S * 4 + 255) & ~(size_t)255));
   const dim3 grid((unsigned)((rows * S + 255) / 256));
   const dim3 tgrid((unsigned)((rows + 255) / 256));
+  const dim3 tgrid2((unsigned)((2 * rows + 255) / 256));
 #define WR_TRL(LS, CC)                                                                                                \
   hipLaunchKernelGGL((trellis_viterbi_kernel<LS, CC>), grid, dim3(256), 0, ctx->stream, T, ldt, rows, (int)n, values,    \
                      start_state, bp, end_state);                                                                       \
@@ -478,7 +538,7 @@ int wr_trellis_quantize_impl(wr_ctx* ctx, const float* T, int64_t ldt, int64_t r
 #define WR_TRL2(LS, CC)                                                                                               \
   hipLaunchKernelGGL((trellis_viterbi2_kernel<LS, CC>), grid, dim3(256), 0, ctx->stream, T, ldt, rows, (int)n, values,    \
                      start_state, bp, end_state);                                                                        \
-  hipLaunchKernelGGL((trellis_traceback2_kernel<LS, CC>), tgrid, dim3(256), 0, ctx->stream, T, ldt, rows, (int)n, values, \
+  hipLaunchKernelGGL((trellis_traceback2_kernel<LS, CC>), tgrid2, dim3(256), 0, ctx->stream, T, ldt, rows, (int)n, values, \
                      bp, end_state, codes, ldc, recon, ldr, cost)
 #define WR_TRL_C(M, LS)                \
   switch (coset_size) {                \
