@@ -50,6 +50,19 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ t, int ch, 
   }
 }
 
+// the 32 targets of chunk ch of a row, which lies wholly before n
+__device__ __forceinline__ void load_full(const float* __restrict__ t, int ch, float (&x)[32]) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(t + ch * 32 + 4 * q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[4 * q + e] = v[e];
+  }
+}
+
+using full_chunk = std::integral_constant<bool, true>;
+using tail_chunk = std::integral_constant<bool, false>;
+
 template <int LOGS, int C>
 __global__ __launch_bounds__(256) void trellis_viterbi_kernel(const float* __restrict__ T, int64_t ldt, int64_t rows,
                                                               int n, const float* __restrict__ values, int start,
@@ -77,6 +90,10 @@ __global__ __launch_bounds__(256) void trellis_viterbi_kernel(const float* __res
   float cost = s == start ? 0.0f : INFINITY;
   float xs[32], nx[32];
   load_chunk(t, 0, n, xs);
+  // the first chunk has arrived before the loop: otherwise the compiler, which cannot tell the
+  // first iteration's registers from later ones, waits inside every chunk for the next
+  // chunk's loads that were just issued
+  __builtin_amdgcn_s_waitcnt(0);
   for (int ch = 0; ch < nchunk; ++ch) {
     if (ch + 1 < nchunk) load_chunk(t, ch + 1, n, nx);
     uint32_t word = 0;
@@ -268,18 +285,18 @@ __global__ __launch_bounds__(256) void trellis_viterbi2_kernel(const float* __re
     vmb[c] = tab[(mb * 2 + u2) * C + c];
   }
   const int64_t stride = rows * S;  // words per 32-step chunk
-  const int nchunk = (n + 31) >> 5;
+  const int nfull = n >> 5;
   float cost = s == start ? 0.0f : INFINITY;
   float xs[32], nx[32];
-  load_chunk(t, 0, n, xs);
-  for (int ch = 0; ch < nchunk; ++ch) {
-    if (ch + 1 < nchunk) load_chunk(t, ch + 1, n, nx);
+  // one chunk of 32 steps on the targets in xc (FULL: all of them before n)
+  auto chunk = [&](auto full, int ch, const float (&xc)[32]) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full)::value;
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int k = ch * 32 + 2 * i;
-      if (k < n) {
-        const float x1 = xs[2 * i], x2 = xs[2 * i + 1];
+      if (FULL || k < n) {
+        const float x1 = xc[2 * i], x2 = xc[2 * i + 1];
         float pc[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) pc[j] = __shfl(cost, plane[j]);
@@ -298,7 +315,7 @@ __global__ __launch_bounds__(256) void trellis_viterbi2_kernel(const float* __re
         const bool upa = ca1 < ca0, upb = cb1 < cb0;  // a tie keeps the smaller state
         const float cA = upa ? ca1 : ca0, cB = upb ? cb1 : cb0;
         float ba = 0.0f, bb = 0.0f;  // an odd last step is paired with a step of zero cost
-        if (k + 1 < n) {
+        if (FULL || k + 1 < n) {
           float ma2 = fabsf(x2 - vma[0]), mb2 = fabsf(x2 - vmb[0]);
 #pragma unroll
           for (int c = 1; c < C; ++c) {
@@ -311,7 +328,8 @@ __global__ __launch_bounds__(256) void trellis_viterbi2_kernel(const float* __re
         const float fa = cA + ba, fb = cB + bb;
         const bool up2 = fb < fa;
         cost = up2 ? fb : fa;
-        word |= ((uint32_t)up2 | ((uint32_t)(up2 ? upb : upa) << 1)) << (2 * i);
+        const uint32_t da = upa ? 2u : 0u, db = upb ? 3u : 1u;
+        word |= (up2 ? db : da) << (2 * i);
         if ((i & 7) == 7) {
           float m = cost;
 #pragma unroll
@@ -335,8 +353,27 @@ __global__ __launch_bounds__(256) void trellis_viterbi2_kernel(const float* __re
       word = (s & o) ? (word & mo) | ((other >> (E * o)) & ~mo) : (word & ~mo) | ((other << (E * o)) & mo);
     }
     if (live) bp[(int64_t)ch * stride + row * S + s] = word;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) xs[j] = nx[j];
+  };
+  // Whole chunks two per iteration, the buffers trading roles (no copies), each chunk's
+  // targets loaded one chunk ahead.  The loop holds only unconditional vector loads (the
+  // index clamped at the last whole chunk) and the first chunk has arrived before it: with a
+  // conditional or ragged load in the loop the compiler's wait counts, merged over both paths,
+  // would wait inside every chunk for the loads just issued.  The ragged last chunk follows.
+  if (nfull > 0) load_full(t, 0, xs);
+  __builtin_amdgcn_s_waitcnt(0);
+  int ch = 0;
+  for (; ch + 1 < nfull; ch += 2) {
+    load_full(t, ch + 1, nx);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads a whole chunk ahead of their use
+    chunk(full_chunk{}, ch, xs);
+    load_full(t, ch + 2 < nfull ? ch + 2 : ch + 1, xs);
+    __builtin_amdgcn_sched_barrier(0);
+    chunk(full_chunk{}, ch + 1, nx);
+  }
+  if (ch < nfull) chunk(full_chunk{}, ch++, xs);
+  if (ch * 32 < n) {
+    load_chunk(t, ch, n, nx);
+    chunk(tail_chunk{}, ch, nx);
   }
   float bc = cost;
   int bs = s;
@@ -377,48 +414,42 @@ __global__ __launch_bounds__(256) void trellis_traceback2_kernel(const float* __
   const int64_t row = live ? row0 : rows - 1;
   const float* t = T + row * ldt + 16 * h;
   const int64_t stride = rows * S;
-  const int nchunk = (n + 31) >> 5;
+  const int nfull = n >> 5;
   const bool vec = ldc % 16 == 0 && (reinterpret_cast<uintptr_t>(codes) & 15) == 0 &&
                    (!recon || (ldr % 4 == 0 && (reinterpret_cast<uintptr_t>(recon) & 15) == 0));
-  // this lane's 16 targets of chunk ch (zeros past n)
+  // this lane's 16 targets of a whole chunk ch, and of the ragged last chunk (zeros past n)
   auto load_half = [&](int ch, float (&x)[16]) {
-    const int k0 = ch * 32 + 16 * h;
-    if (k0 + 16 <= n) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(t + ch * 32 + 4 * q);
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(t + ch * 32 + 4 * q);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * q + e] = v[e];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) x[j] = k0 + j < n ? t[ch * 32 + j] : 0.0f;
+      for (int e = 0; e < 4; ++e) x[4 * q + e] = v[e];
     }
+  };
+  auto load_tail_half = [&](int ch, float (&x)[16]) {
+    const int k0 = ch * 32 + 16 * h;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = k0 + j < n ? t[ch * 32 + j] : 0.0f;
   };
   float xs[16], nx[16];
   uint32_t w[S], nw[S];
   int cur = end_state[row];
   double acc = 0.0;
-  {
-    const uint32_t* src = bp + (int64_t)(nchunk - 1) * stride + row * S;
+  auto load_words = [&](int ch, uint32_t (&wd)[S]) {
+    const uint32_t* src = bp + (int64_t)ch * stride + row * S;
 #pragma unroll
-    for (int j = 0; j < S; ++j) w[j] = src[j];
-  }
-  load_half(nchunk - 1, xs);
-  for (int ch = nchunk - 1; ch >= 0; --ch) {
-    if (ch > 0) {
-      const uint32_t* ps = bp + (int64_t)(ch - 1) * stride + row * S;
-#pragma unroll
-      for (int j = 0; j < S; ++j) nw[j] = ps[j];
-      load_half(ch - 1, nx);
-    }
+    for (int j = 0; j < S; ++j) wd[j] = src[j];
+  };
+  // chunk ch on the decision words wc and targets xc (FULL: all 32 steps before n)
+  auto chunk = [&](auto full, int ch, const uint32_t (&wc)[S], const float (&xc)[16]) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full)::value;
     // walk the chunk's pairs of steps; br[2m + e] = the branch (2 p + u) taken into step
     // 16 h + 2 m + e: lane 1 keeps pairs 8..15, lane 0 pairs 0..7
     int br[16];
 #pragma unroll
     for (int i = 15; i >= 0; --i) {
-      if (ch * 32 + 2 * i < n) {
-        const uint32_t d = __builtin_amdgcn_ubfe(w[i / P], (uint32_t)(E * cur + 2 * (i % P)), 2u);
+      if (FULL || ch * 32 + 2 * i < n) {
+        const uint32_t d = __builtin_amdgcn_ubfe(wc[i / P], (uint32_t)(E * cur + 2 * (i % P)), 2u);
         const int mid = (cur >> 1) + (int)(d & 1u) * (S / 2);
         const int p = (mid >> 1) + (int)(d >> 1) * (S / 2);
         const int bhi = 2 * mid + (cur & 1), blo = 2 * p + (mid & 1);
@@ -459,7 +490,7 @@ __global__ __launch_bounds__(256) void trellis_traceback2_kernel(const float* __
     float rv[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float x = xs[e];
+      const float x = xc[e];
       int vb = 0;
       float rb = cv[e][0];
       float db = (x - rb) * (x - rb);
@@ -474,15 +505,15 @@ __global__ __launch_bounds__(256) void trellis_traceback2_kernel(const float* __
       }
       rv[e] = rb;
       cw[e >> 2] |= (uint32_t)((br[e] & 1) | (vb << 1)) << (8 * (e & 3));
-      if (k0 + e < n) {
+      if (FULL || k0 + e < n) {
         const double dd = (double)x - (double)rb;
         acc = fma(dd, dd, acc);
       }
     }
-    if (live && k0 < n) {
+    if (live && (FULL || k0 < n)) {
       uint8_t* cd = codes + row * ldc + k0;
       float* rd = recon ? recon + row * ldr + k0 : nullptr;
-      if (vec && k0 + 16 <= n) {
+      if (vec && (FULL || k0 + 16 <= n)) {
         *reinterpret_cast<u32x4*>(cd) = u32x4{cw[0], cw[1], cw[2], cw[3]};
         if (rd) {
 #pragma unroll
@@ -498,13 +529,34 @@ __global__ __launch_bounds__(256) void trellis_traceback2_kernel(const float* __
           }
       }
     }
-    if (ch > 0) {
-#pragma unroll
-      for (int j = 0; j < S; ++j) w[j] = nw[j];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) xs[j] = nx[j];
-    }
+  };
+  // The ragged last chunk first, then whole chunks two per iteration with the buffers trading
+  // roles, each chunk's words and targets loaded one chunk ahead by unconditional vector loads
+  // (index clamped at 0), as in the forward kernel.
+  const bool ragged = nfull * 32 < n;
+  if (ragged) {
+    load_words(nfull, nw);
+    load_tail_half(nfull, nx);
   }
+  if (nfull > 0) {
+    load_words(nfull - 1, w);
+    load_half(nfull - 1, xs);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  if (ragged) chunk(tail_chunk{}, nfull, nw, nx);
+  int ch = nfull - 1;
+  for (; ch >= 1; ch -= 2) {
+    load_words(ch - 1, nw);
+    load_half(ch - 1, nx);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads a whole chunk ahead of their use
+    chunk(full_chunk{}, ch, w, xs);
+    const int c2 = ch >= 2 ? ch - 2 : 0;
+    load_words(c2, w);
+    load_half(c2, xs);
+    __builtin_amdgcn_sched_barrier(0);
+    chunk(full_chunk{}, ch - 1, nw, nx);
+  }
+  if (ch == 0) chunk(full_chunk{}, 0, w, xs);
   const int lo = __shfl_xor(__double2loint(acc), 1), hi = __shfl_xor(__double2hiint(acc), 1);
   const double other = __hiloint2double(hi, lo);
   if (live && h == 0 && cost_out) cost_out[row] = acc + other;
