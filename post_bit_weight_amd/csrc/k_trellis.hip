@@ -254,28 +254,32 @@ __global__ __launch_bounds__(256) void trellis_traceback_kernel(const float* __r
 // state and pair of steps (bit 0: mid_b taken; bit 1: the chosen middle state came from its
 // larger predecessor).  An odd last step is paired with a step of zero cost.
 template <int LOGS, int C>
-__global__ __launch_bounds__(256) void trellis_viterbi2_kernel(const float* __restrict__ T, int64_t ldt, int64_t rows,
+__global__ __launch_bounds__(256, 4) void trellis_viterbi2_kernel(const float* __restrict__ T, int64_t ldt, int64_t rows,
                                                                int n, const float* __restrict__ values, int start,
                                                                uint32_t* __restrict__ bp, int32_t* __restrict__ end_state) {
   constexpr int S = 1 << LOGS;
   static_assert(S >= 4, "two steps per exchange need four predecessors");
   __shared__ float tab[S * 2 * C];
+  // costs exchanged through LDS: state p of a row at slot (p mod S/4) * 4 + p / (S/4) of the
+  // row's S slots, so that the four predecessors p_j = q + j S/4 of a state sit at slots
+  // 4q .. 4q + 3 and one 16-byte read fetches them in order.  A row's lanes are in one wave,
+  // whose LDS operations complete in order: no barrier between the write and the reads.
+  __shared__ __align__(16) float xcost[256];
   for (int i = threadIdx.x; i < S * 2 * C; i += blockDim.x) tab[i] = values[i];
   __syncthreads();
   const int s = threadIdx.x & (S - 1);
-  const int gbase = (threadIdx.x & 63) & ~(S - 1);
   const int64_t row0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> LOGS;
   const bool live = row0 < rows;
   const int64_t row = live ? row0 : rows - 1;  // every lane takes part in the exchanges
   const float* t = T + row * ldt;
   const int q = s >> 2, u1 = (s >> 1) & 1, u2 = s & 1;
   const int ma = s >> 1, mb = ma + S / 2;
-  int plane[4];
+  float* const wslot = xcost + (threadIdx.x & ~(S - 1)) + (s % (S / 4)) * 4 + s / (S / 4);
+  const f32x4* const rslot = reinterpret_cast<const f32x4*>(xcost + (threadIdx.x & ~(S - 1)) + 4 * q);
   float va[4][C], vma[C], vmb[C];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int pj = q + j * (S / 4);
-    plane[j] = gbase + pj;
 #pragma unroll
     for (int c = 0; c < C; ++c) va[j][c] = tab[(pj * 2 + u1) * C + c];
   }
@@ -288,42 +292,63 @@ __global__ __launch_bounds__(256) void trellis_viterbi2_kernel(const float* __re
   const int nfull = n >> 5;
   float cost = s == start ? 0.0f : INFINITY;
   float xs[32], nx[32];
-  // one chunk of 32 steps on the targets in xc (FULL: all of them before n)
-  auto chunk = [&](auto full, int ch, const float (&xc)[32]) __attribute__((always_inline)) {
+  // When every branch into this lane's state two steps on carries the same coset at the first
+  // step, and both middle states' branches the same coset at the second (as for a coset chosen
+  // by the state's low bit and the branch bit, with 8 or more states), each metric is computed
+  // once: the same numbers, fewer operations.  Decided per wave from the table, so uniformly.
+  bool same = S >= 8;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+#pragma unroll
+    for (int j = 1; j < 4; ++j) same = same && va[j][c] == va[0][c];
+    same = same && vmb[c] == vma[c];
+  }
+  const bool shared = __all(same);
+  // one chunk of 32 steps on the targets in xc (FULL: all of them before n; SHARED: the
+  // metrics above are shared)
+  auto chunk = [&](auto full, auto shared_tag, int ch, const float (&xc)[32]) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full)::value;
+    constexpr bool SHARED = decltype(shared_tag)::value;
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int k = ch * 32 + 2 * i;
       if (FULL || k < n) {
         const float x1 = xc[2 * i], x2 = xc[2 * i + 1];
-        float pc[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pc[j] = __shfl(cost, plane[j]);
+        *wslot = cost;
+        __builtin_amdgcn_wave_barrier();
+        const f32x4 pcv = *rslot;
+        __builtin_amdgcn_wave_barrier();
+        const float pc[4] = {pcv[0], pcv[1], pcv[2], pcv[3]};
         // the smallest squared distance to a coset is the square of the smallest distance
         // (squaring and its rounding are monotone): one min with |.| operands per value
         float b1[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < (SHARED ? 1 : 4); ++j) {
           float m = fabsf(x1 - va[j][0]);
 #pragma unroll
           for (int c = 1; c < C; ++c) m = fminf(m, fabsf(x1 - va[j][c]));
           b1[j] = m * m;
         }
+        if constexpr (SHARED) b1[1] = b1[2] = b1[3] = b1[0];
         const float ca0 = pc[0] + b1[0], ca1 = pc[2] + b1[2];
         const float cb0 = pc[1] + b1[1], cb1 = pc[3] + b1[3];
         const bool upa = ca1 < ca0, upb = cb1 < cb0;  // a tie keeps the smaller state
         const float cA = upa ? ca1 : ca0, cB = upb ? cb1 : cb0;
         float ba = 0.0f, bb = 0.0f;  // an odd last step is paired with a step of zero cost
         if (FULL || k + 1 < n) {
-          float ma2 = fabsf(x2 - vma[0]), mb2 = fabsf(x2 - vmb[0]);
+          float ma2 = fabsf(x2 - vma[0]);
 #pragma unroll
-          for (int c = 1; c < C; ++c) {
-            ma2 = fminf(ma2, fabsf(x2 - vma[c]));
-            mb2 = fminf(mb2, fabsf(x2 - vmb[c]));
-          }
+          for (int c = 1; c < C; ++c) ma2 = fminf(ma2, fabsf(x2 - vma[c]));
           ba = ma2 * ma2;
-          bb = mb2 * mb2;
+          if constexpr (SHARED) {
+            bb = ba;
+          } else {
+            float mb2 = fabsf(x2 - vmb[0]);
+#pragma unroll
+            for (int c = 1; c < C; ++c) mb2 = fminf(mb2, fabsf(x2 - vmb[c]));
+            bb = mb2 * mb2;
+          }
         }
         const float fa = cA + ba, fb = cB + bb;
         const bool up2 = fb < fa;
@@ -359,22 +384,28 @@ __global__ __launch_bounds__(256) void trellis_viterbi2_kernel(const float* __re
   // index clamped at the last whole chunk) and the first chunk has arrived before it: with a
   // conditional or ragged load in the loop the compiler's wait counts, merged over both paths,
   // would wait inside every chunk for the loads just issued.  The ragged last chunk follows.
-  if (nfull > 0) load_full(t, 0, xs);
-  __builtin_amdgcn_s_waitcnt(0);
-  int ch = 0;
-  for (; ch + 1 < nfull; ch += 2) {
-    load_full(t, ch + 1, nx);
-    __builtin_amdgcn_sched_barrier(0);  // keep the loads a whole chunk ahead of their use
-    chunk(full_chunk{}, ch, xs);
-    load_full(t, ch + 2 < nfull ? ch + 2 : ch + 1, xs);
-    __builtin_amdgcn_sched_barrier(0);
-    chunk(full_chunk{}, ch + 1, nx);
-  }
-  if (ch < nfull) chunk(full_chunk{}, ch++, xs);
-  if (ch * 32 < n) {
-    load_chunk(t, ch, n, nx);
-    chunk(tail_chunk{}, ch, nx);
-  }
+  auto run = [&](auto shared_tag) __attribute__((always_inline)) {
+    if (nfull > 0) load_full(t, 0, xs);
+    __builtin_amdgcn_s_waitcnt(0);
+    int ch = 0;
+    for (; ch + 1 < nfull; ch += 2) {
+      load_full(t, ch + 1, nx);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads a whole chunk ahead of their use
+      chunk(full_chunk{}, shared_tag, ch, xs);
+      load_full(t, ch + 2 < nfull ? ch + 2 : ch + 1, xs);
+      __builtin_amdgcn_sched_barrier(0);
+      chunk(full_chunk{}, shared_tag, ch + 1, nx);
+    }
+    if (ch < nfull) chunk(full_chunk{}, shared_tag, ch++, xs);
+    if (ch * 32 < n) {
+      load_chunk(t, ch, n, nx);
+      chunk(tail_chunk{}, shared_tag, ch, nx);
+    }
+  };
+  if (shared)
+    run(std::integral_constant<bool, true>{});
+  else
+    run(std::integral_constant<bool, false>{});
   float bc = cost;
   int bs = s;
 #pragma unroll
