@@ -131,8 +131,8 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&w)[BITS]
 // together, x' (a few KB, in LDS or cache-resident) just before its use.  Workgroup: 16 row
 // groups.
 // With XLDS the workgroup forms x' = R x_pad itself, in LDS (batch x n_store floats; the host
-// checks they fit): x is read from global memory, the Hadamard butterflies run stage by stage in
-// LDS, and 1/sqrt(m) is applied to the outputs (the product is linear in x').  The first chunk's
+// checks they fit): x is read from global memory, the Hadamard butterflies run three stages per
+// pass through LDS, and 1/sqrt(m) is applied to the outputs (the product is linear in x').  The first chunk's
 // codes are requested before that, so their latency overlaps the butterflies.  Without XLDS, x'
 // (already scaled) comes from the workspace.  Either way the chunk's sum of x' is formed in the
 // main loop, once for the RPL rows.
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ i
 #pragma unroll
         for (int r = 0; r < RPL; ++r) {
           load_codes<BITS>(cp[r] + (int64_t)q * (GV_CHUNK / 8) * BITS, w[g][r]);
-          sb[g][r] = sp[r][2 * gi] | (sp[r][2 * gi + 1] << 8);
+          sb[g][r] = *reinterpret_cast<const uint16_t*>(sp[r] + 2 * gi);  // 2-aligned: rowbytes is even
         }
       }
     }
@@ -185,16 +185,38 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ i
       xl[xswz(i)] = v;
     }
     __syncthreads();
-    for (int lh = 0; lh < log2m; ++lh) {
+    // up to three butterfly stages per pass, in registers: a thread takes the 2^ns elements
+    // base + k h that those stages combine (blocks of m never straddle: m | n_store), so a
+    // pass costs one barrier; every element sees the same additions as stage by stage
+    auto pass = [&](auto ns_tag, int lh) __attribute__((always_inline)) {
+      constexpr int NS = decltype(ns_tag)::value, G = 1 << NS;
       const int h = 1 << lh;
-      for (int i = threadIdx.x; i < tot / 2; i += 256) {
-        const int lo = ((i >> lh) << (lh + 1)) | (i & (h - 1));  // blocks of m never straddle: m | n_store
-        const int pa = xswz(lo), pb = xswz(lo + h);
-        const float a = xl[pa], c = xl[pb];
-        xl[pa] = a + c;
-        xl[pb] = a - c;
+      for (int gi = threadIdx.x; gi < tot / G; gi += 256) {
+        const int base = ((gi >> lh) << (lh + NS)) | (gi & (h - 1));
+        float v[G];
+#pragma unroll
+        for (int k = 0; k < G; ++k) v[k] = xl[xswz(base + k * h)];
+#pragma unroll
+        for (int st = 0; st < NS; ++st)
+#pragma unroll
+          for (int k = 0; k < G; ++k)
+            if (!(k & (1 << st))) {
+              const float a = v[k], c = v[k + (1 << st)];
+              v[k] = a + c;
+              v[k + (1 << st)] = a - c;
+            }
+#pragma unroll
+        for (int k = 0; k < G; ++k) xl[xswz(base + k * h)] = v[k];
       }
       __syncthreads();
+    };
+    for (int lh = 0; lh < log2m; lh += 3) {
+      if (log2m - lh >= 3)
+        pass(std::integral_constant<int, 3>{}, lh);
+      else if (log2m - lh == 2)
+        pass(std::integral_constant<int, 2>{}, lh);
+      else
+        pass(std::integral_constant<int, 1>{}, lh);
     }
     xr = xl;
   }
