@@ -65,7 +65,8 @@ def test_page_toy(wr, ctx, golden):
 
 @pytest.mark.parametrize("log2s,C,rows,n,start", [(1, 1, 37, 1000, 0), (2, 2, 37, 2560, 1), (3, 2, 37, 2560, 0),
                                                    (3, 4, 20, 777, 5), (4, 2, 33, 1024, 9), (4, 1, 9, 65, 0),
-                                                   (2, 4, 70, 31, 3)])
+                                                   (2, 4, 70, 31, 3), (3, 2, 10, 96, 2), (3, 2, 11, 161, 0),
+                                                   (2, 2, 5, 1, 0)])
 def test_random_trellises_match_the_oracle(wr, ctx, log2s, C, rows, n, start):
     rng = np.random.default_rng(log2s * 100 + C * 10 + rows)
     S = 1 << log2s
@@ -75,6 +76,23 @@ def test_random_trellises_match_the_oracle(wr, ctx, log2s, C, rows, n, start):
     ref = oracle.trellis_viterbi(T.astype(np.float64), vals.astype(np.float64), start)
     same = _check(T, vals, start, codes, recon, cost, ref)
     assert same >= 0.99, same
+
+
+@pytest.mark.parametrize("log2s,C,n", [(3, 2, 96), (3, 2, 101), (3, 2, 31), (3, 2, 1), (3, 2, 2), (3, 2, 33),
+                                         (3, 2, 2559), (4, 2, 161), (4, 4, 64), (3, 1, 70)])
+def test_coset_by_low_bit_trellis_matches_the_oracle(wr, ctx, log2s, C, n):
+    """Tables whose coset depends only on the predecessor's low bit and the branch bit, like the
+    workload trellis: every branch into a state carries one coset, so the forward kernel computes
+    each metric once.  Lengths with an odd number of whole 32-step chunks, a ragged chunk, fewer
+    than 32 steps and a single step."""
+    rng = np.random.default_rng(log2s * 1000 + C * 100 + n)
+    S = 1 << log2s
+    base = np.sort(rng.uniform(-3, 3, size=(2, 2, C)), axis=2)
+    vals = np.stack([base[p & 1] for p in range(S)]).astype(np.float32)
+    T = rng.normal(0, 1.5, size=(13, n)).astype(np.float32)
+    codes, recon, cost = _run(wr, ctx, T, log2s, vals, 0)
+    ref = oracle.trellis_viterbi(T.astype(np.float64), vals.astype(np.float64), 0)
+    _check(T, vals, 0, codes, recon, cost, ref)
 
 
 def test_workload_trellis_full_size_sampled_rows(wr, ctx):
