@@ -51,6 +51,8 @@ CASES = [  # rows, n_store, n_in, bits, group, had_block, batch
     (9, 96, 90, 2, 32, 32, 1),
     (40, 2560, 2560, 3, 64, 512, 5),
     (20, 4096, 4096, 2, 64, 256, 6),  # x' too large for LDS: rotation kernel + product from global memory
+    (33, 512, 500, 2, 64, 64, 2),     # blocks of one wave's 64 lanes, one element each
+    (7, 1024, 1024, 3, 32, 128, 1),
 ]
 
 
