@@ -15,6 +15,9 @@
 namespace wr {
 
 constexpr int GV_CHUNK = 32;
+// threads of a product workgroup: 32 row groups of RPL rows, so that a module of a few tens of
+// thousands of rows makes about one workgroup per CU and each forms x' once
+constexpr int GV_THREADS = 512;
 
 // one workgroup per (segment, vector): a Hadamard block of m columns (or 256 columns without a
 // rotation); x' = R x_pad goes to the workspace (used when x' does not fit in LDS)
@@ -128,7 +131,7 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&w)[BITS]
 
 // 16 lanes per group of RPL rows: lane l handles the chunks l, l + 16, ... of all RPL rows, so one
 // read of x' serves RPL rows; the codes and scales of NG chunks (the HBM traffic) are requested
-// together, x' (a few KB, in LDS or cache-resident) just before its use.  Workgroup: 16 row
+// together, x' (a few KB, in LDS or cache-resident) just before its use.  Workgroup: GV_THREADS / 16 row
 // groups.
 // With XLDS the workgroup forms x' = R x_pad itself, in LDS (batch x n_store floats; the host
 // checks they fit): x is read from global memory, the Hadamard butterflies run three stages per
@@ -137,7 +140,7 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&w)[BITS]
 // (already scaled) comes from the workspace.  Either way the chunk's sum of x' is formed in the
 // main loop, once for the RPL rows.
 template <int BITS, int BMAX, bool XLDS>
-__global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ in, int64_t rows, int n_store, int group,
+__global__ __launch_bounds__(GV_THREADS) void gemv_kernel(const uint8_t* __restrict__ in, int64_t rows, int n_store, int group,
                                                    const float* __restrict__ xr_g, int batch, float* __restrict__ y,
                                                    int64_t ldy, const float* __restrict__ x, int64_t ldx, int n_in,
                                                    int log2m, const int8_t* __restrict__ signs, float out_scale) {
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ i
   constexpr int NG = 2;   // chunks whose codes and scales are requested together
   extern __shared__ float xl[];
   const int l16 = threadIdx.x & 15;
-  const int64_t rbase = ((int64_t)blockIdx.x * 16 + (threadIdx.x >> 4)) * RPL;
+  const int64_t rbase = ((int64_t)blockIdx.x * (GV_THREADS / 16) + (threadIdx.x >> 4)) * RPL;
   const int nch = n_store / GV_CHUNK;
   const int64_t rowbytes = (int64_t)(n_store / 8) * BITS;
   const int nb = n_store / group;
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ i
   const float* xr = xr_g;
   if constexpr (XLDS) {
     const int tot = batch * n_store;
-    for (int i = threadIdx.x; i < tot; i += 256) {
+    for (int i = threadIdx.x; i < tot; i += GV_THREADS) {
       const int bi = i / n_store, j = i - bi * n_store;
       float v = j < n_in ? x[(int64_t)bi * ldx + j] : 0.0f;
       if (log2m > 0) v *= (float)signs[j];
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ i
     auto pass = [&](auto ns_tag, int lh) __attribute__((always_inline)) {
       constexpr int NS = decltype(ns_tag)::value, G = 1 << NS;
       const int h = 1 << lh;
-      for (int gi = threadIdx.x; gi < tot / G; gi += 256) {
+      for (int gi = threadIdx.x; gi < tot / G; gi += GV_THREADS) {
         const int base = ((gi >> lh) << (lh + NS)) | (gi & (h - 1));
         float v[G];
 #pragma unroll
@@ -296,13 +299,13 @@ int wr_packed_gemv_impl(wr_ctx* ctx, const uint8_t* in, int64_t rows, int64_t n_
                        (int)n_store, m, log2m, signs, rs, xr);
     WR_CHECK_LAUNCH();
   }
-  const dim3 grid((unsigned)((rows + 63) / 64));
+  const dim3 grid((unsigned)((rows + GV_THREADS / 4 - 1) / (GV_THREADS / 4)));
 #define WR_GV(BT, BM)                                                                                                 \
   if (fused)                                                                                                          \
-    hipLaunchKernelGGL((gemv_kernel<BT, BM, true>), grid, dim3(256), lds, ctx->stream, in, rows, (int)n_store, group, \
+    hipLaunchKernelGGL((gemv_kernel<BT, BM, true>), grid, dim3(GV_THREADS), lds, ctx->stream, in, rows, (int)n_store, group, \
                        xr, batch, y, ldy, x, ldx, (int)n_in, log2m, signs, rs);                                       \
   else                                                                                                                \
-    hipLaunchKernelGGL((gemv_kernel<BT, BM, false>), grid, dim3(256), 0, ctx->stream, in, rows, (int)n_store, group,  \
+    hipLaunchKernelGGL((gemv_kernel<BT, BM, false>), grid, dim3(GV_THREADS), 0, ctx->stream, in, rows, (int)n_store, group,  \
                        xr, batch, y, ldy, x, ldx, (int)n_in, log2m, signs, 1.0f)
 #define WR_GV_B(BT)        \
   if (batch == 1) {        \
