@@ -425,18 +425,26 @@ __global__ void reverse_copy_kernel(const float* __restrict__ H, int64_t ldh, in
 
 // M[i][j] = L[n-1-i][n-1-j] / L[n-1-j][n-1-j] for i < j; 0 on and below the diagonal
 // (the unit diagonal is implicit).
-__global__ void build_m_kernel(const double* __restrict__ L, int n, float* __restrict__ M,
-                               const int32_t* __restrict__ dev_info) {
+__global__ __launch_bounds__(256) void build_m_kernel(const double* __restrict__ L, int n, float* __restrict__ M,
+                                                      const int32_t* __restrict__ dev_info) {
+  // one 64 x 64 tile of M per workgroup; the 64 diagonal entries its columns divide by are read
+  // once into LDS (they lie on 64 different rows of L)
   if (*dev_info != 0) return;
-  const int i = blockIdx.x;
-  const int64_t ri = n - 1 - i;
-  for (int j = threadIdx.x; j < n; j += blockDim.x) {
-    float v = 0.0f;
-    if (j > i) {
-      const int64_t rj = n - 1 - j;
-      v = (float)(L[ri * n + rj] / L[rj * n + rj]);
+  __shared__ double dg[64];
+  const int i0 = 64 * blockIdx.y, j0 = 64 * blockIdx.x;
+  const int c = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    const int64_t rj = n - 1 - (j0 + c);
+    dg[c] = j0 + c < n ? L[rj * n + rj] : 1.0;
+  }
+  __syncthreads();
+  for (int r = threadIdx.x >> 6; r < 64; r += 4) {
+    const int i = i0 + r, j = j0 + c;
+    if (i < n && j < n) {
+      float v = 0.0f;
+      if (j > i) v = (float)(L[(int64_t)(n - 1 - i) * n + (n - 1 - j)] / dg[c]);
+      M[(int64_t)i * n + j] = v;
     }
-    M[(int64_t)i * n + j] = v;
   }
 }
 
@@ -469,7 +477,8 @@ int wr_factor_m(hipStream_t st, const float* H, int64_t ldh, int n, void* ws, fl
                        Xinv[(s + 1) & 1], n, kb, two_phase, dev_info);
     WR_CHECK_LAUNCH();
   }
-  hipLaunchKernelGGL(build_m_kernel, dim3(n), dim3(256), 0, st, Lf, n, M, dev_info);
+  hipLaunchKernelGGL(build_m_kernel, dim3((unsigned)((n + 63) / 64), (unsigned)((n + 63) / 64)), dim3(256), 0, st, Lf, n,
+                     M, dev_info);
   WR_CHECK_LAUNCH();
   return WR_OK;
 }

@@ -334,15 +334,38 @@ __global__ void damp_round_kernel(const double* __restrict__ Hd, int64_t n_store
     H[i * ldh + j] = (float)(Hd[i * n_store + j] + (i == j ? delta : 0.0));
 }
 
-__global__ void finalize_kernel(const double* __restrict__ S, int n, int64_t n_store, double inv_rows,
-                                const double* __restrict__ delta64, float* __restrict__ H, int64_t ldh) {
-  const int64_t i = blockIdx.y;
+// H = S/N + delta I (S's lower triangle mirrored, zero padding to n_store, delta on the whole
+// diagonal), rounded to fp32.  One workgroup per lower 64 x 64 tile (I, J) of the padded matrix:
+// the tile of S is read once, coalesced, into LDS and written to H at (I, J) and transposed at
+// (J, I); a diagonal tile takes its upper half from its own lower half.
+constexpr int FZ_T = 64;
+__global__ __launch_bounds__(256) void finalize_kernel(const double* __restrict__ S, int n, int64_t n_store,
+                                                       double inv_rows, const double* __restrict__ delta64,
+                                                       float* __restrict__ H, int64_t ldh) {
+  __shared__ double t[FZ_T][FZ_T + 1];
+  int I, J;
+  tri_tile(blockIdx.x, I, J);
   const double delta = *delta64;
-  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n_store; j += (int64_t)gridDim.x * blockDim.x) {
-    double v = 0.0;
-    if (i < n && j < n) v = (i >= j ? S[i * n + j] : S[j * n + i]) * inv_rows;
-    if (i == j) v += delta;
-    H[i * ldh + j] = (float)v;
+  const int c = threadIdx.x & (FZ_T - 1);
+  const int64_t i0 = (int64_t)FZ_T * I, j0 = (int64_t)FZ_T * J;
+  for (int r = threadIdx.x / FZ_T; r < FZ_T; r += 256 / FZ_T) {
+    const int64_t i = i0 + r, j = j0 + c;
+    t[r][c] = (i < n && j < n && i >= j) ? S[i * n + j] : 0.0;
+  }
+  __syncthreads();
+  // element (i, j) of H from the tile: S[i][j] for i >= j, else S[j][i]
+  for (int r = threadIdx.x / FZ_T; r < FZ_T; r += 256 / FZ_T) {
+    const int64_t i = i0 + r, j = j0 + c;
+    if (i < n_store && j < n_store) {
+      double v = (I != J || r >= c ? t[r][c] : t[c][r]) * inv_rows;
+      if (i == j) v += delta;
+      H[i * ldh + j] = (float)v;
+    }
+  }
+  if (I == J) return;
+  for (int r = threadIdx.x / FZ_T; r < FZ_T; r += 256 / FZ_T) {  // H[j0 + r][i0 + c] = S[i0 + c][j0 + r]
+    const int64_t i = j0 + r, j = i0 + c;
+    if (i < n_store && j < n_store) H[i * ldh + j] = (float)(t[c][r] * inv_rows);
   }
 }
 
@@ -473,8 +496,9 @@ int wr_hessian_finalize_impl(wr_ctx* ctx, const double* S, int64_t n, int64_t to
   WR_CHECK_LAUNCH();
   const unsigned gx = (unsigned)std::min<int64_t>((n_store + 255) / 256, 64);
   if (!had_block) {
-    hipLaunchKernelGGL(finalize_kernel, dim3(gx, (unsigned)n_store), dim3(256), 0, ctx->stream, S, (int)n, n_store,
-                       inv_rows, delta64, H, ldh);
+    const int64_t nt = (n_store + FZ_T - 1) / FZ_T;
+    hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)(nt * (nt + 1) / 2)), dim3(256), 0, ctx->stream, S, (int)n,
+                       n_store, inv_rows, delta64, H, ldh);
     WR_CHECK_LAUNCH();
     return WR_OK;
   }

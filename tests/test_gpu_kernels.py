@@ -128,6 +128,27 @@ def test_hessian_finalize_pads_and_damps(wr, ctx, toy):
     assert np.array_equal(H.cpu().numpy(), H.cpu().numpy().T)
 
 
+@pytest.mark.parametrize("n,n_store,extra", [(100, 130, 6), (64, 64, 0), (200, 256, 3)])
+def test_hessian_finalize_ragged_tiles(wr, ctx, n, n_store, extra):
+    """Sizes off the 64-wide tiles of the finalize kernel, H a row-major view with ld > n_store;
+    S's upper triangle holds garbage the kernel must not read."""
+    rng = np.random.default_rng(n + n_store)
+    A = rng.standard_normal((n, n))
+    S0 = A @ A.T
+    Sg = np.tril(S0) + np.triu(rng.standard_normal((n, n)) * 1e6, 1)
+    S = torch.from_numpy(Sg).cuda()
+    Hbig = torch.full((n_store, n_store + extra), float("nan"), dtype=torch.float32, device="cuda")
+    H = Hbig[:, :n_store]
+    delta = torch.empty(1, dtype=torch.float32, device="cuda")
+    wr.wr_hessian_finalize(ctx, S, 7, 0.01, H, delta)
+    ref, d = oracle.damp(oracle.pad_square(S0 / 7, n_store), 0.01)
+    got = H.cpu().double().numpy()
+    assert abs(delta.item() - d) <= 1e-6 * d
+    assert _rel(got, ref) < 1e-6
+    assert np.array_equal(got, got.T)
+    assert np.all(np.isnan(Hbig[:, n_store:].cpu().numpy()))
+
+
 # ------------------------------------------------------------------------- rotation
 @pytest.mark.parametrize("m,n,rows", [(4, 8, 3), (64, 256, 17), (1024, 2048, 5), (512, 1536, 4)])
 def test_rotation_rows_and_inverse(wr, ctx, m, n, rows):
