@@ -811,10 +811,16 @@ static int wring_core(wr_ctx* ctx, char* ws, size_t ws_bytes, const void* target
   WR_CHECK_LAUNCH();
   if (nb <= 64) {
     const dim3 grid((unsigned)rows);
+    // the unrolled factorization costs NB^2 broadcasts and fmas whatever nb is: buckets of 8
+    // (40 blocks for a 2560-wide layer with groups of 64)
     if (nb <= 16)
       hipLaunchKernelGGL(row_solve_wave_kernel<16>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, dev_info);
+    else if (nb <= 24)
+      hipLaunchKernelGGL(row_solve_wave_kernel<24>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, dev_info);
     else if (nb <= 32)
       hipLaunchKernelGGL(row_solve_wave_kernel<32>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, dev_info);
+    else if (nb <= 40)
+      hipLaunchKernelGGL(row_solve_wave_kernel<40>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, dev_info);
     else if (nb <= 48)
       hipLaunchKernelGGL(row_solve_wave_kernel<48>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, dev_info);
     else
