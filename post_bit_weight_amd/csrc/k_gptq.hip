@@ -324,6 +324,26 @@ __global__ __launch_bounds__(256) void split_mt_kernel(const float* __restrict__
     t[i][j] = k0 + i < n && c0 + j < n ? M[(int64_t)(k0 + i) * n + c0 + j] : 0.0f;
   }
   __syncthreads();
+  if (n % 8 == 0) {  // eight consecutive output columns per thread: one 16-byte store per plane
+    for (int e = tid; e < 64 * 8; e += 256) {
+      const int j = e >> 3, i0 = 8 * (e & 7);  // output row c0 + j, columns k0 + i0 .. + 7
+      if (c0 + j < n && k0 + i0 < n) {
+        uint16_t p[3][8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) split3(t[i0 + q][j], p[0][q], p[1][q], p[2][q]);
+        const int64_t o = (int64_t)(c0 + j) * n + k0 + i0;
+        uint16_t* dst[3] = {Mt0, Mt1, Mt2};
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          u32x4 w;
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) w[e2] = (uint32_t)p[q][2 * e2] | ((uint32_t)p[q][2 * e2 + 1] << 16);
+          *reinterpret_cast<u32x4*>(dst[q] + o) = w;
+        }
+      }
+    }
+    return;
+  }
   for (int e = tid; e < 64 * 64; e += 256) {
     const int j = e >> 6, i = e & 63;  // output row c0 + j, column k0 + i
     if (c0 + j < n && k0 + i < n) {
