@@ -406,8 +406,9 @@ __global__ __launch_bounds__(64, (LOGA >= 5 ? 4 : 5)) void materialize_chunk_ker
           qc -= nch;
           ++rc;
         }
-        if (64 * qc < n_out)  // chunks past n_out are the cropped padding
-          *reinterpret_cast<u32x4*>(out + rc * ldo + 64 * qc + 8 * k) = tile[c * 8 + (k ^ (c & 7))];
+        if (64 * qc < n_out)  // chunks past n_out are the cropped padding; streamed past the caches
+          __builtin_nontemporal_store(tile[c * 8 + (k ^ (c & 7))],
+                                      reinterpret_cast<u32x4*>(out + rc * ldo + 64 * qc + 8 * k));
       }
     }
   } else if (live) {
