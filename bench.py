@@ -276,8 +276,8 @@ def progress(msg):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
-              "(the solve shards over calibration rows and weight rows, see DESIGN.md)", file=sys.stderr)
+        print("bench.py: the solve runs on one GPU; --gpus must be 1 (across GPUs it would shard over "
+              "calibration rows for H and over weight rows for the sweep and the wring)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -48,7 +48,7 @@ enum wr_status {
   WR_EINVAL = 1,       /* invalid argument (null pointer, bad size, bad flag) */
   WR_EWORKSPACE = 2,   /* registered workspace missing or too small */
   WR_EHIP = 3,         /* a HIP runtime call failed */
-  WR_EUNSUPPORTED = 4  /* valid request this build does not implement */
+  WR_EUNSUPPORTED = 4  /* valid request the library does not implement */
 };
 
 enum wr_dtype { WR_F32 = 0, WR_BF16 = 1 };
@@ -145,7 +145,7 @@ int wr_hadamard_rotate(wr_ctx* ctx, float* M, int64_t rows, int64_t n, int64_t l
  * its error is pushed onto the later columns in the proportions set by the
  * damped H (n x n fp32, ld ldh, symmetric positive definite).
  * bits: device uint8 per row (2, 3 or 4).  n % group == 0, group % 8 == 0,
- * lazy_batch % group == 0; this build implements group in {32, 64, 128} and
+ * lazy_batch % group == 0; the library implements group in {32, 64, 128} and
  * lazy_batch = 128 (other valid values return WR_EUNSUPPORTED).
  * Outputs: codes (rows x n uint8, ld n), scales (rows x n/group fp16 bit
  * patterns).  dev_info as above.  Workspace: WR_OP_GPTQ.
