@@ -254,7 +254,7 @@ __global__ __launch_bounds__(64, (LOGA >= 5 ? 4 : 5)) void materialize_chunk_ker
   float s[NS];
 #pragma unroll
   for (int t = 0; t < NS; ++t)
-    s[t] = f16_bits_to_f32((uint16_t)(sp[2 * (gi0 + t)] | (sp[2 * (gi0 + t) + 1] << 8)));
+    s[t] = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sp + 2 * (gi0 + t)));  // rows start at even offsets
   constexpr bool rotate = LOGA >= 0;
   constexpr int L = (1 << BITS) - 1;
   float v[64];
