@@ -568,31 +568,49 @@ __global__ __launch_bounds__(64) void row_solve_wave_kernel(const float* __restr
 }
 
 // Per row: (G + lambda mu I) s = h + lambda mu s0 in fp64 (packed lower Cholesky in LDS), s -> fp16.
-__global__ __launch_bounds__(64) void row_solve_kernel(const float* __restrict__ Gm, const float* __restrict__ rhs,
-                                                       int64_t rows, int nb, float lambda, uint16_t* __restrict__ scales,
-                                                       const int32_t* __restrict__ dev_info) {
+// One 256-thread workgroup per row: G is read row by row (coalesced) into the packed lower
+// triangle; per pivot the column below it is scaled, then every element of the trailing triangle
+// is updated once, the elements spread evenly over the threads (element t of the triangle is
+// row ii, column jj with ii (ii + 1) / 2 <= t < (ii + 1) (ii + 2) / 2); then the two
+// substitutions.  The trace is a 64-lane butterfly in the first wave.
+constexpr int RS_THREADS = 256;
+__global__ __launch_bounds__(RS_THREADS) void row_solve_kernel(const float* __restrict__ Gm, const float* __restrict__ rhs,
+                                                               int64_t rows, int nb, float lambda,
+                                                               uint16_t* __restrict__ scales,
+                                                               const int32_t* __restrict__ dev_info) {
   extern __shared__ double sh[];
   if (*dev_info != 0) return;
   const int64_t row = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
   double* a = sh;                               // packed lower: a[i(i+1)/2 + j]
   double* y = sh + (size_t)nb * (nb + 1) / 2;
   __shared__ int failed;
+  __shared__ double sreg;
   const float* g = Gm + (size_t)row * nb * nb;
-  double tr = 0.0;
-  for (int i = lane; i < nb; i += 64) tr += (double)g[(size_t)i * nb + i];
+  if (tid < 64) {
+    double tr = 0.0;
+    for (int i = tid; i < nb; i += 64) tr += (double)g[(size_t)i * nb + i];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) tr += __shfl_xor(tr, o);
-  const double reg = (double)lambda * tr / nb;
-  for (int i = 0; i < nb; ++i)
-    for (int j = lane; j <= i; j += 64) a[(size_t)i * (i + 1) / 2 + j] = (double)g[(size_t)j * nb + i] + (i == j ? reg : 0.0);
-  for (int i = lane; i < nb; i += 64)
+    for (int o = 32; o > 0; o >>= 1) tr += __shfl_xor(tr, o);
+    if (tid == 0) {
+      sreg = (double)lambda * tr / nb;
+      failed = 0;
+    }
+  }
+  __syncthreads();
+  const double reg = sreg;
+  // element (j, i), j >= i, of the lower triangle from G[i][j] (G symmetric: the upper half, read
+  // along rows)
+  for (int t = tid; t < nb * nb; t += RS_THREADS) {
+    const int i = t / nb, j = t - i * nb;
+    if (j >= i) a[(size_t)j * (j + 1) / 2 + i] = (double)g[t] + (i == j ? reg : 0.0);
+  }
+  for (int i = tid; i < nb; i += RS_THREADS)
     y[i] = (double)rhs[(size_t)row * nb + i] + reg * (double)f16_bits_to_f32(scales[(size_t)row * nb + i]);
-  if (lane == 0) failed = 0;
   __syncthreads();
   for (int k = 0; k < nb; ++k) {
     const size_t kk = (size_t)k * (k + 1) / 2 + k;
-    if (lane == 0) {
+    if (tid == 0) {
       const double d = a[kk];
       if (!(d > 0.0)) failed = 1;
       else a[kk] = sqrt(d);
@@ -600,31 +618,35 @@ __global__ __launch_bounds__(64) void row_solve_kernel(const float* __restrict__
     __syncthreads();
     if (failed) return;  // only reachable with lambda == 0 and a singular G: keep the incoming scales
     const double dk = a[kk];
-    for (int i = k + 1 + lane; i < nb; i += 64) a[(size_t)i * (i + 1) / 2 + k] /= dk;
+    for (int i = k + 1 + tid; i < nb; i += RS_THREADS) a[(size_t)i * (i + 1) / 2 + k] /= dk;
     __syncthreads();
-    for (int i = k + 1; i < nb; ++i) {
-      const double aik = a[(size_t)i * (i + 1) / 2 + k];
-      for (int j = k + 1 + lane; j <= i; j += 64) a[(size_t)i * (i + 1) / 2 + j] -= aik * a[(size_t)j * (j + 1) / 2 + k];
+    const int m = nb - k - 1;  // trailing rows and columns k + 1 .. nb - 1
+    for (int t = tid; t < m * (m + 1) / 2; t += RS_THREADS) {
+      int ii = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+      while (ii * (ii + 1) / 2 > t) --ii;
+      while ((ii + 1) * (ii + 2) / 2 <= t) ++ii;
+      const int i = k + 1 + ii, j = k + 1 + (t - ii * (ii + 1) / 2);
+      a[(size_t)i * (i + 1) / 2 + j] -= a[(size_t)i * (i + 1) / 2 + k] * a[(size_t)j * (j + 1) / 2 + k];
     }
     __syncthreads();
   }
   // L z = y
   for (int k = 0; k < nb; ++k) {
-    if (lane == 0) y[k] /= a[(size_t)k * (k + 1) / 2 + k];
+    if (tid == 0) y[k] /= a[(size_t)k * (k + 1) / 2 + k];
     __syncthreads();
     const double zk = y[k];
-    for (int i = k + 1 + lane; i < nb; i += 64) y[i] -= a[(size_t)i * (i + 1) / 2 + k] * zk;
+    for (int i = k + 1 + tid; i < nb; i += RS_THREADS) y[i] -= a[(size_t)i * (i + 1) / 2 + k] * zk;
     __syncthreads();
   }
   // L^T s = z
   for (int k = nb - 1; k >= 0; --k) {
-    if (lane == 0) y[k] /= a[(size_t)k * (k + 1) / 2 + k];
+    if (tid == 0) y[k] /= a[(size_t)k * (k + 1) / 2 + k];
     __syncthreads();
     const double uk = y[k];
-    for (int i = lane; i < k; i += 64) y[i] -= a[(size_t)k * (k + 1) / 2 + i] * uk;
+    for (int i = tid; i < k; i += RS_THREADS) y[i] -= a[(size_t)k * (k + 1) / 2 + i] * uk;
     __syncthreads();
   }
-  for (int i = lane; i < nb; i += 64) scales[(size_t)row * nb + i] = f64_to_f16_bits_clamped(y[i]);
+  for (int i = tid; i < nb; i += RS_THREADS) scales[(size_t)row * nb + i] = f64_to_f16_bits_clamped(y[i]);
 }
 
 // Block scale search (the finisher "nearest-point codes + block scale search"): for each block
@@ -864,8 +886,8 @@ static int wring_core(wr_ctx* ctx, char* ws, size_t ws_bytes, const void* target
       hipFuncSetAttribute(reinterpret_cast<const void*>(row_solve_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)shbytes) != hipSuccess)
     return WR_EHIP;
-  hipLaunchKernelGGL(row_solve_kernel, dim3((unsigned)rows), dim3(64), shbytes, st, Gm, rh, rows, nb, lambda, scales,
-                     dev_info);
+  hipLaunchKernelGGL(row_solve_kernel, dim3((unsigned)rows), dim3(RS_THREADS), shbytes, st, Gm, rh, rows, nb, lambda,
+                     scales, dev_info);
   WR_CHECK_LAUNCH();
   return WR_OK;
 }

@@ -304,6 +304,24 @@ def test_joint_scales_toy(wr, ctx, toy):
     assert u.max() <= 1 and (u > 0).mean() < 0.01
 
 
+@pytest.mark.parametrize("n,g,rows", [(2560, 32, 24), (4608, 64, 9)])
+def test_joint_scales_many_blocks(wr, ctx, n, g, rows):
+    """Rows with more than 64 blocks (80 and 72 here) take the solve with the factor in LDS."""
+    from post_bit_weight_amd import synth
+    W = synth.gaussian((rows, n), 0.02, seed=n + g)
+    X = synth.SpectralSource(n, seed=n + 1, n_outliers=3).chunk(0, 2 * n, dtype=torch.float32)
+    H, _ = oracle.damp(oracle.second_moment(X.double().numpy()), 0.01)
+    H32 = H.astype(np.float32)
+    rng = np.random.default_rng(n)
+    codes0 = rng.integers(0, 4, size=(rows, n))
+    scales0 = oracle.fp16_rne(rng.uniform(0.005, 0.02, size=(rows, n // g)))
+    codes, scales, info = _joint(wr, ctx, H32, codes0, scales0, 2, g, 0.01, target=W)
+    assert info == 0 and np.array_equal(codes, codes0)
+    ref, _ = oracle.joint_scales(codes0, 2, g, H32.astype(np.float64), W.double().numpy(), scales0, 0.01)
+    u = scale_ulps(scales, ref)
+    assert u.max() <= 1 and (u > 0).mean() < 0.02
+
+
 def test_wring_toy(wr, ctx, toy):
     H32 = toy["H"].astype(np.float32)
     Hd = H32.astype(np.float64)
