@@ -570,9 +570,8 @@ __global__ __launch_bounds__(64) void row_solve_wave_kernel(const float* __restr
 // Per row: (G + lambda mu I) s = h + lambda mu s0 in fp64 (packed lower Cholesky in LDS), s -> fp16.
 // One 256-thread workgroup per row: G is read row by row (coalesced) into the packed lower
 // triangle; per pivot the column below it is scaled, then every element of the trailing triangle
-// is updated once, the elements spread evenly over the threads (element t of the triangle is
-// row ii, column jj with ii (ii + 1) / 2 <= t < (ii + 1) (ii + 2) / 2); then the two
-// substitutions.  The trace is a 64-lane butterfly in the first wave.
+// is updated once, thread (r, c) of a 16 x 16 grid taking the rows r (mod 16) and in them the
+// columns c (mod 16); then the two substitutions.  The trace is a 64-lane butterfly in the first wave.
 constexpr int RS_THREADS = 256;
 __global__ __launch_bounds__(RS_THREADS) void row_solve_kernel(const float* __restrict__ Gm, const float* __restrict__ rhs,
                                                                int64_t rows, int nb, float lambda,
@@ -621,12 +620,14 @@ __global__ __launch_bounds__(RS_THREADS) void row_solve_kernel(const float* __re
     for (int i = k + 1 + tid; i < nb; i += RS_THREADS) a[(size_t)i * (i + 1) / 2 + k] /= dk;
     __syncthreads();
     const int m = nb - k - 1;  // trailing rows and columns k + 1 .. nb - 1
-    for (int t = tid; t < m * (m + 1) / 2; t += RS_THREADS) {
-      int ii = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
-      while (ii * (ii + 1) / 2 > t) --ii;
-      while ((ii + 1) * (ii + 2) / 2 <= t) ++ii;
-      const int i = k + 1 + ii, j = k + 1 + (t - ii * (ii + 1) / 2);
-      a[(size_t)i * (i + 1) / 2 + j] -= a[(size_t)i * (i + 1) / 2 + k] * a[(size_t)j * (j + 1) / 2 + k];
+    for (int ii = tid >> 4; ii < m; ii += RS_THREADS / 16) {  // rows ii = tid / 16 (mod 16)
+      const int i = k + 1 + ii;
+      const size_t ri = (size_t)i * (i + 1) / 2;
+      const double aik = a[ri + k];
+      for (int jj = tid & 15; jj <= ii; jj += 16) {  // columns jj = tid (mod 16)
+        const int j = k + 1 + jj;
+        a[ri + j] -= aik * a[(size_t)j * (j + 1) / 2 + k];
+      }
     }
     __syncthreads();
   }
