@@ -13,7 +13,7 @@ ties to even.
 
 Since the rounding is taken once, the weights before it must carry no rounding
 of their own where it could move a bf16 decision.  R^T v = diag(d) H_m v / sqrt(m)
-(Wringer paper, the rotation section): the product H_m v of the unnormalised
+(Pingala-8 post, "Trick 1: rotate the weights first"): the product H_m v of the unnormalised
 Sylvester matrix with v is exact in fp64 here (each entry of v is an odd level
 below 16 times an fp16 scale, so every partial sum is an integer multiple of the
 smallest scale's ulp below 2^53 of it), and the one division by sqrt(m) rounds

@@ -115,3 +115,95 @@ def test_joint_scales_do_not_increase_the_weighted_error():
     e_new = oracle.proxy_loss(T, oracle.dequant(codes, s, 2, 4), H)
     e_old = oracle.proxy_loss(T, oracle.dequant(codes, s0, 2, 4), H)
     assert e_new <= e_old
+
+
+def _tiny_wring_case(seed=44):
+    """n = 8, group 4, 2 bits: a seeded row quantized as the pipeline does (GPTQ sweep, joint scales
+    against W), then a rank-2 adapter of std 0.08 (relative to the weights about the size of the
+    workloads' rank-128 adapters); returns what the wring starts from."""
+    rng = np.random.default_rng(seed)
+    n, g, bits = 8, 4, 2
+    Xc = rng.standard_normal((64, n))
+    Xc[:, 3] *= 4.0                                   # one strong channel, as in the calibration model
+    H, _ = oracle.damp(Xc.T @ Xc / 64, 0.01)
+    w = 0.02 * rng.standard_t(5, size=(1, n))
+    g0 = oracle.gptq_sweep(w, H, bits, g)
+    s1, _ = oracle.joint_scales(g0["codes"], bits, g, H, w, g0["scales"], 0.01)
+    B = 0.08 * rng.standard_normal((1, 2))
+    A = 0.08 * rng.standard_normal((2, n))
+    return H, g0["codes"], s1, B, A, n, g, bits
+
+
+def _f16_step(x, k):
+    """The fp16 value k representable steps away from the fp16 value x (x > 0)."""
+    bits = np.float16(x).view(np.int16).astype(np.int32) + k
+    return float(np.int16(bits).view(np.float16))
+
+
+def _objective_lstsq_stack(H, lev, g, t, s0, lam):
+    """min over s of (t - Q s)^T H (t - Q s) + lam mu ||s - s0||^2 via least squares on the stacked
+    system [C Q; sqrt(lam mu) I] s ~ [C t; sqrt(lam mu) s0] with H = C^T C, solved by QR; for a
+    batch of level vectors lev (K x n).  Returns (objective values, minimisers)."""
+    K, n = lev.shape
+    nb = n // g
+    C = np.linalg.cholesky(H).T
+    Q = np.zeros((K, n, nb))
+    for b in range(nb):
+        Q[:, b * g:(b + 1) * g, b] = lev[:, b * g:(b + 1) * g]
+    CQ = np.einsum("ij,kjb->kib", C, Q)
+    mu = np.einsum("kib,kib->k", CQ, CQ) / nb            # trace(Q^T H Q) / nb
+    M = np.concatenate([CQ, np.sqrt(lam * mu)[:, None, None] * np.eye(nb)[None]], axis=1)
+    rhs = np.concatenate([np.broadcast_to(C @ t, (K, n)), np.sqrt(lam * mu)[:, None] * s0[None, :]], axis=1)
+    Qm, Rm = np.linalg.qr(M)
+    s = np.linalg.solve(Rm, np.einsum("kib,ki->kb", Qm, rhs)[..., None])[..., 0]
+    d = t[None, :] - np.einsum("kjb,kb->kj", Q, s)
+    f = np.einsum("kj,jl,kl->k", d, H, d) + lam * mu * np.sum((s - s0[None, :]) ** 2, axis=1)
+    return f, s
+
+
+def test_projected_scales_are_the_best_fp16_neighbours_on_a_tiny_block():
+    """Brute force over fp16 scales: on the seeded n = 8, g = 4, 2-bit wring, every combination
+    of +-3 fp16 steps around the fp16-rounded joint scales is evaluated on the objective
+    (t - Q s)^T H (t - Q s) + lam mu ||s - s0||^2; the rounded solution attains the least
+    value among those 49 points.  (An observation on this case, not a theorem: with coupled
+    blocks the best fp16 point need not be the rounding of the real optimum.)  A dropped prior,
+    a wrong sign on it or a transposed Q would move the solution by many fp16 steps."""
+    H, c0, s0, B, A, n, g, bits = _tiny_wring_case()
+    out = oracle.wring(c0, s0, bits, g, B, A, 2.0, H, 0.01)
+    t = out["target"][0]
+    lev = oracle.level_of(out["codes"][0], 3).astype(float)
+    Q = _dense_Q(lev, g)
+    best, arg = np.inf, None
+    for i in range(-3, 4):
+        for j in range(-3, 4):
+            s = np.array([_f16_step(out["scales"][0, 0], i), _f16_step(out["scales"][0, 1], j)])
+            v = _objective(s, Q, H, t, s0[0], 0.01)
+            if v < best:
+                best, arg = v, (i, j)
+    assert arg == (0, 0)
+
+
+def test_wring_is_a_zero_gradient_but_not_global_optimum_by_enumeration():
+    """All 4^8 code vectors of the tiny block, each with its own least-squares scales (QR of the
+    stacked system, not the oracle's closed form): the wring's codes are one of them, their
+    objective value equals the enumerated one, the oracle's unrounded scales are that code
+    vector's minimiser (zero gradient), and some other code vector does strictly better -- the
+    wring's nearest-point codes are a valid local choice, not the global optimum."""
+    import itertools
+    H, c0, s0, B, A, n, g, bits = _tiny_wring_case()
+    out = oracle.wring(c0, s0, bits, g, B, A, 2.0, H, 0.01)
+    assert (out["codes"] != c0).any()                 # the recode moved some codes
+    t = out["target"][0]
+    allc = np.array(list(itertools.product(range(4), repeat=n)))
+    f, s = _objective_lstsq_stack(H, 2 * allc - 3, g, t, s0[0], 0.01)
+    idx = int(np.flatnonzero((allc == out["codes"][0]).all(axis=1))[0])
+    assert np.allclose(s[idx], out["scales_unrounded"][0], rtol=1e-10)
+    lev = oracle.level_of(out["codes"][0], 3).astype(float)
+    assert np.isclose(_objective(out["scales_unrounded"][0], _dense_Q(lev, g), H, t, s0[0], 0.01), f[idx], rtol=1e-10)
+    assert f[idx] >= f.min()
+    assert f.min() < f[idx] * (1 - 1e-6)
+    # every code vector's least-squares scales have zero gradient: spot-check the oracle's closed form
+    pick = np.random.default_rng(3).choice(len(allc), 64, replace=False)
+    _, s_or = oracle.joint_scales(allc[pick], bits, g, H, np.broadcast_to(t, (64, n)),
+                                  np.broadcast_to(s0[0], (64, 2)), 0.01)
+    assert np.allclose(s_or, s[pick], rtol=1e-9, atol=1e-14)
