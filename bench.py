@@ -1,23 +1,29 @@
-"""Throughput of the whole per-module quantization solve on one MI355X.
+"""Throughput of the per-linear-layer quantization solve on one MI355X.
 
-One step = H accumulation over all calibration rows + finalize/damping + GPTQ
-sweep + joint scales + wring (rank-128 adapter, nearest-point recode, joint
-scales) + packing, for a Qwen3-4B-shaped q_proj (W 4096 x 2560 bf16, X
-131072 x 2560 bf16, 2-bit, group 64, lazy batch 128, lambda 0.01).  Inputs are
-synthetic and resident in HBM before the timed region.  The metric is weights
-quantized per second.
+Default workload: the whole 36-layer Qwen3-4B-shaped body (36 x 7 modules,
+3 633 315 840 weights).  One step = for every layer and each of its three input
+dimensions (2560: q k v gate up; 4096: o; 9728: down): H accumulation over
+262144 calibration rows + finalize with the random-sign Hadamard rotation
+(blocks of 512) and damping + rotation of the weights + factorisation and GPTQ
+sweep of the stacked rows sharing that H + joint scales + the wring of every
+module against its rank-128 adapter (nearest-point codes, joint scales) +
+packing and unpacking of every module.  Inputs (weights, adapters, calibration
+rows) are synthetic and resident in HBM before the timed region: the body's
+calibration rows (309 GB) exceed the 288 GB of HBM, so `--calib-sets` distinct
+per-layer calibration sets are kept resident and layer l reads set l mod
+calib_sets (the work per layer does not depend on the values).  The metric is
+weights quantized per second.
 
 Also reported: the roofline of the dominant kernel (the bf16 SYRK that
 accumulates H: N n (n + 1) useful flops per call, timed live with HIP events on
-the stream it runs on) and the CPU oracle timed on a bounded sample of the same
-workload on the host cores, and, outside the timed step, the materializer (packed
-module -> bf16 weights) against the HBM peak, the finisher variant with GPTQ
-codes (wring by a GPTQ sweep of the watered target instead of nearest-point
-codes), the trellis-coded quantizer (Viterbi search) against the VALU peak, and
-the packed-module product (decode-time GEMV from the container) against the HBM
-peak.
+the stream it runs on), a per-call breakdown of one separate untimed pass, and
+the CPU oracle timed on a bounded sample of the same workload on the host cores.
+`--workload q_proj` times one q_proj module (4096 x 2560) instead, with the
+materializer, finisher variants, trellis quantizer and packed-module product
+timed beside it.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras | --extras-only]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload body|q_proj] [--no-cpu-baseline]
+       python bench.py --kernel-summary RESULTS_DB   (per-kernel table of a rocprofv3 kernel trace)
 """
 
 import argparse
@@ -45,29 +51,39 @@ WORKLOAD = {
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=1)
+    p.add_argument("--workload", choices=("body", "q_proj"), default="body")
+    p.add_argument("--layers", type=int, default=36, help="body: layers per step (the workload has 36)")
+    p.add_argument("--calib-sets", type=int, default=4,
+                   help="body: distinct per-layer calibration sets kept resident (layer l reads set l mod K)")
+    p.add_argument("--no-breakdown", action="store_true", help="body: skip the untimed per-call breakdown pass")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=128, help="weight rows in the oracle sample")
-    p.add_argument("--cpu-calib", type=int, default=8192, help="calibration rows in the oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=None, help="weight rows in the oracle sample")
+    p.add_argument("--cpu-calib", type=int, default=None, help="calibration rows in the oracle sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="before the warmup, copy MIB mebibytes device to device once (a plain copy kernel of known "
                         "size, the yardstick for the FETCH_SIZE / WRITE_SIZE counters)")
     p.add_argument("--no-extras", action="store_true",
-                   help="time the solve step only (no materializer or finisher-variant timing)")
+                   help="q_proj: time the solve step only (no materializer or finisher-variant timing)")
     p.add_argument("--extras-only", action="store_true",
-                   help="one untimed step (for H), then only the materializer and the finisher-variant timings")
+                   help="q_proj: one untimed step (for H), then only the materializer and the finisher-variant timings")
+    p.add_argument("--kernel-summary", metavar="RESULTS_DB", default=None,
+                   help="print the per-kernel table of a rocprofv3 kernel trace (rocpd database) and exit")
+    p.add_argument("--trace-steps", type=int, default=1,
+                   help="with --kernel-summary: body steps the trace covers (warmup + timed + breakdown)")
     return p.parse_args()
 
 
-def traffic_from_profile():
-    """HBM bytes per SYRK launch from the committed rocprofv3 counter summary, if it matches this source.
+def traffic_from_profile(name):
+    """HBM bytes of the SYRK launches from a committed rocprofv3 counter summary, if it matches this source.
 
-    The summary holds `bytes_per_launch:` (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the
-    counter reads for a plain 512 MiB copy) and `source_sha256:` of the kernel source it was taken on; once
-    the source has changed the figure no longer describes the kernel and None is returned.
+    The summary (profiles/<name>) holds `bytes_per_launch:` (FETCH_SIZE and WRITE_SIZE per dispatch, each
+    scaled by what the counter reads for a plain copy of known size; for the body, summed over one step's
+    launches) and `source_sha256:` of the kernel source it was taken on; once the source has changed the
+    figure no longer describes the kernel and None is returned.
     """
-    path = os.path.join(ROOT, "profiles", "syrk_bf16_q_proj_traffic.txt")
+    path = os.path.join(ROOT, "profiles", name)
     src = os.path.join(ROOT, "post_bit_weight_amd", "csrc", "k_hessian.hip")
     try:
         rec = {}
@@ -83,7 +99,7 @@ def traffic_from_profile():
         return None
 
 
-def cpu_baseline(X_host, W_host, B_host, A_host, cfg, n_rows, n_calib):
+def cpu_baseline(X_host, W_host, B_host, A_host, cfg, n_rows=128, n_calib=8192):
     """The oracle, unchanged, on a bounded sample; extrapolated to the full workload."""
     import numpy as np
     import oracle
@@ -273,12 +289,7 @@ def progress(msg):
     print(f"bench.py: {msg}", file=sys.stderr, flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: the solve runs on one GPU; --gpus must be 1 (across GPUs it would shard over "
-              "calibration rows for H and over weight rows for the sweep and the wring)", file=sys.stderr)
-        sys.exit(2)
+def main_q_proj(args):
     import numpy as np
     import torch
     from post_bit_weight_amd import _lib as wr
@@ -376,7 +387,7 @@ def main():
     flops_h = float(N) * n * (n + 1)
     t_h = per_stage["hessian"] * 1e-3
     achieved = flops_h / t_h / 1e12
-    traffic = traffic_from_profile()
+    traffic = traffic_from_profile("syrk_bf16_q_proj_traffic.txt")
     line = {
         "metric": "weights quantized/s (H accum+GPTQ sweep+wring); % MFMA/HBM peak, 1 GPU",
         "value": rows * n / (ms * 1e-3),
@@ -414,8 +425,408 @@ def main():
         Wh = W.float().cpu().numpy()
         Bh = B.float().cpu().numpy()
         Ah = A.float().cpu().numpy()
-        line["cpu_baseline"] = cpu_baseline(Xh, Wh, Bh, Ah, cfg, args.cpu_rows, args.cpu_calib)
+        line["cpu_baseline"] = cpu_baseline(Xh, Wh, Bh, Ah, cfg, args.cpu_rows or 128, args.cpu_calib or 8192)
     print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------- body
+BODY = {"layers": 36, "calib_rows": 262144, "chunk": 16384, "had_block": 512, "group": 64, "rank": 128,
+        "lazy_batch": 128, "damp": 0.01, "lam": 0.01, "seed": 2026}
+
+
+def body_flops_syrk(layers, calib_rows, dims):
+    return float(layers) * sum(float(calib_rows) * n * (n + 1) for n in dims)
+
+
+class BodyInputs:
+    """Everything one body step reads and writes, allocated and drawn before the timed region.
+
+    Per layer and input dim: the stacked weights of the modules sharing that H (bf16, module rows
+    consecutive, as the batched sweep takes them), each module's adapter B, A, the per-row bit
+    widths; outputs codes/scales per layer (the result), the packed module and its unpacked codes
+    and scales (the round trip).  Calibration rows: `calib_sets` resident sets per input dim."""
+
+    def __init__(self, torch, wr, body, synth, layers, calib_sets, cfg, log):
+        dev = torch.device("cuda", 0)
+        self.layers, self.P, self.cfg = layers, calib_sets, cfg
+        N, chunk, g, r, seed = cfg["calib_rows"], cfg["chunk"], cfg["group"], cfg["rank"], cfg["seed"]
+        self.dims = body.DIMS
+        self.X = {n: [] for n in self.dims}
+        for n in self.dims:
+            src = body.CalibrationStream(n, seed * 31 + n, dev)
+            for p in range(calib_sets):
+                X = torch.empty(N, n, dtype=torch.bfloat16, device=dev)
+                for k in range(N // chunk):
+                    X[k * chunk:(k + 1) * chunk] = src.chunk(p, k, chunk)
+                self.X[n].append(X)
+            log(f"calibration sets drawn for input dim {n}")
+        self.signs = {n: synth.signs(n, seed=seed * 7 + n, device=dev) for n in self.dims}
+        self.S = {n: torch.empty(n, n, dtype=torch.float64, device=dev) for n in self.dims}
+        self.H = {n: torch.empty(n, n, dtype=torch.float32, device=dev) for n in self.dims}
+        self.none = {n: torch.empty(0, n, dtype=torch.bfloat16, device=dev) for n in self.dims}
+        self.delta = torch.empty(1, dtype=torch.float32, device=dev)
+        names = [m[0] for m in body.MODULES]
+        self.groups = []
+        for layer in range(layers):
+            per = {}
+            for n in self.dims:
+                mods = [(name, rows) for name, rows, dim in body.MODULES if dim == n]
+                total = sum(rows for _, rows in mods)
+                W = torch.empty(total, n, dtype=torch.bfloat16, device=dev)
+                bits = torch.empty(total, dtype=torch.uint8, device=dev)
+                entries, r0 = [], 0
+                for name, rows in mods:
+                    ms = seed * 100003 + 1000 * layer + 10 * names.index(name)
+                    W[r0:r0 + rows] = synth.student_t((rows, n), seed=ms, device=dev, dtype=torch.bfloat16)
+                    b = body.module_bits(layer, name, cfg["layers"])
+                    bits[r0:r0 + rows] = b
+                    entries.append(dict(
+                        name=name, r0=r0, r1=r0 + rows, bits=b,
+                        B=synth.gaussian((rows, r), 0.01, seed=ms + 1, device=dev, dtype=torch.bfloat16),
+                        A=synth.gaussian((r, n), 0.01, seed=ms + 2, device=dev, dtype=torch.bfloat16),
+                        packed=torch.empty(wr.packed_nbytes(rows, n, b, g), dtype=torch.uint8, device=dev)))
+                    r0 += rows
+                per[n] = dict(W=W, bits=bits, mods=entries,
+                              codes=torch.empty(total, n, dtype=torch.uint8, device=dev),
+                              scales=torch.empty(total, n // g, dtype=torch.float16, device=dev),
+                              ucodes=torch.empty(total, n, dtype=torch.uint8, device=dev),
+                              uscales=torch.empty(total, n // g, dtype=torch.float16, device=dev),
+                              info=torch.full((2 + len(entries),), -7, dtype=torch.int32, device=dev))
+            self.groups.append(per)
+        rows_max = {n: self.groups[0][n]["W"].shape[0] for n in self.dims}
+        self.Wst = {n: torch.empty(rows_max[n], n, dtype=torch.float32, device=dev) for n in self.dims}
+        self.weights = sum(int(v["W"].numel()) for per in self.groups for v in per.values())
+        self.payload = sum(int(m["packed"].numel()) for per in self.groups for v in per.values() for m in v["mods"])
+        ws = 0
+        for n in self.dims:
+            rows = rows_max[n]
+            ws = max(ws, wr.wr_workspace_bytes(wr.WR_OP_HESSIAN, N, n),
+                     wr.wr_workspace_bytes(wr.WR_OP_FINALIZE, 0, n),
+                     wr.wr_workspace_bytes(wr.WR_OP_GPTQ, rows, n, g, 0, cfg["lazy_batch"]),
+                     wr.wr_workspace_bytes(wr.WR_OP_WRING, rows, n, g, r, 0))
+        self.ws_bytes = ws
+
+
+def body_step(wr, ctx, I, mark=None):
+    """One pass of the whole solve over the body.  mark(kind, n) is called between library calls when
+    given (it records timing events on the library's stream)."""
+    cfg = I.cfg
+    g, lam, hb, N = cfg["group"], cfg["lam"], cfg["had_block"], cfg["calib_rows"]
+    m = mark or (lambda kind, n: None)
+    for layer in range(I.layers):
+        p = layer % I.P
+        for n in I.dims:
+            G = I.groups[layer][n]
+            rows = G["W"].shape[0]
+            Wst = I.Wst[n][:rows]
+            wr.wr_hessian_accumulate(ctx, I.none[n], I.S[n], zero=True)       # S = 0
+            m("hessian", n)
+            wr.wr_hessian_accumulate(ctx, I.X[n][p], I.S[n])
+            m("finalize", n)
+            wr.wr_hessian_finalize(ctx, I.S[n], N, cfg["damp"], I.H[n], I.delta, hb, I.signs[n])
+            m("rotate", n)
+            Wst.copy_(G["W"])                                                    # widen to fp32
+            wr.wr_hadamard_rotate(ctx, Wst, hb, I.signs[n], wr.WR_ROT_ROWS)
+            m("gptq", n)
+            wr.wr_gptq_sweep(ctx, Wst, I.H[n], G["bits"], g, cfg["lazy_batch"], G["codes"], G["scales"],
+                             G["info"][0:1])
+            m("joint", n)
+            wr.wr_wring_solve(ctx, I.H[n], G["bits"], g, lam, G["codes"], G["scales"], G["info"][1:2], target=Wst)
+            for k, mod in enumerate(G["mods"]):
+                sl = slice(mod["r0"], mod["r1"])
+                m("wring", n)
+                wr.wr_wring_solve(ctx, I.H[n], G["bits"][sl], g, lam, G["codes"][sl], G["scales"][sl],
+                                  G["info"][2 + k:3 + k], B=mod["B"], A=mod["A"], alpha=float(cfg["rank"]),
+                                  recode=True)
+                m("pack", n)
+                wr.wr_pack(ctx, G["codes"][sl], G["scales"][sl], mod["bits"], g, mod["packed"])
+                m("unpack", n)
+                wr.wr_unpack(ctx, mod["packed"], mod["r1"] - mod["r0"], n, mod["bits"], g, G["ucodes"][sl],
+                             G["uscales"][sl])
+            m("end", n)
+
+
+def body_check(torch, I):
+    """After a step: every dev_info is 0 and every module's unpacked codes and scales equal the codes
+    and scales it was packed from."""
+    for layer, per in enumerate(I.groups):
+        for n, G in per.items():
+            info = G["info"].cpu().tolist()
+            if any(v != 0 for v in info):
+                raise RuntimeError(f"layer {layer}, input dim {n}: dev_info {info}")
+            if not (torch.equal(G["ucodes"], G["codes"]) and
+                    torch.equal(G["uscales"].view(torch.int16), G["scales"].view(torch.int16))):
+                raise RuntimeError(f"layer {layer}, input dim {n}: pack/unpack round trip differs")
+
+
+def cpu_baseline_body(I, body, torch, n_rows=2, h_rows=None):
+    """The oracle, unchanged, on a bounded sample of the body; extrapolated to the 36 layers.
+
+    Per input dim (layer 0): H over h_rows calibration rows of the resident set, the fp64 rotation of
+    H, damping, the GPTQ sweep (with its factorisation), joint scales, wring and packing of n_rows rows
+    of the group's first module, and (2560, 4096) the factorisation alone.  Per layer: H scaled to
+    262144 rows + rotation + factorisation + per-row costs x the group's rows.  At 9728 the per-row
+    sweep cost is the 4096 one scaled by n^2 (the factorisation at 9728 is timed once, inside the
+    sweep call)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    cfg = I.cfg
+    g, hb, lam, r = cfg["group"], cfg["had_block"], cfg["lam"], cfg["rank"]
+    per_layer, measured, sweep_row = 0.0, 0.0, {}
+    parts = []
+    for n in I.dims:
+        hr = h_rows or (512 if n > 4096 else 1024)
+        G = I.groups[0][n]
+        mod = G["mods"][0]
+        Xh = I.X[n][0][:hr].float().cpu().numpy().astype(np.float64)
+        sd = I.signs[n].double().cpu().numpy()
+        W = G["W"][:n_rows].float().cpu().numpy().astype(np.float64)
+        B = mod["B"][:n_rows].float().cpu().numpy().astype(np.float64)
+        A = mod["A"].float().cpu().numpy().astype(np.float64)
+        bits = mod["bits"]
+        t0 = time.perf_counter()
+        H0 = oracle.second_moment(Xh)
+        t_h = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        H0 = oracle.rotate_sym(H0, hb, sd)
+        t_rot = time.perf_counter() - t0
+        H, _ = oracle.damp(H0, cfg["damp"])
+        Wr = oracle.rotate_rows(W, hb, sd)
+        t0 = time.perf_counter()
+        gq = oracle.gptq_sweep(Wr, H, bits, g)
+        t_sweep = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        s1, _ = oracle.joint_scales(gq["codes"], bits, g, H, Wr, gq["scales"], lam)
+        w = oracle.wring(gq["codes"], s1, bits, g, B, A, float(r), H, lam)
+        oracle.pack(w["codes"], w["scales"], bits, g)
+        t_rest = time.perf_counter() - t0
+        t_fact = None
+        if n <= 4096:
+            t0 = time.perf_counter()
+            oracle.upper_cholesky_of_inverse(H)
+            t_fact = time.perf_counter() - t0
+            sweep_row[n] = max(t_sweep - t_fact, 0.0) / n_rows
+        else:
+            sweep_row[n] = sweep_row[4096] * (n / 4096.0) ** 2
+            t_fact = max(t_sweep - n_rows * sweep_row[n], 0.0)
+        rows = G["W"].shape[0]
+        per_layer += t_h * cfg["calib_rows"] / hr + t_rot + t_fact + rows * (sweep_row[n] + t_rest / n_rows)
+        measured += t_h + t_rot + t_sweep + t_rest + (t_fact if n <= 4096 else 0.0)
+        parts.append(f"dim {n}: H over {hr} rows, {n_rows} weight rows")
+    total = per_layer * cfg["layers"]
+    weights = sum(rows * n for _, rows, n in body.MODULES) * cfg["layers"]
+    return {"value": weights / total, "unit": "weights/s", "cores": int(threads), "kind": "oracle",
+            "sample": "layer 0 of the body, per input dim: H over a few calibration rows, the fp64 rotation of H, "
+                      "damping, factorisation, GPTQ sweep, joint scales, wring and packing of a few weight rows ("
+                      + "; ".join(parts) + "); extrapolated linearly to 262144 calibration rows, every row of the "
+                      f"layer and 36 layers (measured {measured:.1f} s)"}
+
+
+def main_body(args):
+    import numpy as np
+    import torch
+    from post_bit_weight_amd import _lib as wr
+    from post_bit_weight_amd import body, synth
+
+    cfg = dict(BODY)
+    layers = args.layers
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    ctx = wr.Context(0)
+    st = ctx.stream
+
+    progress(f"drawing the synthetic inputs ({args.calib_sets} resident calibration sets, {layers} layers)")
+    I = BodyInputs(torch, wr, body, synth, layers, args.calib_sets, cfg, progress)
+    ctx.ensure_workspace(I.ws_bytes)
+    torch.cuda.synchronize()
+
+    if args.copy_calibration > 0:
+        nbytes = args.copy_calibration << 20
+        src_buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst_buf = torch.empty_like(src_buf)
+        dst_buf.copy_(src_buf)
+        torch.cuda.synchronize()
+        del src_buf, dst_buf
+
+    progress(f"warmup ({args.warmup} steps)")
+    for _ in range(args.warmup):
+        body_step(wr, ctx, I)
+    torch.cuda.synchronize()
+    if args.warmup:
+        body_check(torch, I)
+
+    # timed steps: events only around the H accumulation (the roofline's kernel), recorded on the
+    # library's stream
+    progress(f"timing {args.steps} steps")
+    syrk = []
+
+    def mark_syrk(kind, n):
+        if kind in ("hessian", "finalize"):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(st)
+            syrk.append((kind, n, e))
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        body_step(wr, ctx, I, mark_syrk)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    progress("checking dev_info and the pack/unpack round trips")
+    body_check(torch, I)
+    ms = elapsed * 1e3 / args.steps
+    h_ms = {n: 0.0 for n in I.dims}
+    for (k0, n0, e0), (k1, n1, e1) in zip(syrk[0::2], syrk[1::2]):
+        assert k0 == "hessian" and k1 == "finalize" and n0 == n1
+        h_ms[n0] += e0.elapsed_time(e1) / args.steps
+    N = cfg["calib_rows"]
+    flops = {n: float(layers) * N * n * (n + 1) for n in I.dims}
+    syrk_ms = sum(h_ms.values())
+    achieved = sum(flops.values()) / (syrk_ms * 1e-3) / 1e12
+
+    stage = None
+    if not args.no_breakdown:
+        progress("per-call breakdown (one separate, untimed step)")
+        evs = []
+
+        def mark_all(kind, n):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(st)
+            evs.append((kind, n, e))
+
+        body_step(wr, ctx, I, mark_all)
+        torch.cuda.synchronize()
+        stage = {}
+        for (k0, n0, e0), (_, _, e1) in zip(evs[:-1], evs[1:]):
+            if k0 == "end":
+                continue
+            stage[k0] = stage.get(k0, 0.0) + e0.elapsed_time(e1)
+
+    traffic = traffic_from_profile("syrk_bf16_body_traffic.txt") if layers == 36 else None
+    w_desc = (f"36-layer Qwen3-4B-shaped body ({layers} layers timed): q 4096x2560, k/v 1024x2560, gate/up "
+              "9728x2560, o 2560x4096, down 2560x9728 bf16 (Student-t nu=5, std 0.02); per layer one H per input "
+              "dim from 262144 calibration rows (spectral + 1% outlier channels; post-SwiGLU-like product model "
+              "for 9728), random-sign Hadamard rotation blocks of 512, damping 0.01; batched GPTQ sweep per H "
+              "(lazy batch 128), joint scales lambda 0.01, rank-128 wring alpha 128 per module, 2/3-bit mix "
+              "(3-bit v, o, down, and k in layers 0-17), group 64, fp16 scales; pack + unpack round trip of every "
+              "module")
+    line = {
+        "metric": "weights quantized/s (H accum+GPTQ sweep+wring); % MFMA/HBM peak, 1 GPU",
+        "value": I.weights / (ms * 1e-3),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16-mfma/fp32/fp64",
+        "data": "synthetic",
+        "config": {"workload": w_desc, "layers": layers, "weights": I.weights, "calib_rows_per_H": N,
+                   "calib_sets_resident": args.calib_sets, "had_block": cfg["had_block"], "group": cfg["group"],
+                   "rank": cfg["rank"], "lambda": cfg["lam"], "payload_bytes": I.payload,
+                   "bits_per_weight": 8.0 * I.payload / I.weights, "parallelism": "none (1 GPU)"},
+        "roofline": {
+            "kernel": "syrk_bf16 (H accumulation incl. its split-K reduction), all launches of a step",
+            "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+            "algorithmic_flops_per_step": sum(flops.values()), "syrk_ms_per_step": syrk_ms,
+            "per_input_dim": {str(n): {"ms": h_ms[n], "tflops": flops[n] / (h_ms[n] * 1e-3) / 1e12,
+                                       "frac": flops[n] / (h_ms[n] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+                              for n in I.dims},
+        },
+    }
+    if stage is not None:
+        line["stage_ms"] = stage
+    if not args.no_cpu_baseline:
+        progress("timing the oracle on a bounded sample")
+        line["cpu_baseline"] = cpu_baseline_body(I, body, torch, n_rows=args.cpu_rows or 2, h_rows=args.cpu_calib)
+    print(json.dumps(line), flush=True)
+
+
+def kernel_summary(db_path, steps, layers):
+    """Markdown table of the library's kernels in a rocprofv3 kernel trace (rocpd database): calls,
+    total and average duration, per-step time, and the roofline of the kernels whose algorithmic
+    work per body step is stated (bf16 MFMA flops, fp64 flops, HBM bytes)."""
+    import collections
+    import re
+    import sqlite3
+    con = sqlite3.connect(db_path)
+    cols = [r[1] for r in con.execute("pragma table_info(kernels)")]
+    name_col = "name" if "name" in cols else "kernel_name"
+    agg = collections.OrderedDict()
+    for name, start, end in con.execute(f"select {name_col}, start, end from kernels order by start"):
+        m = re.search(r"wr::([A-Za-z0-9_]+(?:<[^>]*>)?)", name)
+        if not m:
+            continue
+        a = agg.setdefault(m.group(1), [0, 0.0])
+        a[0] += 1
+        a[1] += (end - start) * 1e-3
+    total = sum(v[1] for v in agg.values())
+    out = [f"library kernels: {total / 1e3:.2f} ms over {steps} step(s) = {total / 1e3 / steps:.2f} ms per step", "",
+           "| kernel | calls | total ms | avg us | ms per step | share |", "|---|---|---|---|---|---|"]
+    for k, (c, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        out.append(f"| `{k}` | {c} | {t / 1e3:.2f} | {t / c:.1f} | {t / 1e3 / steps:.2f} | {100 * t / total:.1f} % |")
+    # algorithmic work of one body step (all layers) for the kernels with a stated roofline
+    from post_bit_weight_amd import body as _body
+    N, g = BODY["calib_rows"], BODY["group"]
+    groups = {}
+    for name, rows, n in _body.MODULES:
+        groups.setdefault(n, []).append((name, rows))
+    work = {"syrk": 0.0, "chol": 0.0, "sweep": 0.0, "recode": 0.0, "pack": 0.0, "gram": 0.0, "rowsolve": 0.0}
+    for layer in range(layers):
+        for n, mods in groups.items():
+            rows = sum(r for _, r in mods)
+            nb = n // g
+            work["syrk"] += float(N) * n * (n + 1)
+            work["chol"] += n ** 3 / 3.0
+            work["sweep"] += rows * n * (4 + 1 + 2.0 / g) + n * n * 2.0
+            for name, r in mods:
+                b = _body.module_bits(layer, name, BODY["layers"])
+                work["recode"] += r * n * (2 + 2.0 / g)
+                work["pack"] += r * n * (1 + 2.0 / g) + r * n * b / 8.0 + r * n * 2.0 / g
+            work["gram"] += 2 * 3.0 * rows * n * n                 # W'H + Gram, both joint solves
+            work["rowsolve"] += 2 * rows * nb ** 3 / 3.0
+    kinds = [("syrk", r"^syrk_bf16_kernel|^syrk_reduce_kernel", "bf16 MFMA", PEAK_BF16_TFLOPS * 1e12, "TFLOP/s"),
+             ("chol", r"^chol_", "fp64", 78.6e12, "TFLOP/s"),
+             ("sweep", r"^sweep_panel_kernel|^trail_wide_kernel|^split_mt_kernel|^build_m_kernel", "HBM",
+              PEAK_HBM_GBS * 1e9, "GB/s"),
+             ("recode", r"^wring_prep_kernel", "HBM", PEAK_HBM_GBS * 1e9, "GB/s"),
+             ("pack", r"^pack_codes_kernel|^pack_scales_kernel", "HBM", PEAK_HBM_GBS * 1e9, "GB/s"),
+             ("gram", r"^gram_lh_kernel|^rhs_sum_kernel", "bf16 MFMA", PEAK_BF16_TFLOPS * 1e12, "TFLOP/s"),
+             ("rowsolve", r"^row_solve", "fp64", 78.6e12, "TFLOP/s")]
+    out += ["", f"Rooflines per step ({layers} layers; algorithmic work as stated in the design notes):", "",
+            "| step | kernels | bound | ms per step | achieved | peak | fraction |", "|---|---|---|---|---|---|---|"]
+    for key, pat, bound, peak, unit in kinds:
+        t = sum(v[1] for k, v in agg.items() if re.search(pat, k)) / steps
+        if t <= 0:
+            continue
+        rate = work[key] / (t * 1e-6)
+        scale = 1e12 if unit == "TFLOP/s" else 1e9
+        out.append(f"| {key} | `{pat}` | {bound} | {t / 1e3:.2f} | {rate / scale:.1f} {unit} | "
+                   f"{peak / scale:.0f} {unit} | {rate / peak:.3f} |")
+    return "\n".join(out)
+
+
+def main():
+    args = parse()
+    if args.kernel_summary:
+        print(kernel_summary(args.kernel_summary, args.trace_steps, args.layers))
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: the solve runs on one GPU; --gpus must be 1 (across GPUs it would shard over "
+              "calibration rows for H and over weight rows for the sweep and the wring)", file=sys.stderr)
+        sys.exit(2)
+    if args.workload == "q_proj":
+        main_q_proj(args)
+    else:
+        main_body(args)
 
 
 if __name__ == "__main__":
