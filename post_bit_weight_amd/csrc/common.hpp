@@ -5,7 +5,10 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
+#include <set>
 #include <type_traits>
+#include <utility>
 
 #include "../../include/wringer.h"
 
@@ -30,6 +33,21 @@ struct wr_ctx {
 namespace wr {
 
 constexpr int kWave = 64;
+
+// Raise a kernel's dynamic LDS limit to `bytes` on the current device, once per (kernel, device,
+// size); thread-safe.  Returns false if the runtime refuses.
+inline bool lds_limit(const void* kernel, int bytes) {
+  static std::mutex mu;
+  static std::set<std::pair<std::pair<const void*, int>, int>> done;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(std::make_pair(kernel, dev), bytes);
+  if (done.count(key)) return true;
+  if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess) return false;
+  done.insert(key);
+  return true;
+}
 
 // ---------------------------------------------------------------- conversions
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }

@@ -598,13 +598,7 @@ int wr_gptq_sweep_impl(wr_ctx* ctx, const void* W, int w_dtype, int64_t rows, in
     if (rc) return rc;
     const int s0 = b0 - b0 % kSuper, s1 = std::min(s0 + kSuper, n);
     if (b0 + ncols == s1 && s1 < n) {  // the group is complete and full (s1 - s0 == kSuper)
-      static bool lds_attr = false;
-      if (!lds_attr) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(trail_wide_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 3 * TW_STAGE) != hipSuccess)
-          return WR_EHIP;
-        lds_attr = true;
-      }
+      if (!lds_limit(reinterpret_cast<const void*>(trail_wide_kernel), 3 * TW_STAGE)) return WR_EHIP;
       const dim3 grid((unsigned)((n - s1 + TW_T - 1) / TW_T), (unsigned)((rows + TW_T - 1) / TW_T));
       hipLaunchKernelGGL(trail_wide_kernel, grid, dim3(256), 3 * TW_STAGE, st, rows, n - s1, n, kSuper, s0, s1, E[0],
                          E[1], E[2], kSuper, Mt[0], Mt[1], Mt[2], Cb, dev_info);

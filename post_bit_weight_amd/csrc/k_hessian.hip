@@ -418,13 +418,7 @@ size_t wr_hessian_ws_bytes(int64_t rows, int64_t n, int x_dtype, int num_cu) {
 // One SYRK pass S_lower += XA^T XB (bf16 sources, ld ldx), with its split-K reduction.
 static int syrk_pass(wr_ctx* ctx, const uint16_t* XA, const uint16_t* XB, int64_t rows, int64_t n, int64_t ldx,
                      double* S, float* partial, bool precise) {
-  static bool lds_attr = false;
-  if (!lds_attr) {
-    if (hipFuncSetAttribute((const void*)syrk_bf16_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            SY_LDS_BYTES) != hipSuccess)
-      return WR_EHIP;
-    lds_attr = true;
-  }
+  if (!lds_limit((const void*)syrk_bf16_kernel, SY_LDS_BYTES)) return WR_EHIP;
   hipStream_t st = ctx->stream;
   const int tiles = syrk_tiles(n);
   const int ks = syrk_ksplit(rows, n, kSplitCUs, precise);
@@ -452,12 +446,12 @@ static int syrk_pass(wr_ctx* ctx, const uint16_t* XA, const uint16_t* XB, int64_
 int wr_hessian_accumulate_impl(wr_ctx* ctx, const void* X, int x_dtype, int64_t rows, int64_t n, int64_t ldx,
                                double* S, int flags) {
   hipStream_t st = ctx->stream;
+  if (rows > 0 && ctx->ws_bytes < wr_hessian_ws_bytes(rows, n, x_dtype, kSplitCUs)) return WR_EWORKSPACE;
   if (flags & WR_H_ZERO) {
     hipLaunchKernelGGL(zero_lower_kernel, dim3((unsigned)n), dim3(256), 0, st, S, (int)n);
     WR_CHECK_LAUNCH();
   }
   if (rows == 0) return WR_OK;
-  if (ctx->ws_bytes < wr_hessian_ws_bytes(rows, n, x_dtype, kSplitCUs)) return WR_EWORKSPACE;
   char* ws = static_cast<char*>(ctx->ws);
   float* partial = reinterpret_cast<float*>(ws + 256);
   if (x_dtype == WR_BF16) {

@@ -771,6 +771,9 @@ size_t wr_wring_gptq_ws_bytes(int64_t rows, int64_t n, int32_t group, int32_t ra
   return align256((size_t)rows * n * 4) + (a > b ? a : b);
 }
 
+// LDS of the per-row solve above 64 blocks: the packed factor and the right-hand side in fp64.
+static size_t row_solve_lds_bytes(int64_t nb) { return ((size_t)nb * (nb + 1) / 2 + nb) * sizeof(double); }
+
 // The joint solve on workspace ws.  With T_only the target T is formed there (codes and
 // scales untouched) and nothing else is done; reset_info = false keeps a status already in
 // dev_info (the later kernels do nothing when it is nonzero).
@@ -844,13 +847,7 @@ static int wring_core(wr_ctx* ctx, char* ws, size_t ws_bytes, const void* target
   WR_CHECK_LAUNCH();
   dim3 ggrid((unsigned)((rows + 127) / 128), (unsigned)nb);
   if (lh) {
-    static bool lds_attr = false;
-    if (!lds_attr) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(gram_lh_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              2 * LH_STAGE) != hipSuccess)
-        return WR_EHIP;
-      lds_attr = true;
-    }
+    if (!lds_limit(reinterpret_cast<const void*>(gram_lh_kernel), 2 * LH_STAGE)) return WR_EHIP;
     float* hp = reinterpret_cast<float*>(ws + lay.hp);
     hipLaunchKernelGGL(gram_lh_kernel, ggrid, dim3(256), 2 * LH_STAGE, st, Lev, T, rows, n, H0, H1, H2, Gm, hp, dev_info);
     WR_CHECK_LAUNCH();
@@ -881,11 +878,9 @@ static int wring_core(wr_ctx* ctx, char* ws, size_t ws_bytes, const void* target
     WR_CHECK_LAUNCH();
     return WR_OK;
   }
-  const size_t shbytes = ((size_t)nb * (nb + 1) / 2 + nb) * sizeof(double);
-  if (shbytes > 160 * 1024) return WR_EUNSUPPORTED;
-  if (shbytes > 64 * 1024 &&
-      hipFuncSetAttribute(reinterpret_cast<const void*>(row_solve_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)shbytes) != hipSuccess)
+  const size_t shbytes = row_solve_lds_bytes(nb);
+  if (shbytes > 160 * 1024) return WR_EUNSUPPORTED;  // refused by wr_wring_solve_impl before any launch
+  if (shbytes > 64 * 1024 && !lds_limit(reinterpret_cast<const void*>(row_solve_kernel), (int)shbytes))
     return WR_EHIP;
   hipLaunchKernelGGL(row_solve_kernel, dim3((unsigned)rows), dim3(RS_THREADS), shbytes, st, Gm, rh, rows, nb, lambda,
                      scales, dev_info);
@@ -914,6 +909,9 @@ int wr_wring_solve_impl(wr_ctx* ctx, const void* target, int t_dtype, int64_t ld
                         int32_t rank, float alpha, int ab_dtype, const float* H, int64_t ldh, int64_t rows, int64_t n,
                         const uint8_t* bits, int32_t group, float lambda, int flags, uint8_t* codes, uint16_t* scales,
                         int32_t* dev_info) {
+  // requests that the per-row solve cannot hold in LDS are refused before anything is launched
+  if (!(flags & WR_RECODE_SEARCH) && n / group > 64 && row_solve_lds_bytes(n / group) > 160 * 1024)
+    return WR_EUNSUPPORTED;
   if (flags & WR_RECODE_SEARCH) {
     // the watered target into the joint solve's T slot, then the search (no joint solve)
     if (group != 32 && group != 64 && group != 128) return WR_EUNSUPPORTED;

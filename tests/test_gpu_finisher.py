@@ -15,11 +15,10 @@ import pytest
 import torch
 
 import oracle
-from parity import code_parity, f16_bits, scale_ulps
+from parity import TIE, code_parity, f16_bits, scale_ulps
 
 pytestmark = pytest.mark.gpu
 
-TIE = 5e-3
 
 
 @pytest.fixture(scope="module")

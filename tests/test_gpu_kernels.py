@@ -9,11 +9,10 @@ import pytest
 import torch
 
 import oracle
-from parity import code_parity, f16_bits, scale_ulps
+from parity import TIE, code_parity, f16_bits, scale_ulps
 
 pytestmark = pytest.mark.gpu
 
-TIE = 5e-3  # a code may differ only where the oracle's pre-rounding value is this close to a threshold
 # bf16 X: products are exact; the MFMAs sum a split of m <= 1024 steps of 16 rows in
 # fp32 (rms relative error about 2^-24 sqrt(m / 3) of the split's sum, under 6e-7) and
 # the splits are added in fp64, so |S_gpu - S|_F / |S|_F stays near 2e-7 or below.  The
@@ -349,3 +348,24 @@ def test_wring_zero_adapter_is_a_fixed_point(wr, ctx, toy):
     codes, scales, info = _joint(wr, ctx, H32, codes0, s0, 2, 32, 0.01, B=torch.zeros(64, 8), A=torch.zeros(8, 512),
                                  alpha=8.0, recode=True)
     assert info == 0 and np.array_equal(codes, codes0) and np.array_equal(f16_bits(scales), f16_bits(s0))
+
+
+def test_wring_refuses_too_many_blocks_before_any_launch(wr, ctx):
+    """201 blocks per row (groups of 32 on a 6432-wide input) would need more than the 160 KB of
+    LDS for the per-row solve: the call must return WR_EUNSUPPORTED before launching anything, so
+    codes, scales and dev_info keep what they held."""
+    rows, g = 2, 32
+    n = 201 * g
+    H = torch.eye(n, dtype=torch.float32, device="cuda")
+    codes = torch.full((rows, n), 1, dtype=torch.uint8, device="cuda")
+    scales = torch.ones(rows, n // g, dtype=torch.float16, device="cuda")
+    info = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    bits = torch.full((rows,), 2, dtype=torch.uint8, device="cuda")
+    B = torch.zeros(rows, 4, dtype=torch.float32, device="cuda")
+    A = torch.zeros(4, n, dtype=torch.float32, device="cuda")
+    for recode in (False, True, "gptq"):
+        with pytest.raises(wr.WringerError) as e:
+            wr.wr_wring_solve(ctx, H, bits, g, 0.01, codes, scales, info, B=B, A=A, alpha=4.0, recode=recode)
+        assert e.value.status == wr.WR_EUNSUPPORTED
+    torch.cuda.synchronize()
+    assert bool((codes == 1).all()) and bool((scales == 1).all()) and int(info.item()) == 7

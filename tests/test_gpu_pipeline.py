@@ -4,13 +4,19 @@ import pytest
 import torch
 
 import oracle
-from parity import stage_check
+from parity import TIE, stage_check
 
 pytestmark = pytest.mark.gpu
-# Each side forms its own H here (GPU: exact products, fp32 segments of 512 rows added in fp64;
-# oracle: fp64), so a row's first differing code may sit a little further from a threshold than
-# in the same-H kernel tests: within 0.02 level units, 1 % of the spacing between thresholds.
-TIE = 2e-2
+# Each side forms its own H from the same inputs and the two H must agree within 1e-5 (relative
+# Frobenius); the later stages are then compared on the GPU's H and stored weights, widened to
+# fp64 (see tests/parity.py for why).
+
+
+def _same_h_ref(out, bits, g, B, A, alpha):
+    """The oracle's sweep, joint scales and wring on the GPU's H and stored (rotated) weights."""
+    H = out["H"].cpu().double().numpy()
+    W = out["W"].float().cpu().double().numpy()
+    return oracle.solve_rows(W, H, bits, g, 0.01, B, A, alpha)
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +36,10 @@ def test_toy_layer_end_to_end(ctx):
                                 A.cuda(), 8.0, keep_stages=True)
     ref = oracle.solve_module(W.double().numpy(), X.double().numpy(), 2, 32, 0.01, 0.01, B.double().numpy(),
                               A.double().numpy(), 8.0)
-    codes, scales = stage_check(out, ref, ref["H0"], 2, 32, 3, TIE, strict_loss=True)
+    Hg = out["H"].cpu().double().numpy()
+    assert np.linalg.norm(Hg - ref["H"]) <= 1e-5 * np.linalg.norm(ref["H"])
+    same = _same_h_ref(out, 2, 32, B.double().numpy(), A.double().numpy(), 8.0)
+    codes, scales = stage_check(out, same, ref["H0"], 2, 32, 3, TIE, strict_loss=True)
     # the packed container is bit-exact given identical codes and scales
     from post_bit_weight_amd import _lib as wr
     buf = torch.empty(oracle.packed_bytes(256, 512, 2, 32), dtype=torch.uint8, device="cuda")
@@ -55,7 +64,9 @@ def test_rotated_padded_layer_end_to_end(ctx):
                               A.double().numpy(), 8.0, had_block=m, signs=s.double().numpy(), n_store=n)
     Hg = out["H"].cpu().double().numpy()
     assert np.linalg.norm(Hg - ref["H"]) <= 1e-5 * np.linalg.norm(ref["H"])
-    stage_check(out, ref, ref["H0"], 2, 64, 3, TIE)
+    assert np.abs(out["W"].cpu().double().numpy() - ref["W"]).max() <= 1e-6 * np.abs(ref["W"]).max()
+    same = _same_h_ref(out, 2, 64, B.double().numpy(), A.double().numpy(), 8.0)
+    stage_check(out, same, ref["H0"], 2, 64, 3, TIE)
 
 
 def test_mixed_bits_shared_H(ctx):
@@ -75,4 +86,39 @@ def test_mixed_bits_shared_H(ctx):
                             A.cuda(), 16.0, keep_stages=True)
     ref = oracle.solve_module(W.double().numpy(), X.double().numpy(), bits, g, 0.01, 0.01, B.double().numpy(),
                               A.double().numpy(), 16.0)
-    stage_check(out, ref, ref["H0"], bits, g, oracle.levels_count(bits), TIE)
+    Hg = H.cpu().double().numpy()
+    assert np.linalg.norm(Hg - ref["H"]) <= 1e-5 * np.linalg.norm(ref["H"])
+    same = oracle.solve_rows(W.double().numpy(), Hg, bits, g, 0.01, B.double().numpy(), A.double().numpy(), 16.0)
+    stage_check(out, same, ref["H0"], bits, g, oracle.levels_count(bits), TIE)
+
+
+def test_zero_rows_and_zero_blocks(ctx):
+    """All-zero rows and all-zero first blocks through sweep, joint scales and wring.  Reading of the
+    pages (block scales are the block's absmax over L): an all-zero block gets scale 0 and the
+    middle upper code (L + 1) / 2, which dequantises to 0; a zero row makes no error, so it stays
+    zero through the sweep and its joint scales are 0; the wring's target is then B A alone."""
+    from post_bit_weight_amd import pipeline, synth
+    n, g, rows = 256, 64, 48
+    X = synth.SpectralSource(n, seed=501).chunk(0, 3000, dtype=torch.bfloat16)
+    W = synth.student_t((rows, n), seed=502)
+    W[::5] = 0.0                          # whole rows
+    W[1::7, 0:g] = 0.0                    # the first block (no earlier column feeds it)
+    W[2::3, n - g:] = 0.0                 # the last block (the feedback of earlier columns fills it)
+    B = synth.gaussian((rows, 8), 0.01, seed=503)
+    A = synth.gaussian((8, n), 0.01, seed=504)
+    out = pipeline.solve_module(ctx, W.cuda(), [X.cuda()], 2, g, 0.01, 0.01, B.cuda(), A.cuda(), 8.0,
+                                keep_stages=True)
+    torch.cuda.synchronize()
+    assert (out["dev_info"].cpu().numpy() == 0).all()
+    gs = out["gptq_scales"].cpu().numpy().astype(np.float64)
+    gc = out["gptq_codes"].cpu().numpy()
+    zr = np.arange(rows) % 5 == 0
+    zb = (np.arange(rows) % 7 == 1) | zr
+    assert np.all(gs[zb, 0] == 0.0) and np.all(gc[zb, :g] == 2)
+    assert np.all(gs[zr] == 0.0) and np.all(gc[zr] == 2)
+    assert np.all(out["joint_scales"].cpu().numpy()[zr] == 0.0)
+    assert np.isfinite(out["scales"].cpu().numpy().astype(np.float64)).all()
+    H0 = oracle.second_moment(X.double().numpy())
+    same = _same_h_ref(out, 2, g, B.double().numpy(), A.double().numpy(), 8.0)
+    assert np.all(same["gptq_scales"][zb, 0] == 0.0)
+    stage_check(out, same, H0, 2, g, 3, TIE, strict_loss=True)
