@@ -19,7 +19,9 @@
  *     anything is launched and leave every output untouched.
  *   - The library allocates no device memory.  Entry points that need scratch
  *     space use the workspace registered with wr_set_workspace; its size comes
- *     from wr_workspace_bytes.
+ *     from wr_workspace_bytes.  (The one exception, wr_hessian_accumulate_noalloc,
+ *     uses a static device array that the HIP runtime places with the library's
+ *     code on each GPU.)
  *   - Numerical failures are reported LAPACK-style through a device int32
  *     `dev_info` (read it after synchronising the stream): 0 = success;
  *     k > 0 = H is not numerically positive definite (the Cholesky
@@ -48,8 +50,12 @@ enum wr_status {
   WR_EINVAL = 1,       /* invalid argument (null pointer, bad size, bad flag) */
   WR_EWORKSPACE = 2,   /* registered workspace missing or too small */
   WR_EHIP = 3,         /* a HIP runtime call failed */
-  WR_EUNSUPPORTED = 4  /* valid request the library does not implement */
+  WR_EUNSUPPORTED = 4, /* valid request the library does not implement */
+  WR_ESCRATCH = 5      /* request too large for the static scratch of an allocation-free entry point */
 };
+
+/* Device scratch, per GPU, of the allocation-free entry point (wr_hessian_accumulate_noalloc). */
+#define WR_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
 
 enum wr_dtype { WR_F32 = 0, WR_BF16 = 1 };
 
@@ -100,6 +106,25 @@ int wr_set_workspace(wr_ctx* ctx, void* dev_ptr, size_t bytes);
  */
 int wr_hessian_accumulate(wr_ctx* ctx, const void* X, int x_dtype, int64_t rows, int64_t n, int64_t ldx,
                           double* S, int flags);
+
+/*
+ * Allocation-free variant of wr_hessian_accumulate, for callers that cannot allocate device
+ * memory or register a workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, operation and accuracy; the registered workspace is
+ * not used.  Its scratch (the row splits' fp32 partial sums, and for fp32 X the three bf16 parts)
+ * is a static device array of WR_STATIC_SCRATCH_BYTES per GPU, which the library holds from the
+ * first wr_create on that GPU until the process ends.  bf16 X of any size: when the splits'
+ * partials would not fit, fewer splits run at a time over row slices (each split still sums at
+ * most 16384 rows in fp32); the result is bit-identical to wr_hessian_accumulate's when
+ * wr_workspace_bytes(WR_OP_HESSIAN, rows, n, ...) <= WR_STATIC_SCRATCH_BYTES.  fp32 X: row
+ * slices whose parts and partials fit; WR_ESCRATCH when not even 512 rows fit (n above 21845),
+ * checked before any launch.  The call allocates nothing.  Every call on one GPU uses
+ * that GPU's one array: calls that overlap on the same GPU (several streams, contexts or threads)
+ * race and give wrong results; calls queued on one stream are safe.  Nothing in the array needs
+ * to start at zero (every call writes what it reads).
+ */
+int wr_hessian_accumulate_noalloc(wr_ctx* ctx, const void* X, int x_dtype, int64_t rows, int64_t n, int64_t ldx,
+                                  double* S, int flags);
 
 /*
  * (a)+(b) Finalize, rotate and damp.  Writes the full symmetric H (n_store x

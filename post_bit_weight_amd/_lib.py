@@ -14,7 +14,8 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwringer.so")
 
-WR_OK, WR_EINVAL, WR_EWORKSPACE, WR_EHIP, WR_EUNSUPPORTED = 0, 1, 2, 3, 4
+WR_OK, WR_EINVAL, WR_EWORKSPACE, WR_EHIP, WR_EUNSUPPORTED, WR_ESCRATCH = 0, 1, 2, 3, 4, 5
+WR_STATIC_SCRATCH_BYTES = 64 << 20
 WR_F32, WR_BF16 = 0, 1
 (WR_OP_HESSIAN, WR_OP_GPTQ, WR_OP_WRING, WR_OP_ROTATE, WR_OP_FINALIZE, WR_OP_WRING_GPTQ, WR_OP_TRELLIS,
  WR_OP_GEMV) = range(8)
@@ -26,7 +27,7 @@ WR_RECODE_SEARCH = 4
 
 EXPORTED = (
     "wr_create", "wr_destroy", "wr_workspace_bytes", "wr_set_workspace",
-    "wr_hessian_accumulate", "wr_hessian_finalize", "wr_hadamard_rotate",
+    "wr_hessian_accumulate", "wr_hessian_accumulate_noalloc", "wr_hessian_finalize", "wr_hadamard_rotate",
     "wr_gptq_sweep", "wr_wring_solve", "wr_pack", "wr_unpack", "wr_materialize", "wr_trellis_quantize",
     "wr_packed_gemv", "wr_strerror",
 )
@@ -61,6 +62,7 @@ def load():
         "wr_workspace_bytes": (SZ, [I, I64, I64, c.c_int32, c.c_int32, c.c_int32]),
         "wr_set_workspace": (I, [P, P, SZ]),
         "wr_hessian_accumulate": (I, [P, P, I, I64, I64, I64, P, I]),
+        "wr_hessian_accumulate_noalloc": (I, [P, P, I, I64, I64, I64, P, I]),
         "wr_hessian_finalize": (I, [P, P, I64, I64, F, I64, P, I64, P, c.c_int32, P]),
         "wr_hadamard_rotate": (I, [P, P, I64, I64, I64, c.c_int32, P, I]),
         "wr_gptq_sweep": (I, [P, P, I, I64, I64, I64, P, I64, P, c.c_int32, c.c_int32, P, P, P]),
@@ -162,6 +164,18 @@ def wr_hessian_accumulate(ctx, X, S, zero=False):
         raise ValueError("S must be a contiguous n x n fp64 tensor")
     ctx.ensure_workspace(wr_workspace_bytes(WR_OP_HESSIAN, rows, n))
     _check("wr_hessian_accumulate", load().wr_hessian_accumulate(
+        ctx.handle, _ptr(X), _wdtype(X), rows, n, ldx, _ptr(S), WR_H_ZERO if zero else 0))
+
+
+def wr_hessian_accumulate_noalloc(ctx, X, S, zero=False):
+    """As wr_hessian_accumulate, without the registered workspace (the library's static scratch)."""
+    _dev(X, "X", FLOATS)
+    _dev(S, "S", (torch.float64,))
+    rows, n = X.shape
+    ldx = _rowmajor(X, "X")
+    if tuple(S.shape) != (n, n) or not S.is_contiguous():
+        raise ValueError("S must be a contiguous n x n fp64 tensor")
+    _check("wr_hessian_accumulate_noalloc", load().wr_hessian_accumulate_noalloc(
         ctx.handle, _ptr(X), _wdtype(X), rows, n, ldx, _ptr(S), WR_H_ZERO if zero else 0))
 
 

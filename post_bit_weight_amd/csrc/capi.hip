@@ -8,6 +8,8 @@ size_t wr_gptq_ws_bytes(int64_t rows, int64_t n);
 size_t wr_wring_ws_bytes(int64_t rows, int64_t n, int32_t group, int32_t rank);
 size_t wr_wring_gptq_ws_bytes(int64_t rows, int64_t n, int32_t group, int32_t rank);
 int wr_hessian_accumulate_impl(wr_ctx*, const void*, int, int64_t, int64_t, int64_t, double*, int);
+int wr_hessian_accumulate_static_impl(wr_ctx*, const void*, int, int64_t, int64_t, int64_t, double*, int);
+int wr_static_scratch_init(int device);
 int wr_hessian_finalize_impl(wr_ctx*, const double*, int64_t, int64_t, float, int64_t, float*, int64_t, float*, int32_t,
                              const int8_t*);
 size_t wr_finalize_ws_bytes(int64_t n_store);
@@ -68,6 +70,9 @@ int wr_create(wr_ctx** out, int device, void* hip_stream) {
   c->ws = nullptr;
   c->ws_bytes = 0;
   c->num_cu = cus > 0 ? cus : kDefaultCUs;
+  // device address of the allocation-free entry point's static scratch, once per device (a
+  // failure here is reported by that entry point, which tries again)
+  (void)wr_static_scratch_init(device);
   *out = c;
   return WR_OK;
 }
@@ -118,6 +123,22 @@ int wr_hessian_accumulate(wr_ctx* ctx, const void* X, int x_dtype, int64_t rows,
   DeviceScope ds(ctx->device);
   if (!ds.ok) return WR_EHIP;
   return wr_hessian_accumulate_impl(ctx, X, x_dtype, rows, n, ldx, S, flags);
+}
+
+int wr_hessian_accumulate_noalloc(wr_ctx* ctx, const void* X, int x_dtype, int64_t rows, int64_t n, int64_t ldx,
+                                  double* S, int flags) {
+  if (!ctx || !S || !valid_dtype(x_dtype) || rows < 0 || n <= 0 || n > 65536 || ldx < n || (flags & ~WR_H_ZERO))
+    return WR_EINVAL;
+  if (rows > 0 && !X) return WR_EINVAL;
+  if (n % 8 != 0) return WR_EINVAL;
+  if (rows > 0 && x_dtype == WR_BF16 && (ldx % 8 != 0 || !aligned(X, 16))) return WR_EINVAL;
+  if (rows > 65535 * 4096) return WR_EINVAL;
+  if (ldx > ((int64_t)1 << 24)) return WR_EUNSUPPORTED;
+  if (!aligned(S, 8)) return WR_EINVAL;
+  DeviceScope ds(ctx->device);
+  if (!ds.ok) return WR_EHIP;
+  if (wr_static_scratch_init(ctx->device) != WR_OK) return WR_EHIP;
+  return wr_hessian_accumulate_static_impl(ctx, X, x_dtype, rows, n, ldx, S, flags);
 }
 
 int wr_hessian_finalize(wr_ctx* ctx, const double* S, int64_t n, int64_t total_rows, float damp_frac, int64_t n_store,
@@ -262,6 +283,7 @@ const char* wr_strerror(int status) {
     case WR_EWORKSPACE: return "workspace missing or too small";
     case WR_EHIP: return "HIP runtime error";
     case WR_EUNSUPPORTED: return "unsupported configuration";
+    case WR_ESCRATCH: return "request exceeds the static scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }

@@ -17,6 +17,8 @@
 // fill the chip; calls longer than 16384 rows become one launch per 16384-row
 // slice), or the rows are cut into splits whose fp32 sums a second kernel adds
 // into S in a fixed order.  Deterministic, no atomics.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace wr {
@@ -417,11 +419,11 @@ size_t wr_hessian_ws_bytes(int64_t rows, int64_t n, int x_dtype, int num_cu) {
 
 // One SYRK pass S_lower += XA^T XB (bf16 sources, ld ldx), with its split-K reduction.
 static int syrk_pass(wr_ctx* ctx, const uint16_t* XA, const uint16_t* XB, int64_t rows, int64_t n, int64_t ldx,
-                     double* S, float* partial, bool precise) {
+                     double* S, float* partial, bool precise, int ks_cap = 64) {
   if (!lds_limit((const void*)syrk_bf16_kernel, SY_LDS_BYTES)) return WR_EHIP;
   hipStream_t st = ctx->stream;
   const int tiles = syrk_tiles(n);
-  const int ks = syrk_ksplit(rows, n, kSplitCUs, precise);
+  const int ks = std::min(syrk_ksplit(rows, n, kSplitCUs, precise), std::max(ks_cap, 1));
   if (ks == 1 && rows > SY_MAX_ROWS) {
     for (int64_t r0 = 0; r0 < rows; r0 += SY_MAX_ROWS) {
       const int64_t rc = std::min<int64_t>(SY_MAX_ROWS, rows - r0);
@@ -470,6 +472,110 @@ int wr_hessian_accumulate_impl(wr_ctx* ctx, const void* X, int x_dtype, int64_t 
   for (const auto& t : terms) {
     const int rc = syrk_pass(ctx, P[t[0]], P[t[1]], rows, n, n, S, partial, true);
     if (rc) return rc;
+  }
+  return WR_OK;
+}
+
+// ---------------------------------------------------------------- allocation-free variant
+// Device scratch of the allocation-free accumulate: a file-scope array, one copy per GPU, held
+// until the process ends.  In host code `scratch` names a host-side stand-in, never the device
+// memory: its device address comes from hipGetSymbolAddress, taken once per device (with that
+// device current) by wr_static_scratch_init, which wr_create calls; only that address reaches
+// the kernels.
+static __device__ __align__(256) unsigned char scratch[WR_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int wr_static_scratch_init(int device) {
+  if (device < 0 || device >= kMaxDevices) return WR_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device]) return WR_OK;
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) return WR_EHIP;
+  if (prev != device && hipSetDevice(device) != hipSuccess) return WR_EHIP;
+  void* ptr = nullptr;
+  const hipError_t err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (prev != device) (void)hipSetDevice(prev);
+  if (err != hipSuccess || !ptr) return WR_EHIP;
+  g_scratch_ptr[device] = ptr;
+  return WR_OK;
+}
+
+static void* static_scratch(int device) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return device >= 0 && device < kMaxDevices ? g_scratch_ptr[device] : nullptr;
+}
+
+// Partial-sum bytes of k row splits of the fp32 path (a single split adds into S directly).
+static size_t f32_partial_bytes(int64_t k, int64_t n) {
+  return k > 1 ? (((size_t)k * syrk_tiles(n) * SY_T * SY_T * sizeof(float) + 255) & ~(size_t)255) : 0;
+}
+
+// Rows of fp32 input whose three bf16 planes and split partials fit in `bytes` (512 k rows for
+// k splits of 512 rows, the split length of the fp32 path), or 0 when not even 512 rows fit.
+static int64_t f32_rows_fitting(int64_t n, size_t bytes) {
+  for (int64_t k = 64; k >= 1; k /= 2) {
+    const int64_t c = 512 * k;
+    const size_t need = 256 + f32_partial_bytes(k, n) + 3 * (((size_t)c * n * 2 + 255) & ~(size_t)255);
+    if (need <= bytes) return c;
+  }
+  return 0;
+}
+
+// Same result as wr_hessian_accumulate_impl (bit-identical when its workspace need fits the static
+// scratch), with the scratch taken from the per-device static array: bf16 input with fewer row
+// splits at a time when their partials would not fit (each split still sums at most 16384 rows in
+// fp32), fp32 input in row slices whose bf16 planes and partials fit.
+int wr_hessian_accumulate_static_impl(wr_ctx* ctx, const void* X, int x_dtype, int64_t rows, int64_t n,
+                                      int64_t ldx, double* S, int flags) {
+  char* ws = static_cast<char*>(static_scratch(ctx->device));
+  if (!ws) return WR_EHIP;
+  const size_t cap = WR_STATIC_SCRATCH_BYTES;
+  hipStream_t st = ctx->stream;
+  if (rows > 0 && x_dtype == WR_F32 && f32_rows_fitting(n, cap) == 0) return WR_ESCRATCH;
+  if (flags & WR_H_ZERO) {
+    hipLaunchKernelGGL(zero_lower_kernel, dim3((unsigned)n), dim3(256), 0, st, S, (int)n);
+    WR_CHECK_LAUNCH();
+  }
+  if (rows == 0) return WR_OK;
+  float* partial = reinterpret_cast<float*>(ws + 256);
+  const size_t part = (size_t)syrk_tiles(n) * SY_T * SY_T * sizeof(float);
+  if (x_dtype == WR_BF16) {
+    const uint16_t* Xb = static_cast<const uint16_t*>(X);
+    const int ks_fit = (int)std::min<size_t>(64, (cap - 256) / part);
+    if (ks_fit >= syrk_ksplit(rows, n, kSplitCUs, false))
+      return syrk_pass(ctx, Xb, Xb, rows, n, ldx, S, partial, false);
+    if (ks_fit < 2) return syrk_pass(ctx, Xb, Xb, rows, n, ldx, S, partial, false, 1);
+    const int64_t slice = (int64_t)ks_fit * SY_MAX_ROWS;
+    for (int64_t r0 = 0; r0 < rows; r0 += slice) {
+      const int rc = syrk_pass(ctx, Xb + r0 * ldx, Xb + r0 * ldx, std::min(slice, rows - r0), n, ldx, S, partial,
+                               false, ks_fit);
+      if (rc) return rc;
+    }
+    return WR_OK;
+  }
+  const int64_t slice = f32_rows_fitting(n, cap);
+  const size_t plane_cap = ((size_t)slice * n * 2 + 255) & ~(size_t)255;
+  const int kmax = (int)(slice / 512);
+  uint16_t* P[3];
+  for (int k = 0; k < 3; ++k)
+    P[k] = reinterpret_cast<uint16_t*>(ws + 256 + f32_partial_bytes(kmax, n) + k * plane_cap);
+  const float* Xf = static_cast<const float*>(X);
+  static const int terms[6][2] = {{2, 0}, {1, 1}, {0, 2}, {1, 0}, {0, 1}, {0, 0}};  // small terms first
+  for (int64_t r0 = 0; r0 < rows; r0 += slice) {
+    const int64_t rc_rows = std::min(slice, rows - r0);
+    const unsigned gx = (unsigned)std::min<int64_t>((n + 255) / 256, 16);
+    hipLaunchKernelGGL(split3_kernel, dim3(gx, (unsigned)rc_rows), dim3(256), 0, st, Xf + r0 * ldx, rc_rows, (int)n,
+                       ldx, P[0], P[1], P[2]);
+    WR_CHECK_LAUNCH();
+    for (const auto& t : terms) {
+      const int rc = syrk_pass(ctx, P[t[0]], P[t[1]], rc_rows, n, n, S, partial, true, kmax);
+      if (rc) return rc;
+    }
   }
   return WR_OK;
 }
