@@ -58,6 +58,7 @@ def parse():
     p.add_argument("--calib-sets", type=int, default=4,
                    help="body: distinct per-layer calibration sets kept resident (layer l reads set l mod K)")
     p.add_argument("--no-breakdown", action="store_true", help="body: skip the untimed per-call breakdown pass")
+    p.add_argument("--no-measures", action="store_true", help="body: skip the model cards' measures of layer 0")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=None, help="weight rows in the oracle sample")
     p.add_argument("--cpu-calib", type=int, default=None, help="calibration rows in the oracle sample")
@@ -559,6 +560,37 @@ def body_check(torch, I):
                 raise RuntimeError(f"layer {layer}, input dim {n}: pack/unpack round trip differs")
 
 
+def body_measures(wr, ctx, I, torch, layer=0):
+    """The model cards' measures for every module of one layer (off the timed path): grid distance of
+    the parent and the filled weights, GPTQ-vs-nearest code disagreement without and with the adapter,
+    one-ulp moves of the fp16 projection.  Returns {module: {measure: value}} and the weight-averaged
+    values."""
+    from post_bit_weight_amd import measures, pipeline
+    cfg = I.cfg
+    g, lam, hb, N = cfg["group"], cfg["lam"], cfg["had_block"], cfg["calib_rows"]
+    per, tot, wsum = {}, {}, 0
+    for n in I.dims:
+        G = I.groups[layer][n]
+        wr.wr_hessian_accumulate(ctx, I.X[n][layer % I.P], I.S[n], zero=True)
+        H, _ = pipeline.finalize_hessian(ctx, I.S[n], N, cfg["damp"], n, hb, I.signs[n])
+        mods = [dict(name=m["name"], bits=m["bits"], W=pipeline.prepare_weights(ctx, G["W"][m["r0"]:m["r1"]], n, hb,
+                                                                                I.signs[n]))
+                for m in G["mods"]]
+        res = pipeline.solve_group(ctx, mods, H, g, lam, cfg["lazy_batch"], keep_stages=True)
+        for m, mod in zip(G["mods"], mods):
+            r = res[m["name"]]
+            bits_t = G["bits"][m["r0"]:m["r1"]]
+            vals = measures.module_measures(ctx, H, mod["W"], bits_t, g, lam, r["gptq_codes"], r["joint_scales"],
+                                            m["B"], m["A"], float(cfg["rank"]))
+            per[m["name"]] = vals
+            w = mod["W"].numel()
+            wsum += w
+            for k, v in vals.items():
+                tot[k] = tot.get(k, 0.0) + v * w
+        del res, mods, H
+    return per, {k: v / wsum for k, v in tot.items()}
+
+
 def cpu_baseline_body(I, body, torch, n_rows=2, h_rows=None):
     """The oracle, unchanged, on a bounded sample of the body; extrapolated to the 36 layers.
 
@@ -744,6 +776,10 @@ def main_body(args):
     }
     if stage is not None:
         line["stage_ms"] = stage
+    if not args.no_measures:
+        progress("the model cards' measures for layer 0 (untimed)")
+        per, mean = body_measures(wr, ctx, I, torch)
+        line["measures_layer0"] = {"weighted_mean": mean, "per_module": per}
     if not args.no_cpu_baseline:
         progress("timing the oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline_body(I, body, torch, n_rows=args.cpu_rows or 2, h_rows=args.cpu_calib)

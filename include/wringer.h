@@ -67,7 +67,8 @@ enum wr_op {             /* operations that need workspace, for wr_workspace_byt
   WR_OP_FINALIZE = 4,    /* n = n_store; needed by wr_hessian_finalize with a rotation */
   WR_OP_WRING_GPTQ = 5,  /* rows, n, group, rank: wr_wring_solve with WR_RECODE_GPTQ */
   WR_OP_TRELLIS = 6,     /* rows, n, group = number of trellis states: wr_trellis_quantize */
-  WR_OP_GEMV = 7         /* rows = number of input vectors, n = n_store: wr_packed_gemv */
+  WR_OP_GEMV = 7,        /* rows = number of input vectors, n = n_store: wr_packed_gemv */
+  WR_OP_STATS = 8        /* rows: wr_quant_stats */
 };
 
 enum wr_hessian_flags { WR_H_ZERO = 1 };               /* zero S before accumulating */
@@ -284,6 +285,46 @@ int wr_trellis_quantize(wr_ctx* ctx, const float* T, int64_t ldt, int64_t rows, 
 int wr_packed_gemv(wr_ctx* ctx, const uint8_t* in, size_t in_bytes, int64_t rows, int64_t n_store, int32_t bits,
                    int32_t group, int32_t had_block, const int8_t* signs, const float* x, int64_t n_in, int64_t ldx,
                    int32_t batch, float* y, int64_t ldy);
+
+/*
+ * Measures of a quantized module (Wringer Qwen3-4B model card, "Why the solver changed": the
+ * relative Frobenius distance of weights to their nearest representation on the joint-scale grid,
+ * and the share of codes on which the GPTQ and nearest-point solvers disagree; Agents-A1 model
+ * card, "Honest caveats": the share of bf16 weights that projecting the scales to fp16 at solve
+ * time moves by one ulp).  Off the solve's own path; three calls serve them:
+ *
+ * wr_set_scale_trace: when raw is non-null, every later joint scale solve on this context (the
+ * joint solve of wr_wring_solve, with or without a recode; not WR_RECODE_SEARCH, which solves
+ * none) also writes each row's solution before the fp16 projection, as fp32, to raw (rows x n/group
+ * of that call, row-major); capacity (elements) smaller than a call's rows * n/group makes that
+ * call return WR_EINVAL before launching anything.  raw = null stops it.
+ */
+int wr_set_scale_trace(wr_ctx* ctx, float* raw, int64_t capacity);
+
+/*
+ * wr_wring_target: the watered target alone, T_out (rows x n fp32, contiguous) = target (dtype
+ * t_dtype, ld ldt) or, when target is null, dequant(codes, scales), plus (alpha / rank) B A when B and
+ * A are non-null -- exactly the target wr_wring_solve forms.  codes and scales are read only.
+ * dev_info: 0, or -1 for a non-finite value.  Workspace: WR_OP_WRING (rows, n, group, rank).
+ */
+int wr_wring_target(wr_ctx* ctx, const void* target, int t_dtype, int64_t ldt, const void* B, const void* A,
+                    int32_t rank, float alpha, int ab_dtype, int64_t rows, int64_t n, const uint8_t* bits,
+                    int32_t group, const uint8_t* codes, const uint16_t* scales, float* T_out, int32_t* dev_info);
+
+/*
+ * wr_quant_stats: sums over the module (rows x n codes of per-row `bits`, fp16 scales per `group`),
+ * in fp64 and a fixed order (deterministic), written to out (device, 4 doubles):
+ *   out[0] = sum (t - (2c - L) s)^2 and out[1] = sum t^2 over T (rows x n fp32, ld ldt), or 0 when
+ *            T is null (the distance to the grid is sqrt(out[0] / out[1]));
+ *   out[2] = the number of codes different from codes_ref (rows x n uint8), or 0 when null;
+ *   out[3] = the number of weights whose bf16 rounding (nearest, ties to even) of (2c - L) s differs
+ *            from that of (2c - L) s_raw, s_raw the unprojected fp32 scales (rows x n/group, as
+ *            wr_set_scale_trace writes them), or 0 when null.
+ * Workspace: WR_OP_STATS (rows).
+ */
+int wr_quant_stats(wr_ctx* ctx, const float* T, int64_t ldt, const uint8_t* codes, const uint16_t* scales,
+                   const uint8_t* bits, int64_t rows, int64_t n, int32_t group, const uint8_t* codes_ref,
+                   const float* scales_raw, double* out);
 
 /* Static description of a status code. */
 const char* wr_strerror(int status);

@@ -36,7 +36,8 @@ from .gptq import upper_cholesky_of_inverse, feedback_sweep, gptq_sweep, integer
 from .joint import joint_scales, row_gram
 from .wring import wring_target, wring, wring_gptq, wring_scale_search, scale_search_block
 from .pack import pack, unpack, packed_bytes, code_bytes_per_row
-from .metrics import proxy_loss, ledger_bits_per_weight, threshold_distance
+from .metrics import (proxy_loss, ledger_bits_per_weight, threshold_distance, grid_representation,
+                      grid_distance, code_disagreement, projection_ulp_moves)
 from .solve import solve_module, solve_rows
 from .materialize import bf16_rne_bits, bf16_bits_to_f64, materialize, materialize_exact
 from .trellis import viterbi as trellis_viterbi, greedy as trellis_greedy, decode as trellis_decode
@@ -50,7 +51,8 @@ __all__ = [
     "joint_scales", "row_gram",
     "wring_target", "wring", "wring_gptq", "wring_scale_search", "scale_search_block",
     "pack", "unpack", "packed_bytes", "code_bytes_per_row",
-    "proxy_loss", "ledger_bits_per_weight", "threshold_distance",
+    "proxy_loss", "ledger_bits_per_weight", "threshold_distance", "grid_representation", "grid_distance",
+    "code_disagreement", "projection_ulp_moves",
     "solve_module", "solve_rows",
     "bf16_rne_bits", "bf16_bits_to_f64", "materialize", "materialize_exact",
     "trellis_viterbi", "trellis_greedy", "trellis_decode",

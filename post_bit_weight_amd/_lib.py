@@ -18,7 +18,7 @@ WR_OK, WR_EINVAL, WR_EWORKSPACE, WR_EHIP, WR_EUNSUPPORTED, WR_ESCRATCH = 0, 1, 2
 WR_STATIC_SCRATCH_BYTES = 64 << 20
 WR_F32, WR_BF16 = 0, 1
 (WR_OP_HESSIAN, WR_OP_GPTQ, WR_OP_WRING, WR_OP_ROTATE, WR_OP_FINALIZE, WR_OP_WRING_GPTQ, WR_OP_TRELLIS,
- WR_OP_GEMV) = range(8)
+ WR_OP_GEMV, WR_OP_STATS) = range(9)
 WR_H_ZERO = 1
 WR_ROT_ROWS, WR_ROT_ROWS_INVERSE, WR_ROT_SYM = 0, 1, 2
 WR_RECODE_NEAREST = 1
@@ -29,7 +29,7 @@ EXPORTED = (
     "wr_create", "wr_destroy", "wr_workspace_bytes", "wr_set_workspace",
     "wr_hessian_accumulate", "wr_hessian_accumulate_noalloc", "wr_hessian_finalize", "wr_hadamard_rotate",
     "wr_gptq_sweep", "wr_wring_solve", "wr_pack", "wr_unpack", "wr_materialize", "wr_trellis_quantize",
-    "wr_packed_gemv", "wr_strerror",
+    "wr_packed_gemv", "wr_set_scale_trace", "wr_wring_target", "wr_quant_stats", "wr_strerror",
 )
 
 
@@ -73,6 +73,9 @@ def load():
         "wr_trellis_quantize": (I, [P, P, I64, I64, I64, c.c_int32, c.c_int32, P, c.c_int32, P, I64, P, I64, P]),
         "wr_packed_gemv": (I, [P, P, SZ, I64, I64, c.c_int32, c.c_int32, c.c_int32, P, P, I64, I64, c.c_int32, P,
                                I64]),
+        "wr_set_scale_trace": (I, [P, P, I64]),
+        "wr_wring_target": (I, [P, P, I, I64, P, P, c.c_int32, F, I, I64, I64, P, c.c_int32, P, P, P, P]),
+        "wr_quant_stats": (I, [P, P, I64, P, P, P, I64, I64, c.c_int32, P, P, P]),
         "wr_strerror": (c.c_char_p, [I]),
     }
     for name, (res, args) in sig.items():
@@ -341,3 +344,64 @@ def wr_packed_gemv(ctx, buf, rows, n_store, bits, group, x, y, had_block=0, sign
     _check("wr_packed_gemv", load().wr_packed_gemv(ctx.handle, _ptr(buf), buf.numel(), rows, n_store, int(bits),
                                                    int(group), int(had_block), _ptr(signs), _ptr(x), x.shape[1],
                                                    _rowmajor(x, "x"), batch, _ptr(y), _rowmajor(y, "y")))
+
+
+def wr_set_scale_trace(ctx, raw=None):
+    """Later joint solves on ctx also write their unprojected scales (fp32) into raw; None stops it."""
+    _dev(raw, "raw", (torch.float32,))
+    if raw is not None and not raw.is_contiguous():
+        raise ValueError("raw must be contiguous")
+    _check("wr_set_scale_trace", load().wr_set_scale_trace(ctx.handle, _ptr(raw), raw.numel() if raw is not None else 0))
+    ctx.scale_trace = raw
+
+
+def wr_wring_target(ctx, bits, group, T_out, dev_info, target=None, codes=None, scales=None, B=None, A=None,
+                    alpha=0.0):
+    """T_out (rows x n fp32) = target or dequant(codes, scales), plus (alpha / r) B A."""
+    _dev(target, "target", FLOATS)
+    _dev(B, "B", FLOATS)
+    _dev(A, "A", FLOATS)
+    _dev(bits, "bits", (torch.uint8,))
+    _dev(codes, "codes", (torch.uint8,))
+    _dev(scales, "scales", (torch.float16, torch.int16, torch.uint16))
+    _dev(T_out, "T_out", (torch.float32,))
+    _dev(dev_info, "dev_info", (torch.int32,))
+    rows, n = T_out.shape
+    if not T_out.is_contiguous():
+        raise ValueError("T_out must be contiguous")
+    ldt = _rowmajor(target, "target") if target is not None else 0
+    rank, ab_dtype = 0, WR_F32
+    if B is not None:
+        if A is None or B.dtype != A.dtype or not B.is_contiguous() or not A.is_contiguous():
+            raise ValueError("B and A must be contiguous tensors of one dtype")
+        rank = A.shape[0]
+        if tuple(B.shape) != (rows, rank) or tuple(A.shape) != (rank, n):
+            raise ValueError("B must be rows x r and A r x n")
+        ab_dtype = _wdtype(A)
+    ctx.ensure_workspace(wr_workspace_bytes(WR_OP_WRING, rows, n, group, rank, 0))
+    _check("wr_wring_target", load().wr_wring_target(
+        ctx.handle, _ptr(target), _wdtype(target) if target is not None else WR_F32, ldt, _ptr(B), _ptr(A), rank,
+        float(alpha), ab_dtype, rows, n, _ptr(bits), int(group), _ptr(codes), _ptr(scales), _ptr(T_out),
+        _ptr(dev_info)))
+
+
+def wr_quant_stats(ctx, codes, scales, bits, group, out, T=None, codes_ref=None, scales_raw=None):
+    """out (4 fp64, device): [sum (t - dequant)^2, sum t^2, codes differing from codes_ref,
+    weights whose bf16 rounding moves between the fp16 and the unprojected scales]."""
+    _dev(T, "T", (torch.float32,))
+    _dev(codes, "codes", (torch.uint8,))
+    _dev(codes_ref, "codes_ref", (torch.uint8,))
+    _dev(scales, "scales", (torch.float16, torch.int16, torch.uint16))
+    _dev(scales_raw, "scales_raw", (torch.float32,))
+    _dev(bits, "bits", (torch.uint8,))
+    _dev(out, "out", (torch.float64,))
+    rows, n = codes.shape
+    for t, name in ((codes, "codes"), (scales, "scales"), (codes_ref, "codes_ref"), (scales_raw, "scales_raw")):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if out.numel() < 4:
+        raise ValueError("out must hold 4 values")
+    ctx.ensure_workspace(wr_workspace_bytes(WR_OP_STATS, rows, n))
+    _check("wr_quant_stats", load().wr_quant_stats(
+        ctx.handle, _ptr(T), _rowmajor(T, "T") if T is not None else 0, _ptr(codes), _ptr(scales), _ptr(bits), rows, n,
+        int(group), _ptr(codes_ref), _ptr(scales_raw), _ptr(out)))

@@ -32,7 +32,7 @@ import time
 import torch
 
 from . import _lib as wr
-from . import pipeline, synth
+from . import measures, pipeline, synth
 
 MODULES = [  # name, output rows, input dim
     ("q", 4096, 2560), ("k", 1024, 2560), ("v", 1024, 2560), ("gate", 9728, 2560), ("up", 9728, 2560),
@@ -97,8 +97,10 @@ class _Timer:
 
 
 def quantize_layer(ctx, layer, streams, layers=36, calib_rows=262144, chunk=16384, had_block=512, group=64,
-                   rank=128, seed=2026, keep=None, on_group=None, timer=None):
-    """One layer: returns {name: dict(packed (device uint8), rows, n, bits, roundtrip_ok)}."""
+                   rank=128, seed=2026, keep=None, on_group=None, timer=None, measure=False):
+    """One layer: returns {name: dict(packed (device uint8), rows, n, bits, roundtrip_ok[, measures])}.
+    With measure, each module also gets the model cards' measures (measures.module_measures), computed
+    after the layer's solve and outside the timer."""
     dev = ctx.device
     out = {}
     tick = timer.start if timer is not None else (lambda: None)
@@ -130,7 +132,7 @@ def quantize_layer(ctx, layer, streams, layers=36, calib_rows=262144, chunk=1638
             mods.append(dict(name=name, bits=module_bits(layer, name, layers),
                              W=pipeline.prepare_weights(ctx, W, n, had_block, signs), W_raw=W, B=B, A=A,
                              alpha=float(rank)))
-        res = pipeline.solve_group(ctx, mods, H, group, keep_stages=keep is not None)
+        res = pipeline.solve_group(ctx, mods, H, group, keep_stages=keep is not None or measure)
         tock(e)
         for m in mods:
             r = res[m["name"]]
@@ -140,6 +142,10 @@ def quantize_layer(ctx, layer, streams, layers=36, calib_rows=262144, chunk=1638
             wr.wr_unpack(ctx, r["packed"], rows, n, m["bits"], group, c2, s2)
             ok = bool(torch.equal(c2, r["codes"]) and torch.equal(s2.view(torch.int16), r["scales"].view(torch.int16)))
             out[m["name"]] = dict(packed=r["packed"], rows=rows, n=n, bits=m["bits"], roundtrip_ok=ok)
+            if measure:
+                bits_t = torch.full((rows,), m["bits"], dtype=torch.uint8, device=dev)
+                out[m["name"]]["measures"] = measures.module_measures(
+                    ctx, H, m["W"], bits_t, group, 0.01, r["gptq_codes"], r["joint_scales"], m["B"], m["A"], m["alpha"])
         if on_group is not None:
             on_group(n, dict(S=S, H=H, total=total, signs=signs, modules=mods, result=res, stream=stream))
         info = res["_dev_info"]
@@ -150,22 +156,25 @@ def quantize_layer(ctx, layer, streams, layers=36, calib_rows=262144, chunk=1638
 
 
 def sweep_body(ctx, layers=36, calib_rows=262144, chunk=16384, had_block=512, group=64, rank=128, seed=2026,
-               layer_ids=None, log=print):
+               layer_ids=None, log=print, measure_layers=()):
     """Quantize layers (all, or layer_ids) and build the container.  Returns (container bytes, report)."""
     dev = ctx.device
     streams = {n: CalibrationStream(n, seed * 31 + n, dev) for n in DIMS}
     entries, meta = [], {"format": "wringer", "group": group, "had_block": had_block, "rank": rank, "modules": {}}
     roundtrip = True
+    measured = {}
     t0 = time.perf_counter()
     timer = _Timer(ctx.stream)
     ids = list(range(layers)) if layer_ids is None else list(layer_ids)
     for layer in ids:
         res = quantize_layer(ctx, layer, streams, layers, calib_rows, chunk, had_block, group, rank, seed,
-                             timer=timer)
+                             timer=timer, measure=layer in measure_layers)
         for name, r in res.items():
             key = f"layers.{layer}.{name}"
             entries.append((key + ".packed", r["packed"].cpu().numpy()))
             meta["modules"][key] = {"rows": r["rows"], "n": r["n"], "bits": r["bits"]}
+            if "measures" in r:
+                measured[key] = r["measures"]
             roundtrip &= r["roundtrip_ok"]
         log(f"layer {layer}: done ({time.perf_counter() - t0:.1f} s elapsed)")
     blob = pipeline.container_bytes(entries, meta)
@@ -174,6 +183,8 @@ def sweep_body(ctx, layers=36, calib_rows=262144, chunk=16384, had_block=512, gr
     report = {"layers": len(ids), "weights": weights, "payload_bytes": payload,
               "bits_per_weight": 8.0 * payload / weights, "container_bytes": len(blob),
               "roundtrip_bit_exact": roundtrip, "wall_s": time.perf_counter() - t0}
+    if measured:
+        report["measures"] = measured
     solve_ms = timer.total_ms()
     report["solve_gpu_ms"] = solve_ms
     report["weights_per_s"] = weights / (solve_ms * 1e-3)
@@ -185,10 +196,13 @@ def main():
     p.add_argument("--layers", type=int, default=36)
     p.add_argument("--calib-rows", type=int, default=262144)
     p.add_argument("--out", default=None, help="write the container here")
+    p.add_argument("--measure", default="", help="comma-separated layers whose modules also get the model cards' "
+                                                  "measures (grid distance, solver disagreement, projection moves)")
     args = p.parse_args()
     ctx = wr.Context(0)
+    ml = tuple(int(x) for x in args.measure.split(",") if x.strip())
     blob, report = sweep_body(ctx, layers=args.layers, calib_rows=args.calib_rows,
-                              log=lambda m: print(m, flush=True))
+                              log=lambda m: print(m, flush=True), measure_layers=ml)
     if args.out:
         with open(args.out, "wb") as f:
             f.write(blob)

@@ -22,6 +22,11 @@ int wr_pack_impl(wr_ctx*, const uint8_t*, const uint16_t*, int64_t, int64_t, int
 int wr_unpack_impl(wr_ctx*, const uint8_t*, int64_t, int64_t, int32_t, int32_t, uint8_t*, uint16_t*, uint16_t*);
 size_t wr_trellis_ws_bytes(int64_t rows, int64_t n, int32_t states);
 size_t wr_gemv_ws_bytes(int64_t n_store, int32_t batch);
+size_t wr_stats_ws_bytes(int64_t rows);
+int wr_quant_stats_impl(wr_ctx*, const float*, int64_t, const uint8_t*, const uint16_t*, const uint8_t*, int64_t,
+                        int64_t, int32_t, const uint8_t*, const float*, double*);
+int wr_wring_target_impl(wr_ctx*, const void*, int, int64_t, const void*, const void*, int32_t, float, int, int64_t,
+                         int64_t, const uint8_t*, int32_t, const uint8_t*, const uint16_t*, float*, int32_t*);
 int wr_packed_gemv_impl(wr_ctx*, const uint8_t*, int64_t, int64_t, int32_t, int32_t, int32_t, const int8_t*, const float*,
                         int64_t, int64_t, int32_t, float*, int64_t);
 int wr_trellis_quantize_impl(wr_ctx*, const float*, int64_t, int64_t, int64_t, int32_t, int32_t, const float*, int32_t,
@@ -70,6 +75,8 @@ int wr_create(wr_ctx** out, int device, void* hip_stream) {
   c->ws = nullptr;
   c->ws_bytes = 0;
   c->num_cu = cus > 0 ? cus : kDefaultCUs;
+  c->scale_trace = nullptr;
+  c->scale_trace_count = 0;
   // device address of the allocation-free entry point's static scratch, once per device (a
   // failure here is reported by that entry point, which tries again)
   (void)wr_static_scratch_init(device);
@@ -99,6 +106,7 @@ size_t wr_workspace_bytes(int op, int64_t rows, int64_t n, int32_t group, int32_
     case WR_OP_WRING_GPTQ: return group > 0 ? wr_wring_gptq_ws_bytes(rows, n, group, rank > 0 ? rank : 0) : 0;
     case WR_OP_TRELLIS: return group >= 2 && group <= 16 ? wr_trellis_ws_bytes(rows, n, group) : 0;
     case WR_OP_GEMV: return rows >= 1 && rows <= 8 ? wr_gemv_ws_bytes(n, (int32_t)rows) : 0;
+    case WR_OP_STATS: return wr_stats_ws_bytes(rows > 0 ? rows : 1);
     default: return 0;
   }
 }
@@ -274,6 +282,41 @@ int wr_packed_gemv(wr_ctx* ctx, const uint8_t* in, size_t in_bytes, int64_t rows
   DeviceScope ds(ctx->device);
   if (!ds.ok) return WR_EHIP;
   return wr_packed_gemv_impl(ctx, in, rows, n_store, bits, group, had_block, signs, x, n_in, ldx, batch, y, ldy);
+}
+
+int wr_set_scale_trace(wr_ctx* ctx, float* raw, int64_t capacity) {
+  if (!ctx || (raw && capacity <= 0) || (raw && !aligned(raw, 4))) return WR_EINVAL;
+  ctx->scale_trace = raw;
+  ctx->scale_trace_count = raw ? capacity : 0;
+  return WR_OK;
+}
+
+int wr_wring_target(wr_ctx* ctx, const void* target, int t_dtype, int64_t ldt, const void* B, const void* A,
+                    int32_t rank, float alpha, int ab_dtype, int64_t rows, int64_t n, const uint8_t* bits,
+                    int32_t group, const uint8_t* codes, const uint16_t* scales, float* T_out, int32_t* dev_info) {
+  if (!ctx || !dev_info || rows < 0 || rows > 65535 || n <= 0 || n > 65536 || group <= 0 || n % group != 0 ||
+      group % 8 != 0)
+    return WR_EINVAL;
+  if (target && (!valid_dtype(t_dtype) || ldt < n)) return WR_EINVAL;
+  if ((B != nullptr) != (A != nullptr)) return WR_EINVAL;
+  if (B && (rank <= 0 || rank % 4 != 0 || !valid_dtype(ab_dtype))) return WR_EINVAL;
+  if (rows > 0 && (!bits || !T_out || (!target && (!codes || !scales)))) return WR_EINVAL;
+  if (codes && !aligned(codes, 16)) return WR_EINVAL;
+  DeviceScope ds(ctx->device);
+  if (!ds.ok) return WR_EHIP;
+  return wr_wring_target_impl(ctx, target, t_dtype, ldt, B, A, rank, alpha, ab_dtype, rows, n, bits, group, codes,
+                              scales, T_out, dev_info);
+}
+
+int wr_quant_stats(wr_ctx* ctx, const float* T, int64_t ldt, const uint8_t* codes, const uint16_t* scales,
+                   const uint8_t* bits, int64_t rows, int64_t n, int32_t group, const uint8_t* codes_ref,
+                   const float* scales_raw, double* out) {
+  if (!ctx || !out || rows < 0 || rows > 2147483647 || n <= 0 || n > 65536 || group <= 0 || n % group != 0)
+    return WR_EINVAL;
+  if (rows > 0 && (!codes || !scales || !bits || (T && ldt < n))) return WR_EINVAL;
+  DeviceScope ds(ctx->device);
+  if (!ds.ok) return WR_EHIP;
+  return wr_quant_stats_impl(ctx, T, ldt, codes, scales, bits, rows, n, group, codes_ref, scales_raw, out);
 }
 
 const char* wr_strerror(int status) {

@@ -23,6 +23,8 @@ struct wr_ctx {
   void* ws;
   size_t ws_bytes;
   int num_cu;
+  float* scale_trace;         // wr_set_scale_trace: unprojected joint scales, or null
+  int64_t scale_trace_count;  // its capacity in elements
 };
 
 #define WR_CHECK_LAUNCH()                                       \
@@ -87,6 +89,18 @@ __device__ __forceinline__ uint16_t f64_to_f16_bits_clamped(double d) {
   if (r > 65504.0) r = 65504.0;
   _Float16 v = (_Float16)(float)r;        // exact conversion
   return sign | __builtin_bit_cast(uint16_t, v);
+}
+
+// fp64 -> bf16 round-to-nearest-even with a single rounding (normal range: |d| in [2^-126, 2^128)).
+// The bf16 quantum q of |d| is a power of two, |d|/q is exact and rint() rounds it to nearest even.
+__device__ __forceinline__ uint32_t f64_to_bf16_bits(double d) {
+  if (d != d) return 0x7fc0u;
+  const uint32_t sign = d < 0.0 || (d == 0.0 && signbit(d)) ? 0x8000u : 0u;
+  const double a = fabs(d);
+  if (a == 0.0) return sign;
+  const double q = ldexp(1.0, ilogb(a) - 7);
+  const float r = (float)(rint(a / q) * q);  // exact: 8 significant bits
+  return sign | (__float_as_uint(r) >> 16);
 }
 
 // x = x0 + x1 + x2 with each part rounded to bf16 in turn (exact for any fp32 x whose

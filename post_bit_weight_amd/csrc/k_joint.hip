@@ -510,7 +510,7 @@ __device__ __forceinline__ double rsqrt_refined(double d) {
 template <int NB>
 __global__ __launch_bounds__(64) void row_solve_wave_kernel(const float* __restrict__ Gm, const float* __restrict__ rhs,
                                                             int64_t rows, int nb, float lambda,
-                                                            uint16_t* __restrict__ scales,
+                                                            uint16_t* __restrict__ scales, float* __restrict__ raw,
                                                             const int32_t* __restrict__ dev_info) {
   __shared__ double lt[NB * (NB + 1)];
   if (*dev_info != 0) return;
@@ -564,7 +564,10 @@ __global__ __launch_bounds__(64) void row_solve_wave_kernel(const float* __restr
     const double sk = wave_bcast_f64(y, k) / wave_bcast_f64(a[k], k);
     y = lane == k ? sk : (lane < k ? fma(-a[k], sk, y) : y);
   }
-  if (live) scales[(size_t)row * nb + lane] = f64_to_f16_bits_clamped(y);
+  if (live) {
+    scales[(size_t)row * nb + lane] = f64_to_f16_bits_clamped(y);
+    if (raw) raw[(size_t)row * nb + lane] = (float)y;
+  }
 }
 
 // Per row: (G + lambda mu I) s = h + lambda mu s0 in fp64 (packed lower Cholesky in LDS), s -> fp16.
@@ -575,7 +578,7 @@ __global__ __launch_bounds__(64) void row_solve_wave_kernel(const float* __restr
 constexpr int RS_THREADS = 256;
 __global__ __launch_bounds__(RS_THREADS) void row_solve_kernel(const float* __restrict__ Gm, const float* __restrict__ rhs,
                                                                int64_t rows, int nb, float lambda,
-                                                               uint16_t* __restrict__ scales,
+                                                               uint16_t* __restrict__ scales, float* __restrict__ raw,
                                                                const int32_t* __restrict__ dev_info) {
   extern __shared__ double sh[];
   if (*dev_info != 0) return;
@@ -647,7 +650,10 @@ __global__ __launch_bounds__(RS_THREADS) void row_solve_kernel(const float* __re
     for (int i = tid; i < k; i += RS_THREADS) y[i] -= a[(size_t)k * (k + 1) / 2 + i] * uk;
     __syncthreads();
   }
-  for (int i = tid; i < nb; i += RS_THREADS) scales[(size_t)row * nb + i] = f64_to_f16_bits_clamped(y[i]);
+  for (int i = tid; i < nb; i += RS_THREADS) {
+    scales[(size_t)row * nb + i] = f64_to_f16_bits_clamped(y[i]);
+    if (raw) raw[(size_t)row * nb + i] = (float)y[i];
+  }
 }
 
 // Block scale search (the finisher "nearest-point codes + block scale search"): for each block
@@ -799,6 +805,7 @@ static int wring_core(wr_ctx* ctx, char* ws, size_t ws_bytes, const void* target
   uint16_t* H2 = reinterpret_cast<uint16_t*>(ws + lay.H2);
   float* Gm = reinterpret_cast<float*>(ws + lay.Gm);
   float* rh = reinterpret_cast<float*>(ws + lay.rhs);
+  float* raw = ctx->scale_trace;  // unprojected scales for the measures, when the caller asked for them
 
   if (reset_info) {
     hipLaunchKernelGGL(set_int_kernel, dim3(1), dim3(1), 0, st, dev_info, 0);
@@ -864,17 +871,17 @@ static int wring_core(wr_ctx* ctx, char* ws, size_t ws_bytes, const void* target
     // the unrolled factorization costs NB^2 broadcasts and fmas whatever nb is: buckets of 8
     // (40 blocks for a 2560-wide layer with groups of 64)
     if (nb <= 16)
-      hipLaunchKernelGGL(row_solve_wave_kernel<16>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, dev_info);
+      hipLaunchKernelGGL(row_solve_wave_kernel<16>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, raw, dev_info);
     else if (nb <= 24)
-      hipLaunchKernelGGL(row_solve_wave_kernel<24>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, dev_info);
+      hipLaunchKernelGGL(row_solve_wave_kernel<24>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, raw, dev_info);
     else if (nb <= 32)
-      hipLaunchKernelGGL(row_solve_wave_kernel<32>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, dev_info);
+      hipLaunchKernelGGL(row_solve_wave_kernel<32>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, raw, dev_info);
     else if (nb <= 40)
-      hipLaunchKernelGGL(row_solve_wave_kernel<40>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, dev_info);
+      hipLaunchKernelGGL(row_solve_wave_kernel<40>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, raw, dev_info);
     else if (nb <= 48)
-      hipLaunchKernelGGL(row_solve_wave_kernel<48>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, dev_info);
+      hipLaunchKernelGGL(row_solve_wave_kernel<48>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, raw, dev_info);
     else
-      hipLaunchKernelGGL(row_solve_wave_kernel<64>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, dev_info);
+      hipLaunchKernelGGL(row_solve_wave_kernel<64>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, raw, dev_info);
     WR_CHECK_LAUNCH();
     return WR_OK;
   }
@@ -883,7 +890,7 @@ static int wring_core(wr_ctx* ctx, char* ws, size_t ws_bytes, const void* target
   if (shbytes > 64 * 1024 && !lds_limit(reinterpret_cast<const void*>(row_solve_kernel), (int)shbytes))
     return WR_EHIP;
   hipLaunchKernelGGL(row_solve_kernel, dim3((unsigned)rows), dim3(RS_THREADS), shbytes, st, Gm, rh, rows, nb, lambda,
-                     scales, dev_info);
+                     scales, raw, dev_info);
   WR_CHECK_LAUNCH();
   return WR_OK;
 }
@@ -912,6 +919,7 @@ int wr_wring_solve_impl(wr_ctx* ctx, const void* target, int t_dtype, int64_t ld
   // requests that the per-row solve cannot hold in LDS are refused before anything is launched
   if (!(flags & WR_RECODE_SEARCH) && n / group > 64 && row_solve_lds_bytes(n / group) > 160 * 1024)
     return WR_EUNSUPPORTED;
+  if (ctx->scale_trace && ctx->scale_trace_count < rows * (n / group)) return WR_EINVAL;
   if (flags & WR_RECODE_SEARCH) {
     // the watered target into the joint solve's T slot, then the search (no joint solve)
     if (group != 32 && group != 64 && group != 128) return WR_EUNSUPPORTED;
@@ -960,4 +968,16 @@ int wr_wring_solve_impl(wr_ctx* ctx, const void* target, int t_dtype, int64_t ld
   if (rc) return rc;
   return wring_core(ctx, rest, rest_bytes, Tk, WR_F32, n, nullptr, nullptr, 0, 0.0f, WR_F32, H, ldh, rows, n, bits,
                     group, lambda, 0, false, nullptr, codes, scales, dev_info);
+}
+
+// The watered target alone (the filled weights of the model cards): T_out (rows x n fp32,
+// contiguous) = target, or dequant(codes, scales) when target is null, plus (alpha / rank) B A.
+int wr_wring_target_impl(wr_ctx* ctx, const void* target, int t_dtype, int64_t ldt, const void* B, const void* A,
+                         int32_t rank, float alpha, int ab_dtype, int64_t rows, int64_t n, const uint8_t* bits,
+                         int32_t group, const uint8_t* codes, const uint16_t* scales, float* T_out,
+                         int32_t* dev_info) {
+  if (rows == 0) return WR_OK;
+  return wring_core(ctx, static_cast<char*>(ctx->ws), ctx->ws_bytes, target, t_dtype, ldt, B, A, rank, alpha, ab_dtype,
+                    nullptr, n, rows, n, bits, group, 0.0f, 0, true, T_out, const_cast<uint8_t*>(codes),
+                    const_cast<uint16_t*>(scales), dev_info);
 }
