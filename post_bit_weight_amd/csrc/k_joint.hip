@@ -22,7 +22,7 @@
 // nb x nb system is then factored and solved in fp64.  (Solving for the step
 // s - s0 instead would shrink the error only when the scales move little; the
 // joint solve routinely moves them by their own size.)
-#include "common.hpp"
+#include "chol16.hpp"
 
 int wr_gemm_f32(hipStream_t st, int M, int N, int K, const float* A, int64_t lda, const float* B, int64_t ldb,
                 bool b_kn, float* C, int64_t ldc, float alpha, bool accumulate, bool lower_tiles,
@@ -656,6 +656,150 @@ __global__ __launch_bounds__(RS_THREADS) void row_solve_kernel(const float* __re
   }
 }
 
+// Per row, 64 < nb <= 160: the same solve blocked by 16 on the fp64 matrix cores.  One 256-thread
+// workgroup per row; the lower 16 x 16 blocks of A = G + lambda mu I (fp64, padded to a multiple of
+// 16 with the identity) sit in LDS at a pitch of 17 doubles, next to the inverted diagonal factor
+// blocks.  Per block column K: the panel L_IK = A_IK X_K^T (X_K = L_KK^-1) on the matrix cores, one
+// block per wave in turn, and z_K = X_K y_K (the forward substitution carried as an extra column);
+// then wave 0 updates the next diagonal block and factors and inverts it in registers while waves
+// 1-3 update the other trailing blocks, A_IJ -= L_IK L_JK^T, and y_I -= L_IK z_K.  The back
+// substitution L^T s = z runs block by block from the last one, s_K = X_K^T z_K followed by
+// z_J -= L_KJ^T s_K.  Two barriers per block column instead of a few per pivot.
+constexpr int RB_P = 17;             // row pitch of an LDS block, doubles (rows on different banks)
+constexpr int RB_BLK = 16 * RB_P;    // doubles per block
+constexpr int RB_MAXK = 10;          // block rows: up to 160 unknowns
+__device__ __forceinline__ int rb_idx(int I, int J) { return I * (I + 1) / 2 + J; }
+
+__global__ __launch_bounds__(256) void row_solve_blk_kernel(const float* __restrict__ Gm, const float* __restrict__ rhs,
+                                                            int64_t rows, int nb, float lambda,
+                                                            uint16_t* __restrict__ scales, float* __restrict__ raw,
+                                                            const int32_t* __restrict__ dev_info) {
+  extern __shared__ double sh[];
+  __shared__ double sreg;
+  __shared__ int failed;
+  if (*dev_info != 0) return;
+  const int nbk = (nb + 15) >> 4, nbp = 16 * nbk;
+  double* Ab = sh;                                  // lower blocks, rb_idx order
+  double* Xb = sh + (size_t)nbk * (nbk + 1) / 2 * RB_BLK;  // X_K = L_KK^-1
+  double* y = Xb + (size_t)nbk * RB_BLK;            // right-hand side, then z, then s
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const f64x4 zero = {0.0, 0.0, 0.0, 0.0};
+  const float* g = Gm + (size_t)row * nb * nb;
+  if (tid < 64) {
+    double tr = 0.0;
+    for (int i = tid; i < nb; i += 64) tr += (double)g[(size_t)i * nb + i];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) tr += __shfl_xor(tr, o);
+    if (tid == 0) {
+      sreg = (double)lambda * tr / nb;
+      failed = 0;
+    }
+  }
+  __syncthreads();
+  const double reg = sreg;
+  for (int t = tid; t < nbp * nbp; t += 256) {
+    const int i = t / nbp, j = t - i * nbp;
+    if (j > i) continue;
+    double v = i == j ? 1.0 : 0.0;
+    if (i < nb) v = (double)g[(size_t)i * nb + j] + (i == j ? reg : 0.0);
+    Ab[rb_idx(i >> 4, j >> 4) * RB_BLK + (i & 15) * RB_P + (j & 15)] = v;
+  }
+  for (int i = tid; i < nbp; i += 256)
+    y[i] = i < nb ? (double)rhs[(size_t)row * nb + i] + reg * (double)f16_bits_to_f32(scales[(size_t)row * nb + i])
+                  : 0.0;
+  __syncthreads();
+  if (wave == 0) {
+    const int b = chol16_inv_pitch<RB_P>(Ab, Xb, lane);
+    if (b >= 0 && lane == 0) failed = 1;
+  }
+  __syncthreads();
+  for (int K = 0; K < nbk; ++K) {
+    if (failed) return;  // only reachable with lambda == 0 and a singular G: keep the incoming scales
+    const double* XK = Xb + K * RB_BLK;
+    for (int I = K + 1 + wave; I < nbk; I += 4) {
+      double* AIK = Ab + rb_idx(I, K) * RB_BLK;
+      const f64x4 acc = mma16<true>(AIK, RB_P, 0, XK, RB_P, 0, 16, zero, lane);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) AIK[((lane >> 4) + 4 * v) * RB_P + (lane & 15)] = acc[v];
+    }
+    if (wave == 3 || (nbk - K - 1 < 4 && wave == nbk - K - 1)) {
+      // z_K = X_K y_K (by a wave without a panel block, or with the fewest)
+      double z = 0.0;
+      if (lane < 16) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) z = fma(XK[lane * RB_P + c], y[16 * K + c], z);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (lane < 16) y[16 * K + lane] = z;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      if (K + 1 < nbk) {
+        double* D = Ab + rb_idx(K + 1, K + 1) * RB_BLK;
+        const double* P = Ab + rb_idx(K + 1, K) * RB_BLK;
+        const f64x4 acc = mma16<true>(P, RB_P, 0, P, RB_P, 0, 16, zero, lane);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) D[((lane >> 4) + 4 * v) * RB_P + (lane & 15)] -= acc[v];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int b = chol16_inv_pitch<RB_P>(D, Xb + (K + 1) * RB_BLK, lane);
+        if (b >= 0 && lane == 0) failed = 1;
+      }
+    } else {
+      int t = 0;
+      for (int J = K + 1; J < nbk; ++J)
+        for (int I = J; I < nbk; ++I) {
+          if (I == K + 1 && J == K + 1) continue;
+          if (t++ % 3 != wave - 1) continue;
+          const f64x4 acc = mma16<true>(Ab + rb_idx(I, K) * RB_BLK, RB_P, 0, Ab + rb_idx(J, K) * RB_BLK, RB_P, 0, 16,
+                                        zero, lane);
+          double* C = Ab + rb_idx(I, J) * RB_BLK;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) C[((lane >> 4) + 4 * v) * RB_P + (lane & 15)] -= acc[v];
+        }
+      for (int i = 16 * (K + 1) + tid - 64; i < nbp; i += 192) {
+        const double* Li = Ab + rb_idx(i >> 4, K) * RB_BLK + (i & 15) * RB_P;
+        double acc = 0.0;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) acc = fma(Li[c], y[16 * K + c], acc);
+        y[i] -= acc;
+      }
+    }
+    __syncthreads();
+  }
+  if (failed) return;
+  for (int K = nbk - 1; K >= 0; --K) {
+    if (wave == 0) {  // s_K = X_K^T z_K
+      const double* XK = Xb + K * RB_BLK;
+      double sk = 0.0;
+      if (lane < 16) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) sk = fma(XK[c * RB_P + lane], y[16 * K + c], sk);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (lane < 16) y[16 * K + lane] = sk;
+    }
+    __syncthreads();
+    for (int j = tid; j < 16 * K; j += 256) {  // z_J -= L_KJ^T s_K for the blocks J < K
+      const double* LKJ = Ab + rb_idx(K, j >> 4) * RB_BLK + (j & 15);
+      double acc = 0.0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc = fma(LKJ[r * RB_P], y[16 * K + r], acc);
+      y[j] -= acc;
+    }
+    __syncthreads();
+  }
+  for (int i = tid; i < nb; i += 256) {
+    scales[(size_t)row * nb + i] = f64_to_f16_bits_clamped(y[i]);
+    if (raw) raw[(size_t)row * nb + i] = (float)y[i];
+  }
+}
+
+static size_t row_solve_blk_lds_bytes(int64_t nb) {
+  const int64_t k = (nb + 15) / 16;
+  return ((size_t)(k * (k + 1) / 2 + k) * RB_BLK + 16 * k) * sizeof(double);
+}
+
 // Block scale search (the finisher "nearest-point codes + block scale search"): for each block
 // of G weights of T, the candidate scales s_k = fp16((1 - k/64) max|t| / L), k = 0..31, each with
 // the nearest codes of t / s_k (IEEE division, as in the recode); the candidate with the least
@@ -882,6 +1026,14 @@ static int wring_core(wr_ctx* ctx, char* ws, size_t ws_bytes, const void* target
       hipLaunchKernelGGL(row_solve_wave_kernel<48>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, raw, dev_info);
     else
       hipLaunchKernelGGL(row_solve_wave_kernel<64>, grid, dim3(64), 0, st, Gm, rh, rows, nb, lambda, scales, raw, dev_info);
+    WR_CHECK_LAUNCH();
+    return WR_OK;
+  }
+  if ((nb + 15) / 16 <= RB_MAXK) {
+    const size_t bbytes = row_solve_blk_lds_bytes(nb);
+    if (!lds_limit(reinterpret_cast<const void*>(row_solve_blk_kernel), (int)bbytes)) return WR_EHIP;
+    hipLaunchKernelGGL(row_solve_blk_kernel, dim3((unsigned)rows), dim3(256), bbytes, st, Gm, rh, rows, nb, lambda,
+                       scales, raw, dev_info);
     WR_CHECK_LAUNCH();
     return WR_OK;
   }
