@@ -220,7 +220,8 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(const double* __restric
 // Xin and Xout are different buffers (workgroup 0 writes Xout while the others read Xin).
 __global__ __launch_bounds__(256) void chol_step_kernel(double* __restrict__ A, double* __restrict__ L,
                                                         const double* __restrict__ Xin, double* __restrict__ Xout,
-                                                        int n, int kb, int panels_ready, int32_t* __restrict__ dev_info) {
+                                                        int n, int kb, int panels_ready, int wcols,
+                                                        int32_t* __restrict__ dev_info) {
   if (*dev_info != 0) return;
   __shared__ double sL[CB * CP];
   __shared__ double sX[CB * CP];
@@ -269,12 +270,19 @@ __global__ __launch_bounds__(256) void chol_step_kernel(double* __restrict__ A, 
   }
   int ti, tj;
   {
-    const int t = blockIdx.x;  // lower tiles in row-major order; tile 0 is the diagonal block above
-    int i = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
-    while (i * (i + 1) / 2 > t) --i;
-    while ((i + 1) * (i + 2) / 2 <= t) ++i;
-    ti = i;
-    tj = t - i * (i + 1) / 2;
+    // lower tiles in row-major order, only the first wcols tile columns; tile 0 is the diagonal
+    // block above
+    const int t = blockIdx.x, tri = wcols * (wcols + 1) / 2;
+    if (t < tri) {
+      int i = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+      while (i * (i + 1) / 2 > t) --i;
+      while ((i + 1) * (i + 2) / 2 <= t) ++i;
+      ti = i;
+      tj = t - i * (i + 1) / 2;
+    } else {
+      ti = wcols + (t - tri) / wcols;
+      tj = (t - tri) % wcols;
+    }
   }
   const int i0 = base + CB * ti, j0 = base + CB * tj;
   const bool diag = ti == tj;
@@ -323,9 +331,98 @@ __global__ __launch_bounds__(256) void chol_step_kernel(double* __restrict__ A, 
     }
 }
 
-// Block rows of the trailing matrix from which a step solves its panel blocks in a phase of
-// their own (measured at n = 2560: 1.006 ms with 24, 1.069 ms with the single phase throughout).
-static const int kTwoPhaseTiles = 24;
+// The deferred trailing update of a panel of w block columns kb0 .. kb0 + 64 w - 1, all of whose
+// factor blocks are in L: A_ij -= sum_c L_ic L_jc^T for every lower tile of the trailing matrix
+// from base = kb0 + 64 w on, one tile per workgroup (each wave a 32 x 32 quarter), the sum over the
+// w block columns accumulated on the fp64 matrix cores with the two factor blocks of each column
+// staged in LDS (two buffers: two workgroups per CU).  Workgroup 0 takes the diagonal tile at base,
+// applies the same update and factors it (L and the inverted 16 x 16 blocks to Xout), which starts
+// the next panel.  Applying a panel's w columns together reads and writes the trailing matrix
+// once per panel instead of once per block column.
+__global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ A, double* __restrict__ L,
+                                                          double* __restrict__ Xout, int n, int kb0, int w,
+                                                          int32_t* __restrict__ dev_info) {
+  if (*dev_info != 0) return;
+  __shared__ double sP[CB * CP];
+  __shared__ double sQ[CB * CP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int base = kb0 + CB * w;
+  const f64x4 zero = {0.0, 0.0, 0.0, 0.0};
+  int ti, tj;
+  {
+    const int t = blockIdx.x;
+    int i = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+    while (i * (i + 1) / 2 > t) --i;
+    while ((i + 1) * (i + 2) / 2 <= t) ++i;
+    ti = i;
+    tj = t - i * (i + 1) / 2;
+  }
+  const int i0 = base + CB * ti, j0 = base + CB * tj;
+  const bool diag = ti == tj;
+  const int wi = wave >> 1, wj = wave & 1;
+  const bool active = !(diag && wj > wi);
+  double cur[2][2][4];
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      acc[x][y] = zero;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int gi = i0 + 32 * wi + 16 * x + (lane >> 4) + 4 * v;
+        const int gj = j0 + 32 * wj + 16 * y + (lane & 15);
+        cur[x][y][v] = active && gi < n && gj < n ? A[(int64_t)gi * n + gj] : 0.0;
+      }
+    }
+  for (int c = 0; c < w; ++c) {
+    load_block64(L, n, i0, kb0 + CB * c, n, n, sP, tid);
+    if (!diag) load_block64(L, n, j0, kb0 + CB * c, n, n, sQ, tid);
+    lds_sync();
+    const double* Pj = diag ? sP : sQ;
+    if (active) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+          acc[x][y] = mma16<true>(sP, CP, 32 * wi + 16 * x, Pj, CP, 32 * wj + 16 * y, CB, acc[x][y], lane);
+    }
+    lds_sync();
+  }
+  if (blockIdx.x == 0) {
+    // the next diagonal block: updated lower quarters into sP (the strictly upper 16 x 16 parts
+    // of the diagonal quarters are never read by the factorisation), identity past n, factor
+    if (active) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            sP[(32 * wi + 16 * x + (lane >> 4) + 4 * v) * CP + 32 * wj + 16 * y + (lane & 15)] =
+                cur[x][y][v] - acc[x][y][v];
+    }
+    lds_sync();
+    pad_diag(sP, n, base, tid);
+    lds_sync();
+    diag_factor(sP, sQ, n, base, L, Xout, dev_info, tid);
+    return;
+  }
+  if (!active) return;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int gi = i0 + 32 * wi + 16 * x + (lane >> 4) + 4 * v;
+        const int gj = j0 + 32 * wj + 16 * y + (lane & 15);
+        if (gi < n && gj < n && gj <= gi) A[(int64_t)gi * n + gj] = cur[x][y][v] - acc[x][y][v];
+      }
+}
+
+// Block columns per panel of deferred trailing updates.
+static const int kPanel = 4;
 
 // A = J H J (lower triangle), widened to fp64.
 __global__ void reverse_copy_kernel(const float* __restrict__ H, int64_t ldh, int n, double* __restrict__ A) {
@@ -376,17 +473,30 @@ int wr_factor_m(hipStream_t st, const float* H, int64_t ldh, int n, void* ws, fl
   WR_CHECK_LAUNCH();
   hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, st, A, n, Lf, Xinv[0], dev_info);
   WR_CHECK_LAUNCH();
-  for (int kb = 0, s = 0; kb + CB < n; kb += CB, ++s) {
-    const int nt = (n - kb - CB + CB - 1) / CB;
-    // many trailing tiles: solve each panel block once first instead of in every tile
-    const int two_phase = nt >= kTwoPhaseTiles ? 1 : 0;
-    if (two_phase) {
-      hipLaunchKernelGGL(chol_panel_kernel, dim3(nt), dim3(256), 0, st, A, Lf, Xinv[s & 1], n, kb, dev_info);
+  // Panels of kPanel block columns: within a panel each block column updates only the panel's own
+  // later block columns (every tile of its first trailing column also writes the factor blocks
+  // L_ik); after the panel's last block column, its factor blocks below the panel are solved in one
+  // launch and the whole trailing matrix takes the panel's update at once.
+  const int nblk = (n + CB - 1) / CB;
+  for (int k = 0; k + 1 < nblk; ++k) {
+    const int kb = CB * k;
+    const int s0 = k - k % kPanel, s1 = std::min(s0 + kPanel, nblk);
+    const int nt = nblk - k - 1;
+    const int w_rem = s1 - (k + 1);
+    double* Xin = Xinv[k & 1];
+    double* Xout = Xinv[(k + 1) & 1];
+    if (w_rem >= 1) {
+      const int wc = std::min(w_rem, nt);
+      const int tiles = wc * (wc + 1) / 2 + (nt - wc) * wc;
+      hipLaunchKernelGGL(chol_step_kernel, dim3(tiles), dim3(256), 0, st, A, Lf, Xin, Xout, n, kb, 0, wc, dev_info);
+      WR_CHECK_LAUNCH();
+    } else {
+      hipLaunchKernelGGL(chol_panel_kernel, dim3(nt), dim3(256), 0, st, A, Lf, Xin, n, kb, dev_info);
+      WR_CHECK_LAUNCH();
+      hipLaunchKernelGGL(chol_update_kernel, dim3(nt * (nt + 1) / 2), dim3(256), 0, st, A, Lf, Xout, n, CB * s0,
+                         s1 - s0, dev_info);
       WR_CHECK_LAUNCH();
     }
-    hipLaunchKernelGGL(chol_step_kernel, dim3(nt * (nt + 1) / 2), dim3(256), 0, st, A, Lf, Xinv[s & 1],
-                       Xinv[(s + 1) & 1], n, kb, two_phase, dev_info);
-    WR_CHECK_LAUNCH();
   }
   hipLaunchKernelGGL(build_m_kernel, dim3((unsigned)((n + 63) / 64), (unsigned)((n + 63) / 64)), dim3(256), 0, st, Lf, n,
                      M, dev_info);
