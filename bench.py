@@ -69,6 +69,9 @@ def parse():
                    help="q_proj: time the solve step only (no materializer or finisher-variant timing)")
     p.add_argument("--extras-only", action="store_true",
                    help="q_proj: one untimed step (for H), then only the materializer and the finisher-variant timings")
+    p.add_argument("--syrk", type=int, default=0, metavar="N",
+                   help="time only the H accumulation over 262144 Gaussian calibration rows of input dim N (for "
+                        "kernel counters; prints one JSON line and exits)")
     p.add_argument("--kernel-summary", metavar="RESULTS_DB", default=None,
                    help="print the per-kernel table of a rocprofv3 kernel trace (rocpd database) and exit")
     p.add_argument("--trace-steps", type=int, default=1,
@@ -859,10 +862,39 @@ def main():
         print("bench.py: the solve runs on one GPU; --gpus must be 1 (across GPUs it would shard over "
               "calibration rows for H and over weight rows for the sweep and the wring)", file=sys.stderr)
         sys.exit(2)
-    if args.workload == "q_proj":
+    if args.syrk:
+        main_syrk(args)
+    elif args.workload == "q_proj":
         main_q_proj(args)
     else:
         main_body(args)
+
+
+def main_syrk(args):
+    """The H accumulation alone: S = X^T X over 262144 rows of input dim N (bf16, Gaussian; the
+    kernel's time does not depend on the values), `steps` calls timed with HIP events."""
+    import torch
+    from post_bit_weight_amd import _lib as wr
+    n, N = args.syrk, BODY["calib_rows"]
+    ctx = wr.Context(0)
+    gen = torch.Generator(device="cuda").manual_seed(20261203)
+    X = torch.randn(N, n, device="cuda", generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    S = torch.empty(n, n, dtype=torch.float64, device="cuda")
+    empty = torch.empty(0, n, dtype=torch.bfloat16, device="cuda")
+    for _ in range(max(args.warmup, 0)):
+        wr.wr_hessian_accumulate(ctx, X, S, zero=True)
+    ts = []
+    for _ in range(args.steps):
+        wr.wr_hessian_accumulate(ctx, empty, S, zero=True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(ctx.stream)
+        wr.wr_hessian_accumulate(ctx, X, S)
+        e1.record(ctx.stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = sum(ts) / len(ts)
+    tf = float(N) * n * (n + 1) / (ms * 1e-3) / 1e12
+    print(json.dumps({"syrk_n": n, "rows": N, "ms": ms, "tflops": tf, "frac": tf / PEAK_BF16_TFLOPS}), flush=True)
 
 
 if __name__ == "__main__":

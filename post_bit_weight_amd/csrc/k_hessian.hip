@@ -26,7 +26,7 @@ namespace wr {
 constexpr int SY_T = 256;                // tile edge
 constexpr int SY_KT = 32;                // calibration rows per LDS stage
 constexpr int SY_NS = 5;                 // stages in the LDS ring
-constexpr int SY_PF = SY_NS - 1;         // stages in flight ahead of the one being consumed
+constexpr int SY_PF = SY_NS;             // stages issued ahead of the one being consumed (every slot)
 constexpr int SY_PANEL = SY_KT * SY_T * 2;            // one operand panel of a stage, bytes
 constexpr int SY_STAGE_BYTES = 2 * SY_PANEL;
 constexpr int SY_LDS_BYTES = SY_NS * SY_STAGE_BYTES;  // 160 KB
@@ -42,6 +42,37 @@ __device__ __forceinline__ void tri_tile(int t, int& I, int& J) {
   while ((i + 1) * (i + 2) / 2 <= t) ++i;
   I = i;
   J = t - i * (i + 1) / 2;
+}
+
+// Tile t (0 <= t < nt (nt + 1) / 2) of the lower triangle of nt x nt tiles, in blocked order: bands of
+// four tile rows, each band in chunks of eight tile columns (32 tiles that read 12 panels of X),
+// row-major inside a chunk; the columns a band has past its last full chunk, and a last band of fewer
+// than four rows, row-major.
+__device__ __forceinline__ void blocked_tile(int t, int nt, int& I, int& J) {
+  int b = (int)((sqrtf(32.0f * (float)t + 4.0f) - 2.0f) * 0.0625f);  // 8 b^2 + 2 b tiles before band b
+  while (b > 0 && 8 * b * b + 2 * b > t) --b;
+  while (8 * (b + 1) * (b + 1) + 2 * (b + 1) <= t) ++b;
+  int r = t - (8 * b * b + 2 * b);
+  int c0 = 0;
+  if (4 * b + 4 <= nt) {
+    const int nfull = 4 * b >= 7 ? (4 * b - 7) / 8 + 1 : 0;  // chunks entirely on or below the diagonal
+    if (r < 32 * nfull) {
+      I = 4 * b + ((r & 31) >> 3);
+      J = 8 * (r >> 5) + (r & 7);
+      return;
+    }
+    r -= 32 * nfull;
+    c0 = 8 * nfull;
+  }
+  for (int i = 4 * b;; ++i) {
+    const int cnt = i + 1 - c0;
+    if (r < cnt) {
+      I = i;
+      J = c0 + r;
+      return;
+    }
+    r -= cnt;
+  }
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -93,22 +124,31 @@ __global__ __launch_bounds__(SY_THREADS, 1) void syrk_bf16_kernel(const uint16_t
   lds_char* lds = (lds_char*)sy_lds;
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
-  // XCD-aware order: all workgroups of one row split land on the same XCD, so the
-  // X rows they share are fetched into that XCD's L2 once.
-  int tile, split;
+  // XCD-aware order (workgroup b runs on XCD b % 8).  Several splits: all workgroups of one row
+  // split land on the same XCD, so the X rows they share are fetched into that XCD's L2 once.  One
+  // split: each XCD takes a contiguous range of the tiles in blocked order, so the workgroups it
+  // runs at once read few distinct panels of the same rows.  Tiles are numbered row-major over the
+  // triangle for the partial sums.
+  int t, split;
   {
     const int bid = blockIdx.x;
-    if (ksplit % SY_XCD == 0) {
+    if (ksplit == 1) {
+      const int q = tiles / SY_XCD, rem = tiles % SY_XCD, x = bid % SY_XCD, slot = bid / SY_XCD;
+      if (slot >= q + (x < rem ? 1 : 0)) return;  // the grid is rounded up to a multiple of 8
+      split = 0;
+      t = x * q + min(x, rem) + slot;
+    } else if (ksplit % SY_XCD == 0) {
       const int per = SY_XCD * tiles;
       split = (bid % SY_XCD) + SY_XCD * (bid / per);
-      tile = (bid / SY_XCD) % tiles;
+      t = (bid / SY_XCD) % tiles;
     } else {
       split = bid / tiles;
-      tile = bid % tiles;
+      t = bid % tiles;
     }
   }
   int I, J;
-  tri_tile(tile, I, J);
+  blocked_tile(t, (n + SY_T - 1) / SY_T, I, J);
+  const int tile = I * (I + 1) / 2 + J;
   const int64_t r0 = (int64_t)split * rows_per_split;
   const int64_t r1 = r0 + rows_per_split < rows ? r0 + rows_per_split : rows;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -222,8 +262,9 @@ __global__ __launch_bounds__(SY_THREADS, 1) void syrk_bf16_kernel(const uint16_t
         vm_wait<0>();
       }
       lds_barrier();
-      // the slot of stage s - 1 is free: every wave consumed it before this barrier
-      if (s + SY_PF < nst) issue(s + SY_PF, slot == 0 ? SY_NS - 1 : slot - 1);
+      // the slot of stage s is free: every wave finished its reads of it before this barrier (the
+      // second half was read at the top of this iteration, the first half in the previous one)
+      if (s + SY_PF < nst) issue(s + SY_PF, slot);
       read_frags(next, 0, a0, b0);
     }
     mfma_step(a1, b1);
@@ -378,6 +419,10 @@ using namespace wr;
 // Row splits are chosen for a 256-CU part so the workspace size does not depend on the device.
 static constexpr int kSplitCUs = 256;
 
+// Workgroups of a launch: one per tile and split; with one split rounded up to a multiple of the XCD
+// count (the surplus workgroups return at once).
+static int syrk_grid(int tiles, int ks) { return ks == 1 ? (tiles + SY_XCD - 1) / SY_XCD * SY_XCD : tiles * ks; }
+
 static int syrk_tiles(int64_t n) {
   const int nt = (int)((n + SY_T - 1) / SY_T);
   return nt * (nt + 1) / 2;
@@ -427,15 +472,15 @@ static int syrk_pass(wr_ctx* ctx, const uint16_t* XA, const uint16_t* XB, int64_
   if (ks == 1 && rows > SY_MAX_ROWS) {
     for (int64_t r0 = 0; r0 < rows; r0 += SY_MAX_ROWS) {
       const int64_t rc = std::min<int64_t>(SY_MAX_ROWS, rows - r0);
-      hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)tiles), dim3(SY_THREADS), SY_LDS_BYTES, st, XA + r0 * ldx,
-                         XB + r0 * ldx, rc, (int)n, ldx, rc, tiles, 1, S, nullptr);
+      hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)syrk_grid(tiles, 1)), dim3(SY_THREADS), SY_LDS_BYTES, st,
+                         XA + r0 * ldx, XB + r0 * ldx, rc, (int)n, ldx, rc, tiles, 1, S, nullptr);
       WR_CHECK_LAUNCH();
     }
     return WR_OK;
   }
   const int64_t rps = ((rows + ks - 1) / ks + SY_KT - 1) / SY_KT * SY_KT;
-  hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)(tiles * ks)), dim3(SY_THREADS), SY_LDS_BYTES, st, XA, XB, rows, (int)n,
-                     ldx, rps, tiles, ks, S, ks > 1 ? partial : nullptr);
+  hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)syrk_grid(tiles, ks)), dim3(SY_THREADS), SY_LDS_BYTES, st, XA, XB,
+                     rows, (int)n, ldx, rps, tiles, ks, S, ks > 1 ? partial : nullptr);
   WR_CHECK_LAUNCH();
   if (ks > 1) {
     dim3 rgrid((unsigned)((SY_T * SY_T + 255) / 256), (unsigned)tiles);
