@@ -79,7 +79,7 @@ def parse():
     return p.parse_args()
 
 
-def traffic_from_profile(name):
+def traffic_from_profile(name, key="bytes_per_launch"):
     """HBM bytes of the SYRK launches from a committed rocprofv3 counter summary, if it matches this source.
 
     The summary (profiles/<name>) holds `bytes_per_launch:` (FETCH_SIZE and WRITE_SIZE per dispatch, each
@@ -98,7 +98,7 @@ def traffic_from_profile(name):
         digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
         if rec.get("source_sha256") != digest:
             return None
-        return float(rec["bytes_per_launch"])
+        return float(rec[key])
     except (OSError, ValueError, KeyError):
         return None
 
@@ -742,7 +742,7 @@ def main_body(args):
                 continue
             stage[k0] = stage.get(k0, 0.0) + e0.elapsed_time(e1)
 
-    traffic = traffic_from_profile("syrk_bf16_body_traffic.txt") if layers == 36 else None
+    traffic = traffic_from_profile("syrk_bf16_body_traffic.txt", "bytes_per_step") if layers == 36 else None
     w_desc = (f"36-layer Qwen3-4B-shaped body ({layers} layers timed): q 4096x2560, k/v 1024x2560, gate/up "
               "9728x2560, o 2560x4096, down 2560x9728 bf16 (Student-t nu=5, std 0.02); per layer one H per input "
               "dim from 262144 calibration rows (spectral + 1% outlier channels; post-SwiGLU-like product model "
@@ -881,6 +881,11 @@ def main_syrk(args):
     X = torch.randn(N, n, device="cuda", generator=gen, dtype=torch.float32).to(torch.bfloat16)
     S = torch.empty(n, n, dtype=torch.float64, device="cuda")
     empty = torch.empty(0, n, dtype=torch.bfloat16, device="cuda")
+    if args.copy_calibration > 0:
+        src = torch.ones((args.copy_calibration << 20) // 4, dtype=torch.float32, device="cuda")
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
     for _ in range(max(args.warmup, 0)):
         wr.wr_hessian_accumulate(ctx, X, S, zero=True)
     ts = []
@@ -894,7 +899,23 @@ def main_syrk(args):
         ts.append(e0.elapsed_time(e1))
     ms = sum(ts) / len(ts)
     tf = float(N) * n * (n + 1) / (ms * 1e-3) / 1e12
-    print(json.dumps({"syrk_n": n, "rows": N, "ms": ms, "tflops": tf, "frac": tf / PEAK_BF16_TFLOPS}), flush=True)
+    # the platform's GEMM (torch.mm, hipBLASLt) on the same operand layout for context: X^T X over
+    # 16384-row chunks as a full square product (twice the useful flops)
+    Xc = X[:16384]
+    for _ in range(2):
+        torch.mm(Xc.t(), Xc)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(N // 16384):
+        torch.mm(Xc.t(), Xc)
+    e1.record()
+    torch.cuda.synchronize()
+    mm_ms = e0.elapsed_time(e1)
+    mm_tf = 2.0 * N * n * n / (mm_ms * 1e-3) / 1e12
+    print(json.dumps({"syrk_n": n, "rows": N, "ms": ms, "tflops": tf, "frac": tf / PEAK_BF16_TFLOPS,
+                      "torch_mm_full_square_ms": mm_ms, "torch_mm_tflops": mm_tf,
+                      "torch_mm_frac": mm_tf / PEAK_BF16_TFLOPS}), flush=True)
 
 
 if __name__ == "__main__":
