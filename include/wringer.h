@@ -99,7 +99,7 @@ int wr_set_workspace(wr_ctx* ctx, void* dev_ptr, size_t bytes);
  * first.  Call once per chunk of calibration rows.  n % 8 == 0; for bf16 X,
  * ldx % 8 == 0 and X 16-byte aligned; ldx <= 2^24 (WR_EUNSUPPORTED above).
  * Products are exact: bf16 inputs directly, fp32 inputs as three bf16 parts
- * (x = x0 + x1 + x2, six cross terms).  The matrix cores sum at most 16384 rows
+ * (x = x0 + x1 + x2, six cross terms).  The matrix cores sum at most 32768 rows
  * (512 for fp32 X) in fp32 before the sums are added into S in fp64, in a fixed
  * order: the result is deterministic with a relative error near 1e-7.
  * Workspace: WR_OP_HESSIAN with (rows, n).  rows may be 0 (no-op unless
@@ -116,7 +116,7 @@ int wr_hessian_accumulate(wr_ctx* ctx, const void* X, int x_dtype, int64_t rows,
  * is a static device array of WR_STATIC_SCRATCH_BYTES per GPU, which the library holds from the
  * first wr_create on that GPU until the process ends.  bf16 X of any size: when the splits'
  * partials would not fit, fewer splits run at a time over row slices (each split still sums at
- * most 16384 rows in fp32); the result is bit-identical to wr_hessian_accumulate's when
+ * most 32768 rows in fp32); the result is bit-identical to wr_hessian_accumulate's when
  * wr_workspace_bytes(WR_OP_HESSIAN, rows, n, ...) <= WR_STATIC_SCRATCH_BYTES.  fp32 X: row
  * slices whose parts and partials fit; WR_ESCRATCH when not even 512 rows fit (n above 21845),
  * checked before any launch.  The call allocates nothing.  Every call on one GPU uses

@@ -12,9 +12,9 @@
 // LDS-DMA loads (global_load_lds, no registers, several stages in flight) and
 // transposed on the way out by the gfx950 transposing LDS read
 // (ds_read_b64_tr_b16).  bf16 x bf16 products are exact in fp32; the MFMAs sum at
-// most 16384 rows in fp32 before the sums reach S in fp64: either every
+// most 32768 rows in fp32 before the sums reach S in fp64: either every
 // workgroup adds its tile into S itself (one split per tile, when the tiles alone
-// fill the chip; calls longer than 16384 rows become one launch per 16384-row
+// fill the chip; calls longer than 32768 rows become one launch per 32768-row
 // slice), or the rows are cut into splits whose fp32 sums a second kernel adds
 // into S in a fixed order.  Deterministic, no atomics.
 #include <mutex>
@@ -33,7 +33,8 @@ constexpr int SY_LDS_BYTES = SY_NS * SY_STAGE_BYTES;  // 160 KB
 constexpr int SY_THREADS = 512;          // eight waves
 constexpr int SY_DMA_PER_WAVE = (SY_STAGE_BYTES / 1024) / (SY_THREADS / 64);  // 1 KB per wave-wide DMA
 constexpr int SY_XCD = 8;                // workgroups are dispatched round-robin over 8 XCDs
-constexpr int SY_MAX_ROWS = 16384;       // rows summed in fp32 before the sums reach S in fp64
+constexpr int SY_MAX_ROWS = 32768;       // rows summed in fp32 before the sums reach S in fp64
+constexpr int SY_SPLIT_ROWS = 16384;     // rows per split when the tiles alone do not fill the chip
 
 // Lower-triangle tile t -> (I, J), J <= I, row-major over the block triangle.
 __device__ __forceinline__ void tri_tile(int t, int& I, int& J) {
@@ -428,10 +429,10 @@ static int syrk_tiles(int64_t n) {
   return nt * (nt + 1) / 2;
 }
 
-// Number of row splits.  A split is summed in fp32 by the MFMAs over at most 16384 rows.  When
+// Number of row splits.  A split is summed in fp32 by the MFMAs over at most 32768 rows.  When
 // the lower 256 x 256 tiles alone give at least one workgroup per CU there is one split per tile
 // and each workgroup adds its sums into S (fp64) itself: no partial buffer (the host then
-// launches once per 16384-row slice).
+// launches once per 32768-row slice).
 // Otherwise the rows are cut into enough splits to fill the CUs (and to keep each at most 16384
 // rows); from 8 splits up their number is a multiple of the XCD count (each XCD works through its
 // own rows).  With `precise` (the fp32-input path, whose six passes rebuild an fp32-accurate S)
@@ -442,7 +443,7 @@ static int syrk_ksplit(int64_t rows, int64_t n, int num_cu, bool precise) {
   const int tiles = syrk_tiles(n);
   if (tiles >= num_cu) return 1;
   if (rows < SY_XCD * 1024) return (int)std::max<int64_t>(1, rows / 1024);
-  int64_t ks = std::max<int64_t>((rows + 16383) / 16384, (num_cu + tiles - 1) / tiles);
+  int64_t ks = std::max<int64_t>((rows + SY_SPLIT_ROWS - 1) / SY_SPLIT_ROWS, (num_cu + tiles - 1) / tiles);
   if (ks >= SY_XCD) {
     ks = (ks + SY_XCD - 1) / SY_XCD * SY_XCD;
     while (ks < 64 && tiles * ks < num_cu && rows / (ks + SY_XCD) >= 1024) ks += SY_XCD;
@@ -573,7 +574,7 @@ static int64_t f32_rows_fitting(int64_t n, size_t bytes) {
 
 // Same result as wr_hessian_accumulate_impl (bit-identical when its workspace need fits the static
 // scratch), with the scratch taken from the per-device static array: bf16 input with fewer row
-// splits at a time when their partials would not fit (each split still sums at most 16384 rows in
+// splits at a time when their partials would not fit (each split still sums at most 32768 rows in
 // fp32), fp32 input in row slices whose bf16 planes and partials fit.
 int wr_hessian_accumulate_static_impl(wr_ctx* ctx, const void* X, int x_dtype, int64_t rows, int64_t n,
                                       int64_t ldx, double* S, int flags) {
