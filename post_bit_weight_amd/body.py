@@ -155,9 +155,46 @@ def quantize_layer(ctx, layer, streams, layers=36, calib_rows=262144, chunk=1638
     return out
 
 
+def read_container(blob):
+    """(entries {name: uint8 numpy array}, wringer_meta dict) of a container written by
+    pipeline.container_bytes (an 8-byte little-endian header length, the JSON header, the blobs)."""
+    import numpy as np
+    hlen = int.from_bytes(blob[:8], "little")
+    header = json.loads(bytes(blob[8:8 + hlen]))
+    meta = json.loads(header.pop("__metadata__")["wringer_meta"])
+    base = 8 + hlen
+    entries = {}
+    for name, spec in header.items():
+        a, b = spec["data_offsets"]
+        entries[name] = np.frombuffer(bytes(blob[base + a:base + b]), dtype=np.uint8)
+    return entries, meta
+
+
+def resumable_layers(meta, layers, group, had_block, rank):
+    """Layers whose seven modules a previous container already holds with this body's shapes and bit
+    mix (the state the pages' v0.3 re-finish starts from is the stored module, keyed by layer and
+    module); raises if the container was made with another group, rotation block or rank."""
+    for key, want in (("group", group), ("had_block", had_block), ("rank", rank)):
+        if meta.get(key) != want:
+            raise ValueError(f"container has {key} {meta.get(key)}, this run {want}")
+    done = set()
+    for layer in range(layers):
+        ok = True
+        for name, rows, n in MODULES:
+            m = meta["modules"].get(f"layers.{layer}.{name}")
+            if m != {"rows": rows, "n": n, "bits": module_bits(layer, name, layers)}:
+                ok = False
+                break
+        if ok:
+            done.add(layer)
+    return done
+
+
 def sweep_body(ctx, layers=36, calib_rows=262144, chunk=16384, had_block=512, group=64, rank=128, seed=2026,
-               layer_ids=None, log=print, measure_layers=()):
-    """Quantize layers (all, or layer_ids) and build the container.  Returns (container bytes, report)."""
+               layer_ids=None, log=print, measure_layers=(), resume=None):
+    """Quantize layers (all, or layer_ids) and build the container.  Returns (container bytes, report).
+    resume: the bytes of an earlier container; the layers it holds completely are copied from it
+    instead of solved again (report["resumed_layers"])."""
     dev = ctx.device
     streams = {n: CalibrationStream(n, seed * 31 + n, dev) for n in DIMS}
     entries, meta = [], {"format": "wringer", "group": group, "had_block": had_block, "rank": rank, "modules": {}}
@@ -166,7 +203,20 @@ def sweep_body(ctx, layers=36, calib_rows=262144, chunk=16384, had_block=512, gr
     t0 = time.perf_counter()
     timer = _Timer(ctx.stream)
     ids = list(range(layers)) if layer_ids is None else list(layer_ids)
+    old_entries, old_meta, done = {}, None, set()
+    if resume is not None:
+        old_entries, old_meta = read_container(resume)
+        done = resumable_layers(old_meta, layers, group, had_block, rank)
+    resumed = []
     for layer in ids:
+        if layer in done:
+            for name, _, _ in MODULES:
+                key = f"layers.{layer}.{name}"
+                entries.append((key + ".packed", old_entries[key + ".packed"]))
+                meta["modules"][key] = old_meta["modules"][key]
+            resumed.append(layer)
+            log(f"layer {layer}: taken from the earlier container")
+            continue
         res = quantize_layer(ctx, layer, streams, layers, calib_rows, chunk, had_block, group, rank, seed,
                              timer=timer, measure=layer in measure_layers)
         for name, r in res.items():
@@ -182,12 +232,13 @@ def sweep_body(ctx, layers=36, calib_rows=262144, chunk=16384, had_block=512, gr
     weights = sum(v["rows"] * v["n"] for v in meta["modules"].values())
     report = {"layers": len(ids), "weights": weights, "payload_bytes": payload,
               "bits_per_weight": 8.0 * payload / weights, "container_bytes": len(blob),
-              "roundtrip_bit_exact": roundtrip, "wall_s": time.perf_counter() - t0}
+              "roundtrip_bit_exact": roundtrip, "wall_s": time.perf_counter() - t0, "resumed_layers": resumed}
     if measured:
         report["measures"] = measured
     solve_ms = timer.total_ms()
     report["solve_gpu_ms"] = solve_ms
-    report["weights_per_s"] = weights / (solve_ms * 1e-3)
+    solved = weights - sum(rows * n for _, rows, n in MODULES) * len(resumed)
+    report["weights_per_s"] = solved / (solve_ms * 1e-3) if solve_ms > 0 else None
     return blob, report
 
 
@@ -198,11 +249,13 @@ def main():
     p.add_argument("--out", default=None, help="write the container here")
     p.add_argument("--measure", default="", help="comma-separated layers whose modules also get the model cards' "
                                                   "measures (grid distance, solver disagreement, projection moves)")
+    p.add_argument("--resume", default=None, help="an earlier container: its complete layers are kept, the rest solved")
     args = p.parse_args()
     ctx = wr.Context(0)
     ml = tuple(int(x) for x in args.measure.split(",") if x.strip())
+    resume = open(args.resume, "rb").read() if args.resume else None
     blob, report = sweep_body(ctx, layers=args.layers, calib_rows=args.calib_rows,
-                              log=lambda m: print(m, flush=True), measure_layers=ml)
+                              log=lambda m: print(m, flush=True), measure_layers=ml, resume=resume)
     if args.out:
         with open(args.out, "wb") as f:
             f.write(blob)

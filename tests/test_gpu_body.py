@@ -131,4 +131,12 @@ def test_body_two_layers_full_size():
     hlen = int.from_bytes(blob[:8], "little")
     meta = json.loads(json.loads(blob[8:8 + hlen])["__metadata__"]["wringer_meta"])
     assert meta["modules"]["layers.0.k"]["bits"] == 3 and meta["modules"]["layers.35.k"]["bits"] == 2
+    # resume from that container: layers 0 and 35 are taken from it, layer 1 is solved
+    _log("body: resume with layers 0, 35 stored and layer 1 to solve")
+    blob2, rep2 = body.sweep_body(ctx, layer_ids=[0, 1, 35], log=_log, resume=blob)
+    assert rep2["resumed_layers"] == [0, 35] and rep2["roundtrip_bit_exact"]
+    back2 = st.load(blob2)
+    assert len(back2) == 21
+    for key, buf in back.items():
+        assert np.array_equal(back2[key], buf)
     _log(f"body: {json.dumps(report)}")
