@@ -346,131 +346,181 @@ __device__ __forceinline__ void lh_vm_wait() {
 // complete before it.
 __device__ __forceinline__ void lh_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-constexpr int LH_ROWS = 128;                      // weight rows per workgroup (32 per wave)
-constexpr int LH_PLANE = 64 * 64 * 2;             // one H split tile, bf16
-constexpr int LH_STAGE = 3 * LH_PLANE + LH_ROWS * 64 * 2;  // + the level tile: 40 KB
-constexpr int LH_DMA = LH_STAGE / 1024 / 4;       // 1 KB DMAs per wave per stage
+constexpr int LH_ROWS = 256;                     // weight rows per workgroup (64 per wave)
+constexpr int LH_PLANE = 64 * 64 * 2;            // one H split tile, 64 x 64 bf16: 8 KB
+constexpr int LH_LEV = LH_ROWS * 64 * 2;         // the rows' level tile, 256 x 64 bf16: 32 KB
+constexpr int LH_STAGE = 6 * LH_PLANE + LH_LEV;  // two blocks b: 80 KB, two stages fill the LDS
+constexpr int LH_DMA = LH_STAGE / 1024 / 8;      // 1 KB DMAs per wave per stage
+constexpr int LH_XCD = 8;                        // workgroups are dispatched round-robin over 8 XCDs
 
-// Position of the 16-byte unit (row j, 8-column octet q) in a tile of 64 bf16 columns:
-// eight consecutive rows at one octet fall on eight distinct 16-byte bank groups of a
-// 128-byte line, and sixteen consecutive rows on sixteen of a 256-byte line.
-__device__ __forceinline__ int lh_unit(int j, int q) { return j * 8 + (q ^ (j & 7) ^ ((j >> 3) & 1)); }
+// Position of the 16-byte unit (row j, octet q of 64 bf16 columns) in a tile of 128-byte rows:
+// eight consecutive rows at one octet fall on eight distinct units of a 128-byte line, and
+// sixteen consecutive rows on sixteen of a 256-byte line.
+__device__ __forceinline__ int lh_unit(int j, int q) { return 8 * j + (q ^ (j & 7) ^ ((j >> 3) & 1)); }
 
 __device__ __forceinline__ bf16x8 lh_frag(const lds_char* p) {
   const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)p;
   return as_bf16x8(v);
 }
 
-// One workgroup: 128 weight rows x block b, looping over the column blocks c.  Per c the
-// three H split tiles H_i[b, c] and the rows' levels on block c are DMAed into LDS one
-// stage ahead; wave w multiplies them into D (64 j x its 32 rows, two 32 x 32 MFMA
-// blocks) and reduces D with the rows' levels and targets on block b (kept in
-// registers).  Outputs: G[r][b][c] = G[r][c][b] for b <= c; hp[b][c][r] = block b's
-// share of h_c.
-__global__ __launch_bounds__(256, 2) void gram_lh_kernel(const uint16_t* __restrict__ Lev, const float* __restrict__ T,
-                                                         int64_t rows, int n, const uint16_t* __restrict__ H0,
-                                                         const uint16_t* __restrict__ H1, const uint16_t* __restrict__ H2,
-                                                         float* __restrict__ Gm, float* __restrict__ hp,
-                                                         const int32_t* __restrict__ dev_info) {
+// Workgroups of the Gram launch: one per (row tile, pair of blocks b), rounded up to a multiple
+// of the XCD count.
+static unsigned gram_lh_grid(int64_t rows, int nb) {
+  const int64_t tiles = (rows + LH_ROWS - 1) / LH_ROWS * ((nb + 1) / 2);
+  return (unsigned)((tiles + LH_XCD - 1) / LH_XCD * LH_XCD);
+}
+
+// One workgroup: 256 weight rows x the blocks b = 2 bp, 2 bp + 1, looping over the column blocks
+// c.  Per c the three H split tiles H_i[b, c] of both blocks and the rows' levels on c are DMAed
+// into one of two LDS stages while the other is multiplied; waves 4 h .. 4 h + 3 take block
+// 2 bp + h, wave w multiplying into D (64 j x its 64 rows, four 32 x 32 MFMA blocks) and reducing
+// D with the rows' levels and targets on its block (kept in registers).  The level tile serves
+// both blocks: per weight row and block pair the levels are read once, per block pair and 256
+// rows the H stripes once.  Tiles are numbered with the row tiles of one pair consecutive, and
+// each XCD takes a contiguous range of them, so the workgroups it runs at once share the H
+// stripes.  Outputs: G[r][b][c] = G[r][c][b] for b <= c; hp[b][c][r] = block b's share of h_c.
+// With nb odd the second block of the last pair repeats the first and writes nothing.
+__global__ __launch_bounds__(512) void gram_lh_kernel(const uint16_t* __restrict__ Lev, const float* __restrict__ T,
+                                                      int64_t rows, int n, const uint16_t* __restrict__ H0,
+                                                      const uint16_t* __restrict__ H1, const uint16_t* __restrict__ H2,
+                                                      float* __restrict__ Gm, float* __restrict__ hp,
+                                                      const int32_t* __restrict__ dev_info) {
   extern __shared__ __attribute__((aligned(1024))) char lh_lds[];
   if (*dev_info != 0) return;
+  const int nb = n / 64, np = (nb + 1) / 2;
+  const int gx = (int)((rows + LH_ROWS - 1) / LH_ROWS);
+  int bp, xt;
+  {
+    const int tiles = gx * np, bid = blockIdx.x;
+    const int q = tiles / LH_XCD, rem = tiles % LH_XCD, x = bid % LH_XCD, slot = bid / LH_XCD;
+    if (slot >= q + (x < rem ? 1 : 0)) return;  // the grid is rounded up to a multiple of 8
+    const int t = x * q + min(x, rem) + slot;
+    bp = t / gx;
+    xt = t % gx;
+  }
   const lds_char* lds = (const lds_char*)lh_lds;
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
-  const int nb = n / 64;
-  const int b = blockIdx.y;
-  const int64_t r0 = (int64_t)blockIdx.x * LH_ROWS;
+  const int64_t r0 = (int64_t)xt * LH_ROWS;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rl = 32 * wave + (lane & 31);
-  const int64_t r = r0 + rl;
-  const bool rok = r < rows;
+  const int half = wave >> 2, wr = wave & 3;
+  const bool bok = 2 * bp + half < nb;          // this wave's block exists
+  const int b = std::min(2 * bp + half, nb - 1);
+  const int bdma1 = std::min(2 * bp + 1, nb - 1);  // the second block's H stripe (the first's if none)
   const int rmax = (int)std::min<int64_t>(rows - 1 - r0, LH_ROWS - 1);
 
-  // DMA q (0..39 per stage) fills LDS bytes [1024 q, 1024 q + 1024) of the stage:
-  // q < 24 the H split tile q / 8, else the level tile.  Wave w issues q = w + 4 i.
+  // DMA q (0..79 per stage) fills LDS bytes [1024 q, 1024 q + 1024) of the stage: q < 48 the H
+  // split tile (q % 24) / 8 of block 2 bp + q / 24, else the level tile.  Wave w issues q = w + 8 i.
   uint32_t voff[LH_DMA];
 #pragma unroll
   for (int i = 0; i < LH_DMA; ++i) {
-    const int q = wave + 4 * i;
-    if (q < 24) {
-      const int u = (q & 7) * 64 + lane, j = u >> 3;
-      const int oct = (u & 7) ^ (j & 7) ^ ((j >> 3) & 1);
-      voff[i] = (uint32_t)((j * n + oct * 8) * 2);
-    } else {
-      const int u = (q - 24) * 64 + lane, row = u >> 3;
-      const int oct = (u & 7) ^ (row & 7) ^ ((row >> 3) & 1);
-      voff[i] = (uint32_t)((std::min(row, rmax) * n + oct * 8) * 2);
-    }
+    const int q = wave + 8 * i;
+    const int u = (q < 48 ? (q & 7) : q - 48) * 64 + lane, j = u >> 3;
+    const int oct = (u & 7) ^ (j & 7) ^ ((j >> 3) & 1);
+    voff[i] = (uint32_t)(((q < 48 ? j : std::min(j, rmax)) * n + oct * 8) * 2);
   }
-  auto issue = [&](int c, int slot) {
-    const uint32_t base = lds_base + slot * LH_STAGE;
-    const int64_t hoff = (int64_t)64 * b * n + 64 * c;
-    const int64_t loff = r0 * n + 64 * c;
+  auto issue = [&](int s) {
+    const uint32_t base = lds_base + (s & 1) * LH_STAGE;
+    const int64_t col = (int64_t)64 * s;  // stage s: block c = s
+    const int64_t hoff0 = (int64_t)64 * (2 * bp) * n + col;
+    const int64_t hoff1 = (int64_t)64 * bdma1 * n + col;
+    const int64_t loff = r0 * n + col;
 #pragma unroll
     for (int i = 0; i < LH_DMA; ++i) {
-      const int q = wave + 4 * i;
-      const uint16_t* src = q < 8 ? H0 + hoff : q < 16 ? H1 + hoff : q < 24 ? H2 + hoff : Lev + loff;
+      const int q = wave + 8 * i;
+      const int pl = (q % 24) >> 3;
+      const int64_t hoff = q < 24 ? hoff0 : hoff1;
+      const uint16_t* src = q >= 48 ? Lev + loff : pl == 0 ? H0 + hoff : pl == 1 ? H1 + hoff : H2 + hoff;
       lh_dma16(src, voff[i], base + q * 1024);
     }
   };
 
-  // levels and targets of this lane's row on block b at the accumulator rows
-  float lv[2][16], tv[2][16];
+  // levels (bf16 pairs) and targets of this lane's rows on block b at the accumulator positions:
+  // four consecutive j per group of accumulator registers, read as one vector (rows past the end
+  // read the last row and are zeroed), all issued before the first use
+  uint32_t lvp[2][2][8];
+  float tv[2][2][16];
 #pragma unroll
-  for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t e = (rok ? r : 0) * n + 64 * b + 32 * jt + acc_row(v, lane);
-      lv[jt][v] = rok ? bf16_bits_to_f32(Lev[e]) : 0.0f;
-      tv[jt][v] = rok ? T[e] : 0.0f;
-    }
-
-  issue(0, 0);
-  for (int c = 0; c < nb; ++c) {
-    const int slot = c & 1;
-    if (c + 1 < nb) {
-      issue(c + 1, slot ^ 1);
-      lh_vm_wait<LH_DMA>();
-    } else {
-      lh_vm_wait<0>();
-    }
-    lh_barrier();
-    const lds_char* st = lds + slot * LH_STAGE;
-    f32x16 acc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int oct = 2 * ks + (lane >> 5);
-      const bf16x8 fb = lh_frag(st + 3 * LH_PLANE + lh_unit(rl, oct) * 16);
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        const int ua = lh_unit(32 * jt + (lane & 31), oct) * 16;
-        const bf16x8 a2 = lh_frag(st + 2 * LH_PLANE + ua);
-        const bf16x8 a1 = lh_frag(st + LH_PLANE + ua);
-        const bf16x8 a0 = lh_frag(st + ua);
-        acc[jt] = mfma32x32x16_bf16(a2, fb, acc[jt]);  // smallest terms first
-        acc[jt] = mfma32x32x16_bf16(a1, fb, acc[jt]);
-        acc[jt] = mfma32x32x16_bf16(a0, fb, acc[jt]);
-      }
-    }
-    lh_barrier();  // every wave is done with this slot before the next stage's DMA into it
-    float hpart = 0.0f, gpart = 0.0f;
+  for (int rt = 0; rt < 2; ++rt) {
+    const int64_t r = r0 + 64 * wr + 32 * rt + (lane & 31);
+    const bool rok = r < rows;
+    const int64_t rc = rok ? r : rows - 1;
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) hpart = fmaf(tv[jt][v], acc[jt][v], hpart);
-    hpart += __shfl_xor(hpart, 32);
-    if (b <= c) {
+      for (int g = 0; g < 4; ++g) {
+        const int64_t e = rc * n + 64 * b + 32 * jt + 8 * g + 4 * (lane >> 5);
+        const float4 t4 = *reinterpret_cast<const float4*>(T + e);
+        const uint2 l2 = *reinterpret_cast<const uint2*>(Lev + e);
+        tv[jt][rt][4 * g + 0] = rok ? t4.x : 0.0f;
+        tv[jt][rt][4 * g + 1] = rok ? t4.y : 0.0f;
+        tv[jt][rt][4 * g + 2] = rok ? t4.z : 0.0f;
+        tv[jt][rt][4 * g + 3] = rok ? t4.w : 0.0f;
+        lvp[jt][rt][2 * g] = rok ? l2.x : 0u;
+        lvp[jt][rt][2 * g + 1] = rok ? l2.y : 0u;
+      }
+  }
+
+  issue(0);
+  f32x16 acc[2][2];
+  const int hsel = half * 3 * LH_PLANE;
+  for (int s = 0; s < nb; ++s) {
+    lh_vm_wait<0>();
+    lh_barrier();  // stage s is in LDS for every wave, and every wave is done with stage s - 1
+    if (s + 1 < nb) issue(s + 1);  // into the other buffer
+    const lds_char* st = lds + (s & 1) * LH_STAGE;
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) acc[jt][rt] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int oct = 2 * ks + (lane >> 5);
+      bf16x8 fb[2];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+        fb[rt] = lh_frag(st + 6 * LH_PLANE + lh_unit(64 * wr + 32 * rt + (lane & 31), oct) * 16);
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        const int ua = hsel + lh_unit(32 * jt + (lane & 31), oct) * 16;
+        const bf16x8 a2 = lh_frag(st + 2 * LH_PLANE + ua);
+        const bf16x8 a1 = lh_frag(st + LH_PLANE + ua);
+        const bf16x8 a0 = lh_frag(st + ua);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          acc[jt][rt] = mfma32x32x16_bf16(a2, fb[rt], acc[jt][rt]);  // smallest terms first
+          acc[jt][rt] = mfma32x32x16_bf16(a1, fb[rt], acc[jt][rt]);
+          acc[jt][rt] = mfma32x32x16_bf16(a0, fb[rt], acc[jt][rt]);
+        }
+      }
+    }
+    const int c = s;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int64_t r = r0 + 64 * wr + 32 * rt + (lane & 31);
+      float hpart = 0.0f, gpart = 0.0f;
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) gpart = fmaf(lv[jt][v], acc[jt][v], gpart);
-      gpart += __shfl_xor(gpart, 32);
-    }
-    if (lane < 32 && rok) {
-      hp[((size_t)b * nb + c) * rows + r] = hpart;
+        for (int v = 0; v < 16; ++v) hpart = fmaf(tv[jt][rt][v], acc[jt][rt][v], hpart);
+      hpart += __shfl_xor(hpart, 32);
       if (b <= c) {
-        Gm[((size_t)r * nb + b) * nb + c] = gpart;
-        Gm[((size_t)r * nb + c) * nb + b] = gpart;
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const uint32_t w2 = lvp[jt][rt][v >> 1];
+            const float l = __uint_as_float((v & 1) ? (w2 & 0xffff0000u) : (w2 << 16));
+            gpart = fmaf(l, acc[jt][rt][v], gpart);
+          }
+        gpart += __shfl_xor(gpart, 32);
+      }
+      if (bok && lane < 32 && r < rows) {
+        hp[((size_t)b * nb + c) * rows + r] = hpart;
+        if (b <= c) {
+          Gm[((size_t)r * nb + b) * nb + c] = gpart;
+          Gm[((size_t)r * nb + c) * nb + b] = gpart;
+        }
       }
     }
   }
@@ -1000,7 +1050,8 @@ static int wring_core(wr_ctx* ctx, char* ws, size_t ws_bytes, const void* target
   if (lh) {
     if (!lds_limit(reinterpret_cast<const void*>(gram_lh_kernel), 2 * LH_STAGE)) return WR_EHIP;
     float* hp = reinterpret_cast<float*>(ws + lay.hp);
-    hipLaunchKernelGGL(gram_lh_kernel, ggrid, dim3(256), 2 * LH_STAGE, st, Lev, T, rows, n, H0, H1, H2, Gm, hp, dev_info);
+    hipLaunchKernelGGL(gram_lh_kernel, dim3(gram_lh_grid(rows, nb)), dim3(512), 2 * LH_STAGE, st, Lev, T, rows, n,
+                       H0, H1, H2, Gm, hp, dev_info);
     WR_CHECK_LAUNCH();
     const unsigned sx = (unsigned)std::min<int64_t>((rows + 255) / 256, 64);
     hipLaunchKernelGGL(rhs_sum_kernel, dim3(sx, (unsigned)nb), dim3(256), 0, st, hp, rows, nb, rh, dev_info);
