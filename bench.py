@@ -58,6 +58,11 @@ def parse():
     p.add_argument("--calib-sets", type=int, default=4,
                    help="body: distinct per-layer calibration sets kept resident (layer l reads set l mod K)")
     p.add_argument("--no-breakdown", action="store_true", help="body: skip the untimed per-call breakdown pass")
+    p.add_argument("--streams", type=int, choices=(1, 3), default=3,
+                   help="body: 3 runs each input dim's solves on a stream of its own (they overlap), 1 in order")
+    p.add_argument("--lag", type=int, default=0,
+                   help="body, 3 streams: a stream starts layer l once the others have finished layer l - lag "
+                        "(0: no coupling)")
     p.add_argument("--no-measures", action="store_true", help="body: skip the model cards' measures of layer 0")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=None, help="weight rows in the oracle sample")
@@ -511,15 +516,32 @@ class BodyInputs:
         self.ws_bytes = ws
 
 
-def body_step(wr, ctx, I, mark=None):
-    """One pass of the whole solve over the body.  mark(kind, n) is called between library calls when
-    given (it records timing events on the library's stream)."""
+def body_step(wr, ctxs, I, mark=None, lag=0):
+    """One pass of the whole solve over the body.  ctxs: one library context for every input dim (the
+    calls run in order on its stream), or a dict input dim -> context: each dim's solves then run on
+    that context's stream and overlap with the other dims' (a dim's buffers are only touched on its
+    own stream, so the streams share nothing).  With lag > 0 a dim's stream starts layer l only after
+    every other dim's stream has finished layer l - lag (the streams stay within lag layers of each
+    other).  mark(kind, n) is called between library calls when given (it records timing events on dim
+    n's stream)."""
+    import torch
+    if not isinstance(ctxs, dict):
+        ctxs = {n: ctxs for n in I.dims}
     cfg = I.cfg
     g, lam, hb, N = cfg["group"], cfg["lam"], cfg["had_block"], cfg["calib_rows"]
     m = mark or (lambda kind, n: None)
+    multi = len({id(c) for c in ctxs.values()}) > 1
+    done = []  # per layer: {n: event at the end of layer on dim n's stream}
     for layer in range(I.layers):
         p = layer % I.P
+        if multi and lag > 0:
+            done.append({})
         for n in I.dims:
+            ctx = ctxs[n]
+            if multi and lag > 0 and layer >= lag:
+                for n2, ev in done[layer - lag].items():
+                    if n2 != n:
+                        ctx.stream.wait_event(ev)
             G = I.groups[layer][n]
             rows = G["W"].shape[0]
             Wst = I.Wst[n][:rows]
@@ -529,7 +551,8 @@ def body_step(wr, ctx, I, mark=None):
             m("finalize", n)
             wr.wr_hessian_finalize(ctx, I.S[n], N, cfg["damp"], I.H[n], I.delta, hb, I.signs[n])
             m("rotate", n)
-            Wst.copy_(G["W"])                                                    # widen to fp32
+            with torch.cuda.stream(ctx.stream):
+                Wst.copy_(G["W"])                                                # widen to fp32
             wr.wr_hadamard_rotate(ctx, Wst, hb, I.signs[n], wr.WR_ROT_ROWS)
             m("gptq", n)
             wr.wr_gptq_sweep(ctx, Wst, I.H[n], G["bits"], g, cfg["lazy_batch"], G["codes"], G["scales"],
@@ -548,6 +571,10 @@ def body_step(wr, ctx, I, mark=None):
                 wr.wr_unpack(ctx, mod["packed"], mod["r1"] - mod["r0"], n, mod["bits"], g, G["ucodes"][sl],
                              G["uscales"][sl])
             m("end", n)
+            if multi and lag > 0:
+                ev = torch.cuda.Event()
+                ev.record(ctx.stream)
+                done[layer][n] = ev
 
 
 def body_check(torch, I):
@@ -678,6 +705,11 @@ def main_body(args):
     progress(f"drawing the synthetic inputs ({args.calib_sets} resident calibration sets, {layers} layers)")
     I = BodyInputs(torch, wr, body, synth, layers, args.calib_sets, cfg, progress)
     ctx.ensure_workspace(I.ws_bytes)
+    # the timed steps' contexts: one, or one per input dim on streams of their own (default priority)
+    ctxs = ctx if args.streams == 1 else {n: wr.Context(0, stream=torch.cuda.Stream(dev)) for n in I.dims}
+    if isinstance(ctxs, dict):
+        for c in ctxs.values():
+            c.ensure_workspace(I.ws_bytes)
     torch.cuda.synchronize()
 
     if args.copy_calibration > 0:
@@ -690,26 +722,26 @@ def main_body(args):
 
     progress(f"warmup ({args.warmup} steps)")
     for _ in range(args.warmup):
-        body_step(wr, ctx, I)
+        body_step(wr, ctxs, I, lag=args.lag)
     torch.cuda.synchronize()
     if args.warmup:
         body_check(torch, I)
 
     # timed steps: events only around the H accumulation (the roofline's kernel), recorded on the
-    # library's stream
+    # stream the accumulation runs on
     progress(f"timing {args.steps} steps")
     syrk = []
 
     def mark_syrk(kind, n):
         if kind in ("hessian", "finalize"):
             e = torch.cuda.Event(enable_timing=True)
-            e.record(st)
+            e.record(ctxs[n].stream if isinstance(ctxs, dict) else st)
             syrk.append((kind, n, e))
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        body_step(wr, ctx, I, mark_syrk)
+        body_step(wr, ctxs, I, mark_syrk, lag=args.lag)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     progress("checking dev_info and the pack/unpack round trips")
@@ -766,7 +798,8 @@ def main_body(args):
         "config": {"workload": w_desc, "layers": layers, "weights": I.weights, "calib_rows_per_H": N,
                    "calib_sets_resident": args.calib_sets, "had_block": cfg["had_block"], "group": cfg["group"],
                    "rank": cfg["rank"], "lambda": cfg["lam"], "payload_bytes": I.payload,
-                   "bits_per_weight": 8.0 * I.payload / I.weights, "parallelism": "none (1 GPU)"},
+                   "bits_per_weight": 8.0 * I.payload / I.weights, "parallelism": "none (1 GPU)",
+                   "streams": args.streams, "layer_lag": args.lag},
         "roofline": {
             "kernel": "syrk_bf16 (H accumulation incl. its split-K reduction), all launches of a step",
             "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -779,6 +812,11 @@ def main_body(args):
     }
     if stage is not None:
         line["stage_ms"] = stage
+        # the same launches timed alone: the breakdown pass runs every call in order on one stream
+        excl = sum(flops.values()) / (stage["hessian"] * 1e-3) / 1e12
+        line["roofline"]["exclusive"] = {
+            "note": "breakdown pass, one stream (no other work on the GPU during the H accumulation)",
+            "syrk_ms_per_step": stage["hessian"], "achieved": excl, "frac": excl / PEAK_BF16_TFLOPS}
     if not args.no_measures:
         progress("the model cards' measures for layer 0 (untimed)")
         per, mean = body_measures(wr, ctx, I, torch)
