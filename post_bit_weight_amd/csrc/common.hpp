@@ -146,4 +146,35 @@ __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
 
+// Tile t (0 <= t < nt (nt + 1) / 2) of the lower triangle of nt x nt tiles, in blocked order: bands of
+// four tile rows, each band in chunks of eight tile columns (32 tiles that read the operand rows of
+// only 12 tile rows and columns), row-major inside a chunk; the columns a band has past its last full
+// chunk, and a last band of fewer than four rows, row-major.  Tile 0 is (0, 0).
+__device__ __forceinline__ void blocked_tile(int t, int nt, int& I, int& J) {
+  int b = (int)((sqrtf(32.0f * (float)t + 4.0f) - 2.0f) * 0.0625f);  // 8 b^2 + 2 b tiles before band b
+  while (b > 0 && 8 * b * b + 2 * b > t) --b;
+  while (8 * (b + 1) * (b + 1) + 2 * (b + 1) <= t) ++b;
+  int r = t - (8 * b * b + 2 * b);
+  int c0 = 0;
+  if (4 * b + 4 <= nt) {
+    const int nfull = 4 * b >= 7 ? (4 * b - 7) / 8 + 1 : 0;  // chunks entirely on or below the diagonal
+    if (r < 32 * nfull) {
+      I = 4 * b + ((r & 31) >> 3);
+      J = 8 * (r >> 5) + (r & 7);
+      return;
+    }
+    r -= 32 * nfull;
+    c0 = 8 * nfull;
+  }
+  for (int i = 4 * b;; ++i) {
+    const int cnt = i + 1 - c0;
+    if (r < cnt) {
+      I = i;
+      J = c0 + r;
+      return;
+    }
+    r -= cnt;
+  }
+}
+
 }  // namespace wr

@@ -27,6 +27,7 @@ namespace wr {
 
 constexpr int CB = 64;        // block edge
 constexpr int CP = CB + 1;    // LDS row pitch in doubles: rows start on different banks
+constexpr int CU_XCD = 8;     // workgroups are dispatched round-robin over 8 XCDs
 
 __device__ __forceinline__ void lds_sync() { lds_sync_f64(); }
 
@@ -56,6 +57,26 @@ __device__ __forceinline__ void load_block64(const double* __restrict__ G, int64
 
 __device__ __forceinline__ int chol16_inv_wave(double* sM, double* sX, int o, int lane) {
   return chol16_inv_pitch<CP>(sM + o * CP + o, sX + o * CP + o, lane);
+}
+
+// acc[x][y] += A_x B_y^T over K for the 16 x 16 blocks A_x = rows r0 + 16 x of SA and B_y = rows
+// c0 + 16 y of SB (both at pitch CP, k along the row): per k step the two row and two column
+// fragments feed four independent MFMAs (each accumulator still sums its k steps in order).
+__device__ __forceinline__ void mma16_2x2(const double* SA, int r0, const double* SB, int c0, int K,
+                                          f64x4 (&acc)[2][2], int lane) {
+  const int li = lane & 15, lk = lane >> 4;
+#pragma unroll 4
+  for (int k0 = 0; k0 < K; k0 += 4) {
+    double fa[2], fb[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) fa[x] = SA[(r0 + 16 * x + li) * CP + k0 + lk];
+#pragma unroll
+    for (int y = 0; y < 2; ++y) fb[y] = SB[(c0 + 16 * y + li) * CP + k0 + lk];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[x], fb[y], acc[x][y], 0, 0, 0);
+  }
 }
 
 // Factor the 64 x 64 diagonal block at kb held in sA (lower part valid, strict upper
@@ -317,18 +338,18 @@ __global__ __launch_bounds__(256) void chol_step_kernel(double* __restrict__ A, 
   }
   if (!active) return;
   const double* Pj = diag ? sP : sQ;
+  f64x4 acc[2][2] = {{zero, zero}, {zero, zero}};
+  mma16_2x2(sP, 32 * wi, Pj, 32 * wj, CB, acc, lane);
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y) {
-      const f64x4 acc = mma16<true>(sP, CP, 32 * wi + 16 * x, Pj, CP, 32 * wj + 16 * y, CB, zero, lane);
+    for (int y = 0; y < 2; ++y)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int gi = i0 + 32 * wi + 16 * x + (lane >> 4) + 4 * v;
         const int gj = j0 + 32 * wj + 16 * y + (lane & 15);
-        if (gi < n && gj < n && gj <= gi) A[(int64_t)gi * n + gj] = cur[x][y][v] - acc[v];
+        if (gi < n && gj < n && gj <= gi) A[(int64_t)gi * n + gj] = cur[x][y][v] - acc[x][y][v];
       }
-    }
 }
 
 // The deferred trailing update of a panel of w block columns kb0 .. kb0 + 64 w - 1, all of whose
@@ -348,14 +369,15 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ A
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int base = kb0 + CB * w;
   const f64x4 zero = {0.0, 0.0, 0.0, 0.0};
-  int ti, tj;
+  int t, ti, tj;
   {
-    const int t = blockIdx.x;
-    int i = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
-    while (i * (i + 1) / 2 > t) --i;
-    while ((i + 1) * (i + 2) / 2 <= t) ++i;
-    ti = i;
-    tj = t - i * (i + 1) / 2;
+    // each XCD (workgroup b runs on XCD b % 8) takes a contiguous range of the tiles in blocked
+    // order, so the workgroups it runs at once read the factor rows of few tile rows and columns
+    const int nt = (n - base + CB - 1) / CB, tiles = nt * (nt + 1) / 2, bid = blockIdx.x;
+    const int q = tiles / CU_XCD, rem = tiles % CU_XCD, x = bid % CU_XCD, slot = bid / CU_XCD;
+    if (slot >= q + (x < rem ? 1 : 0)) return;  // the grid is rounded up to a multiple of 8
+    t = x * q + min(x, rem) + slot;
+    blocked_tile(t, nt, ti, tj);
   }
   const int i0 = base + CB * ti, j0 = base + CB * tj;
   const bool diag = ti == tj;
@@ -380,16 +402,10 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ A
     if (!diag) load_block64(L, n, j0, kb0 + CB * c, n, n, sQ, tid);
     lds_sync();
     const double* Pj = diag ? sP : sQ;
-    if (active) {
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y)
-          acc[x][y] = mma16<true>(sP, CP, 32 * wi + 16 * x, Pj, CP, 32 * wj + 16 * y, CB, acc[x][y], lane);
-    }
+    if (active) mma16_2x2(sP, 32 * wi, Pj, 32 * wj, CB, acc, lane);
     lds_sync();
   }
-  if (blockIdx.x == 0) {
+  if (t == 0) {
     // the next diagonal block: updated lower quarters into sP (the strictly upper 16 x 16 parts
     // of the diagonal quarters are never read by the factorisation), identity past n, factor
     if (active) {
@@ -493,8 +509,9 @@ int wr_factor_m(hipStream_t st, const float* H, int64_t ldh, int n, void* ws, fl
     } else {
       hipLaunchKernelGGL(chol_panel_kernel, dim3(nt), dim3(256), 0, st, A, Lf, Xin, n, kb, dev_info);
       WR_CHECK_LAUNCH();
-      hipLaunchKernelGGL(chol_update_kernel, dim3(nt * (nt + 1) / 2), dim3(256), 0, st, A, Lf, Xout, n, CB * s0,
-                         s1 - s0, dev_info);
+      const int tiles = nt * (nt + 1) / 2;
+      hipLaunchKernelGGL(chol_update_kernel, dim3((tiles + CU_XCD - 1) / CU_XCD * CU_XCD), dim3(256), 0, st, A, Lf,
+                         Xout, n, CB * s0, s1 - s0, dev_info);
       WR_CHECK_LAUNCH();
     }
   }

@@ -45,37 +45,6 @@ __device__ __forceinline__ void tri_tile(int t, int& I, int& J) {
   J = t - i * (i + 1) / 2;
 }
 
-// Tile t (0 <= t < nt (nt + 1) / 2) of the lower triangle of nt x nt tiles, in blocked order: bands of
-// four tile rows, each band in chunks of eight tile columns (32 tiles that read 12 panels of X),
-// row-major inside a chunk; the columns a band has past its last full chunk, and a last band of fewer
-// than four rows, row-major.
-__device__ __forceinline__ void blocked_tile(int t, int nt, int& I, int& J) {
-  int b = (int)((sqrtf(32.0f * (float)t + 4.0f) - 2.0f) * 0.0625f);  // 8 b^2 + 2 b tiles before band b
-  while (b > 0 && 8 * b * b + 2 * b > t) --b;
-  while (8 * (b + 1) * (b + 1) + 2 * (b + 1) <= t) ++b;
-  int r = t - (8 * b * b + 2 * b);
-  int c0 = 0;
-  if (4 * b + 4 <= nt) {
-    const int nfull = 4 * b >= 7 ? (4 * b - 7) / 8 + 1 : 0;  // chunks entirely on or below the diagonal
-    if (r < 32 * nfull) {
-      I = 4 * b + ((r & 31) >> 3);
-      J = 8 * (r >> 5) + (r & 7);
-      return;
-    }
-    r -= 32 * nfull;
-    c0 = 8 * nfull;
-  }
-  for (int i = 4 * b;; ++i) {
-    const int cnt = i + 1 - c0;
-    if (r < cnt) {
-      I = i;
-      J = c0 + r;
-      return;
-    }
-    r -= cnt;
-  }
-}
-
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -265,10 +234,13 @@ __global__ __launch_bounds__(SY_THREADS, 1) void syrk_bf16_kernel(const uint16_t
       lds_barrier();
       // the slot of stage s is free: every wave finished its reads of it before this barrier (the
       // second half was read at the top of this iteration, the first half in the previous one)
-      if (s + SY_PF < nst) issue(s + SY_PF, slot);
+      // waves 0-3 refill the slot now, waves 4-7 (the other wave on each SIMD) after their MFMAs, so
+      // that one wave of a SIMD issues matrix work while the other waits to hand over its DMAs
+      if (s + SY_PF < nst && wave < 4) issue(s + SY_PF, slot);
       read_frags(next, 0, a0, b0);
     }
     mfma_step(a1, b1);
+    if (s + 1 < nst && s + SY_PF < nst && wave >= 4) issue(s + SY_PF, slot);
     slot = next;
   }
 
