@@ -163,18 +163,18 @@ __device__ __forceinline__ void pad_diag(double* sA, int n, int kb, int tid) {
   }
 }
 
-// First diagonal block (kb = 0).
-__global__ __launch_bounds__(256) void chol_diag_kernel(const double* __restrict__ A, int n, double* __restrict__ L,
+// The diagonal block at kb (its trailing update done): factor it (L) and invert its 16 x 16 blocks.
+__global__ __launch_bounds__(256) void chol_diag_kernel(const double* __restrict__ A, int n, int kb, double* __restrict__ L,
                                                         double* __restrict__ Xinv, int32_t* __restrict__ dev_info) {
   if (*dev_info != 0) return;
   __shared__ double sA[CB * CP];
   __shared__ double sX[CB * CP];
   const int tid = threadIdx.x;
-  load_block64(A, n, 0, 0, n, n, sA, tid);
+  load_block64(A, n, kb, kb, n, n, sA, tid);
   __syncthreads();
-  pad_diag(sA, n, 0, tid);
+  pad_diag(sA, n, kb, tid);
   __syncthreads();
-  diag_factor(sA, sX, n, 0, L, Xinv, dev_info, tid);
+  diag_factor(sA, sX, n, kb, L, Xinv, dev_info, tid);
 }
 
 // Blocked triangular solve P L_kk^T = A in place for rows 16 w .. 16 w + 15 of a 64-row
@@ -437,8 +437,128 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ A
       }
 }
 
+// The same deferred update on 128 x 128 tiles for trailing matrices of many tiles: twice the
+// multiply-adds per factor byte fetched, and 8 MFMAs per 6 fragment reads.  Eight waves (two per
+// SIMD), each a 64 x 32 part of the tile (4 x 2 blocks of 16 x 16); one workgroup per CU (the two
+// 128-row factor blocks of a column take 130 KB of LDS), the next column's blocks fetched into
+// registers while the current one is multiplied, and the tile of A while the last one is; tiles in
+// blocked order, a contiguous range per XCD.
+// The next diagonal block is left to chol_diag_kernel.
+constexpr int CB2 = 128;
+constexpr int CU2_LDS = 2 * CB2 * CP * (int)sizeof(double);
+
+__device__ __forceinline__ void fetch_block128(const double* __restrict__ G, int64_t ld, int r0, int c0, int nr, int nc,
+                                               double2 (&v)[8], int tid) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int e = tid + 512 * q;  // pair index: row e / 32, columns 2 (e % 32) .. +1
+    const int r = e >> 5, c = 2 * (e & 31);
+    const bool ok = r0 + r < nr && c0 + c + 1 < nc;  // nc is even
+    const int64_t off = ok ? (int64_t)(r0 + r) * ld + c0 + c : 0;
+    v[q] = *reinterpret_cast<const double2*>(G + off);
+    if (!ok) v[q] = double2{0.0, 0.0};
+  }
+}
+
+__device__ __forceinline__ void put_block128(const double2 (&v)[8], double* sM, int tid) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int e = tid + 512 * q;
+    const int r = e >> 5, c = 2 * (e & 31);
+    sM[r * CP + c] = v[q].x;
+    sM[r * CP + c + 1] = v[q].y;
+  }
+}
+
+__global__ __launch_bounds__(512) void chol_update128_kernel(double* __restrict__ A, const double* __restrict__ L,
+                                                             int n, int kb0, int w, const int32_t* __restrict__ dev_info) {
+  if (*dev_info != 0) return;
+  extern __shared__ double cu2_lds[];
+  double* sP = cu2_lds;
+  double* sQ = cu2_lds + CB2 * CP;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int base = kb0 + CB * w;
+  const f64x4 zero = {0.0, 0.0, 0.0, 0.0};
+  int ti, tj;
+  {
+    const int nt2 = (n - base + CB2 - 1) / CB2, tiles = nt2 * (nt2 + 1) / 2, bid = blockIdx.x;
+    const int q = tiles / CU_XCD, rem = tiles % CU_XCD, x = bid % CU_XCD, slot = bid / CU_XCD;
+    if (slot >= q + (x < rem ? 1 : 0)) return;  // the grid is rounded up to a multiple of 8
+    blocked_tile(x * q + min(x, rem) + slot, nt2, ti, tj);
+  }
+  const int i0 = base + CB2 * ti, j0 = base + CB2 * tj;
+  const bool diag = ti == tj;
+  const int wi = wave >> 2, wj = wave & 3;
+  const bool active = !(diag && 32 * wj >= 64 * wi + 64);  // parts wholly above the diagonal: nothing
+  const int li = lane & 15, lk = lane >> 4;
+  f64x4 acc[4][2];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = zero;
+  double2 pv[8], qv[8];
+  fetch_block128(L, n, i0, kb0, n, n, pv, tid);
+  if (!diag) fetch_block128(L, n, j0, kb0, n, n, qv, tid);
+  const double* Pj = diag ? sP : sQ;
+  auto multiply = [&]() {
+    if (!active) return;
+#pragma unroll 2
+    for (int k0 = 0; k0 < CB; k0 += 4) {
+      double fa[4], fb[2];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) fa[x] = sP[(64 * wi + 16 * x + li) * CP + k0 + lk];
+#pragma unroll
+      for (int y = 0; y < 2; ++y) fb[y] = Pj[(32 * wj + 16 * y + li) * CP + k0 + lk];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[x], fb[y], acc[x][y], 0, 0, 0);
+    }
+  };
+  for (int c = 0; c + 1 < w; ++c) {
+    if (c > 0) lds_sync();  // every wave is done with column c - 1
+    put_block128(pv, sP, tid);
+    if (!diag) put_block128(qv, sQ, tid);
+    lds_sync();
+    fetch_block128(L, n, i0, kb0 + CB * (c + 1), n, n, pv, tid);
+    if (!diag) fetch_block128(L, n, j0, kb0 + CB * (c + 1), n, n, qv, tid);
+    multiply();
+  }
+  if (w > 1) lds_sync();
+  put_block128(pv, sP, tid);
+  if (!diag) put_block128(qv, sQ, tid);
+  lds_sync();
+  // the wave's part of A_ij, fetched while the last column is multiplied (in the registers the
+  // factor blocks used)
+  double cur[4][2][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int gi = i0 + 64 * wi + 16 * x + lk + 4 * v;
+        const int gj = j0 + 32 * wj + 16 * y + li;
+        cur[x][y][v] = active && gi < n && gj < n ? A[(int64_t)gi * n + gj] : 0.0;
+      }
+  multiply();
+  if (!active) return;
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int gi = i0 + 64 * wi + 16 * x + lk + 4 * v;
+        const int gj = j0 + 32 * wj + 16 * y + li;
+        if (gi < n && gj < n && gj <= gi) A[(int64_t)gi * n + gj] = cur[x][y][v] - acc[x][y][v];
+      }
+}
+
 // Block columns per panel of deferred trailing updates.
 static const int kPanel = 4;
+// Trailing matrices of at least this many 64-wide tile rows take the 128 x 128 tile update.
+static const int kBigUpdate = 40;
 
 // A = J H J (lower triangle), widened to fp64.
 __global__ void reverse_copy_kernel(const float* __restrict__ H, int64_t ldh, int n, double* __restrict__ A) {
@@ -487,7 +607,7 @@ int wr_factor_m(hipStream_t st, const float* H, int64_t ldh, int n, void* ws, fl
   double* Xinv[2] = {Lf + (size_t)n * n, Lf + (size_t)n * n + 4 * 256};  // alternate per block column
   hipLaunchKernelGGL(reverse_copy_kernel, dim3(n), dim3(256), 0, st, H, ldh, n, A);
   WR_CHECK_LAUNCH();
-  hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, st, A, n, Lf, Xinv[0], dev_info);
+  hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, st, A, n, 0, Lf, Xinv[0], dev_info);
   WR_CHECK_LAUNCH();
   // Panels of kPanel block columns: within a panel each block column updates only the panel's own
   // later block columns (every tile of its first trailing column also writes the factor blocks
@@ -509,9 +629,19 @@ int wr_factor_m(hipStream_t st, const float* H, int64_t ldh, int n, void* ws, fl
     } else {
       hipLaunchKernelGGL(chol_panel_kernel, dim3(nt), dim3(256), 0, st, A, Lf, Xin, n, kb, dev_info);
       WR_CHECK_LAUNCH();
-      const int tiles = nt * (nt + 1) / 2;
-      hipLaunchKernelGGL(chol_update_kernel, dim3((tiles + CU_XCD - 1) / CU_XCD * CU_XCD), dim3(256), 0, st, A, Lf,
-                         Xout, n, CB * s0, s1 - s0, dev_info);
+      if (nt >= kBigUpdate) {
+        // 128 x 128 tiles, then the next panel's first diagonal block on its own
+        const int nt2 = (nt + 1) / 2, tiles = nt2 * (nt2 + 1) / 2;
+        if (!lds_limit(reinterpret_cast<const void*>(chol_update128_kernel), CU2_LDS)) return WR_EHIP;
+        hipLaunchKernelGGL(chol_update128_kernel, dim3((tiles + CU_XCD - 1) / CU_XCD * CU_XCD), dim3(512), CU2_LDS, st,
+                           A, Lf, n, CB * s0, s1 - s0, dev_info);
+        WR_CHECK_LAUNCH();
+        hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, st, A, n, CB * s1, Lf, Xout, dev_info);
+      } else {
+        const int tiles = nt * (nt + 1) / 2;
+        hipLaunchKernelGGL(chol_update_kernel, dim3((tiles + CU_XCD - 1) / CU_XCD * CU_XCD), dim3(256), 0, st, A, Lf,
+                           Xout, n, CB * s0, s1 - s0, dev_info);
+      }
       WR_CHECK_LAUNCH();
     }
   }
