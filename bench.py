@@ -817,6 +817,23 @@ def main_body(args):
         line["roofline"]["exclusive"] = {
             "note": "breakdown pass, one stream (no other work on the GPU during the H accumulation)",
             "syrk_ms_per_step": stage["hessian"], "achieved": excl, "frac": excl / PEAK_BF16_TFLOPS}
+        # HBM-bound steps against the stage times of the breakdown pass (a stage holds every kernel of
+        # its calls, so the sweep's and the recode's figures are lower bounds; the per-kernel figures
+        # are in the kernel-trace summary)
+        work = body_work(layers)
+
+        def hbm(key, st, note):
+            gbs = work[key] / (stage[st] * 1e-3) / 1e9
+            return {"bytes_per_step": work[key], "stage_ms": stage[st], "achieved": gbs, "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "note": note}
+        line["stage_rooflines"] = {
+            "sweep": hbm("sweep", "gptq", "W fp32 read, codes and scales written, M's upper half read, per H; "
+                         "the stage also holds the fp64 factorisation"),
+            "recode": hbm("recode", "wring", "codes in and out and the scales of the nearest-point recode; the "
+                          "stage also holds the Gram/RHS products and the per-row solves"),
+            "pack": hbm("pack", "pack", "codes and scales read, packed stream and scales written"),
+            "unpack": hbm("pack", "unpack", "packed stream and scales read, codes and scales written"),
+        }
     if not args.no_measures:
         progress("the model cards' measures for layer 0 (untimed)")
         per, mean = body_measures(wr, ctx, I, torch)
@@ -827,30 +844,9 @@ def main_body(args):
     print(json.dumps(line), flush=True)
 
 
-def kernel_summary(db_path, steps, layers):
-    """Markdown table of the library's kernels in a rocprofv3 kernel trace (rocpd database): calls,
-    total and average duration, per-step time, and the roofline of the kernels whose algorithmic
-    work per body step is stated (bf16 MFMA flops, fp64 flops, HBM bytes)."""
-    import collections
-    import re
-    import sqlite3
-    con = sqlite3.connect(db_path)
-    cols = [r[1] for r in con.execute("pragma table_info(kernels)")]
-    name_col = "name" if "name" in cols else "kernel_name"
-    agg = collections.OrderedDict()
-    for name, start, end in con.execute(f"select {name_col}, start, end from kernels order by start"):
-        m = re.search(r"wr::([A-Za-z0-9_]+(?:<[^>]*>)?)", name)
-        if not m:
-            continue
-        a = agg.setdefault(m.group(1), [0, 0.0])
-        a[0] += 1
-        a[1] += (end - start) * 1e-3
-    total = sum(v[1] for v in agg.values())
-    out = [f"library kernels: {total / 1e3:.2f} ms over {steps} step(s) = {total / 1e3 / steps:.2f} ms per step", "",
-           "| kernel | calls | total ms | avg us | ms per step | share |", "|---|---|---|---|---|---|"]
-    for k, (c, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
-        out.append(f"| `{k}` | {c} | {t / 1e3:.2f} | {t / c:.1f} | {t / 1e3 / steps:.2f} | {100 * t / total:.1f} % |")
-    # algorithmic work of one body step (all layers) for the kernels with a stated roofline
+def body_work(layers):
+    """Algorithmic work of one body step over `layers` layers, per step of the path: bf16 MFMA flops
+    (syrk, gram), fp64 flops (chol, rowsolve) and HBM bytes (sweep, recode, pack)."""
     from post_bit_weight_amd import body as _body
     N, g = BODY["calib_rows"], BODY["group"]
     groups = {}
@@ -870,6 +866,42 @@ def kernel_summary(db_path, steps, layers):
                 work["pack"] += r * n * (1 + 2.0 / g) + r * n * b / 8.0 + r * n * 2.0 / g
             work["gram"] += 2 * 3.0 * rows * n * n                 # W'H + Gram, both joint solves
             work["rowsolve"] += 2 * rows * nb ** 3 / 3.0
+    return work
+
+
+def kernel_summary(db_path, steps, layers):
+    """Markdown table of the library's kernels in a rocprofv3 kernel trace (rocpd database): calls,
+    total and average duration, per-step time, and the roofline of the kernels whose algorithmic
+    work per body step is stated (bf16 MFMA flops, fp64 flops, HBM bytes)."""
+    import collections
+    import re
+    import sqlite3
+    con = sqlite3.connect(db_path)
+    cols = [r[1] for r in con.execute("pragma table_info(kernels)")]
+    name_col = "name" if "name" in cols else "kernel_name"
+    agg = collections.OrderedDict()
+    busy, reach = 0.0, None  # time with at least one library kernel running (streams overlap)
+    for name, start, end in con.execute(f"select {name_col}, start, end from kernels order by start"):
+        m = re.search(r"wr::([A-Za-z0-9_]+(?:<[^>]*>)?)", name)
+        if not m:
+            continue
+        a = agg.setdefault(m.group(1), [0, 0.0])
+        a[0] += 1
+        a[1] += (end - start) * 1e-3
+        if reach is None or start >= reach:
+            busy += (end - start) * 1e-3
+            reach = end
+        elif end > reach:
+            busy += (end - reach) * 1e-3
+            reach = end
+    total = sum(v[1] for v in agg.values())
+    out = [f"library kernels: {total / 1e3:.2f} ms of kernel time over {steps} step(s) = {total / 1e3 / steps:.2f} ms "
+           f"per step; {busy / 1e3 / steps:.2f} ms per step with at least one of them running (kernels on "
+           "different streams overlap, and then each one's duration includes the time it shares the chip)", "",
+           "| kernel | calls | total ms | avg us | ms per step | share |", "|---|---|---|---|---|---|"]
+    for k, (c, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        out.append(f"| `{k}` | {c} | {t / 1e3:.2f} | {t / c:.1f} | {t / 1e3 / steps:.2f} | {100 * t / total:.1f} % |")
+    work = body_work(layers)
     kinds = [("syrk", r"^syrk_bf16_kernel|^syrk_reduce_kernel", "bf16 MFMA", PEAK_BF16_TFLOPS * 1e12, "TFLOP/s"),
              ("chol", r"^chol_", "fp64", 78.6e12, "TFLOP/s"),
              ("sweep", r"^sweep_panel_kernel|^trail_wide_kernel|^split_mt_kernel|^build_m_kernel", "HBM",

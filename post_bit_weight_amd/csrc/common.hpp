@@ -146,6 +146,15 @@ __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
 
+// Lower-triangle tile t -> (I, J), J <= I, row-major over the block triangle.
+__device__ __forceinline__ void tri_tile(int t, int& I, int& J) {
+  int i = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+  while (i * (i + 1) / 2 > t) --i;
+  while ((i + 1) * (i + 2) / 2 <= t) ++i;
+  I = i;
+  J = t - i * (i + 1) / 2;
+}
+
 // Tile t (0 <= t < nt (nt + 1) / 2) of the lower triangle of nt x nt tiles, in blocked order: bands of
 // four tile rows, each band in chunks of eight tile columns (32 tiles that read the operand rows of
 // only 12 tile rows and columns), row-major inside a chunk; the columns a band has past its last full

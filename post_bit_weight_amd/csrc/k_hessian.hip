@@ -1,4 +1,4 @@
-// Calibration second moment S += X^T X (lower triangle) and H = S/N + delta I.
+// Calibration second moment S += X^T X (lower triangle).
 //
 // H is the average of x x^T over calibration inputs (Pingala-8 post, "Trick 2:
 // round with error feedback"); delta is the Tikhonov damping of the GPTQ solve
@@ -35,15 +35,6 @@ constexpr int SY_DMA_PER_WAVE = (SY_STAGE_BYTES / 1024) / (SY_THREADS / 64);  //
 constexpr int SY_XCD = 8;                // workgroups are dispatched round-robin over 8 XCDs
 constexpr int SY_MAX_ROWS = 32768;       // rows summed in fp32 before the sums reach S in fp64
 constexpr int SY_SPLIT_ROWS = 16384;     // rows per split when the tiles alone do not fill the chip
-
-// Lower-triangle tile t -> (I, J), J <= I, row-major over the block triangle.
-__device__ __forceinline__ void tri_tile(int t, int& I, int& J) {
-  int i = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
-  while (i * (i + 1) / 2 > t) --i;
-  while ((i + 1) * (i + 2) / 2 <= t) ++i;
-  I = i;
-  J = t - i * (i + 1) / 2;
-}
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
@@ -311,80 +302,6 @@ __global__ void zero_lower_kernel(double* S, int n) {
   for (int j = threadIdx.x; j <= i; j += blockDim.x) S[(size_t)i * n + j] = 0.0;
 }
 
-// delta = damp * trace(S / N) / n_store, summed in a fixed order by one workgroup.
-__global__ __launch_bounds__(1024) void trace_kernel(const double* __restrict__ S, int n, double inv_rows,
-                                                     double damp_over_nstore, double* __restrict__ delta64,
-                                                     float* __restrict__ delta_out) {
-  __shared__ double red[1024];
-  double acc = 0.0;
-  for (int i = threadIdx.x; i < n; i += 1024) acc += S[(size_t)i * n + i];
-  red[threadIdx.x] = acc;
-  __syncthreads();
-  for (int w = 512; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    const double d = damp_over_nstore * red[0] * inv_rows;
-    *delta64 = d;
-    if (delta_out) *delta_out = (float)d;
-  }
-}
-
-// Hd (n_store x n_store fp64, full) = pad(S / N), for a rotation in fp64 before rounding to fp32.
-__global__ void expand_kernel(const double* __restrict__ S, int n, int64_t n_store, double inv_rows,
-                              double* __restrict__ Hd) {
-  const int64_t i = blockIdx.y;
-  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n_store; j += (int64_t)gridDim.x * blockDim.x) {
-    double v = 0.0;
-    if (i < n && j < n) v = (i >= j ? S[i * n + j] : S[j * n + i]) * inv_rows;
-    Hd[i * n_store + j] = v;
-  }
-}
-
-__global__ void damp_round_kernel(const double* __restrict__ Hd, int64_t n_store, const double* __restrict__ delta64,
-                                  float* __restrict__ H, int64_t ldh) {
-  const int64_t i = blockIdx.y;
-  const double delta = *delta64;
-  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n_store; j += (int64_t)gridDim.x * blockDim.x)
-    H[i * ldh + j] = (float)(Hd[i * n_store + j] + (i == j ? delta : 0.0));
-}
-
-// H = S/N + delta I (S's lower triangle mirrored, zero padding to n_store, delta on the whole
-// diagonal), rounded to fp32.  One workgroup per lower 64 x 64 tile (I, J) of the padded matrix:
-// the tile of S is read once, coalesced, into LDS and written to H at (I, J) and transposed at
-// (J, I); a diagonal tile takes its upper half from its own lower half.
-constexpr int FZ_T = 64;
-__global__ __launch_bounds__(256) void finalize_kernel(const double* __restrict__ S, int n, int64_t n_store,
-                                                       double inv_rows, const double* __restrict__ delta64,
-                                                       float* __restrict__ H, int64_t ldh) {
-  __shared__ double t[FZ_T][FZ_T + 1];
-  int I, J;
-  tri_tile(blockIdx.x, I, J);
-  const double delta = *delta64;
-  const int c = threadIdx.x & (FZ_T - 1);
-  const int64_t i0 = (int64_t)FZ_T * I, j0 = (int64_t)FZ_T * J;
-  for (int r = threadIdx.x / FZ_T; r < FZ_T; r += 256 / FZ_T) {
-    const int64_t i = i0 + r, j = j0 + c;
-    t[r][c] = (i < n && j < n && i >= j) ? S[i * n + j] : 0.0;
-  }
-  __syncthreads();
-  // element (i, j) of H from the tile: S[i][j] for i >= j, else S[j][i]
-  for (int r = threadIdx.x / FZ_T; r < FZ_T; r += 256 / FZ_T) {
-    const int64_t i = i0 + r, j = j0 + c;
-    if (i < n_store && j < n_store) {
-      double v = (I != J || r >= c ? t[r][c] : t[c][r]) * inv_rows;
-      if (i == j) v += delta;
-      H[i * ldh + j] = (float)v;
-    }
-  }
-  if (I == J) return;
-  for (int r = threadIdx.x / FZ_T; r < FZ_T; r += 256 / FZ_T) {  // H[j0 + r][i0 + c] = S[i0 + c][j0 + r]
-    const int64_t i = j0 + r, j = i0 + c;
-    if (i < n_store && j < n_store) H[i * ldh + j] = (float)(t[c][r] * inv_rows);
-  }
-}
-
 }  // namespace wr
 
 using namespace wr;
@@ -595,40 +512,5 @@ int wr_hessian_accumulate_static_impl(wr_ctx* ctx, const void* X, int x_dtype, i
       if (rc) return rc;
     }
   }
-  return WR_OK;
-}
-
-int wr_rotate_sym_f64(wr_ctx* ctx, double* M, int64_t n, int64_t ld, int32_t m, const int8_t* signs);
-
-size_t wr_finalize_ws_bytes(int64_t n_store) { return 256 + (size_t)n_store * n_store * sizeof(double); }
-
-int wr_hessian_finalize_impl(wr_ctx* ctx, const double* S, int64_t n, int64_t total_rows, float damp_frac,
-                             int64_t n_store, float* H, int64_t ldh, float* delta_out, int32_t had_block,
-                             const int8_t* signs) {
-  const size_t need = had_block ? wr_finalize_ws_bytes(n_store) : 256;
-  if (ctx->ws_bytes < need) return WR_EWORKSPACE;
-  double* delta64 = static_cast<double*>(ctx->ws);
-  const double inv_rows = 1.0 / (double)total_rows;
-  hipLaunchKernelGGL(trace_kernel, dim3(1), dim3(1024), 0, ctx->stream, S, (int)n, inv_rows,
-                     (double)damp_frac / (double)n_store, delta64, delta_out);
-  WR_CHECK_LAUNCH();
-  const unsigned gx = (unsigned)std::min<int64_t>((n_store + 255) / 256, 64);
-  if (!had_block) {
-    const int64_t nt = (n_store + FZ_T - 1) / FZ_T;
-    hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)(nt * (nt + 1) / 2)), dim3(256), 0, ctx->stream, S, (int)n,
-                       n_store, inv_rows, delta64, H, ldh);
-    WR_CHECK_LAUNCH();
-    return WR_OK;
-  }
-  // H = R pad(S/N) R^T + delta I, rotated in fp64 and rounded to fp32 once
-  double* Hd = reinterpret_cast<double*>(static_cast<char*>(ctx->ws) + 256);
-  hipLaunchKernelGGL(expand_kernel, dim3(gx, (unsigned)n_store), dim3(256), 0, ctx->stream, S, (int)n, n_store,
-                     inv_rows, Hd);
-  WR_CHECK_LAUNCH();
-  const int rc = wr_rotate_sym_f64(ctx, Hd, n_store, n_store, had_block, signs);
-  if (rc) return rc;
-  hipLaunchKernelGGL(damp_round_kernel, dim3(gx, (unsigned)n_store), dim3(256), 0, ctx->stream, Hd, n_store, delta64,
-                     H, ldh);
-  WR_CHECK_LAUNCH();
   return WR_OK;
 }
