@@ -58,8 +58,9 @@ def parse():
     p.add_argument("--calib-sets", type=int, default=4,
                    help="body: distinct per-layer calibration sets kept resident (layer l reads set l mod K)")
     p.add_argument("--no-breakdown", action="store_true", help="body: skip the untimed per-call breakdown pass")
-    p.add_argument("--streams", type=int, choices=(1, 3), default=3,
-                   help="body: 3 runs each input dim's solves on a stream of its own (they overlap), 1 in order")
+    p.add_argument("--streams", type=int, choices=(1, 3, 4), default=3,
+                   help="body: 3 runs each input dim's solves on a stream of its own (they overlap); 4 also "
+                        "alternates the widest dim's layers between two streams and buffer sets; 1 in order")
     p.add_argument("--lag", type=int, default=0,
                    help="body, 3 streams: a stream starts layer l once the others have finished layer l - lag "
                         "(0: no coupling)")
@@ -473,7 +474,7 @@ class BodyInputs:
         self.S = {n: torch.empty(n, n, dtype=torch.float64, device=dev) for n in self.dims}
         self.H = {n: torch.empty(n, n, dtype=torch.float32, device=dev) for n in self.dims}
         self.none = {n: torch.empty(0, n, dtype=torch.bfloat16, device=dev) for n in self.dims}
-        self.delta = torch.empty(1, dtype=torch.float32, device=dev)
+        self.delta = {n: torch.empty(1, dtype=torch.float32, device=dev) for n in self.dims}
         names = [m[0] for m in body.MODULES]
         self.groups = []
         for layer in range(layers):
@@ -504,6 +505,10 @@ class BodyInputs:
             self.groups.append(per)
         rows_max = {n: self.groups[0][n]["W"].shape[0] for n in self.dims}
         self.Wst = {n: torch.empty(rows_max[n], n, dtype=torch.float32, device=dev) for n in self.dims}
+        # per input dim, the buffer sets its layers cycle through (S, H, rotated weights, delta): one,
+        # or two for a dim whose layers alternate between two streams (add_set)
+        self.sets = {n: [dict(S=self.S[n], H=self.H[n], Wst=self.Wst[n], delta=self.delta[n])] for n in self.dims}
+        self._dev, self._rows_max = dev, rows_max
         self.weights = sum(int(v["W"].numel()) for per in self.groups for v in per.values())
         self.payload = sum(int(m["packed"].numel()) for per in self.groups for v in per.values() for m in v["mods"])
         ws = 0
@@ -515,63 +520,71 @@ class BodyInputs:
                      wr.wr_workspace_bytes(wr.WR_OP_WRING, rows, n, g, r, 0))
         self.ws_bytes = ws
 
+    def add_set(self, torch, n):
+        """A second buffer set for input dim n (layers then alternate between the two)."""
+        dev = self._dev
+        self.sets[n].append(dict(S=torch.empty(n, n, dtype=torch.float64, device=dev),
+                                 H=torch.empty(n, n, dtype=torch.float32, device=dev),
+                                 Wst=torch.empty(self._rows_max[n], n, dtype=torch.float32, device=dev),
+                                 delta=torch.empty(1, dtype=torch.float32, device=dev)))
+
 
 def body_step(wr, ctxs, I, mark=None, lag=0):
-    """One pass of the whole solve over the body.  ctxs: one library context for every input dim (the
-    calls run in order on its stream), or a dict input dim -> context: each dim's solves then run on
-    that context's stream and overlap with the other dims' (a dim's buffers are only touched on its
-    own stream, so the streams share nothing).  With lag > 0 a dim's stream starts layer l only after
-    every other dim's stream has finished layer l - lag (the streams stay within lag layers of each
-    other).  mark(kind, n) is called between library calls when given (it records timing events on dim
-    n's stream)."""
+    """One pass of the whole solve over the body.  ctxs: one library context for every call (they run
+    in order on its stream), or a dict (input dim, buffer set) -> context: the solves of a dim's layers
+    that use set k of its buffers run on that context's stream and overlap with the others (a set's
+    buffers are only touched on its own stream, so the streams share nothing; with two sets a dim's
+    even and odd layers alternate).  With lag > 0 a stream starts layer l only after every other
+    stream has finished layer l - lag.  mark(kind, n, stream) is called between library calls when
+    given (it records timing events on the stream of the call)."""
     import torch
-    if not isinstance(ctxs, dict):
-        ctxs = {n: ctxs for n in I.dims}
+    single = not isinstance(ctxs, dict)
     cfg = I.cfg
     g, lam, hb, N = cfg["group"], cfg["lam"], cfg["had_block"], cfg["calib_rows"]
-    m = mark or (lambda kind, n: None)
-    multi = len({id(c) for c in ctxs.values()}) > 1
-    done = []  # per layer: {n: event at the end of layer on dim n's stream}
+    m = mark or (lambda kind, n, stream: None)
+    done = []  # per layer: {n: event at the end of layer on its stream}
     for layer in range(I.layers):
         p = layer % I.P
-        if multi and lag > 0:
+        if not single and lag > 0:
             done.append({})
         for n in I.dims:
-            ctx = ctxs[n]
-            if multi and lag > 0 and layer >= lag:
+            k = 0 if single else layer % len(I.sets[n])
+            buf = I.sets[n][k]
+            ctx = ctxs if single else ctxs[(n, k)]
+            if not single and lag > 0 and layer >= lag:
                 for n2, ev in done[layer - lag].items():
                     if n2 != n:
                         ctx.stream.wait_event(ev)
             G = I.groups[layer][n]
             rows = G["W"].shape[0]
-            Wst = I.Wst[n][:rows]
-            wr.wr_hessian_accumulate(ctx, I.none[n], I.S[n], zero=True)       # S = 0
-            m("hessian", n)
-            wr.wr_hessian_accumulate(ctx, I.X[n][p], I.S[n])
-            m("finalize", n)
-            wr.wr_hessian_finalize(ctx, I.S[n], N, cfg["damp"], I.H[n], I.delta, hb, I.signs[n])
-            m("rotate", n)
+            S, H, Wst = buf["S"], buf["H"], buf["Wst"][:rows]
+            wr.wr_hessian_accumulate(ctx, I.none[n], S, zero=True)          # S = 0
+            m("hessian", n, ctx.stream)
+            wr.wr_hessian_accumulate(ctx, I.X[n][p], S)
+            m("finalize", n, ctx.stream)
+            wr.wr_hessian_finalize(ctx, S, N, cfg["damp"], H, buf["delta"], hb, I.signs[n])
+            m("rotate", n, ctx.stream)
             with torch.cuda.stream(ctx.stream):
                 Wst.copy_(G["W"])                                                # widen to fp32
             wr.wr_hadamard_rotate(ctx, Wst, hb, I.signs[n], wr.WR_ROT_ROWS)
-            m("gptq", n)
-            wr.wr_gptq_sweep(ctx, Wst, I.H[n], G["bits"], g, cfg["lazy_batch"], G["codes"], G["scales"],
+            m("gptq", n, ctx.stream)
+            wr.wr_gptq_sweep(ctx, Wst, H, G["bits"], g, cfg["lazy_batch"], G["codes"], G["scales"],
                              G["info"][0:1])
-            m("joint", n)
-            wr.wr_wring_solve(ctx, I.H[n], G["bits"], g, lam, G["codes"], G["scales"], G["info"][1:2], target=Wst)
-            for k, mod in enumerate(G["mods"]):
+            m("joint", n, ctx.stream)
+            wr.wr_wring_solve(ctx, H, G["bits"], g, lam, G["codes"], G["scales"], G["info"][1:2], target=Wst)
+            for kk, mod in enumerate(G["mods"]):
                 sl = slice(mod["r0"], mod["r1"])
-                m("wring", n)
-                wr.wr_wring_solve(ctx, I.H[n], G["bits"][sl], g, lam, G["codes"][sl], G["scales"][sl],
-                                  G["info"][2 + k:3 + k], B=mod["B"], A=mod["A"], alpha=float(cfg["rank"]),
+                m("wring", n, ctx.stream)
+                wr.wr_wring_solve(ctx, H, G["bits"][sl], g, lam, G["codes"][sl], G["scales"][sl],
+                                  G["info"][2 + kk:3 + kk], B=mod["B"], A=mod["A"], alpha=float(cfg["rank"]),
                                   recode=True)
-                m("pack", n)
+                m("pack", n, ctx.stream)
                 wr.wr_pack(ctx, G["codes"][sl], G["scales"][sl], mod["bits"], g, mod["packed"])
-                m("unpack", n)
+                m("unpack", n, ctx.stream)
                 wr.wr_unpack(ctx, mod["packed"], mod["r1"] - mod["r0"], n, mod["bits"], g, G["ucodes"][sl],
                              G["uscales"][sl])
-            m("end", n)
-            if multi and lag > 0:
+            m("end", n, ctx.stream)
+            if not single and lag > 0:
                 ev = torch.cuda.Event()
                 ev.record(ctx.stream)
                 done[layer][n] = ev
@@ -705,9 +718,13 @@ def main_body(args):
     progress(f"drawing the synthetic inputs ({args.calib_sets} resident calibration sets, {layers} layers)")
     I = BodyInputs(torch, wr, body, synth, layers, args.calib_sets, cfg, progress)
     ctx.ensure_workspace(I.ws_bytes)
-    # the timed steps' contexts: one, or one per input dim on streams of their own (default priority)
-    ctxs = ctx if args.streams == 1 else {n: wr.Context(0, stream=torch.cuda.Stream(dev)) for n in I.dims}
-    if isinstance(ctxs, dict):
+    # the timed steps' contexts: one, or one per input dim and buffer set on streams of their own
+    # (default priority); with 4 streams the widest dim's layers alternate between two
+    ctxs = ctx
+    if args.streams > 1:
+        if args.streams == 4:
+            I.add_set(torch, max(I.dims))
+        ctxs = {(n, k): wr.Context(0, stream=torch.cuda.Stream(dev)) for n in I.dims for k in range(len(I.sets[n]))}
         for c in ctxs.values():
             c.ensure_workspace(I.ws_bytes)
     torch.cuda.synchronize()
@@ -732,10 +749,10 @@ def main_body(args):
     progress(f"timing {args.steps} steps")
     syrk = []
 
-    def mark_syrk(kind, n):
+    def mark_syrk(kind, n, stream):
         if kind in ("hessian", "finalize"):
             e = torch.cuda.Event(enable_timing=True)
-            e.record(ctxs[n].stream if isinstance(ctxs, dict) else st)
+            e.record(stream)
             syrk.append((kind, n, e))
 
     torch.cuda.synchronize()
@@ -757,17 +774,32 @@ def main_body(args):
     achieved = sum(flops.values()) / (syrk_ms * 1e-3) / 1e12
 
     stage = None
+    same_as_one_stream = None
     if not args.no_breakdown:
-        progress("per-call breakdown (one separate, untimed step)")
+        progress("per-call breakdown (one separate, untimed step, every call in order on one stream)")
         evs = []
 
-        def mark_all(kind, n):
+        def mark_all(kind, n, stream):
             e = torch.cuda.Event(enable_timing=True)
-            e.record(st)
+            e.record(stream)
             evs.append((kind, n, e))
 
+        timed = [(G["codes"].clone(), G["scales"].clone()) for per in I.groups for G in per.values()]
         body_step(wr, ctx, I, mark_all)
         torch.cuda.synchronize()
+        # the timed steps' codes and scales must equal the in-order step's bit for bit (the kernels are
+        # deterministic; a difference would mean the streams raced)
+        redo = [(layer, n, G["codes"], G["scales"]) for layer, per in enumerate(I.groups) for n, G in per.items()]
+        diff = []
+        for (c0, s0), (layer, n, c1, s1) in zip(timed, redo):
+            dc = int((c0 != c1).sum())
+            ds = int((s0.view(torch.int16) != s1.view(torch.int16)).sum())
+            if dc or ds:
+                diff.append(f"layer {layer} dim {n}: {dc} codes, {ds} scales")
+        same_as_one_stream = not diff
+        del timed
+        if diff:
+            raise RuntimeError("the timed steps' codes or scales differ from the in-order step's: " + "; ".join(diff[:12]))
         stage = {}
         for (k0, n0, e0), (_, _, e1) in zip(evs[:-1], evs[1:]):
             if k0 == "end":
@@ -812,6 +844,7 @@ def main_body(args):
     }
     if stage is not None:
         line["stage_ms"] = stage
+        line["timed_equals_in_order"] = same_as_one_stream
         # the same launches timed alone: the breakdown pass runs every call in order on one stream
         excl = sum(flops.values()) / (stage["hessian"] * 1e-3) / 1e12
         line["roofline"]["exclusive"] = {

@@ -773,8 +773,9 @@ __global__ __launch_bounds__(256) void row_solve_blk_kernel(const float* __restr
 #pragma unroll
       for (int v = 0; v < 4; ++v) AIK[((lane >> 4) + 4 * v) * RB_P + (lane & 15)] = acc[v];
     }
-    if (wave == 3 || (nbk - K - 1 < 4 && wave == nbk - K - 1)) {
-      // z_K = X_K y_K (by a wave without a panel block, or with the fewest)
+    // z_K = X_K y_K by exactly one wave (it reads y_K and then overwrites it): the first wave
+    // without a panel block, or wave 3 (the last panel blocks' wave) when all four have one
+    if (wave == (nbk - K - 1 < 4 ? nbk - K - 1 : 3)) {
       double z = 0.0;
       if (lane < 16) {
 #pragma unroll

@@ -321,6 +321,45 @@ def test_joint_scales_many_blocks(wr, ctx, n, g, rows):
     assert u.max() <= 1 and (u > 0).mean() < 0.02
 
 
+def test_blocked_row_solve_is_the_same_under_concurrency(wr, ctx):
+    """The blocked per-row solve (152 blocks: the 9728-wide shape) returns bit-identical scales when it
+    runs alone and when two copies run on two streams beside an H accumulation on a third.  Regression
+    test: two waves once both formed z_K = X_K y_K in the last block columns, one reading y_K while
+    the other overwrote it, which only showed when other work skewed the waves."""
+    from post_bit_weight_amd import synth
+    rows, n, g = 512, 9728, 64
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    X = torch.randn(2 * n, n, device="cuda", generator=gen) / (2 * n) ** 0.5
+    H = (X.t() @ X + 0.05 * torch.eye(n, device="cuda")).contiguous()
+    del X
+    W = synth.gaussian((rows, n), 0.02, seed=9).cuda()
+    codes = torch.randint(0, 8, (rows, n), device="cuda", dtype=torch.uint8, generator=gen)
+    scales = (0.01 + 0.01 * torch.rand(rows, n // g, device="cuda", generator=gen)).half()
+    bits = torch.full((rows,), 3, dtype=torch.uint8, device="cuda")
+
+    def inputs():
+        return codes.clone(), scales.clone(), torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    c0, alone, info = inputs()
+    wr.wr_wring_solve(ctx, H, bits, g, 0.01, c0, alone, info, target=W)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
+    s1, s2, s3 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    k1, k2, k3 = wr.Context(0, stream=s1), wr.Context(0, stream=s2), wr.Context(0, stream=s3)
+    Xb = torch.randn(65536, 4096, device="cuda", generator=gen).to(torch.bfloat16)
+    S = torch.empty(4096, 4096, dtype=torch.float64, device="cuda")
+    for _ in range(3):
+        (ca, a, ia), (cb, b, ib) = inputs(), inputs()
+        torch.cuda.synchronize()  # inputs made on the default stream before the three streams start
+        wr.wr_hessian_accumulate(k3, Xb, S, zero=True)
+        wr.wr_wring_solve(k1, H, bits, g, 0.01, ca, a, ia, target=W)
+        wr.wr_wring_solve(k2, H, bits, g, 0.01, cb, b, ib, target=W)
+        torch.cuda.synchronize()
+        assert int(ia.item()) == 0 and int(ib.item()) == 0
+        assert torch.equal(a.view(torch.int16), alone.view(torch.int16))
+        assert torch.equal(b.view(torch.int16), alone.view(torch.int16))
+
+
 def test_wring_toy(wr, ctx, toy):
     H32 = toy["H"].astype(np.float32)
     Hd = H32.astype(np.float64)
