@@ -368,48 +368,68 @@ __device__ __forceinline__ void tw_vm_wait() {
 }
 __device__ __forceinline__ void tw_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-constexpr int TW_T = 128;                  // output tile edge
-constexpr int TW_KC = 32;                  // k per stage
-constexpr int TW_PLANE = TW_T * TW_KC * 2; // one bf16 part of one operand tile: 8 KB
-constexpr int TW_STAGE = 6 * TW_PLANE;     // E0..2 then Mt0..2: 48 KB
-constexpr int TW_DMA = TW_STAGE / 1024 / 4;  // 1 KB DMAs per wave per stage: 12
+constexpr int TW_R = 256;                    // output tile rows (weight rows)
+constexpr int TW_C = 128;                    // output tile columns
+constexpr int TW_KC = 32;                    // k per stage
+constexpr int TW_EPLANE = TW_R * TW_KC * 2;  // one bf16 part of the E tile: 16 KB
+constexpr int TW_MPLANE = TW_C * TW_KC * 2;  // one bf16 part of the M tile: 8 KB
+constexpr int TW_STAGE = 3 * TW_EPLANE + 3 * TW_MPLANE;  // E0..2 then Mt0..2: 72 KB, two stages
+constexpr int TW_DMA = TW_STAGE / 1024 / 8;  // 1 KB DMAs per wave per stage: 9
+constexpr int TW_XCD = 8;                    // workgroups are dispatched round-robin over 8 XCDs
 
-// 16-byte unit (row r, k-octet q) of a 128 x 32 bf16 tile: sixteen consecutive rows at one
+// 16-byte unit (row r, k-octet q) of a tile of 32 bf16 columns: sixteen consecutive rows at one
 // octet fall on sixteen distinct 16-byte bank groups of a 256-byte line.
 __device__ __forceinline__ int tw_unit(int r, int q) { return r * 4 + (q ^ ((r >> 2) & 3)); }
 
+static unsigned trail_wide_grid(int64_t rows, int N) {
+  const int64_t tiles = (rows + TW_R - 1) / TW_R * ((N + TW_C - 1) / TW_C);
+  return (unsigned)((tiles + TW_XCD - 1) / TW_XCD * TW_XCD);
+}
+
 // The wide trailing update C[r][c0 + c] += sum_{k < K} E[r][k] M[b0 + k][c0 + c] (K a multiple
 // of 32; E and M as three bf16 planes each, E_i rows x K with leading dimension lde, Mt_i n x n
-// transposed; the six part products with i + j <= 2, smallest first).  128 x 128 tile per
-// workgroup, wave w owns rows 64 (w / 2).., columns 64 (w % 2).. as 2 x 2 blocks of 32 x 32.
-// The operand tiles go to LDS by DMA two 32-wide k stages ahead (three stages, 144 KB).
-__global__ __launch_bounds__(256, 1) void trail_wide_kernel(int64_t rows, int N, int n, int K, int b0, int c0,
-                                                            const uint16_t* __restrict__ E0,
-                                                            const uint16_t* __restrict__ E1,
-                                                            const uint16_t* __restrict__ E2, int lde,
-                                                            const uint16_t* __restrict__ Mt0,
-                                                            const uint16_t* __restrict__ Mt1,
-                                                            const uint16_t* __restrict__ Mt2, float* __restrict__ C,
-                                                            const int32_t* __restrict__ dev_info) {
+// transposed; the six part products with i + j <= 2, smallest first).  256 x 128 tile per
+// workgroup of eight waves (two per SIMD); wave w owns rows 64 (w / 2).., columns 64 (w % 2).. as
+// 2 x 2 blocks of 32 x 32.  The operand tiles of a 32-wide k stage go to LDS by DMA into one of two
+// stages while the other is multiplied.  Tiles are numbered with the column tiles of one row tile
+// consecutive, and each XCD takes a contiguous range of them, so the workgroups it runs at once
+// share E rows and M columns.
+__global__ __launch_bounds__(512) void trail_wide_kernel(int64_t rows, int N, int n, int K, int b0, int c0,
+                                                         const uint16_t* __restrict__ E0,
+                                                         const uint16_t* __restrict__ E1,
+                                                         const uint16_t* __restrict__ E2, int lde,
+                                                         const uint16_t* __restrict__ Mt0,
+                                                         const uint16_t* __restrict__ Mt1,
+                                                         const uint16_t* __restrict__ Mt2, float* __restrict__ C,
+                                                         const int32_t* __restrict__ dev_info) {
   extern __shared__ __attribute__((aligned(1024))) char tw_lds[];
   if (*dev_info != 0) return;
+  int64_t R0;
+  int C0;
+  {
+    const int gx = (N + TW_C - 1) / TW_C;
+    const int tiles = (int)((rows + TW_R - 1) / TW_R) * gx, bid = blockIdx.x;
+    const int q = tiles / TW_XCD, rem = tiles % TW_XCD, x = bid % TW_XCD, slot = bid / TW_XCD;
+    if (slot >= q + (x < rem ? 1 : 0)) return;  // the grid is rounded up to a multiple of 8
+    const int t = x * q + min(x, rem) + slot;
+    R0 = (int64_t)(t / gx) * TW_R;
+    C0 = (t % gx) * TW_C;
+  }
   const tw_lds_char* lds = (const tw_lds_char*)tw_lds;
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t R0 = (int64_t)blockIdx.y * TW_T;
-  const int C0 = blockIdx.x * TW_T;
-  const int rmax = (int)std::min<int64_t>(rows - 1 - R0, TW_T - 1);
-  const int cmax = std::min(N - 1 - C0, TW_T - 1);
-  // DMA q (0..47 per stage) fills LDS bytes [1024 q, +1024): q / 8 is the plane (E0, E1, E2,
-  // Mt0, Mt1, Mt2), q % 8 the 1 KB part of it.  Wave w issues q = w + 4 i.
+  const int rmax = (int)std::min<int64_t>(rows - 1 - R0, TW_R - 1);
+  const int cmax = std::min(N - 1 - C0, TW_C - 1);
+  // DMA q (0..71 per stage) fills LDS bytes [1024 q, +1024): q < 48 the E plane q / 16 (its 1 KB
+  // part q % 16), else the M plane (q - 48) / 8 (part (q - 48) % 8).  Wave w issues q = w + 8 i.
   uint32_t voff[TW_DMA];
 #pragma unroll
   for (int i = 0; i < TW_DMA; ++i) {
-    const int q = wave + 4 * i;
-    const int u = (q & 7) * 64 + lane, r = u >> 2;
+    const int q = wave + 8 * i;
+    const int u = (q < 48 ? (q & 15) : ((q - 48) & 7)) * 64 + lane, r = u >> 2;
     const int oct = (u & 3) ^ ((r >> 2) & 3);
-    voff[i] = q < 24 ? (uint32_t)((std::min(r, rmax) * (int64_t)lde + 8 * oct) * 2)
+    voff[i] = q < 48 ? (uint32_t)((std::min(r, rmax) * (int64_t)lde + 8 * oct) * 2)
                      : (uint32_t)(((int64_t)std::min(r, cmax) * n + 8 * oct) * 2);
   }
   auto issue = [&](int k0, int slot) {
@@ -418,9 +438,9 @@ __global__ __launch_bounds__(256, 1) void trail_wide_kernel(int64_t rows, int N,
     const int64_t mo = (int64_t)(c0 + C0) * n + b0 + k0;
 #pragma unroll
     for (int i = 0; i < TW_DMA; ++i) {
-      const int q = wave + 4 * i;
-      const uint16_t* src = q < 8 ? E0 + eo : q < 16 ? E1 + eo : q < 24 ? E2 + eo
-                          : q < 32 ? Mt0 + mo : q < 40 ? Mt1 + mo : Mt2 + mo;
+      const int q = wave + 8 * i;
+      const uint16_t* src = q < 16 ? E0 + eo : q < 32 ? E1 + eo : q < 48 ? E2 + eo
+                          : q < 56 ? Mt0 + mo : q < 64 ? Mt1 + mo : Mt2 + mo;
       tw_dma16(src, voff[i], base + q * 1024);
     }
   };
@@ -430,27 +450,22 @@ __global__ __launch_bounds__(256, 1) void trail_wide_kernel(int64_t rows, int N,
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
-  auto frag = [&](const tw_lds_char* st, int plane, int r, int q) {
-    const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(st + plane * TW_PLANE + tw_unit(r, q) * 16);
+  auto fragE = [&](const tw_lds_char* st, int plane, int r, int q) {
+    const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(st + plane * TW_EPLANE + tw_unit(r, q) * 16);
     return as_bf16x8(v);
   };
-  const int nst = K / TW_KC;  // >= 2
+  auto fragM = [&](const tw_lds_char* st, int plane, int r, int q) {
+    const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(st + 3 * TW_EPLANE + plane * TW_MPLANE +
+                                                                       tw_unit(r, q) * 16);
+    return as_bf16x8(v);
+  };
+  const int nst = K / TW_KC;
   issue(0, 0);
-  issue(TW_KC, 1);
   for (int stg = 0; stg < nst; ++stg) {
-    const int slot = stg % 3;
-    // the slot of stage stg + 2 held stage stg - 1, which every wave finished before the
-    // barrier that ended the previous iteration
-    if (stg + 2 < nst) {
-      issue(TW_KC * (stg + 2), (stg + 2) % 3);
-      tw_vm_wait<2 * TW_DMA>();
-    } else if (stg + 1 < nst) {
-      tw_vm_wait<TW_DMA>();
-    } else {
-      tw_vm_wait<0>();
-    }
-    tw_barrier();
-    const tw_lds_char* st = lds + slot * TW_STAGE;
+    tw_vm_wait<0>();
+    tw_barrier();  // stage stg is in LDS for every wave, and every wave is done with stage stg - 1
+    if (stg + 1 < nst) issue(TW_KC * (stg + 1), (stg + 1) & 1);  // into the other stage
+    const tw_lds_char* st = lds + (stg & 1) * TW_STAGE;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int q = 2 * ks + (lane >> 5);
@@ -459,8 +474,8 @@ __global__ __launch_bounds__(256, 1) void trail_wide_kernel(int64_t rows, int N,
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
-          a[p][t] = frag(st, p, wr0 + 32 * t + (lane & 31), q);
-          b[p][t] = frag(st, 3 + p, wc0 + 32 * t + (lane & 31), q);
+          a[p][t] = fragE(st, p, wr0 + 32 * t + (lane & 31), q);
+          b[p][t] = fragM(st, p, wc0 + 32 * t + (lane & 31), q);
         }
       }
 #pragma unroll
@@ -477,7 +492,6 @@ __global__ __launch_bounds__(256, 1) void trail_wide_kernel(int64_t rows, int N,
           acc[x][y] = v;
         }
     }
-    tw_barrier();  // every wave is done with this slot before the next stage's DMA into it
   }
 #pragma unroll
   for (int x = 0; x < 2; ++x)
@@ -598,10 +612,9 @@ int wr_gptq_sweep_impl(wr_ctx* ctx, const void* W, int w_dtype, int64_t rows, in
     if (rc) return rc;
     const int s0 = b0 - b0 % kSuper, s1 = std::min(s0 + kSuper, n);
     if (b0 + ncols == s1 && s1 < n) {  // the group is complete and full (s1 - s0 == kSuper)
-      if (!lds_limit(reinterpret_cast<const void*>(trail_wide_kernel), 3 * TW_STAGE)) return WR_EHIP;
-      const dim3 grid((unsigned)((n - s1 + TW_T - 1) / TW_T), (unsigned)((rows + TW_T - 1) / TW_T));
-      hipLaunchKernelGGL(trail_wide_kernel, grid, dim3(256), 3 * TW_STAGE, st, rows, n - s1, n, kSuper, s0, s1, E[0],
-                         E[1], E[2], kSuper, Mt[0], Mt[1], Mt[2], Cb, dev_info);
+      if (!lds_limit(reinterpret_cast<const void*>(trail_wide_kernel), 2 * TW_STAGE)) return WR_EHIP;
+      hipLaunchKernelGGL(trail_wide_kernel, dim3(trail_wide_grid(rows, n - s1)), dim3(512), 2 * TW_STAGE, st, rows,
+                         n - s1, n, kSuper, s0, s1, E[0], E[1], E[2], kSuper, Mt[0], Mt[1], Mt[2], Cb, dev_info);
       WR_CHECK_LAUNCH();
     }
   }
