@@ -98,6 +98,41 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Block-start substitution of the sweep panel, x = M_bb^-T c_b (the corrections a block's columns will
+// receive from the block's own earlier columns, for the block's scale), as a product with the
+// precomputed Y_b = (I + U_b^T)^-1 (U_b the strictly upper part of M's diagonal G x G block b; Y_b is
+// unit lower triangular) instead of a serial chain of G dependent steps.  Y_b's strictly lower part
+// is stored by columns, column k holding Y[k + 1 .. G - 1][k] from offset sub_col(k), and each block
+// at a stride of sub_stride(G) floats (groups of up to 64 columns).
+__host__ __device__ constexpr int sub_col(int k, int G) { return k * (2 * G - k - 1) / 2; }
+__host__ __device__ constexpr int sub_stride(int G) { return G == 32 ? 512 : 2048; }
+
+template <int G>
+__global__ __launch_bounds__(G) void sub_inverse_kernel(const float* __restrict__ M, int n, float* __restrict__ Y,
+                                                        const int32_t* __restrict__ dev_info) {
+  __shared__ float sU[G][G + 1];   // sU[i][j] = M[b0 + j][b0 + i] for j < i, else 0 (M is fp32)
+  __shared__ double sY[G][G + 1];  // column k of Y_b in sY[.][k]
+  if (*dev_info != 0) return;
+  const int b0 = blockIdx.x * G, k = threadIdx.x;
+  for (int e = k; e < G * G; e += G) {
+    const int r = e / G, c = e % G;
+    sU[c][r] = r < c ? M[(int64_t)(b0 + r) * n + b0 + c] : 0.0f;
+  }
+  __syncthreads();
+  // column k: y_i = 0 (i < k), 1 (i = k), -sum_{j < i} U^T[i][j] y_j (i > k), in fp64
+  for (int i = 0; i < G; ++i) {
+    double acc = 0.0;
+    for (int j = 0; j < i; ++j) acc = fma((double)sU[i][j], sY[j][k], acc);
+    sY[i][k] = i < k ? 0.0 : (i == k ? 1.0 : -acc);
+  }
+  __syncthreads();
+  float* dst = Y + (size_t)blockIdx.x * sub_stride(G);
+  for (int e = k; e < G * G; e += G) {
+    const int i = e / G, kk = e % G;
+    if (kk < i) dst[sub_col(kk, G) + i - kk - 1] = (float)sY[i][kk];
+  }
+}
+
 // One lazy batch of BATCH columns starting at b0 (ncols <= BATCH valid columns).  The
 // errors of the kprev columns before b0 in the batch's group (E0..E2: three bf16 parts,
 // leading dimension lde, this batch's slot at column kprev) are first applied to this
@@ -115,6 +150,7 @@ __global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict
                                                           const uint16_t* __restrict__ Mt1,
                                                           const uint16_t* __restrict__ Mt2,
                                                           uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
+                                                          const float* __restrict__ Ysub, int use_inv,
                                                           const int32_t* __restrict__ dev_info) {
   constexpr int S = BATCH / P;       // columns per lane
   constexpr int NBLK = BATCH / G;    // blocks per batch
@@ -127,6 +163,19 @@ __global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict
   const int p = tid % P;
   const int64_t row = (int64_t)blockIdx.x * R + tid / P;
   const bool active = row < rows;
+  // groups of up to 64 columns, with use_inv (many rows: the serial chain would dominate): the batch's
+  // Y blocks, fetched now and staged in LDS before each block (the first in La's space once La is
+  // read, later ones in the rows of Ms the previous block used)
+  constexpr bool kInv = G <= 64;
+  constexpr int YPT = kInv ? sub_stride(G) / 256 : 1;  // floats per thread and block
+  float yreg[NBLK][YPT];
+  if (kInv && use_inv) {
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+      for (int u = 0; u < YPT; ++u)
+        yreg[blk][u] = blk * G < ncols ? Ysub[(size_t)(b0 / G + blk) * sub_stride(G) + tid * YPT + u] : 0.0f;
+  }
 
   if (kprev > 0) {
     // wave w: columns 32 w .. 32 w + 31 as two 16 x 16 blocks on v_mfma_f32_16x16x32_bf16
@@ -224,6 +273,12 @@ __global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict
 #pragma unroll
     for (int i = 0; i < S; ++i) c[i] += La[(tid / P) * BATCH + p + P * i];
   }
+  if (kInv && use_inv) {
+    __syncthreads();  // La has been read
+#pragma unroll
+    for (int u = 0; u < YPT; ++u) La[tid * YPT + u] = yreg[0][u];
+    __syncthreads();
+  }
 
   static_for<0, NBLK>([&](auto BLK) {
     constexpr int blk = BLK;
@@ -233,6 +288,19 @@ __global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict
     float x[SB];
 #pragma unroll
     for (int q = 0; q < SB; ++q) x[q] = c[blk * SB + q];
+    if (kInv && use_inv) {
+      // x_i = c_i + sum_{k < i} Y[i][k] c_k, k in order; lane p's columns i = p + P q
+      const float* Yl = blk == 0 ? La : Ms + (blk - 1) * G * BATCH;
+      static_for<0, G>([&](auto KK) {
+        constexpr int k = KK;
+        const float ck = group_bcast<P, k % P>(c[blk * SB + k / P]);
+#pragma unroll
+        for (int q = k / P; q < SB; ++q) {
+          const int i = p + P * q;
+          if (i > k) x[q] = fmaf(Yl[sub_col(k, G) + i - k - 1], ck, x[q]);
+        }
+      });
+    } else {
     // M's rows are read one step ahead so that their LDS latency stays off the serial chain
     float mx[SB];
 #pragma unroll
@@ -254,6 +322,7 @@ __global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict
         for (int q = 0; q < SB; ++q) mx[q] = mn[q];
       }
     });
+    }
     float m = 0.0f;
 #pragma unroll
     for (int q = 0; q < SB; ++q) m = fmaxf(m, fabsf(w[blk * SB + q] + x[q]));
@@ -289,6 +358,14 @@ __global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict
         for (int i = 0; i < S; ++i) mc[i] = mn[i];
       }
     });
+    if constexpr (kInv && blk + 1 < NBLK) {
+      if (use_inv && (blk + 1) * G < ncols) {  // uniform
+        __syncthreads();  // every lane is done with Ms's rows of this block
+#pragma unroll
+        for (int u = 0; u < YPT; ++u) Ms[blk * G * BATCH + tid * YPT + u] = yreg[blk + 1][u];
+        __syncthreads();
+      }
+    }
   });
 
   if (!active) return;
@@ -512,11 +589,12 @@ using namespace wr;
 
 static constexpr int kBatch = 128;
 static constexpr int kSuper = 4 * kBatch;  // columns whose errors one wide trailing update applies
+static constexpr int64_t kInvRows = 4096;  // rows from which the panels use the precomputed inverses
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct GptqLayout {
-  size_t M, C, E[3], Mt[3], total;
+  size_t M, C, E[3], Mt[3], Y, total;
 };
 
 static GptqLayout gptq_layout(int64_t rows, int64_t n) {
@@ -531,6 +609,7 @@ static GptqLayout gptq_layout(int64_t rows, int64_t n) {
   l.C = take((size_t)rows * n * 4);                                    // corrections C
   for (int i = 0; i < 3; ++i) l.E[i] = take((size_t)rows * kSuper * 2);  // errors of 4 batches, bf16 parts
   for (int i = 0; i < 3; ++i) l.Mt[i] = take((size_t)n * n * 2);          // M transposed, bf16 parts
+  l.Y = take((size_t)n * 32 * 4);  // the blocks' Y_b (n / 64 x 2048 or n / 32 x 512 floats)
   l.total = off;
   return l;
 }
@@ -540,22 +619,23 @@ size_t wr_gptq_ws_bytes(int64_t rows, int64_t n) { return gptq_layout(rows, n).t
 template <int P, int G>
 static void launch_panel(hipStream_t st, const void* W, int w_dtype, int64_t rows, int n, int64_t ldw, const float* Mm,
                          const uint8_t* bits, int b0, int ncols, float* Cb, uint16_t* const* E, uint16_t* const* Mt,
-                         uint8_t* codes, uint16_t* scales, const int32_t* dev_info) {
+                         uint8_t* codes, uint16_t* scales, const float* Ysub, const int32_t* dev_info) {
   const unsigned grid = (unsigned)((rows + (256 / P) - 1) / (256 / P));
   const int eoff = b0 % kSuper;  // this batch's slot among the errors of its group of four
   hipLaunchKernelGGL((sweep_panel_kernel<P, kBatch, G>), dim3(grid), dim3(256), 0, st, W, w_dtype, rows, n, ldw, Mm,
                      bits, b0, ncols, Cb, kSuper, eoff, E[0] + eoff, E[1] + eoff, E[2] + eoff, Mt[0], Mt[1], Mt[2],
-                     codes, scales, dev_info);
+                     codes, scales, Ysub, Ysub != nullptr ? 1 : 0, dev_info);
 }
 
 template <int P>
 static int launch_panel_g(hipStream_t st, int G, const void* W, int w_dtype, int64_t rows, int n, int64_t ldw,
                           const float* Mm, const uint8_t* bits, int b0, int ncols, float* Cb, uint16_t* const* E,
-                          uint16_t* const* Mt, uint8_t* codes, uint16_t* scales, const int32_t* dev_info) {
+                          uint16_t* const* Mt, uint8_t* codes, uint16_t* scales, const float* Ysub,
+                          const int32_t* dev_info) {
   switch (G) {
-    case 32: launch_panel<P, 32>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, Mt, codes, scales, dev_info); break;
-    case 64: launch_panel<P, 64>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, Mt, codes, scales, dev_info); break;
-    case 128: launch_panel<P, 128>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, Mt, codes, scales, dev_info); break;
+    case 32: launch_panel<P, 32>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, Mt, codes, scales, Ysub, dev_info); break;
+    case 64: launch_panel<P, 64>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, Mt, codes, scales, Ysub, dev_info); break;
+    case 128: launch_panel<P, 128>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, Mt, codes, scales, Ysub, dev_info); break;
     default: return WR_EUNSUPPORTED;
   }
   WR_CHECK_LAUNCH();
@@ -580,6 +660,7 @@ int wr_gptq_sweep_impl(wr_ctx* ctx, const void* W, int w_dtype, int64_t rows, in
     E[i] = reinterpret_cast<uint16_t*>(ws + lay.E[i]);
     Mt[i] = reinterpret_cast<uint16_t*>(ws + lay.Mt[i]);
   }
+  float* Ysub = reinterpret_cast<float*>(ws + lay.Y);
 
   hipLaunchKernelGGL(sweep_set_int_kernel, dim3(1), dim3(1), 0, st, dev_info, 0);
   WR_CHECK_LAUNCH();
@@ -601,13 +682,25 @@ int wr_gptq_sweep_impl(wr_ctx* ctx, const void* W, int w_dtype, int64_t rows, in
     hipLaunchKernelGGL(split_mt_kernel, dim3(nt, nt), dim3(256), 0, st, Mm, n, Mt[0], Mt[1], Mt[2], dev_info);
     WR_CHECK_LAUNCH();
   }
+  // The block-start substitution as a product with precomputed inverses pays where many rows keep
+  // the chip busy (4096 rows and more: 148 -> 131 us per panel at 25600 rows); with few rows the
+  // panel is latency-bound and the serial chain is shorter (23 us against 28 us at 2560 rows).
+  if (rows < kInvRows || group > 64) {
+    Ysub = nullptr;
+  } else {
+    if (group == 64)
+      hipLaunchKernelGGL(sub_inverse_kernel<64>, dim3((unsigned)(n / 64)), dim3(64), 0, st, Mm, n, Ysub, dev_info);
+    else
+      hipLaunchKernelGGL(sub_inverse_kernel<32>, dim3((unsigned)(n / 32)), dim3(32), 0, st, Mm, n, Ysub, dev_info);
+    WR_CHECK_LAUNCH();
+  }
   // Batches go in groups of four (kSuper columns).  A batch's panel applies the errors of
   // the earlier batches of its group to its own columns; after a group's last batch its
   // errors reach every column after the group at once (K = 512), so the corrections C of
   // the far columns are read and written once per group, not per batch.
   for (int b0 = 0; b0 < n; b0 += kBatch) {
     const int ncols = std::min(kBatch, n - b0);
-    rc = launch_panel_g<16>(st, group, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, Mt, codes, scales,
+    rc = launch_panel_g<16>(st, group, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, Mt, codes, scales, Ysub,
                             dev_info);
     if (rc) return rc;
     const int s0 = b0 - b0 % kSuper, s1 = std::min(s0 + kSuper, n);

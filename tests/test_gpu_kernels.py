@@ -250,6 +250,29 @@ def test_gptq_several_column_groups(wr, ctx):
         assert scale_ulps(scales[ok], ref["scales"][ok]).max() <= 1
 
 
+def test_gptq_many_rows_take_the_inverse_substitution(wr, ctx):
+    """4133 rows (from 4096 rows on, the panels form the block-start substitution as a product with the
+    precomputed inverse blocks; a ragged last panel): sampled rows against the oracle, groups 64 and 32."""
+    rng = np.random.default_rng(29)
+    rows, n = 4133, 1280
+    A = rng.standard_normal((2 * n, n)) * np.sqrt(10.0 ** (-2 * np.arange(n) / (n - 1)))
+    A[:, :8] *= 10
+    H = A.T @ A / (2 * n)
+    H, _ = oracle.damp(H, 0.01)
+    H32 = H.astype(np.float32)
+    W = torch.from_numpy(0.02 * rng.standard_normal((rows, n))).to(torch.bfloat16)
+    bits_rows = np.where(np.arange(rows) % 4 == 0, 3, 2)
+    sample = np.r_[np.arange(0, rows, 97), rows - 5:rows]
+    for g in (64, 32):
+        codes, scales, info = _sweep(wr, ctx, W, H32, bits_rows, g)
+        assert info == 0
+        ref = oracle.gptq_sweep(W[sample].double().numpy(), H32.astype(np.float64), bits_rows[sample], g)
+        cp = code_parity(codes[sample], ref["codes"], ref["t"], oracle.levels_count(bits_rows[sample]))
+        assert len(cp["rows"]) <= 2 and cp["worst_first"] <= TIE, (g, cp)
+        ok = cp["identical_rows"]
+        assert scale_ulps(scales[sample][ok], ref["scales"][ok]).max() <= 1
+
+
 def test_gptq_diagonal_H_is_plain_rounding(wr, ctx, toy):
     W = toy["W"]
     d = np.linspace(0.5, 2.0, 512)
