@@ -148,6 +148,27 @@ def test_hessian_finalize_ragged_tiles(wr, ctx, n, n_store, extra):
     assert np.all(np.isnan(Hbig[:, n_store:].cpu().numpy()))
 
 
+@pytest.mark.parametrize("n,n_store,m", [(200, 256, 64), (1000, 1024, 1024), (96, 128, 32), (2000, 2048, 2048)])
+def test_hessian_finalize_rotated(wr, ctx, n, n_store, m):
+    """H = R pad(S/N) R^T + delta I: the two-pass form (blocks of 64..1024, padding, S's upper triangle
+    garbage the kernels must not read) and the row-pass/transpose form (blocks of 32 and 2048)."""
+    rng = np.random.default_rng(n + m)
+    A = rng.standard_normal((n, n))
+    S0 = A @ A.T
+    Sg = np.tril(S0) + np.triu(rng.standard_normal((n, n)) * 1e6, 1)
+    s = rng.choice([-1, 1], size=n_store).astype(np.int8)
+    ctx.ensure_workspace(wr.wr_workspace_bytes(wr.WR_OP_FINALIZE, 0, n_store))
+    H = torch.empty(n_store, n_store, dtype=torch.float32, device="cuda")
+    delta = torch.empty(1, dtype=torch.float32, device="cuda")
+    wr.wr_hessian_finalize(ctx, torch.from_numpy(Sg).cuda(), 7, 0.01, H, delta, m, dev(torch.from_numpy(s)))
+    ref, d = oracle.damp(oracle.rotate_sym(oracle.pad_square(S0 / 7, n_store), m, s.astype(np.float64)), 0.01)
+    got = H.cpu().double().numpy()
+    assert abs(delta.item() - d) <= 1e-6 * d
+    assert _rel(got, ref) < 1e-6
+    # rows then columns: H[i][j] and H[j][i] sum in different orders, symmetric to fp32 rounding
+    assert np.abs(got - got.T).max() <= 2e-7 * np.abs(got).max()
+
+
 # ------------------------------------------------------------------------- rotation
 @pytest.mark.parametrize("m,n,rows", [(4, 8, 3), (64, 256, 17), (1024, 2048, 5), (512, 1536, 4)])
 def test_rotation_rows_and_inverse(wr, ctx, m, n, rows):
