@@ -90,18 +90,20 @@ def traffic_from_profile(name, key="bytes_per_launch"):
 
     The summary (profiles/<name>) holds `bytes_per_launch:` (FETCH_SIZE and WRITE_SIZE per dispatch, each
     scaled by what the counter reads for a plain copy of known size; for the body, summed over one step's
-    launches) and `source_sha256:` of the kernel source it was taken on; once the source has changed the
-    figure no longer describes the kernel and None is returned.
+    launches) and `source_sha256:` of the kernel source it was taken on (k_hessian.hip followed by
+    common.hpp, which holds its tile order); once the source has changed the figure no longer describes
+    the kernel and None is returned.
     """
     path = os.path.join(ROOT, "profiles", name)
-    src = os.path.join(ROOT, "post_bit_weight_amd", "csrc", "k_hessian.hip")
+    csrc = os.path.join(ROOT, "post_bit_weight_amd", "csrc")
     try:
         rec = {}
         for line in open(path):
             if ":" in line and not line.startswith((" ", "#")):
                 k, v = line.split(":", 1)
                 rec[k.strip()] = v.strip()
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        digest = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read()
+                                         for f in ("k_hessian.hip", "common.hpp"))).hexdigest()
         if rec.get("source_sha256") != digest:
             return None
         return float(rec[key])

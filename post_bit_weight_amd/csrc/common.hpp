@@ -156,26 +156,28 @@ __device__ __forceinline__ void tri_tile(int t, int& I, int& J) {
 }
 
 // Tile t (0 <= t < nt (nt + 1) / 2) of the lower triangle of nt x nt tiles, in blocked order: bands of
-// four tile rows, each band in chunks of eight tile columns (32 tiles that read the operand rows of
-// only 12 tile rows and columns), row-major inside a chunk; the columns a band has past its last full
-// chunk, and a last band of fewer than four rows, row-major.  Tile 0 is (0, 0).
+// BH tile rows, each band in chunks of CW tile columns (BH * CW tiles that read the operand rows of
+// only BH + CW tile rows and columns), row-major inside a chunk; the columns a band has past its last
+// full chunk, and a last band of fewer than BH rows, row-major.  Tile 0 is (0, 0).
+template <int BH, int CW>
 __device__ __forceinline__ void blocked_tile(int t, int nt, int& I, int& J) {
-  int b = (int)((sqrtf(32.0f * (float)t + 4.0f) - 2.0f) * 0.0625f);  // 8 b^2 + 2 b tiles before band b
-  while (b > 0 && 8 * b * b + 2 * b > t) --b;
-  while (8 * (b + 1) * (b + 1) + 2 * (b + 1) <= t) ++b;
-  int r = t - (8 * b * b + 2 * b);
+  auto before = [](int b) { return BH * b * (BH * b + 1) / 2; };  // tiles in bands 0 .. b-1
+  int b = (int)((sqrtf(2.0f * (float)t + 0.25f) - 0.5f) * (1.0f / BH));
+  while (b > 0 && before(b) > t) --b;
+  while (before(b + 1) <= t) ++b;
+  int r = t - before(b);
   int c0 = 0;
-  if (4 * b + 4 <= nt) {
-    const int nfull = 4 * b >= 7 ? (4 * b - 7) / 8 + 1 : 0;  // chunks entirely on or below the diagonal
-    if (r < 32 * nfull) {
-      I = 4 * b + ((r & 31) >> 3);
-      J = 8 * (r >> 5) + (r & 7);
+  if (BH * b + BH <= nt) {
+    const int nfull = BH * b >= CW - 1 ? (BH * b - (CW - 1)) / CW + 1 : 0;  // chunks on or below the diagonal
+    if (r < BH * CW * nfull) {
+      I = BH * b + (r % (BH * CW)) / CW;
+      J = CW * (r / (BH * CW)) + r % CW;
       return;
     }
-    r -= 32 * nfull;
-    c0 = 8 * nfull;
+    r -= BH * CW * nfull;
+    c0 = CW * nfull;
   }
-  for (int i = 4 * b;; ++i) {
+  for (int i = BH * b;; ++i) {
     const int cnt = i + 1 - c0;
     if (r < cnt) {
       I = i;

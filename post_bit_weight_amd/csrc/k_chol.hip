@@ -377,7 +377,7 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ A
     const int q = tiles / CU_XCD, rem = tiles % CU_XCD, x = bid % CU_XCD, slot = bid / CU_XCD;
     if (slot >= q + (x < rem ? 1 : 0)) return;  // the grid is rounded up to a multiple of 8
     t = x * q + min(x, rem) + slot;
-    blocked_tile(t, nt, ti, tj);
+    blocked_tile<4, 8>(t, nt, ti, tj);
   }
   const int i0 = base + CB * ti, j0 = base + CB * tj;
   const bool diag = ti == tj;
@@ -484,7 +484,7 @@ __global__ __launch_bounds__(512) void chol_update128_kernel(double* __restrict_
     const int nt2 = (n - base + CB2 - 1) / CB2, tiles = nt2 * (nt2 + 1) / 2, bid = blockIdx.x;
     const int q = tiles / CU_XCD, rem = tiles % CU_XCD, x = bid % CU_XCD, slot = bid / CU_XCD;
     if (slot >= q + (x < rem ? 1 : 0)) return;  // the grid is rounded up to a multiple of 8
-    blocked_tile(x * q + min(x, rem) + slot, nt2, ti, tj);
+    blocked_tile<4, 8>(x * q + min(x, rem) + slot, nt2, ti, tj);
   }
   const int i0 = base + CB2 * ti, j0 = base + CB2 * tj;
   const bool diag = ti == tj;

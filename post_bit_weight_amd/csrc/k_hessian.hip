@@ -108,7 +108,7 @@ __global__ __launch_bounds__(SY_THREADS, 1) void syrk_bf16_kernel(const uint16_t
     }
   }
   int I, J;
-  blocked_tile(t, (n + SY_T - 1) / SY_T, I, J);
+  blocked_tile<6, 6>(t, (n + SY_T - 1) / SY_T, I, J);
   const int tile = I * (I + 1) / 2 + J;
   const int64_t r0 = (int64_t)split * rows_per_split;
   const int64_t r1 = r0 + rows_per_split < rows ? r0 + rows_per_split : rows;
