@@ -12,7 +12,10 @@ rows) are synthetic and resident in HBM before the timed region: the body's
 calibration rows (309 GB) exceed the 288 GB of HBM, so `--calib-sets` distinct
 per-layer calibration sets are kept resident and layer l reads set l mod
 calib_sets (the work per layer does not depend on the values).  The metric is
-weights quantized per second.
+weights quantized per second.  The timed steps run each input dimension's
+solves on a stream of its own, the widest dimension's layers alternating
+between two streams and buffer sets (four streams), and every H accumulation
+waits for the previous one, so that two never run at once.
 
 Also reported: the roofline of the dominant kernel (the bf16 SYRK that
 accumulates H: N n (n + 1) useful flops per call, timed live with HIP events on
@@ -58,12 +61,21 @@ def parse():
     p.add_argument("--calib-sets", type=int, default=4,
                    help="body: distinct per-layer calibration sets kept resident (layer l reads set l mod K)")
     p.add_argument("--no-breakdown", action="store_true", help="body: skip the untimed per-call breakdown pass")
-    p.add_argument("--streams", type=int, choices=(1, 3, 4), default=3,
-                   help="body: 3 runs each input dim's solves on a stream of its own (they overlap); 4 also "
-                        "alternates the widest dim's layers between two streams and buffer sets; 1 in order")
+    p.add_argument("--streams", type=int, choices=(1, 3, 4, 6), default=4,
+                   help="body: 3 runs each input dim's solves on a stream of its own (they overlap); 4 (the "
+                        "default) also alternates the widest dim's layers between two streams and buffer sets, "
+                        "6 every dim's; 1 runs every call in order")
     p.add_argument("--lag", type=int, default=0,
-                   help="body, 3 streams: a stream starts layer l once the others have finished layer l - lag "
+                   help="body, several streams: a stream starts layer l once the others have finished layer l - lag "
                         "(0: no coupling)")
+    p.add_argument("--hw-queues", type=int, choices=range(1, 33), default=8, metavar="Q",
+                   help="hardware queues HIP gives the process (GPU_MAX_HW_QUEUES, read when its runtime starts; "
+                        "default 8): the body step's four streams and the default stream need five, and two "
+                        "streams that share a queue run one after the other")
+    p.add_argument("--h-chain", choices=("none", "dim", "all"), default="all",
+                   help="body, several streams: an H accumulation waits for the previous one of its input dim "
+                        "(dim) or of any dim (all, the default: accumulations never run at once), or for "
+                        "nothing but its own stream's work (none)")
     p.add_argument("--no-measures", action="store_true", help="body: skip the model cards' measures of layer 0")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=None, help="weight rows in the oracle sample")
@@ -531,13 +543,15 @@ class BodyInputs:
                                  delta=torch.empty(1, dtype=torch.float32, device=dev)))
 
 
-def body_step(wr, ctxs, I, mark=None, lag=0):
+def body_step(wr, ctxs, I, mark=None, lag=0, h_chain=None):
     """One pass of the whole solve over the body.  ctxs: one library context for every call (they run
     in order on its stream), or a dict (input dim, buffer set) -> context: the solves of a dim's layers
     that use set k of its buffers run on that context's stream and overlap with the others (a set's
     buffers are only touched on its own stream, so the streams share nothing; with two sets a dim's
     even and odd layers alternate).  With lag > 0 a stream starts layer l only after every other
-    stream has finished layer l - lag.  mark(kind, n, stream) is called between library calls when
+    stream has finished layer l - lag.  h_chain "dim" (or "all") makes every H
+    accumulation wait for the previous one of its input dim (of any dim), so that accumulations on
+    different streams never run at once.  mark(kind, n, stream) is called between library calls when
     given (it records timing events on the stream of the call)."""
     import torch
     single = not isinstance(ctxs, dict)
@@ -545,6 +559,8 @@ def body_step(wr, ctxs, I, mark=None, lag=0):
     g, lam, hb, N = cfg["group"], cfg["lam"], cfg["had_block"], cfg["calib_rows"]
     m = mark or (lambda kind, n, stream: None)
     done = []  # per layer: {n: event at the end of layer on its stream}
+    chain = h_chain if not single and h_chain != "none" else None
+    h_last = {}  # chain key -> event at the end of the last H accumulation
     for layer in range(I.layers):
         p = layer % I.P
         if not single and lag > 0:
@@ -560,10 +576,17 @@ def body_step(wr, ctxs, I, mark=None, lag=0):
             G = I.groups[layer][n]
             rows = G["W"].shape[0]
             S, H, Wst = buf["S"], buf["H"], buf["Wst"][:rows]
+            key = n if chain == "dim" else 0
+            if chain and key in h_last:
+                ctx.stream.wait_event(h_last[key])
             wr.wr_hessian_accumulate(ctx, I.none[n], S, zero=True)          # S = 0
             m("hessian", n, ctx.stream)
             wr.wr_hessian_accumulate(ctx, I.X[n][p], S)
             m("finalize", n, ctx.stream)
+            if chain:
+                ev = torch.cuda.Event()
+                ev.record(ctx.stream)
+                h_last[key] = ev
             wr.wr_hessian_finalize(ctx, S, N, cfg["damp"], H, buf["delta"], hb, I.signs[n])
             m("rotate", n, ctx.stream)
             with torch.cuda.stream(ctx.stream):
@@ -726,6 +749,9 @@ def main_body(args):
     if args.streams > 1:
         if args.streams == 4:
             I.add_set(torch, max(I.dims))
+        if args.streams == 6:
+            for n in I.dims:
+                I.add_set(torch, n)
         ctxs = {(n, k): wr.Context(0, stream=torch.cuda.Stream(dev)) for n in I.dims for k in range(len(I.sets[n]))}
         for c in ctxs.values():
             c.ensure_workspace(I.ws_bytes)
@@ -741,7 +767,7 @@ def main_body(args):
 
     progress(f"warmup ({args.warmup} steps)")
     for _ in range(args.warmup):
-        body_step(wr, ctxs, I, lag=args.lag)
+        body_step(wr, ctxs, I, lag=args.lag, h_chain=args.h_chain)
     torch.cuda.synchronize()
     if args.warmup:
         body_check(torch, I)
@@ -760,7 +786,7 @@ def main_body(args):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        body_step(wr, ctxs, I, mark_syrk, lag=args.lag)
+        body_step(wr, ctxs, I, mark_syrk, lag=args.lag, h_chain=args.h_chain)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     progress("checking dev_info and the pack/unpack round trips")
@@ -833,7 +859,8 @@ def main_body(args):
                    "calib_sets_resident": args.calib_sets, "had_block": cfg["had_block"], "group": cfg["group"],
                    "rank": cfg["rank"], "lambda": cfg["lam"], "payload_bytes": I.payload,
                    "bits_per_weight": 8.0 * I.payload / I.weights, "parallelism": "none (1 GPU)",
-                   "streams": args.streams, "layer_lag": args.lag},
+                   "streams": args.streams, "layer_lag": args.lag,
+                   "h_chain": args.h_chain, "hw_queues": os.environ.get("GPU_MAX_HW_QUEUES")},
         "roofline": {
             "kernel": "syrk_bf16 (H accumulation incl. its split-K reduction), all launches of a step",
             "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -960,6 +987,8 @@ def kernel_summary(db_path, steps, layers):
 
 def main():
     args = parse()
+    # before anything touches the GPU: HIP reads it once, when its runtime starts
+    os.environ["GPU_MAX_HW_QUEUES"] = str(args.hw_queues)
     if args.kernel_summary:
         print(kernel_summary(args.kernel_summary, args.trace_steps, args.layers))
         return
