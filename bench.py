@@ -61,10 +61,10 @@ def parse():
     p.add_argument("--calib-sets", type=int, default=4,
                    help="body: distinct per-layer calibration sets kept resident (layer l reads set l mod K)")
     p.add_argument("--no-breakdown", action="store_true", help="body: skip the untimed per-call breakdown pass")
-    p.add_argument("--streams", type=int, choices=(1, 3, 4, 6), default=4,
+    p.add_argument("--streams", type=int, choices=(1, 3, 4, 5, 6), default=4,
                    help="body: 3 runs each input dim's solves on a stream of its own (they overlap); 4 (the "
                         "default) also alternates the widest dim's layers between two streams and buffer sets, "
-                        "6 every dim's; 1 runs every call in order")
+                        "5 between three, 6 every dim's between two; 1 runs every call in order")
     p.add_argument("--lag", type=int, default=0,
                    help="body, several streams: a stream starts layer l once the others have finished layer l - lag "
                         "(0: no coupling)")
@@ -747,7 +747,9 @@ def main_body(args):
     # (default priority); with 4 streams the widest dim's layers alternate between two
     ctxs = ctx
     if args.streams > 1:
-        if args.streams == 4:
+        if args.streams in (4, 5):
+            I.add_set(torch, max(I.dims))
+        if args.streams == 5:
             I.add_set(torch, max(I.dims))
         if args.streams == 6:
             for n in I.dims:
