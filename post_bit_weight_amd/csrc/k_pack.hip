@@ -7,6 +7,8 @@
 
 namespace wr {
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 __global__ void pack_codes_kernel(const uint8_t* __restrict__ codes, int64_t groups, int n8, int bits,
                                   uint8_t* __restrict__ out) {
   for (int64_t gidx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gidx < groups;
@@ -46,6 +48,118 @@ __global__ void unpack_codes_kernel(const uint8_t* __restrict__ in, int64_t grou
       if (dequant) dequant[gidx * 8 + e] = (uint16_t)f32_to_bf16_bits((float)(2 * (int)c - L) * s);
     }
   }
+}
+
+// Vector forms for aligned buffers (codes, packed stream and dequant output 16-byte aligned,
+// rows x n a multiple of 32): rows are byte-aligned in the stream, so the codes of the whole
+// module form one continuous bit stream and thread t packs codes 32 t .. 32 t + 31 into the B
+// dwords t B .. t B + B - 1 (two 16-byte loads, B dword stores that the lanes of a wave lay end
+// to end).  The same launch then copies the scales, which are stored in their own byte order
+// (little-endian fp16), 16 bytes per thread when both ends allow it.
+template <int B>
+__device__ __forceinline__ void pack32(const u32x4 lo, const u32x4 hi, uint32_t (&d)[B]) {
+  const uint32_t w[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+  for (int q = 0; q < B; ++q) d[q] = 0u;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    const uint32_t c = (w[e >> 2] >> (8 * (e & 3))) & ((1u << B) - 1u);
+    const int pos = B * e, q = pos >> 5, sh = pos & 31;
+    d[q] |= c << sh;
+    if (sh + B > 32) d[q + 1] |= c >> (32 - sh);
+  }
+}
+
+__device__ __forceinline__ void copy_bytes(const uint8_t* __restrict__ src, int64_t nbytes, uint8_t* __restrict__ dst,
+                                           int64_t tid, int64_t nthreads) {
+  if ((((uintptr_t)src | (uintptr_t)dst) & 15) == 0) {
+    const int64_t nv = nbytes / 16;
+    for (int64_t i = tid; i < nv; i += nthreads)
+      reinterpret_cast<u32x4*>(dst)[i] = reinterpret_cast<const u32x4*>(src)[i];
+    for (int64_t i = 16 * nv + tid; i < nbytes; i += nthreads) dst[i] = src[i];
+  } else {
+    for (int64_t i = tid; i < nbytes; i += nthreads) dst[i] = src[i];
+  }
+}
+
+template <int B>
+__global__ __launch_bounds__(256) void pack_vec_kernel(const uint8_t* __restrict__ codes, int64_t n32,
+                                                       const uint16_t* __restrict__ scales, int64_t scale_bytes,
+                                                       uint8_t* __restrict__ out) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, nthreads = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t t = tid; t < n32; t += nthreads) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(codes + 32 * t);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(codes + 32 * t + 16);
+    uint32_t d[B];
+    pack32<B>(lo, hi, d);
+    uint32_t* o = reinterpret_cast<uint32_t*>(out + 4 * B * t);
+    if constexpr (B == 4) {
+      *reinterpret_cast<u32x4*>(o) = u32x4{d[0], d[1], d[2], d[3]};
+    } else if constexpr (B == 2) {
+      *reinterpret_cast<u32x2*>(o) = u32x2{d[0], d[1]};
+    } else {
+#pragma unroll
+      for (int q = 0; q < B; ++q) o[q] = d[q];
+    }
+  }
+  copy_bytes(reinterpret_cast<const uint8_t*>(scales), scale_bytes, out + 4 * B * n32, tid, nthreads);
+}
+
+// Inverse: thread t reads the B dwords of codes 32 t .. 32 t + 31 and writes the codes (two
+// 16-byte stores) and/or their dequantized bf16 values (four); with n and the group multiples of
+// 32 the 32 codes share one row and one scale.  The same launch copies the scales out.
+template <int B>
+__global__ __launch_bounds__(256) void unpack_vec_kernel(const uint8_t* __restrict__ in, int64_t n32, int n, int group,
+                                                         int64_t scale_bytes, uint8_t* __restrict__ codes,
+                                                         uint16_t* __restrict__ scales, uint16_t* __restrict__ dequant) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, nthreads = (int64_t)gridDim.x * blockDim.x;
+  const uint8_t* sbytes = in + 4 * B * n32;
+  const int nb = n / group, n32row = n / 32;
+  constexpr int L = (1 << B) - 1;
+  for (int64_t t = tid; t < n32; t += nthreads) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(in + 4 * B * t);
+    uint32_t d[B + 1];
+#pragma unroll
+    for (int q = 0; q < B; ++q) d[q] = src[q];
+    d[B] = 0u;
+    uint32_t c[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int pos = B * e, q = pos >> 5, sh = pos & 31;
+      uint32_t v = d[q] >> sh;
+      if (sh + B > 32) v |= d[q + 1] << (32 - sh);
+      c[e] = v & (uint32_t)L;
+    }
+    if (codes) {
+      u32x4 w0, w1;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        w0[q] = c[4 * q] | (c[4 * q + 1] << 8) | (c[4 * q + 2] << 16) | (c[4 * q + 3] << 24);
+        w1[q] = c[16 + 4 * q] | (c[17 + 4 * q] << 8) | (c[18 + 4 * q] << 16) | (c[19 + 4 * q] << 24);
+      }
+      *reinterpret_cast<u32x4*>(codes + 32 * t) = w0;
+      *reinterpret_cast<u32x4*>(codes + 32 * t + 16) = w1;
+    }
+    if (dequant) {
+      const int64_t row = t / n32row;
+      const int col = (int)(t - row * n32row) * 32;
+      const int64_t sb = 2 * (row * nb + col / group);
+      const float s = f16_bits_to_f32((uint16_t)(sbytes[sb] | (sbytes[sb + 1] << 8)));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x4 w;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const int e = 8 * q + 2 * h;
+          const uint32_t lo = f32_to_bf16_bits((float)(2 * (int)c[e] - L) * s);
+          const uint32_t hi = f32_to_bf16_bits((float)(2 * (int)c[e + 1] - L) * s);
+          w[h] = lo | (hi << 16);
+        }
+        *reinterpret_cast<u32x4*>(dequant + 32 * t + 8 * q) = w;
+      }
+    }
+  }
+  if (scales) copy_bytes(sbytes, scale_bytes, reinterpret_cast<uint8_t*>(scales), tid, nthreads);
 }
 
 __global__ void pack_scales_kernel(const uint16_t* __restrict__ scales, int64_t count, uint8_t* __restrict__ out) {
@@ -431,16 +545,32 @@ using namespace wr;
 
 static unsigned grid_for(int64_t work) { return (unsigned)std::max<int64_t>(1, std::min<int64_t>((work + 255) / 256, 8192)); }
 
+// The vector kernels take 16-byte aligned buffers and whole 32-code pieces; others take the
+// byte forms.
+static bool vec_ok(const void* a, const void* b, const void* c, int64_t n, int32_t group) {
+  const uintptr_t m = (uintptr_t)a | (uintptr_t)b | (uintptr_t)c;
+  return (m & 15) == 0 && n % 32 == 0 && group % 32 == 0;
+}
+
 int wr_pack_impl(wr_ctx* ctx, const uint8_t* codes, const uint16_t* scales, int64_t rows, int64_t n, int32_t bits,
                  int32_t group, uint8_t* out) {
   const int64_t groups = rows * (n / 8);
   const int64_t code_bytes = rows * n * bits / 8;
+  const int64_t ns = rows * (n / group);
+  if (rows > 0 && vec_ok(codes, out, nullptr, n, group)) {
+    const int64_t n32 = rows * n / 32;
+    const unsigned grid = grid_for(std::max<int64_t>(n32, 1));
+    if (bits == 2) hipLaunchKernelGGL(pack_vec_kernel<2>, dim3(grid), dim3(256), 0, ctx->stream, codes, n32, scales, 2 * ns, out);
+    else if (bits == 3) hipLaunchKernelGGL(pack_vec_kernel<3>, dim3(grid), dim3(256), 0, ctx->stream, codes, n32, scales, 2 * ns, out);
+    else hipLaunchKernelGGL(pack_vec_kernel<4>, dim3(grid), dim3(256), 0, ctx->stream, codes, n32, scales, 2 * ns, out);
+    WR_CHECK_LAUNCH();
+    return WR_OK;
+  }
   if (groups > 0) {
     hipLaunchKernelGGL(pack_codes_kernel, dim3(grid_for(groups)), dim3(256), 0, ctx->stream, codes, groups, (int)(n / 8),
                        bits, out);
     WR_CHECK_LAUNCH();
   }
-  const int64_t ns = rows * (n / group);
   if (ns > 0) {
     hipLaunchKernelGGL(pack_scales_kernel, dim3(grid_for(ns)), dim3(256), 0, ctx->stream, scales, ns, out + code_bytes);
     WR_CHECK_LAUNCH();
@@ -452,6 +582,18 @@ int wr_unpack_impl(wr_ctx* ctx, const uint8_t* in, int64_t rows, int64_t n, int3
                    uint8_t* codes, uint16_t* scales, uint16_t* dequant) {
   const int64_t groups = rows * (n / 8);
   const int64_t code_bytes = rows * n * bits / 8;
+  if (rows > 0 && (codes || scales || dequant) && vec_ok(in, codes, dequant, n, group) && (uintptr_t)scales % 16 == 0) {
+    const int64_t n32 = rows * n / 32, sbytes = 2 * rows * (n / group);
+    const unsigned grid = grid_for(std::max<int64_t>(n32, 1));
+    if (bits == 2)
+      hipLaunchKernelGGL(unpack_vec_kernel<2>, dim3(grid), dim3(256), 0, ctx->stream, in, n32, (int)n, group, sbytes, codes, scales, dequant);
+    else if (bits == 3)
+      hipLaunchKernelGGL(unpack_vec_kernel<3>, dim3(grid), dim3(256), 0, ctx->stream, in, n32, (int)n, group, sbytes, codes, scales, dequant);
+    else
+      hipLaunchKernelGGL(unpack_vec_kernel<4>, dim3(grid), dim3(256), 0, ctx->stream, in, n32, (int)n, group, sbytes, codes, scales, dequant);
+    WR_CHECK_LAUNCH();
+    return WR_OK;
+  }
   if (groups > 0 && (codes || dequant)) {
     hipLaunchKernelGGL(unpack_codes_kernel, dim3(grid_for(groups)), dim3(256), 0, ctx->stream, in, groups,
                        (int)(n / 8), (int)n, bits, group, in + code_bytes, codes, dequant);

@@ -48,7 +48,11 @@ def dev(t):
 
 
 # ------------------------------------------------------------------------- pack
-@pytest.mark.parametrize("bits,rows,n,g", [(2, 37, 96, 32), (3, 5, 64, 32), (3, 33, 2560, 64), (4, 9, 128, 128)])
+# The first six take the 32-code vector kernels (aligned buffers, n and the group multiples of 32;
+# the scales copied by 16-byte pieces or, when the code bytes leave them unaligned, by bytes; the
+# last one has more 32-code pieces than the grid has threads); n = 72 and 40 the byte kernels.
+@pytest.mark.parametrize("bits,rows,n,g", [(2, 37, 96, 32), (3, 5, 64, 32), (3, 33, 2560, 64), (4, 9, 128, 128),
+                                           (3, 7, 9728, 64), (2, 8200, 8192, 64), (2, 7, 72, 24), (3, 4, 40, 8)])
 def test_pack_unpack_bit_exact(wr, ctx, bits, rows, n, g):
     rng = np.random.default_rng(bits * 100 + rows)
     codes = rng.integers(0, 2 ** bits, size=(rows, n))
@@ -66,6 +70,31 @@ def test_pack_unpack_bit_exact(wr, ctx, bits, rows, n, g):
     assert torch.equal(c2, c_t) and torch.equal(s2.view(torch.int16), s_t.view(torch.int16))
     expect = torch.from_numpy(oracle.dequant(codes, scales, bits, g)).to(torch.bfloat16)
     assert torch.equal(dq.cpu().view(torch.int16), expect.view(torch.int16))
+    # each output alone
+    c3 = torch.zeros_like(c_t)
+    wr.wr_unpack(ctx, buf, rows, n, bits, g, codes=c3)
+    s3 = torch.zeros_like(s_t)
+    wr.wr_unpack(ctx, buf, rows, n, bits, g, scales=s3)
+    assert torch.equal(c3, c_t) and torch.equal(s3.view(torch.int16), s_t.view(torch.int16))
+
+
+def test_pack_unpack_unaligned_buffers(wr, ctx):
+    # a packed stream one byte into its allocation takes the byte kernels; same bytes, same round trip
+    bits, rows, n, g = 3, 6, 256, 64
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 2 ** bits, size=(rows, n))
+    scales = oracle.fp16_rne(rng.uniform(-2, 2, size=(rows, n // g)))
+    ref = oracle.pack(codes, scales, bits, g)
+    c_t = dev(torch.from_numpy(codes.astype(np.uint8)))
+    s_t = dev(torch.from_numpy(scales.astype(np.float16)))
+    big = torch.zeros(ref.shape[0] + 1, dtype=torch.uint8, device="cuda")
+    buf = big[1:]
+    wr.wr_pack(ctx, c_t, s_t, bits, g, buf)
+    assert np.array_equal(buf.cpu().numpy(), ref) and int(big[0]) == 0
+    c2 = torch.empty_like(c_t)
+    s2 = torch.empty_like(s_t)
+    wr.wr_unpack(ctx, buf, rows, n, bits, g, c2, s2)
+    assert torch.equal(c2, c_t) and torch.equal(s2.view(torch.int16), s_t.view(torch.int16))
 
 
 def test_pack_rejects_wrong_size(wr, ctx):
