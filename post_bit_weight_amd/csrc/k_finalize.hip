@@ -161,26 +161,44 @@ __global__ __launch_bounds__(RT_THREADS) void rot_rows_sym_kernel(const double* 
   const int rb = RT_VALS / m, log2rb = RT_LOG2VALS - log2m;  // m, rb powers of two: shifts, no division
   const int64_t i0 = (int64_t)blockIdx.y * rb, j0 = (int64_t)blockIdx.x * m;
   const int tid = threadIdx.x;
+  // every load of the thread is issued before the first LDS store (32 in flight per thread)
+  constexpr int PER = RT_VALS / RT_THREADS;
+  double v[PER];
   if (j0 + m - 1 <= i0) {  // wholly below the diagonal: rows of S
-    for (int e = tid; e < RT_VALS; e += RT_THREADS) {
-      const int r = e >> log2m, c = e & (m - 1);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = tid + RT_THREADS * k, r = e >> log2m, c = e & (m - 1);
       const int64_t i = i0 + r, j = j0 + c;
-      const double val = i < n && j < n ? S[i * n + j] * inv_rows : 0.0;
-      buf[rt_pos(r, c, m)] = val * (double)signs[j];
+      v[k] = i < n && j < n ? S[i * n + j] : 0.0;
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = tid + RT_THREADS * k, r = e >> log2m, c = e & (m - 1);
+      buf[rt_pos(r, c, m)] = v[k] * inv_rows * (double)signs[j0 + c];
     }
   } else if (j0 > i0 + rb - 1) {  // wholly above: S[j][i] for the rows i of the block
-    for (int e = tid; e < RT_VALS; e += RT_THREADS) {
-      const int c = e >> log2rb, r = e & (rb - 1);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = tid + RT_THREADS * k, c = e >> log2rb, r = e & (rb - 1);
       const int64_t i = i0 + r, j = j0 + c;
-      const double val = i < n && j < n ? S[j * n + i] * inv_rows : 0.0;
-      buf[rt_pos(r, c, m)] = val * (double)signs[j];
+      v[k] = i < n && j < n ? S[j * n + i] : 0.0;
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = tid + RT_THREADS * k, c = e >> log2rb, r = e & (rb - 1);
+      buf[rt_pos(r, c, m)] = v[k] * inv_rows * (double)signs[j0 + c];
     }
   } else {
-    for (int e = tid; e < RT_VALS; e += RT_THREADS) {
-      const int r = e >> log2m, c = e & (m - 1);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = tid + RT_THREADS * k, r = e >> log2m, c = e & (m - 1);
       const int64_t i = i0 + r, j = j0 + c;
-      const double val = i < n && j < n ? (i >= j ? S[i * n + j] : S[j * n + i]) * inv_rows : 0.0;
-      buf[rt_pos(r, c, m)] = val * (double)signs[j];
+      v[k] = i < n && j < n ? (i >= j ? S[i * n + j] : S[j * n + i]) : 0.0;
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = tid + RT_THREADS * k, r = e >> log2m, c = e & (m - 1);
+      buf[rt_pos(r, c, m)] = v[k] * inv_rows * (double)signs[j0 + c];
     }
   }
   __syncthreads();
@@ -202,10 +220,18 @@ __global__ __launch_bounds__(RT_THREADS) void rot_cols_damp_kernel(const double*
   const int cw = RT_VALS / m, log2cw = RT_LOG2VALS - log2m;
   const int64_t i0 = (int64_t)blockIdx.y * m, j0 = (int64_t)blockIdx.x * cw;
   const int tid = threadIdx.x;
-  for (int e = tid; e < RT_VALS; e += RT_THREADS) {
-    const int r = e >> log2cw, c = e & (cw - 1);
+  constexpr int PER = RT_VALS / RT_THREADS;
+  double v[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {  // every load issued before the first LDS store
+    const int e = tid + RT_THREADS * k, r = e >> log2cw, c = e & (cw - 1);
     const int64_t j = j0 + c;
-    buf[rt_pos(c, r, m)] = j < ns ? T[(i0 + r) * ns + j] * (double)signs[i0 + r] : 0.0;
+    v[k] = j < ns ? T[(i0 + r) * ns + j] : 0.0;
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int e = tid + RT_THREADS * k, r = e >> log2cw, c = e & (cw - 1);
+    buf[rt_pos(c, r, m)] = j0 + c < ns ? v[k] * (double)signs[i0 + r] : 0.0;
   }
   __syncthreads();
   rt_fwht(buf, m, log2m, tid);
