@@ -199,7 +199,23 @@ def test_hessian_finalize_rotated(wr, ctx, n, n_store, m):
 
 
 # ------------------------------------------------------------------------- rotation
-@pytest.mark.parametrize("m,n,rows", [(4, 8, 3), (64, 256, 17), (1024, 2048, 5), (512, 1536, 4)])
+def _fwht_f32_stages(x, m):
+    """fp32 butterflies over the last axis in blocks of m, stages h = 1, 2, .. m/2 in order (the
+    additions every implementation of the row transform performs, whatever its thread layout)."""
+    y = x.reshape(x.shape[0], -1, m).copy()
+    h = 1
+    while h < m:
+        v = y.reshape(y.shape[0], y.shape[1], m // (2 * h), 2, h)
+        a, b = v[:, :, :, 0, :].copy(), v[:, :, :, 1, :].copy()
+        v[:, :, :, 0, :] = a + b
+        v[:, :, :, 1, :] = a - b
+        h *= 2
+    return y.reshape(x.shape)
+
+
+# m from 64 to 2048 takes the register form (16-byte rows from 256), 4 and 4096 the LDS form
+@pytest.mark.parametrize("m,n,rows", [(4, 8, 3), (64, 256, 17), (1024, 2048, 5), (512, 1536, 4), (128, 384, 9),
+                                      (256, 512, 3), (2048, 4096, 2), (4096, 4096, 2)])
 def test_rotation_rows_and_inverse(wr, ctx, m, n, rows):
     rng = np.random.default_rng(m + n)
     M = rng.standard_normal((rows, n)).astype(np.float32)
@@ -208,9 +224,15 @@ def test_rotation_rows_and_inverse(wr, ctx, m, n, rows):
     st = dev(torch.from_numpy(s))
     wr.wr_hadamard_rotate(ctx, t, m, st, wr.WR_ROT_ROWS)
     ref = oracle.rotate_rows(M.astype(np.float64), m, s.astype(np.float64))
-    assert np.abs(t.cpu().numpy() - ref).max() < 1e-5
+    got = t.cpu().numpy()
+    assert np.abs(got - ref).max() < 1e-5
+    # the stage order fixes every fp32 addition: the result is exact to that order, bit for bit
+    scale = np.float32(1.0) / np.sqrt(np.float32(m))
+    assert np.array_equal(got, _fwht_f32_stages(M * s.astype(np.float32), m) * scale)
     wr.wr_hadamard_rotate(ctx, t, m, st, wr.WR_ROT_ROWS_INVERSE)
-    assert np.abs(t.cpu().numpy() - M).max() < 1e-5
+    back = t.cpu().numpy()
+    assert np.abs(back - M).max() < 1e-5
+    assert np.array_equal(back, (_fwht_f32_stages(got, m) * scale) * s.astype(np.float32))
 
 
 def test_rotation_page_example(wr, ctx, golden):
