@@ -533,7 +533,15 @@ __global__ void rhs_sum_kernel(const float* __restrict__ hp, int64_t rows, int n
   const int c = blockIdx.y;
   for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < rows; r += (int64_t)gridDim.x * blockDim.x) {
     double s = 0.0;
-    for (int b = 0; b < nb; ++b) s += (double)hp[((size_t)b * nb + c) * rows + r];
+    int b = 0;
+    for (; b + 8 <= nb; b += 8) {  // eight loads in flight, then the adds in the order of b
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = hp[((size_t)(b + u) * nb + c) * rows + r];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += (double)v[u];
+    }
+    for (; b < nb; ++b) s += (double)hp[((size_t)b * nb + c) * rows + r];
     rhs[(size_t)r * nb + c] = (float)s;
   }
 }
