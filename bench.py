@@ -896,6 +896,9 @@ def main_body(args):
             "recode": hbm("recode", "wring", "codes in and out and the scales of the nearest-point recode; the "
                           "stage also holds the Gram/RHS products and the per-row solves"),
             "pack": hbm("pack", "pack", "codes and scales read, packed stream and scales written"),
+            "finalize": hbm("finalize", "finalize", "the two fp64 rotation passes of H: S read (mirrored), T written "
+                            "and read, H fp32 written; the stage also holds the trace"),
+            "rotate": hbm("rotate", "rotate", "the weights' rotation: fp32 read and written"),
             "unpack": hbm("pack", "unpack", "packed stream and scales read, codes and scales written"),
         }
     if not args.no_measures:
@@ -916,13 +919,16 @@ def body_work(layers):
     groups = {}
     for name, rows, n in _body.MODULES:
         groups.setdefault(n, []).append((name, rows))
-    work = {"syrk": 0.0, "chol": 0.0, "sweep": 0.0, "recode": 0.0, "pack": 0.0, "gram": 0.0, "rowsolve": 0.0}
+    work = {"syrk": 0.0, "chol": 0.0, "sweep": 0.0, "recode": 0.0, "pack": 0.0, "gram": 0.0, "rowsolve": 0.0,
+            "finalize": 0.0, "rotate": 0.0}
     for layer in range(layers):
         for n, mods in groups.items():
             rows = sum(r for _, r in mods)
             nb = n // g
             work["syrk"] += float(N) * n * (n + 1)
             work["chol"] += n ** 3 / 3.0
+            work["finalize"] += 28.0 * n * n       # rotated: S read twice (mirrored), T fp64 written and read, H fp32
+            work["rotate"] += 8.0 * rows * n        # the weights' rotation: fp32 read and written
             work["sweep"] += rows * n * (4 + 1 + 2.0 / g) + n * n * 2.0
             for name, r in mods:
                 b = _body.module_bits(layer, name, BODY["layers"])
@@ -971,8 +977,12 @@ def kernel_summary(db_path, steps, layers):
              ("sweep", r"^sweep_panel_kernel|^trail_wide_kernel|^split_mt_kernel|^build_m_kernel", "HBM",
               PEAK_HBM_GBS * 1e9, "GB/s"),
              ("recode", r"^wring_prep_kernel", "HBM", PEAK_HBM_GBS * 1e9, "GB/s"),
-             ("pack", r"^pack_codes_kernel|^pack_scales_kernel", "HBM", PEAK_HBM_GBS * 1e9, "GB/s"),
-             ("gram", r"^gram_lh_kernel|^rhs_sum_kernel", "bf16 MFMA", PEAK_BF16_TFLOPS * 1e12, "TFLOP/s"),
+             ("pack", r"^pack_vec_kernel|^pack_codes_kernel|^pack_scales_kernel", "HBM", PEAK_HBM_GBS * 1e9, "GB/s"),
+             ("unpack", r"^unpack_vec_kernel|^unpack_codes_kernel|^unpack_scales_kernel", "HBM", PEAK_HBM_GBS * 1e9,
+              "GB/s"),
+             ("finalize", r"^rot_rows_sym_kernel|^rot_cols_damp_kernel", "HBM", PEAK_HBM_GBS * 1e9, "GB/s"),
+             ("rotate", r"^fwht_rows", "HBM", PEAK_HBM_GBS * 1e9, "GB/s"),
+             ("gram", r"^gram_l[hc]_kernel|^rhs_sum_kernel", "bf16 MFMA", PEAK_BF16_TFLOPS * 1e12, "TFLOP/s"),
              ("rowsolve", r"^row_solve", "fp64", 78.6e12, "TFLOP/s")]
     out += ["", f"Rooflines per step ({layers} layers; algorithmic work as stated in the design notes):", "",
             "| step | kernels | bound | ms per step | achieved | peak | fraction |", "|---|---|---|---|---|---|---|"]
