@@ -899,7 +899,7 @@ def main_body(args):
             "finalize": hbm("finalize", "finalize", "the two fp64 rotation passes of H: S read (mirrored), T written "
                             "and read, H fp32 written; the stage also holds the trace"),
             "rotate": hbm("rotate", "rotate", "the weights' rotation: fp32 read and written"),
-            "unpack": hbm("pack", "unpack", "packed stream and scales read, codes and scales written"),
+            "unpack": hbm("unpack", "unpack", "packed stream and scales read, codes and scales written"),
         }
     if not args.no_measures:
         progress("the model cards' measures for layer 0 (untimed)")
@@ -920,7 +920,7 @@ def body_work(layers):
     for name, rows, n in _body.MODULES:
         groups.setdefault(n, []).append((name, rows))
     work = {"syrk": 0.0, "chol": 0.0, "sweep": 0.0, "recode": 0.0, "pack": 0.0, "gram": 0.0, "rowsolve": 0.0,
-            "finalize": 0.0, "rotate": 0.0}
+            "finalize": 0.0, "rotate": 0.0, "unpack": 0.0}
     for layer in range(layers):
         for n, mods in groups.items():
             rows = sum(r for _, r in mods)
@@ -934,6 +934,7 @@ def body_work(layers):
                 b = _body.module_bits(layer, name, BODY["layers"])
                 work["recode"] += r * n * (2 + 2.0 / g)
                 work["pack"] += r * n * (1 + 2.0 / g) + r * n * b / 8.0 + r * n * 2.0 / g
+                work["unpack"] += r * n * (1 + 2.0 / g) + r * n * b / 8.0 + r * n * 2.0 / g
             work["gram"] += 2 * 3.0 * rows * n * n                 # W'H + Gram, both joint solves
             work["rowsolve"] += 2 * rows * nb ** 3 / 3.0
     return work
