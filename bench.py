@@ -983,7 +983,7 @@ def kernel_summary(db_path, steps, layers):
               "GB/s"),
              ("finalize", r"^rot_rows_sym_kernel|^rot_cols_damp_kernel", "HBM", PEAK_HBM_GBS * 1e9, "GB/s"),
              ("rotate", r"^fwht_rows", "HBM", PEAK_HBM_GBS * 1e9, "GB/s"),
-             ("gram", r"^gram_l[hc]_kernel|^rhs_sum_kernel", "bf16 MFMA", PEAK_BF16_TFLOPS * 1e12, "TFLOP/s"),
+             ("gram", r"^gram_lh_kernel|^rhs_sum_kernel", "bf16 MFMA", PEAK_BF16_TFLOPS * 1e12, "TFLOP/s"),
              ("rowsolve", r"^row_solve", "fp64", 78.6e12, "TFLOP/s")]
     out += ["", f"Rooflines per step ({layers} layers; algorithmic work as stated in the design notes):", "",
             "| step | kernels | bound | ms per step | achieved | peak | fraction |", "|---|---|---|---|---|---|---|"]
