@@ -89,7 +89,8 @@ __device__ __forceinline__ void mma16_2x2(const double* SA, int r0, const double
 // pivot, or -1, in bad0).  sX needs no initial contents.  A pivot that is not
 // positive sets dev_info (first failure wins).
 __device__ __forceinline__ void diag_factor(double* sA, double* sX, int n, int kb, double* L, double* Xinv,
-                                            int32_t* dev_info, int tid, bool first_done = false, int bad0 = -1) {
+                                            int32_t* dev_info, int tid, bool first_done = false, int bad0 = -1,
+                                            int nthr = 256) {
   const int lane = tid & 63, wave = tid >> 6;
   const f64x4 zero = {0.0, 0.0, 0.0, 0.0};
   int bad = bad0;
@@ -130,11 +131,11 @@ __device__ __forceinline__ void diag_factor(double* sA, double* sX, int n, int k
     lds_sync();
   }
   if (wave == 0 && lane == 0 && bad >= 0) atomicCAS(dev_info, 0, kb + bad + 1);
-  for (int e = tid; e < 4 * 256; e += 256) {  // X_ss, compact: [s][16][16]
+  for (int e = tid; e < 4 * 256; e += nthr) {  // X_ss, compact: [s][16][16]
     const int b = e >> 8, r = (e >> 4) & 15, c = e & 15;
     Xinv[e] = sX[(16 * b + r) * CP + 16 * b + c];
   }
-  for (int e = tid; e < CB * CB; e += 256) {
+  for (int e = tid; e < CB * CB; e += nthr) {
     const int r = e / CB, c = e % CB;
     if (c <= r && kb + r < n) L[(int64_t)(kb + r) * n + kb + c] = sA[r * CP + c];
   }
@@ -155,9 +156,9 @@ __device__ __forceinline__ void load_xd(const double* __restrict__ Xc, double* s
 
 // Rows past n of the last, partial block: the identity.  (Entries above the diagonal
 // of a diagonal block are never read into the lower part, so they need no clearing.)
-__device__ __forceinline__ void pad_diag(double* sA, int n, int kb, int tid) {
+__device__ __forceinline__ void pad_diag(double* sA, int n, int kb, int tid, int nthr = 256) {
   if (kb + CB <= n) return;
-  for (int e = tid; e < CB * CB; e += 256) {
+  for (int e = tid; e < CB * CB; e += nthr) {
     const int r = e / CB, c = e % CB;
     if (kb + r >= n && c <= r) sA[r * CP + c] = r == c ? 1.0 : 0.0;
   }
@@ -443,7 +444,9 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ A
 // 128-row factor blocks of a column take 130 KB of LDS), the next column's blocks fetched into
 // registers while the current one is multiplied, and the tile of A while the last one is; tiles in
 // blocked order, a contiguous range per XCD.
-// The next diagonal block is left to chol_diag_kernel.
+// Workgroup 0 (tile (0, 0), dispatched first) also factors the next panel's first diagonal block,
+// the top-left 64 x 64 block of its tile, as chol_update_kernel does: that block goes to LDS instead
+// of A, and its factor and inverted 16 x 16 blocks to L and Xout.
 constexpr int CB2 = 128;
 constexpr int CU2_LDS = 2 * CB2 * CP * (int)sizeof(double);
 
@@ -470,8 +473,9 @@ __device__ __forceinline__ void put_block128(const double2 (&v)[8], double* sM, 
   }
 }
 
-__global__ __launch_bounds__(512) void chol_update128_kernel(double* __restrict__ A, const double* __restrict__ L,
-                                                             int n, int kb0, int w, const int32_t* __restrict__ dev_info) {
+__global__ __launch_bounds__(512) void chol_update128_kernel(double* __restrict__ A, double* __restrict__ L,
+                                                             double* __restrict__ Xout, int n, int kb0, int w,
+                                                             int32_t* __restrict__ dev_info) {
   if (*dev_info != 0) return;
   extern __shared__ double cu2_lds[];
   double* sP = cu2_lds;
@@ -542,17 +546,42 @@ __global__ __launch_bounds__(512) void chol_update128_kernel(double* __restrict_
         cur[x][y][v] = active && gi < n && gj < n ? A[(int64_t)gi * n + gj] : 0.0;
       }
   multiply();
-  if (!active) return;
+  const bool first = diag && ti == 0;  // tile (0, 0): its top-left 64 x 64 block is the next diagonal block
+  if (!first && !active) return;
+  if (active) {
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < 4; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+      for (int y = 0; y < 2; ++y)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int gi = i0 + 64 * wi + 16 * x + lk + 4 * v;
-        const int gj = j0 + 32 * wj + 16 * y + li;
-        if (gi < n && gj < n && gj <= gi) A[(int64_t)gi * n + gj] = cur[x][y][v] - acc[x][y][v];
-      }
+        for (int v = 0; v < 4; ++v) {
+          const int gi = i0 + 64 * wi + 16 * x + lk + 4 * v;
+          const int gj = j0 + 32 * wj + 16 * y + li;
+          const double val = cur[x][y][v] - acc[x][y][v];
+          const bool in_block = first && wi == 0 && wj < 2;
+          if (!in_block && gi < n && gj < n && gj <= gi) A[(int64_t)gi * n + gj] = val;
+          cur[x][y][v] = val;
+        }
+  }
+  if (!first) return;
+  // workgroup 0 only, every wave to the end (the barriers below count all eight): waves 0 and 1 hold
+  // the block's lower part (strictly upper parts are never read by the factorisation); it goes to
+  // LDS once every wave is done with the factor blocks there, then identity past n, then the factor
+  double* sA = sP;
+  double* sX = sP + CB * CP;
+  lds_sync();
+  if (wi == 0 && wj < 2) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sA[(16 * x + lk + 4 * v) * CP + 32 * wj + 16 * y + li] = cur[x][y][v];
+  }
+  lds_sync();
+  pad_diag(sA, n, base, tid, 512);
+  lds_sync();
+  diag_factor(sA, sX, n, base, L, Xout, dev_info, tid, false, -1, 512);
 }
 
 // Block columns per panel of deferred trailing updates.
@@ -630,13 +659,11 @@ int wr_factor_m(hipStream_t st, const float* H, int64_t ldh, int n, void* ws, fl
       hipLaunchKernelGGL(chol_panel_kernel, dim3(nt), dim3(256), 0, st, A, Lf, Xin, n, kb, dev_info);
       WR_CHECK_LAUNCH();
       if (nt >= kBigUpdate) {
-        // 128 x 128 tiles, then the next panel's first diagonal block on its own
+        // 128 x 128 tiles; workgroup 0 factors the next panel's first diagonal block
         const int nt2 = (nt + 1) / 2, tiles = nt2 * (nt2 + 1) / 2;
         if (!lds_limit(reinterpret_cast<const void*>(chol_update128_kernel), CU2_LDS)) return WR_EHIP;
         hipLaunchKernelGGL(chol_update128_kernel, dim3((tiles + CU_XCD - 1) / CU_XCD * CU_XCD), dim3(512), CU2_LDS, st,
-                           A, Lf, n, CB * s0, s1 - s0, dev_info);
-        WR_CHECK_LAUNCH();
-        hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, st, A, n, CB * s1, Lf, Xout, dev_info);
+                           A, Lf, Xout, n, CB * s0, s1 - s0, dev_info);
       } else {
         const int tiles = nt * (nt + 1) / 2;
         hipLaunchKernelGGL(chol_update_kernel, dim3((tiles + CU_XCD - 1) / CU_XCD * CU_XCD), dim3(256), 0, st, A, Lf,
