@@ -139,13 +139,13 @@ __global__ __launch_bounds__(G) void sub_inverse_kernel(const float* __restrict_
 // batch's corrections, C_b += E M[b0 - kprev.., b0..] with M's transposed bf16 parts
 // Mt0..Mt2, on the bf16 matrix cores; Cbuf holds the corrections from the groups before.
 // The batch's errors go to E0..E2 at its slot.
-template <int P, int BATCH, int G>
+template <int P, int BATCH, int G, bool GROUP>
 __global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict__ W, int w_dtype, int64_t rows,
                                                           int n, int64_t ldw, const float* __restrict__ M,
-                                                          const uint8_t* __restrict__ bits, int b0, int ncols,
-                                                          float* __restrict__ Cbuf, int lde, int kprev,
-                                                          uint16_t* __restrict__ E0,
-                                                          uint16_t* __restrict__ E1, uint16_t* __restrict__ E2,
+                                                          const uint8_t* __restrict__ bits, int b0first,
+                                                          int gcols, float* __restrict__ Cbuf, int lde, int kprev0,
+                                                          uint16_t* __restrict__ E0g,
+                                                          uint16_t* __restrict__ E1g, uint16_t* __restrict__ E2g,
                                                           const uint16_t* __restrict__ Mt0,
                                                           const uint16_t* __restrict__ Mt1,
                                                           const uint16_t* __restrict__ Mt2,
@@ -159,10 +159,27 @@ __global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict
   __shared__ __attribute__((aligned(16))) float Ms[BATCH * BATCH];  // [k][p][slot]
   __shared__ __attribute__((aligned(16))) float La[R * BATCH];      // earlier errors of the group, [row][col]
   if (*dev_info != 0) return;
-  const int tid = threadIdx.x;
+  // With GROUP the launch takes the batches of its group one after the other (a batch reads back
+  // only the errors this workgroup's own rows wrote in the earlier batches, behind the barrier that
+  // starts the batch); otherwise it takes the one batch at b0first.  kprev0: the columns of the
+  // group before the launch's first batch.
+  const int nbat = GROUP ? (gcols + BATCH - 1) / BATCH : 1;
+#pragma unroll 1
+  for (int ib = 0; ib < nbat; ++ib) {
+  const int bb = BATCH * ib;
+  // with GROUP the thread index passes through an empty asm each batch, so that nothing computed
+  // from it (row addresses) is hoisted out of the loop and held in registers across the batches
+  int tidv = (int)threadIdx.x;
+  if constexpr (GROUP) asm volatile("" : "+v"(tidv));
+  const int tid = tidv;
   const int p = tid % P;
   const int64_t row = (int64_t)blockIdx.x * R + tid / P;
   const bool active = row < rows;
+  const int b0 = b0first + bb, ncols = min(BATCH, gcols - bb), kprev = kprev0 + bb;
+  uint16_t* const E0 = E0g + kprev;
+  uint16_t* const E1 = E1g + kprev;
+  uint16_t* const E2 = E2g + kprev;
+  if (ib > 0) __syncthreads();  // every lane is done with Ms and La, and the errors are written
   // groups of up to 64 columns, with use_inv (many rows: the serial chain would dominate): the batch's
   // Y blocks, fetched now and staged in LDS before each block (the first in La's space once La is
   // read, later ones in the rows of Ms the previous block used)
@@ -368,21 +385,23 @@ __global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict
     }
   });
 
-  if (!active) return;
+  if (active) {
 #pragma unroll
-  for (int i = 0; i < S; ++i) {
-    const int col = p + P * i;
-    if (col < ncols) {
-      codes[row * n + b0 + col] = code[i];
-      const int64_t e = row * lde + col;
-      split3(d[i], E0[e], E1[e], E2[e]);
+    for (int i = 0; i < S; ++i) {
+      const int col = p + P * i;
+      if (col < ncols) {
+        codes[row * n + b0 + col] = code[i];
+        const int64_t e = row * lde + col;
+        split3(d[i], E0[e], E1[e], E2[e]);
+      }
+    }
+    if (p == 0) {
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk)
+        if (blk * G < ncols) scales[row * (n / G) + (b0 / G) + blk] = f32_to_f16_bits_clamped(sc[blk]);
     }
   }
-  if (p == 0) {
-#pragma unroll
-    for (int blk = 0; blk < NBLK; ++blk)
-      if (blk * G < ncols) scales[row * (n / G) + (b0 / G) + blk] = f32_to_f16_bits_clamped(sc[blk]);
-  }
+  }  // batches
 }
 
 // Mt_i[c][k] = part i of M[k][c] (three bf16 planes of M transposed), for the
@@ -590,6 +609,7 @@ using namespace wr;
 static constexpr int kBatch = 128;
 static constexpr int kSuper = 4 * kBatch;  // columns whose errors one wide trailing update applies
 static constexpr int64_t kInvRows = 4096;  // rows from which the panels use the precomputed inverses
+static constexpr int64_t kGroupRows = 4096;  // rows below which one panel launch takes a group of batches
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -616,26 +636,38 @@ static GptqLayout gptq_layout(int64_t rows, int64_t n) {
 
 size_t wr_gptq_ws_bytes(int64_t rows, int64_t n) { return gptq_layout(rows, n).total; }
 
+// Panels of the group of up to four batches at s0 (a multiple of kSuper), gcols columns.  With
+// few rows (fewer workgroups than CUs, so occupancy does not matter) one launch takes the whole
+// group: a quarter of the launches on the serial chain, each of which waits for free CUs when other
+// streams share the chip.  With many rows one launch per batch keeps the kernel at two waves per
+// SIMD (the loop over batches needs more registers).
 template <int P, int G>
 static void launch_panel(hipStream_t st, const void* W, int w_dtype, int64_t rows, int n, int64_t ldw, const float* Mm,
-                         const uint8_t* bits, int b0, int ncols, float* Cb, uint16_t* const* E, uint16_t* const* Mt,
+                         const uint8_t* bits, int s0, int gcols, float* Cb, uint16_t* const* E, uint16_t* const* Mt,
                          uint8_t* codes, uint16_t* scales, const float* Ysub, const int32_t* dev_info) {
   const unsigned grid = (unsigned)((rows + (256 / P) - 1) / (256 / P));
-  const int eoff = b0 % kSuper;  // this batch's slot among the errors of its group of four
-  hipLaunchKernelGGL((sweep_panel_kernel<P, kBatch, G>), dim3(grid), dim3(256), 0, st, W, w_dtype, rows, n, ldw, Mm,
-                     bits, b0, ncols, Cb, kSuper, eoff, E[0] + eoff, E[1] + eoff, E[2] + eoff, Mt[0], Mt[1], Mt[2],
-                     codes, scales, Ysub, Ysub != nullptr ? 1 : 0, dev_info);
+  const int use_inv = Ysub != nullptr ? 1 : 0;
+  if (rows < kGroupRows) {
+    hipLaunchKernelGGL((sweep_panel_kernel<P, kBatch, G, true>), dim3(grid), dim3(256), 0, st, W, w_dtype, rows, n, ldw,
+                       Mm, bits, s0, gcols, Cb, kSuper, 0, E[0], E[1], E[2], Mt[0], Mt[1], Mt[2], codes, scales, Ysub,
+                       use_inv, dev_info);
+    return;
+  }
+  for (int bb = 0; bb < gcols; bb += kBatch)
+    hipLaunchKernelGGL((sweep_panel_kernel<P, kBatch, G, false>), dim3(grid), dim3(256), 0, st, W, w_dtype, rows, n,
+                       ldw, Mm, bits, s0 + bb, std::min(kBatch, gcols - bb), Cb, kSuper, bb, E[0], E[1], E[2], Mt[0],
+                       Mt[1], Mt[2], codes, scales, Ysub, use_inv, dev_info);
 }
 
 template <int P>
 static int launch_panel_g(hipStream_t st, int G, const void* W, int w_dtype, int64_t rows, int n, int64_t ldw,
-                          const float* Mm, const uint8_t* bits, int b0, int ncols, float* Cb, uint16_t* const* E,
+                          const float* Mm, const uint8_t* bits, int s0, int gcols, float* Cb, uint16_t* const* E,
                           uint16_t* const* Mt, uint8_t* codes, uint16_t* scales, const float* Ysub,
                           const int32_t* dev_info) {
   switch (G) {
-    case 32: launch_panel<P, 32>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, Mt, codes, scales, Ysub, dev_info); break;
-    case 64: launch_panel<P, 64>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, Mt, codes, scales, Ysub, dev_info); break;
-    case 128: launch_panel<P, 128>(st, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, Mt, codes, scales, Ysub, dev_info); break;
+    case 32: launch_panel<P, 32>(st, W, w_dtype, rows, n, ldw, Mm, bits, s0, gcols, Cb, E, Mt, codes, scales, Ysub, dev_info); break;
+    case 64: launch_panel<P, 64>(st, W, w_dtype, rows, n, ldw, Mm, bits, s0, gcols, Cb, E, Mt, codes, scales, Ysub, dev_info); break;
+    case 128: launch_panel<P, 128>(st, W, w_dtype, rows, n, ldw, Mm, bits, s0, gcols, Cb, E, Mt, codes, scales, Ysub, dev_info); break;
     default: return WR_EUNSUPPORTED;
   }
   WR_CHECK_LAUNCH();
@@ -694,17 +726,16 @@ int wr_gptq_sweep_impl(wr_ctx* ctx, const void* W, int w_dtype, int64_t rows, in
       hipLaunchKernelGGL(sub_inverse_kernel<32>, dim3((unsigned)(n / 32)), dim3(32), 0, st, Mm, n, Ysub, dev_info);
     WR_CHECK_LAUNCH();
   }
-  // Batches go in groups of four (kSuper columns).  A batch's panel applies the errors of
-  // the earlier batches of its group to its own columns; after a group's last batch its
-  // errors reach every column after the group at once (K = 512), so the corrections C of
+  // Batches go in groups of four (kSuper columns), one panel launch per group.  A batch
+  // applies the errors of the earlier batches of its group to its own columns; after the
+  // group its errors reach every column after it at once (K = 512), so the corrections C of
   // the far columns are read and written once per group, not per batch.
-  for (int b0 = 0; b0 < n; b0 += kBatch) {
-    const int ncols = std::min(kBatch, n - b0);
-    rc = launch_panel_g<16>(st, group, W, w_dtype, rows, n, ldw, Mm, bits, b0, ncols, Cb, E, Mt, codes, scales, Ysub,
+  for (int s0 = 0; s0 < n; s0 += kSuper) {
+    const int s1 = std::min(s0 + kSuper, n);
+    rc = launch_panel_g<16>(st, group, W, w_dtype, rows, n, ldw, Mm, bits, s0, s1 - s0, Cb, E, Mt, codes, scales, Ysub,
                             dev_info);
     if (rc) return rc;
-    const int s0 = b0 - b0 % kSuper, s1 = std::min(s0 + kSuper, n);
-    if (b0 + ncols == s1 && s1 < n) {  // the group is complete and full (s1 - s0 == kSuper)
+    if (s1 < n) {  // a group followed by more columns is full (s1 - s0 == kSuper)
       if (!lds_limit(reinterpret_cast<const void*>(trail_wide_kernel), 2 * TW_STAGE)) return WR_EHIP;
       hipLaunchKernelGGL(trail_wide_kernel, dim3(trail_wide_grid(rows, n - s1)), dim3(512), 2 * TW_STAGE, st, rows,
                          n - s1, n, kSuper, s0, s1, E[0], E[1], E[2], kSuper, Mt[0], Mt[1], Mt[2], Cb, dev_info);
