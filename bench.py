@@ -14,8 +14,9 @@ per-layer calibration sets are kept resident and layer l reads set l mod
 calib_sets (the work per layer does not depend on the values).  The metric is
 weights quantized per second.  The timed steps run each input dimension's
 solves on a stream of its own, the widest dimension's layers rotating over
-three streams and buffer sets (five streams), and every H accumulation waits
-for the previous one, so that two never run at once.
+three streams and buffer sets and the narrowest's alternating over two (six
+streams), and every H accumulation waits for the previous one, so that two
+never run at once.
 
 Also reported: the roofline of the dominant kernel (the bf16 SYRK that
 accumulates H: N n (n + 1) useful flops per call, timed live with HIP events on
@@ -61,16 +62,17 @@ def parse():
     p.add_argument("--calib-sets", type=int, default=4,
                    help="body: distinct per-layer calibration sets kept resident (layer l reads set l mod K)")
     p.add_argument("--no-breakdown", action="store_true", help="body: skip the untimed per-call breakdown pass")
-    p.add_argument("--streams", type=int, choices=(1, 3, 4, 5, 6), default=5,
+    p.add_argument("--streams", type=int, choices=(1, 3, 4, 5, 6, 7), default=7,
                    help="body: 3 runs each input dim's solves on a stream of its own (they overlap); 4 also "
-                        "alternates the widest dim's layers between two streams and buffer sets, 5 (the default) "
-                        "between three, 6 every dim's between two; 1 runs every call in order")
+                        "alternates the widest dim's layers between two streams and buffer sets, 5 between "
+                        "three, 6 every dim's between two, 7 (the default) the widest dim's over three and the "
+                        "narrowest dim's over two (six streams); 1 runs every call in order")
     p.add_argument("--lag", type=int, default=0,
                    help="body, several streams: a stream starts layer l once the others have finished layer l - lag "
                         "(0: no coupling)")
     p.add_argument("--hw-queues", type=int, choices=range(1, 33), default=8, metavar="Q",
                    help="hardware queues HIP gives the process (GPU_MAX_HW_QUEUES, read when its runtime starts; "
-                        "default 8): the body step's five streams and the default stream need six, and two "
+                        "default 8): the body step's six streams and the default stream need seven, and two "
                         "streams that share a queue run one after the other")
     p.add_argument("--h-chain", choices=("none", "dim", "all"), default="all",
                    help="body, several streams: an H accumulation waits for the previous one of its input dim "
@@ -744,13 +746,16 @@ def main_body(args):
     I = BodyInputs(torch, wr, body, synth, layers, args.calib_sets, cfg, progress)
     ctx.ensure_workspace(I.ws_bytes)
     # the timed steps' contexts: one, or one per input dim and buffer set on streams of their own
-    # (default priority); with 4 (5) streams the widest dim's layers rotate over two (three)
+    # (default priority); with 4 (5, 7) streams the widest dim's layers rotate over two (three), with 7
+    # the narrowest dim's alternate over two
     ctxs = ctx
     if args.streams > 1:
-        if args.streams in (4, 5):
+        if args.streams in (4, 5, 7):
             I.add_set(torch, max(I.dims))
-        if args.streams == 5:
+        if args.streams in (5, 7):
             I.add_set(torch, max(I.dims))
+        if args.streams == 7:
+            I.add_set(torch, min(I.dims))
         if args.streams == 6:
             for n in I.dims:
                 I.add_set(torch, n)
