@@ -62,11 +62,12 @@ def parse():
     p.add_argument("--calib-sets", type=int, default=4,
                    help="body: distinct per-layer calibration sets kept resident (layer l reads set l mod K)")
     p.add_argument("--no-breakdown", action="store_true", help="body: skip the untimed per-call breakdown pass")
-    p.add_argument("--streams", type=int, choices=(1, 3, 4, 5, 6, 7), default=7,
+    p.add_argument("--streams", type=int, choices=(1, 3, 4, 5, 6, 7, 8), default=7,
                    help="body: 3 runs each input dim's solves on a stream of its own (they overlap); 4 also "
                         "alternates the widest dim's layers between two streams and buffer sets, 5 between "
                         "three, 6 every dim's between two, 7 (the default) the widest dim's over three and the "
-                        "narrowest dim's over two (six streams); 1 runs every call in order")
+                        "narrowest dim's over two (six streams), 8 the widest dim's over four and the "
+                        "narrowest dim's over two (seven); 1 runs every call in order")
     p.add_argument("--lag", type=int, default=0,
                    help="body, several streams: a stream starts layer l once the others have finished layer l - lag "
                         "(0: no coupling)")
@@ -750,11 +751,13 @@ def main_body(args):
     # the narrowest dim's alternate over two
     ctxs = ctx
     if args.streams > 1:
-        if args.streams in (4, 5, 7):
+        if args.streams in (4, 5, 7, 8):
             I.add_set(torch, max(I.dims))
-        if args.streams in (5, 7):
+        if args.streams in (5, 7, 8):
             I.add_set(torch, max(I.dims))
-        if args.streams == 7:
+        if args.streams == 8:
+            I.add_set(torch, max(I.dims))
+        if args.streams in (7, 8):
             I.add_set(torch, min(I.dims))
         if args.streams == 6:
             for n in I.dims:
