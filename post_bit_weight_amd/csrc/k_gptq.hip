@@ -133,12 +133,13 @@ __global__ __launch_bounds__(G) void sub_inverse_kernel(const float* __restrict_
   }
 }
 
-// One lazy batch of BATCH columns starting at b0 (ncols <= BATCH valid columns).  The
-// errors of the kprev columns before b0 in the batch's group (E0..E2: three bf16 parts,
-// leading dimension lde, this batch's slot at column kprev) are first applied to this
-// batch's corrections, C_b += E M[b0 - kprev.., b0..] with M's transposed bf16 parts
-// Mt0..Mt2, on the bf16 matrix cores; Cbuf holds the corrections from the groups before.
-// The batch's errors go to E0..E2 at its slot.
+// Lazy batches of BATCH columns: without GROUP the one batch at b0first (gcols <= BATCH valid
+// columns), with GROUP the batches of gcols columns from b0first one after the other.  For a
+// batch at b0 with kprev columns of its group before it, the errors of those columns (E0g..E2g:
+// three bf16 parts, leading dimension lde, slot kprev) are first applied to the batch's
+// corrections, C_b += E M[b0 - kprev.., b0..] with M's transposed bf16 parts Mt0..Mt2, on the
+// bf16 matrix cores; Cbuf holds the corrections from the groups before.  The batch's errors go
+// to its slot.  kprev0: the group's columns before the launch's first batch.
 template <int P, int BATCH, int G, bool GROUP>
 __global__ __launch_bounds__(256) void sweep_panel_kernel(const void* __restrict__ W, int w_dtype, int64_t rows,
                                                           int n, int64_t ldw, const float* __restrict__ M,
